@@ -1,0 +1,364 @@
+"""Pins that tie the CPU oracle to something other than itself.
+
+Each pin takes an ``oracle.Oracle`` and returns a list of failure messages
+(empty = pinned).  tests/test_oracle.py runs them on the real oracle and on
+builds with planted mistakes, where at least one pin must fail.
+
+What each pin rests on:
+  codec        numpy's binary16 conversions (a library routine), all 65536
+               patterns and boundary / tie / subnormal doubles.
+  golden       hand-derived worked blocks in tests/golden/ (the block rule
+               applied by hand; each file shows its derivation).
+  nearest      brute force: every code is the nearest grid point
+               (code - 8) * scale over all 16 (Q4_0) / 255 (Q8_0) codes,
+               ties away from zero; the scale is numpy's
+               float16(float32(absmax) / 7 or 127).
+  invariants   code range, |w - w_hat| <= scale / 2, absmax -> +-7 / +-127,
+               re-quantizing the dequantized weights is the identity.
+  exact_gemv   Fraction sums on tiny shapes (exact rational arithmetic).
+  special      one-hot input returns a weight column bit-exactly, zero input
+               gives zero, linearity, M tokens == M single-token calls.
+  moe          reduces to independent GEMVs of the chosen experts.
+  prefill      equals a float64 matmul (numpy) on the dequantized weights.
+"""
+from __future__ import annotations
+
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import seeded_inputs as si
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+Q4_0, Q8_0 = 0, 1
+
+
+def load_golden(name: str) -> dict:
+    d = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            k, v = line.split(":", 1)
+            d[k.strip()] = v.strip()
+    return d
+
+
+def _fmt(g):
+    return Q4_0 if g["format"] == "q4_0" else Q8_0
+
+
+# ------------------------------------------------------------------ codec
+def pin_codec(orc) -> list:
+    fails = []
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    for h in range(65536):
+        v = orc.half_to_double(h)
+        r = ref[h]
+        if np.isnan(r):
+            if not np.isnan(v):
+                fails.append(f"decode {h:#06x}: {v} vs nan")
+        elif v != r or np.signbit(v) != np.signbit(r):
+            fails.append(f"decode {h:#06x}: {v!r} vs {r!r}")
+        if len(fails) > 5:
+            return fails
+    g = np.random.default_rng(1234)
+    vals = [0.0, -0.0, 65504.0, 65519.99, 65520.0, 65536.0, 1e30, -1e30, 2.0**-24, 2.0**-25,
+            2.0**-25 * 1.0000001, 3 * 2.0**-26, 2.0**-14, 2.0**-14 - 2.0**-25, 1.0 + 2.0**-11,
+            1.0 + 3 * 2.0**-11, 2049.0, 2051.0, -2049.0]
+    vals += list(g.standard_normal(20000) * 10.0 ** g.uniform(-9, 5, 20000))
+    # exact ties at every binade: (odd multiples of half an ulp)
+    for e in range(-24, 16):
+        for m in (1, 3, 2045, 2047):
+            vals.append(m * 2.0 ** (e - 11))
+    for v in vals:
+        with np.errstate(over="ignore"):
+            want = int(np.array([v], np.float64).astype(np.float16).view(np.uint16)[0])
+        got = orc.double_to_half(v)
+        if got != want:
+            fails.append(f"encode {v!r}: {got:#06x} vs {want:#06x}")
+            if len(fails) > 5:
+                break
+    f32 = g.standard_normal(5000).astype(np.float32) * np.float32(0.02)
+    for v in f32:
+        want = int(np.array([v], np.float32).astype(np.float16).view(np.uint16)[0])
+        if orc.float_to_half(v) != want:
+            fails.append(f"encode f32 {v!r}")
+            break
+    return fails
+
+
+# ----------------------------------------------------------------- golden
+def _golden_weights(g):
+    t = np.array([float(v) for v in g["t"].split()], np.float64)
+    return (t * 2.0 ** int(g["weight_unit_log2"])).astype(np.float32).reshape(1, 32)
+
+
+def pin_golden(orc) -> list:
+    fails = []
+    for name in ("q4_0_we1.txt", "q8_0_we2.txt", "q4_0_we3_subnormal.txt"):
+        g = load_golden(name)
+        fmt = _fmt(g)
+        w = _golden_weights(g)
+        p = orc.quantize(fmt, w)
+        nb = 16 if fmt == Q4_0 else 32
+        code_bytes = bytes.fromhex("".join(g["code_bytes"].split()))
+        if bytes(p[:nb]) != code_bytes:
+            fails.append(f"{name}: code bytes {bytes(p[:nb]).hex()} vs {code_bytes.hex()}")
+        s0 = 256
+        sbits = int(p[s0]) | (int(p[s0 + 1]) << 8)
+        if sbits != int(g["scale_bits"], 16):
+            fails.append(f"{name}: scale {sbits:#06x} vs {g['scale_bits']}")
+        codes = np.array([int(c) for c in g["codes"].split()])
+        scale = float(np.array([int(g["scale_bits"], 16)], np.uint16).view(np.float16)[0])
+        wh = orc.dequant(fmt, p, 1, 32, "f64")[0]
+        want = (codes - (8 if fmt == Q4_0 else 0)) * scale
+        if not np.array_equal(wh, want):
+            fails.append(f"{name}: dequant {wh} vs {want}")
+        ones = np.ones((1, 32), np.float16)
+        y, _ = orc.gemv(fmt, p, 1, 32, ones)
+        if y[0, 0] != float(g["y_ones"]):
+            fails.append(f"{name}: y_ones {y[0, 0]!r} vs {g['y_ones']}")
+        for key in g:
+            if key.startswith("y_e"):
+                k = int(key[3:])
+                x = np.zeros((1, 32), np.float16)
+                x[0, k] = 1.0
+                y, _ = orc.gemv(fmt, p, 1, 32, x)
+                if y[0, 0] != float(g[key]):
+                    fails.append(f"{name}: {key} {y[0, 0]!r} vs {g[key]}")
+    # the four-block layout example
+    g = load_golden("q4_0_we4_layout.txt")
+    w1 = _golden_weights(load_golden("q4_0_we1.txt"))[0]
+    N, K = 2, 64
+    w = np.zeros((N, K), np.float32)
+    for n in range(N):
+        for b in range(2):
+            w[n, 32 * b:32 * b + 32] = w1 * np.float32(2.0 ** (2 * n + b))
+    if orc.packed_bytes(Q4_0, N, K) != int(g["packed_bytes"]):
+        fails.append("we4: packed size")
+    p = orc.quantize(Q4_0, w)
+    we1_bytes = bytes.fromhex("".join(load_golden("q4_0_we1.txt")["code_bytes"].split()))
+    for i in range(4):
+        if bytes(p[16 * i:16 * i + 16]) != we1_bytes:
+            fails.append(f"we4: block {i} codes")
+    so = int(g["scale_offset"])
+    for i, sb in enumerate(g["scale_bits"].split()):
+        got = int(p[so + 2 * i]) | (int(p[so + 2 * i + 1]) << 8)
+        if got != int(sb, 16):
+            fails.append(f"we4: scale {i} {got:#06x} vs {sb}")
+    y, _ = orc.gemv(Q4_0, p, N, K, np.ones((1, K), np.float16))
+    if list(y[0]) != [float(v) for v in g["y_ones"].split()]:
+        fails.append(f"we4: y_ones {y[0]}")
+    x = np.zeros((1, K), np.float16)
+    x[0, 37] = 1.0
+    y, _ = orc.gemv(Q4_0, p, N, K, x)
+    if list(y[0]) != [float(v) for v in g["y_e37"].split()]:
+        fails.append(f"we4: y_e37 {y[0]}")
+    return fails
+
+
+# ---------------------------------------------------------------- nearest
+def _parse(fmt, p, N, K):
+    """Codes (signed multipliers) and scales straight from the documented layout."""
+    nb = N * K // 32
+    cb = 16 if fmt == Q4_0 else 32
+    codes_raw = p[:nb * cb].reshape(nb, cb)
+    if fmt == Q4_0:
+        q = np.concatenate([codes_raw & 0x0F, codes_raw >> 4], axis=1).astype(np.int64) - 8
+    else:
+        q = codes_raw.view(np.int8).astype(np.int64)
+    s0 = (nb * cb + 255) // 256 * 256
+    scale = p[s0:s0 + 2 * nb].view(np.uint16).view(np.float16).astype(np.float64)
+    return q, scale
+
+
+def nearest_codes(fmt, w):
+    """Brute force: scale = fp16(fl32(absmax)/qmax); each weight's code is the
+    nearest multiplier c on the grid c * scale (c in -8..7 / -127..127), ties to
+    the larger |c|.  Distances are exact in float64."""
+    qmax = 7 if fmt == Q4_0 else 127
+    blocks = w.reshape(-1, 32)
+    amax = np.abs(blocks).max(axis=1).astype(np.float32)
+    d16 = (amax / np.float32(qmax)).astype(np.float16)
+    d = d16.astype(np.float64)
+    cs = np.arange(-8 if fmt == Q4_0 else -127, qmax + 1, dtype=np.int64)
+    best = np.zeros(blocks.shape, np.int64)
+    bestd = np.full(blocks.shape, np.inf)
+    wv = blocks.astype(np.float64)
+    for c in cs:
+        dist = np.abs(wv - c * d[:, None])
+        better = (dist < bestd) | ((dist == bestd) & (np.abs(c) > np.abs(best)))
+        best = np.where(better, c, best)
+        bestd = np.where(better, dist, bestd)
+    best[d == 0.0] = 0
+    return best, d16
+
+
+def pin_nearest(orc) -> list:
+    fails = []
+    for fmt, n_w in ((Q4_0, 1 << 20), (Q8_0, 1 << 16)):
+        K = 256
+        w = si.weights(n_w // K, K, seed=7)
+        # plant exact ties and tiny/zero blocks
+        w[0, :32] = 0.0
+        w[1, :32] = np.float32(1e-9)
+        w[1, 0] = np.float32(3e-7)
+        w[2, :32] = (np.arange(32) - 14).astype(np.float32) * np.float32(2.0 ** -9)
+        p = orc.quantize(fmt, w)
+        q, scale = _parse(fmt, p, w.shape[0], K)
+        want_q, want_d = nearest_codes(fmt, w)
+        if not np.array_equal(scale, want_d.astype(np.float64)):
+            fails.append(f"fmt{fmt}: scales differ at {np.flatnonzero(scale != want_d)[:5]}")
+        bad = np.flatnonzero((q != want_q).any(axis=1))
+        if bad.size:
+            fails.append(f"fmt{fmt}: {bad.size} blocks with codes off the nearest grid point")
+    return fails
+
+
+def pin_invariants(orc) -> list:
+    fails = []
+    for fmt in (Q4_0, Q8_0):
+        qmax = 7 if fmt == Q4_0 else 127
+        w = si.weights(64, 512, seed=11)
+        p = orc.quantize(fmt, w)
+        q, scale = _parse(fmt, p, 64, 512)
+        wb = w.reshape(-1, 32).astype(np.float64)
+        normal = np.abs(scale) >= 2.0 ** -14
+        if fmt == Q4_0 and (q[normal] < -7).any():
+            fails.append("q4_0: code 0 (multiplier -8) with a normal scale")
+        if (np.abs(q) > (8 if fmt == Q4_0 else 127)).any():
+            fails.append(f"fmt{fmt}: code out of range")
+        wh = orc.dequant(fmt, p, 64, 512, "f64").reshape(-1, 32)
+        if not (np.abs(wb - wh) <= scale[:, None] / 2).all():
+            fails.append(f"fmt{fmt}: |w - w_hat| > scale/2")
+        am = np.abs(wb).argmax(axis=1)
+        if not (np.abs(q[np.arange(q.shape[0]), am]) == qmax).all():
+            fails.append(f"fmt{fmt}: absmax element not at +-{qmax}")
+        p2 = orc.quantize(fmt, orc.dequant(fmt, p, 64, 512, "f32"))
+        if not np.array_equal(p, p2):
+            fails.append(f"fmt{fmt}: quantize(dequant(.)) is not the identity")
+        w16 = orc.dequant(fmt, p, 64, 512, "f16")
+        if not np.array_equal(w16, wh.reshape(64, 512).astype(np.float16)):
+            fails.append(f"fmt{fmt}: fp16 dequant is not RNE of the exact value")
+        f32 = orc.dequant(fmt, p, 64, 512, "f32")
+        if not np.array_equal(f32.astype(np.float64), wh.reshape(64, 512)):
+            fails.append(f"fmt{fmt}: fp32 dequant not exact")
+    return fails
+
+
+# ------------------------------------------------------------- exact gemv
+def pin_exact_gemv(orc) -> list:
+    fails = []
+    for fmt in (Q4_0, Q8_0):
+        for (N, K, M) in ((1, 32, 1), (3, 64, 2), (5, 96, 3), (8, 128, 8)):
+            w = si.weights(N, K, seed=3)
+            x = si.activations(M, K, seed=3)
+            p = orc.quantize(fmt, w)
+            q, scale = _parse(fmt, p, N, K)
+            y, s = orc.gemv(fmt, p, N, K, x)
+            xs = [[Fraction(float(v)) for v in row] for row in x]
+            for m in range(M):
+                for n in range(N):
+                    exact = Fraction(0)
+                    sab = Fraction(0)
+                    for b in range(K // 32):
+                        i = n * (K // 32) + b
+                        dd = Fraction(float(scale[i]))
+                        for k in range(32):
+                            t = int(q[i, k]) * dd * xs[m][32 * b + k]
+                            exact += t
+                            sab += abs(t)
+                    err = abs(Fraction(y[m, n]) - exact)
+                    if err > Fraction(1, 2 ** 50) * sab or abs(s[m, n] - float(sab)) > 2.0 ** -50 * float(sab):
+                        fails.append(f"fmt{fmt} {N}x{K} m{m} n{n}: y {y[m, n]} vs {float(exact)}")
+    return fails
+
+
+def pin_special(orc) -> list:
+    fails = []
+    for fmt in (Q4_0, Q8_0):
+        N, K = 16, 320
+        w = si.weights(N, K, seed=5)
+        p = orc.quantize(fmt, w)
+        wh = orc.dequant(fmt, p, N, K, "f64")
+        for k in (0, 5, 16, 31, 32, 47, 319):
+            x = np.zeros((1, K), np.float16)
+            x[0, k] = 1.0
+            y, _ = orc.gemv(fmt, p, N, K, x)
+            if not np.array_equal(y[0], wh[:, k]):
+                fails.append(f"fmt{fmt}: one-hot e_{k} is not column {k}")
+        y, s = orc.gemv(fmt, p, N, K, np.zeros((1, K), np.float16))
+        if (y != 0).any() or (s != 0).any():
+            fails.append(f"fmt{fmt}: zero input")
+        x = np.zeros((1, K), np.float16)
+        x[0, 64:96] = 1.0
+        y, _ = orc.gemv(fmt, p, N, K, x)
+        if not np.array_equal(y[0], wh[:, 64:96].sum(axis=1)):
+            fails.append(f"fmt{fmt}: ones on block 2")
+        x4 = si.activations(4, K, seed=9)
+        y4, _ = orc.gemv(fmt, p, N, K, x4)
+        for m in range(4):
+            y1, _ = orc.gemv(fmt, p, N, K, x4[m:m + 1])
+            if not np.array_equal(y1[0], y4[m]):
+                fails.append(f"fmt{fmt}: token {m} of a 4-token call differs from a 1-token call")
+        # linearity: x = a + b with a, b on disjoint halves of K
+        a = x4[0].copy()
+        a[K // 2:] = 0
+        b = x4[0].copy()
+        b[:K // 2] = 0
+        ya, sa = orc.gemv(fmt, p, N, K, a[None])
+        yb, sb = orc.gemv(fmt, p, N, K, b[None])
+        if not (np.abs(ya + yb - y4[0]) <= 1e-12 * (sa + sb)).all():
+            fails.append(f"fmt{fmt}: linearity")
+        yr, sr = orc.gemv_rows(fmt, p, N, K, x4, [3, 0, 15])
+        if not (np.array_equal(yr, y4[:, [3, 0, 15]])):
+            fails.append(f"fmt{fmt}: gemv_rows differs from gemv")
+    return fails
+
+
+def pin_moe(orc) -> list:
+    fails = []
+    P, E, N, K = 6, 4, 24, 96
+    pool_w = si.expert_pool(P, N, K, seed=2)
+    stride = orc.packed_bytes(Q4_0, N, K)
+    pool = np.concatenate([orc.quantize(Q4_0, pool_w[j]) for j in range(P)])
+    x = si.activations(E, K, seed=2)
+    for idx in (np.array([5, 0, 3, 1], np.int32), np.array([2, 2, 2, 4], np.int32)):
+        y, s = orc.moe(Q4_0, pool, P, idx, x, N, K)
+        for e in range(E):
+            ye, se = orc.gemv(Q4_0, pool[idx[e] * stride:(idx[e] + 1) * stride], N, K, x[e:e + 1])
+            if not (np.array_equal(ye[0], y[e]) and np.array_equal(se[0], s[e])):
+                fails.append(f"moe: expert slot {e} (pool {idx[e]}) is not its GEMV")
+    perm = np.array([1, 3, 0, 2])
+    idx = np.array([5, 0, 3, 1], np.int32)
+    y, _ = orc.moe(Q4_0, pool, P, idx, x, N, K)
+    yp, _ = orc.moe(Q4_0, pool, P, idx[perm], x[perm], N, K)
+    if not np.array_equal(yp, y[perm]):
+        fails.append("moe: permuting experts does not permute outputs")
+    return fails
+
+
+def pin_prefill(orc) -> list:
+    fails = []
+    N, K, M = 40, 192, 24
+    w = si.weights(N, K, seed=4)
+    X = si.activations(M, K, seed=4)
+    p = orc.quantize(Q4_0, w)
+    Y, S = orc.prefill(p, N, K, X)
+    q, scale = _parse(Q4_0, p, N, K)
+    wh = (q * scale[:, None]).reshape(N, K)
+    ref = X.astype(np.float64) @ wh.T
+    if not (np.abs(Y - ref) <= 1e-12 * S).all():
+        fails.append("prefill: differs from float64 matmul")
+    sref = np.abs(X.astype(np.float64)) @ np.abs(wh.T)
+    if not (np.abs(S - sref) <= 1e-12 * sref).all():
+        fails.append("prefill: s differs from |X| @ |W|^T")
+    return fails
+
+
+ALL_PINS = [pin_codec, pin_golden, pin_nearest, pin_invariants, pin_exact_gemv, pin_special, pin_moe,
+            pin_prefill]
