@@ -1,0 +1,168 @@
+/*
+ * qgemv.h -- C ABI of a gfx950 (MI355X) library for the fused
+ * dequantize-and-multiply of block-quantized LLM weights.
+ *
+ * Formats (32 weights per block, one binary16 scale d per block):
+ *   Q4_0  4-bit codes q in 0..15, weight = (q - 8) * d.  Within a block's 16
+ *         code bytes, byte j holds element j in its low nibble and element
+ *         j + 16 in its high nibble (GGUF Q4_0, group size 32)
+ *         [sm8x-bench, the Q4_0 table and "our kernel";
+ *          volta-kernel-bakeoff, "What's in the race"].
+ *   Q8_0  int8 codes q (two's complement), weight = q * d
+ *         [H100-KERNEL-5X-ROADMAP, Lever 1: int8 codes plus a per-block
+ *          scale; the scale is binary16 here].
+ *
+ * Packed buffer of one N x K matrix (row-major weights, K % 32 == 0, blocks
+ * along K, block index i = n * (K/32) + b):
+ *   codes   at byte 0: 16 B (Q4_0) or 32 B (Q8_0) per block, block i at
+ *           byte 16 i (32 i).
+ *   scales  binary16 little-endian, scale i at byte S0 + 2 i, where S0 is the
+ *           code-region size rounded up to a multiple of 256.
+ *   total   (S0 + 2 N K / 32) rounded up to a multiple of 256, so packed
+ *           matrices can be laid end to end (an MoE expert pool) and stay
+ *           256-byte aligned.
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are caller-owned device memory; the library allocates
+ *     no device memory and keeps no per-call state.  Work is enqueued on
+ *     `stream` (a hipStream_t; NULL = the null stream) and never
+ *     synchronized: results are ready when the caller's stream reaches them.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     non-zero status means nothing was launched.  QG_ERR_LAUNCH reports a
+ *     launch the HIP runtime refused.  Faults inside a kernel surface at the
+ *     caller's next synchronization, as for any HIP kernel.
+ *   - Alignment: packed weights 256 B, fp16 activations 16 B, fp32 outputs
+ *     4 B (QG_ERR_ALIGN otherwise).
+ *   - Outputs are fp32, accumulated in fp32 from exactly dequantized weights
+ *     and fp16 activations (products are exact; only the sums round).
+ *   - Kernels use no atomics; for a fixed shape and launch the results are
+ *     bitwise reproducible.
+ */
+#ifndef QGEMV_H
+#define QGEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int qg_status;
+enum {
+    QG_OK = 0,
+    QG_ERR_NULL = 1,    /* a required pointer is NULL */
+    QG_ERR_SHAPE = 2,   /* N, K, M or E out of range, or K % 32 != 0 */
+    QG_ERR_ALIGN = 3,   /* a pointer breaks the alignment rule above */
+    QG_ERR_RANGE = 4,   /* quantizer: non-finite weight or scale overflows binary16 */
+    QG_ERR_SIZE = 5,    /* output buffer smaller than required */
+    QG_ERR_LAUNCH = 6,  /* the HIP runtime rejected a launch */
+    QG_ERR_DEVICE = 7   /* no usable HIP device / device query failed */
+};
+
+/* Static, human-readable name of a status code. */
+const char *qg_status_str(qg_status s);
+
+/* ------------------------------------------------------------ host side */
+
+/* Bytes of one packed N x K matrix (the layout above); 0 if N <= 0, K <= 0 or
+ * K % 32 != 0. */
+size_t qpacked_bytes_q4_0(int64_t N, int64_t K);
+size_t qpacked_bytes_q8_0(int64_t N, int64_t K);
+
+/* Quantize and pack fp32 weights w[N][K] (host memory) into `packed` (host
+ * memory, at least qpacked_bytes_*(N, K) bytes; padding bytes are zeroed).
+ *   Q4_0: d = fp16(fl32(absmax / 7)), q = clamp(round(w / d) + 8, 0, 15)
+ *   Q8_0: d = fp16(fl32(absmax / 127)), q = clamp(round(w / d), -127, 127)
+ * where absmax is the block's largest |w|, fl32 an IEEE binary32 division,
+ * fp16 round-to-nearest-even to binary16, w / d is taken in binary64 against
+ * the stored binary16 d, and round is half away from zero.  A block whose d
+ * is 0 stores q = 8 (Q4_0) / 0 (Q8_0).  Returns QG_ERR_RANGE (after writing
+ * every block) if a weight is non-finite or a scale overflows binary16.
+ * [the block formats of sm8x-bench, "our kernel", and
+ *  H100-KERNEL-5X-ROADMAP, Lever 1; quantized once, off the timed path:
+ *  H100-KERNEL-5X-ROADMAP, Lever 1, resident device weights] */
+qg_status qquantize_q4_0(const float *w, int64_t N, int64_t K, void *packed, size_t packed_bytes);
+qg_status qquantize_q8_0(const float *w, int64_t N, int64_t K, void *packed, size_t packed_bytes);
+
+/* ----------------------------------------------------------- device side */
+
+/* Fused dequantize-and-multiply, 1 <= M <= 8 tokens:
+ *   y[m][n] = sum_k w[n][k] * x[m][k],  w = (q - 8) * d (Q4_0) or q * d (Q8_0)
+ * Wp: packed N x K matrix (device); x: fp16 bits [M][K] row-major (device);
+ * y: fp32 [M][N] row-major (device, fully overwritten).  1 <= N <= 2^31 - 1,
+ * 32 <= K, K % 32 == 0, K <= 16384 * min(floor(8 / M), 7) (Q4_0) or
+ * 16384 * min(floor(8 / M), 4) (Q8_0).
+ * [volta-kernel-bakeoff, "What's in the race" (fused_q4*, fused_q8: unpack in
+ *  registers, fp32 sums) and "Results" (a few tokens at once: one activation
+ *  load serves several rows); sm8x-bench, "our kernel" (several rows per
+ *  wave for memory-level parallelism, per-shape launch configuration)] */
+qg_status qgemv_q4_0(const void *Wp, const uint16_t *x, float *y, int M, int64_t N, int64_t K,
+                     void *stream);
+qg_status qgemv_q8_0(const void *Wp, const uint16_t *x, float *y, int M, int64_t N, int64_t K,
+                     void *stream);
+
+/* Mixture-of-experts GEMV in one launch, Q4_0: expert slot e (0 <= e < E)
+ * multiplies pool matrix idx[e] by its own token x[e]:
+ *   y[e][n] = sum_k w_{idx[e]}[n][k] * x[e][k]
+ * pool: P packed N x K matrices end to end, stride qpacked_bytes_q4_0(N, K)
+ * (device); idx: int32 [E] (device); x: fp16 bits [E][K]; y: fp32 [E][N].
+ * 1 <= E <= 65535.  Precondition (not checked on the device, since that
+ * would need a synchronization): 0 <= idx[e] < P.  Repeated indices are
+ * allowed.  [volta-kernel-bakeoff, "What's in the race" (moe_*: 8-10
+ *  experts, one token each, one launch) and "Results"] */
+qg_status qmoe_gemv_q4_0(const void *pool, int64_t P, const int32_t *idx, const uint16_t *x, float *y,
+                         int E, int64_t N, int64_t K, void *stream);
+
+/* Prefill (many tokens), Q4_0: Y[m][n] = sum_k w[n][k] * X[m][k] for any
+ * M >= 1.  Weight tiles are dequantized to fp16 (round to nearest even, the
+ * same values qdequant_q4_0 writes with out_fp16 = 1) in LDS and multiplied
+ * on the fp16 matrix cores with fp32 accumulation.  X: fp16 bits [M][K];
+ * Y: fp32 [M][N].
+ * [volta-kernel-bakeoff, "What's in the race" (tc_q4: unpack a tile to
+ *  shared memory, then matrix-core multiply) and "Stage 3" (unpack inside
+ *  the matrix multiply instead of dequantize-then-GEMM)] */
+qg_status qgemm_q4_0_prefill(const void *Wp, const uint16_t *X, float *Y, int64_t M, int64_t N, int64_t K,
+                             void *stream);
+
+/* Dequantize a packed matrix to out[N][K]: fp32 (out_fp16 = 0; exact) or fp16
+ * bits (out_fp16 = 1; the exact value rounded to nearest even, subnormals
+ * kept).  [volta-kernel-bakeoff, "What's in the race": dq4+cublas unpacks to
+ *  fp16 before a dense multiply] */
+qg_status qdequant_q4_0(const void *Wp, int64_t N, int64_t K, int out_fp16, void *out, void *stream);
+qg_status qdequant_q8_0(const void *Wp, int64_t N, int64_t K, int out_fp16, void *out, void *stream);
+
+/* ------------------------------------------------------------ measurement */
+
+/* Arm kernel timing for the next launch this library makes from the calling
+ * thread: that kernel records its own start and end into `start` and `stop`
+ * (hipEvent_t, created by the caller) through hipExtLaunchKernel, so
+ * hipEventElapsedTime(start, stop) is the kernel's execution time without
+ * queueing gaps.  One-shot: the next launch consumes it.  Pass NULLs to
+ * disarm.  Entry points that launch more than one kernel time the first. */
+void qg_time_next_launch(void *start, void *stop);
+
+/* Number of compute units the launch heuristics assume on `device`
+ * (QG_ERR_DEVICE if the query fails). */
+qg_status qg_device_cus(int device, int *cus);
+
+/* Tuning knob for launch-shape sweeps of qgemv_* / qmoe_gemv_q4_0: fixes J
+ * (blocks per lane per row, J * M <= 8), R (rows per group: 1, 2 or 4),
+ * ksplit (waves sharing a row along K), teams per workgroup and the total
+ * number of teams for later calls from the calling thread.  A zero keeps the
+ * built-in per-shape choice for that field; all zeros restore it fully.  An
+ * impossible combination makes the later calls return QG_ERR_SHAPE. */
+void qg_set_gemv_shape(int J, int R, int ksplit, int teams_per_wg, int64_t teams);
+
+/* Memory-bandwidth probe: a streaming 16-byte read of `bytes` (rounded down
+ * to a multiple of 16) of device memory at `buf` by `wgs` workgroups of 256
+ * threads; workgroup g writes one word to sink[g] (device, >= wgs words) so
+ * the reads cannot be dropped.  The measured roofline beside the spec sheet
+ * [sm8x-bench, methodology: a bandwidth probe gives the measured roofline]. */
+qg_status qg_read_probe(const void *buf, size_t bytes, uint32_t *sink, int wgs, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMV_H */

@@ -1,0 +1,366 @@
+// C-ABI entry points: host-side validation, per-shape launch choice and
+// launches on the caller's stream.  Nothing here allocates device memory or
+// synchronizes.
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <mutex>
+
+#include "qgemv.h"
+#include "qgemv_internal.h"
+
+namespace qg {
+
+// ---------------------------------------------------------------- timing hook
+
+namespace {
+thread_local hipEvent_t t_start = nullptr;
+thread_local hipEvent_t t_stop = nullptr;
+}  // namespace
+
+hipError_t launch_raw(const void *fn, dim3 grid, dim3 block, void **args, size_t shmem, hipStream_t stream)
+{
+    if (t_start || t_stop) {
+        hipEvent_t a = t_start, b = t_stop;
+        t_start = t_stop = nullptr;
+        return hipExtLaunchKernel(fn, grid, block, args, shmem, stream, a, b, 0);
+    }
+    return hipLaunchKernel(fn, grid, block, args, shmem, stream);
+}
+
+// ---------------------------------------------------------------- device info
+
+namespace {
+constexpr int kMaxDevices = 64;
+int g_cus[kMaxDevices] = {0};
+std::mutex g_mu;
+
+int device_cus()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return 0;
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (g_cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            return 0;
+        g_cus[dev] = n;
+    }
+    return g_cus[dev];
+}
+
+inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+inline size_t round256(size_t v) { return (v + 255) / 256 * 256; }
+
+inline int64_t scale_offset(int fmt, int64_t N, int64_t K)
+{
+    return static_cast<int64_t>(round256(static_cast<size_t>(N) * static_cast<size_t>(K / 32) *
+                                         (fmt == kQ4_0 ? 16u : 32u)));
+}
+
+// Launch shape for one GEMV / MoE call.
+struct GemvShape {
+    int J, R, ksplit, teams_per_wg;
+    int64_t teams;   // teams per batch item
+};
+
+// Caller-set override for tuning sweeps (thread-local, zeros = heuristic).
+thread_local int o_J = 0, o_R = 0, o_ksplit = 0, o_teams_per_wg = 0;
+thread_local int64_t o_teams = 0;
+
+bool choose_shape(int fmt, int M, int64_t N, int64_t K, int items, int cus, GemvShape &s)
+{
+    const int64_t KB = K / 32;
+    // resident activations: J * M <= 8 blocks per lane; Q8_0 code words are
+    // twice as wide, so it keeps J <= 4
+    const int jmax = std::min(8 / M, fmt == kQ4_0 ? 7 : 4);
+    int ksplit = static_cast<int>((KB + 64 * jmax - 1) / (64 * jmax));
+    if (ksplit > kMaxWavesPerWg)
+        return false;
+    int J = static_cast<int>((KB + 64LL * ksplit - 1) / (64LL * ksplit));
+    const int rj = (fmt == kQ4_0) ? 8 : 4;   // R * J budget of the kernel table
+    int R = (4 * J <= rj) ? 4 : (2 * J <= rj ? 2 : 1);
+    if (M > 2 && R > 2)
+        R = 2;
+    int teams_per_wg = (ksplit == 1) ? 4 : 1;
+    if (o_J) {
+        J = o_J;
+        ksplit = static_cast<int>((KB + 64LL * J - 1) / (64LL * J));
+        if (J * M > 8 || ksplit > kMaxWavesPerWg)
+            return false;
+    }
+    if (o_ksplit) {
+        ksplit = o_ksplit;
+        if (static_cast<int64_t>(ksplit) * 64 * J < KB || ksplit > kMaxWavesPerWg)
+            return false;
+    }
+    if (o_R)
+        R = o_R;
+    if (o_teams_per_wg)
+        teams_per_wg = o_teams_per_wg;
+    if (ksplit > 1)
+        teams_per_wg = 1;   // a workgroup's waves must walk the same row groups
+    if (teams_per_wg * ksplit > kMaxWavesPerWg)
+        teams_per_wg = std::max(1, kMaxWavesPerWg / ksplit);
+    const int64_t ngroups = (N + R - 1) / R;
+    // persistent grid: about 8 waves per compute unit over the whole call
+    int64_t teams = std::max<int64_t>(1, static_cast<int64_t>(cus) * 8 / ksplit / std::max(1, items));
+    if (o_teams)
+        teams = o_teams;
+    teams = std::min(teams, ngroups);
+    s = GemvShape{J, R, ksplit, teams_per_wg, teams};
+    return true;
+}
+
+qg_status run_gemv(int fmt, const void *Wp, const int32_t *idx, int64_t P, const uint16_t *x, float *y, int M,
+                   int items, int64_t N, int64_t K, void *stream)
+{
+    if (!Wp || !x || !y)
+        return QG_ERR_NULL;
+    if (M < 1 || M > 8 || N < 1 || N > INT32_MAX || K < 32 || K % 32 != 0 || K > (1 << 20) || items < 1 ||
+        items > 65535)
+        return QG_ERR_SHAPE;
+    if (!aligned(Wp, 256) || !aligned(x, 16) || !aligned(y, 4))
+        return QG_ERR_ALIGN;
+    const int cus = device_cus();
+    if (cus <= 0)
+        return QG_ERR_DEVICE;
+    GemvShape s;
+    if (!choose_shape(fmt, M, N, K, items, cus, s))
+        return QG_ERR_SHAPE;
+    GemvParams p;
+    p.W = static_cast<const uint8_t *>(Wp);
+    p.idx = idx;
+    p.x = x;
+    p.y = y;
+    p.matrix_stride = static_cast<int64_t>(fmt == kQ4_0 ? qpacked_bytes_q4_0(N, K) : qpacked_bytes_q8_0(N, K));
+    p.scale_offset = scale_offset(fmt, N, K);
+    p.N = static_cast<int>(N);
+    p.K = static_cast<int>(K);
+    p.ksplit = s.ksplit;
+    p.teams_per_wg = s.teams_per_wg;
+    (void)P;
+    const int64_t wgs = (s.teams + s.teams_per_wg - 1) / s.teams_per_wg;
+    dim3 grid(static_cast<unsigned>(wgs), static_cast<unsigned>(items), 1);
+    dim3 block(64 * s.ksplit * s.teams_per_wg, 1, 1);
+    hipError_t e = launch_gemv(fmt, M, s.J, s.R, p, grid, block, static_cast<hipStream_t>(stream));
+    if (e == hipErrorInvalidValue)
+        return QG_ERR_SHAPE;
+    return e == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
+}
+
+// ---------------------------------------------------------------- dequant
+
+// One thread per block of 32 weights: the exact (q - 8) * d (or q * d) in
+// fp32, or that value rounded to nearest-even binary16.
+template <int FMT, bool F16>
+__device__ __forceinline__ void dequant_kernel(const uint8_t *__restrict__ W, int64_t blocks,
+                                                      int64_t scale_off, void *__restrict__ out)
+{
+    const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= blocks)
+        return;
+    const float d = (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t *>(W + scale_off)[b]);
+    float v[32];
+    if constexpr (FMT == kQ4_0) {
+        const uint4 c = reinterpret_cast<const uint4 *>(W)[b];
+        const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const uint32_t byte = (w[j >> 2] >> (8 * (j & 3))) & 0xFFu;
+            v[j] = (float)((int)(byte & 0xFu) - 8) * d;
+            v[j + 16] = (float)((int)(byte >> 4) - 8) * d;
+        }
+    } else {
+        const uint4 *c = reinterpret_cast<const uint4 *>(W + b * 32);
+        const uint4 c0 = c[0], c1 = c[1];
+        const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+        for (int j = 0; j < 32; ++j)
+            v[j] = (float)(int8_t)((w[j >> 2] >> (8 * (j & 3))) & 0xFFu) * d;
+    }
+    if constexpr (F16) {
+        uint4 *o = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(out) + b * 32);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            uint32_t u[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const uint16_t lo = __builtin_bit_cast(uint16_t, (_Float16)v[8 * q + 2 * t]);
+                const uint16_t hi = __builtin_bit_cast(uint16_t, (_Float16)v[8 * q + 2 * t + 1]);
+                u[t] = (uint32_t)lo | ((uint32_t)hi << 16);
+            }
+            o[q] = make_uint4(u[0], u[1], u[2], u[3]);
+        }
+    } else {
+        float4 *o = reinterpret_cast<float4 *>(static_cast<float *>(out) + b * 32);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            o[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+    }
+}
+
+struct DequantArgs {
+    const uint8_t *W;
+    int64_t blocks;
+    int64_t scale_off;
+    void *out;
+};
+
+template <int FMT, bool F16>
+__global__ __launch_bounds__(256) void dequant_entry(DequantArgs a)
+{
+    dequant_kernel<FMT, F16>(a.W, a.blocks, a.scale_off, a.out);
+}
+
+qg_status run_dequant(int fmt, const void *Wp, int64_t N, int64_t K, int out_fp16, void *out, void *stream)
+{
+    if (!Wp || !out)
+        return QG_ERR_NULL;
+    if (N < 1 || K < 32 || K % 32 != 0)
+        return QG_ERR_SHAPE;
+    if (!aligned(Wp, 256) || !aligned(out, 16))
+        return QG_ERR_ALIGN;
+    DequantArgs a{static_cast<const uint8_t *>(Wp), N * (K / 32), scale_offset(fmt, N, K), out};
+    const int64_t wgs = (a.blocks + 255) / 256;
+    if (wgs > INT32_MAX)
+        return QG_ERR_SHAPE;
+    const void *fn;
+    if (fmt == kQ4_0)
+        fn = out_fp16 ? reinterpret_cast<const void *>(&dequant_entry<kQ4_0, true>)
+                      : reinterpret_cast<const void *>(&dequant_entry<kQ4_0, false>);
+    else
+        fn = out_fp16 ? reinterpret_cast<const void *>(&dequant_entry<kQ8_0, true>)
+                      : reinterpret_cast<const void *>(&dequant_entry<kQ8_0, false>);
+    hipError_t e = launch_kernel(fn, dim3(static_cast<unsigned>(wgs)), dim3(256), 0,
+                                 static_cast<hipStream_t>(stream), a);
+    return e == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
+}
+
+}  // namespace
+}  // namespace qg
+
+extern "C" {
+
+qg_status qgemv_q4_0(const void *Wp, const uint16_t *x, float *y, int M, int64_t N, int64_t K, void *stream)
+{
+    return qg::run_gemv(qg::kQ4_0, Wp, nullptr, 1, x, y, M, 1, N, K, stream);
+}
+
+qg_status qgemv_q8_0(const void *Wp, const uint16_t *x, float *y, int M, int64_t N, int64_t K, void *stream)
+{
+    return qg::run_gemv(qg::kQ8_0, Wp, nullptr, 1, x, y, M, 1, N, K, stream);
+}
+
+qg_status qmoe_gemv_q4_0(const void *pool, int64_t P, const int32_t *idx, const uint16_t *x, float *y, int E,
+                         int64_t N, int64_t K, void *stream)
+{
+    if (!idx)
+        return QG_ERR_NULL;
+    if (P < 1 || E < 1)
+        return QG_ERR_SHAPE;
+    if (!qg::aligned(idx, 4))
+        return QG_ERR_ALIGN;
+    return qg::run_gemv(qg::kQ4_0, pool, idx, P, x, y, 1, E, N, K, stream);
+}
+
+qg_status qdequant_q4_0(const void *Wp, int64_t N, int64_t K, int out_fp16, void *out, void *stream)
+{
+    return qg::run_dequant(qg::kQ4_0, Wp, N, K, out_fp16, out, stream);
+}
+
+qg_status qdequant_q8_0(const void *Wp, int64_t N, int64_t K, int out_fp16, void *out, void *stream)
+{
+    return qg::run_dequant(qg::kQ8_0, Wp, N, K, out_fp16, out, stream);
+}
+
+void qg_time_next_launch(void *start, void *stop)
+{
+    qg::t_start = static_cast<hipEvent_t>(start);
+    qg::t_stop = static_cast<hipEvent_t>(stop);
+}
+
+qg_status qg_device_cus(int device, int *cus)
+{
+    if (!cus)
+        return QG_ERR_NULL;
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || n <= 0)
+        return QG_ERR_DEVICE;
+    *cus = n;
+    return QG_OK;
+}
+
+// Tuning knob for launch-shape sweeps: fixes J (blocks per lane), R (rows per
+// group), ksplit (waves along K), teams per workgroup and total teams for the
+// GEMV / MoE calls made afterwards from the calling thread.  Zero keeps the
+// built-in choice for that field.
+void qg_set_gemv_shape(int J, int R, int ksplit, int teams_per_wg, int64_t teams)
+{
+    qg::o_J = J;
+    qg::o_R = R;
+    qg::o_ksplit = ksplit;
+    qg::o_teams_per_wg = teams_per_wg;
+    qg::o_teams = teams;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- HBM probe
+
+namespace qg {
+namespace {
+
+struct ProbeArgs {
+    const uint4 *p;
+    int64_t n16;       // 16-byte words to read
+    uint32_t *sink;    // one word per workgroup keeps the loads live
+};
+
+// Streaming read of a buffer with 16-byte loads, grid-stride, four loads in
+// flight per lane: the achievable read bandwidth of the memory system.
+__global__ __launch_bounds__(256) void read_probe_kernel(ProbeArgs a)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + 3 * stride < a.n16; i += 4 * stride) {
+        const uint4 v0 = a.p[i], v1 = a.p[i + stride], v2 = a.p[i + 2 * stride], v3 = a.p[i + 3 * stride];
+        acc ^= v0.x ^ v0.y ^ v0.z ^ v0.w ^ v1.x ^ v1.y ^ v1.z ^ v1.w;
+        acc ^= v2.x ^ v2.y ^ v2.z ^ v2.w ^ v3.x ^ v3.y ^ v3.z ^ v3.w;
+    }
+    for (; i < a.n16; i += stride) {
+        const uint4 v = a.p[i];
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    __shared__ uint32_t s[256];
+    s[threadIdx.x] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t r = 0;
+        for (int t = 0; t < 256; ++t)
+            r ^= s[t];
+        a.sink[blockIdx.x] = r;
+    }
+}
+
+}  // namespace
+}  // namespace qg
+
+extern "C" qg_status qg_read_probe(const void *buf, size_t bytes, uint32_t *sink, int wgs, void *stream)
+{
+    if (!buf || !sink)
+        return QG_ERR_NULL;
+    if (bytes < 16 || wgs < 1)
+        return QG_ERR_SHAPE;
+    if (!qg::aligned(buf, 16) || !qg::aligned(sink, 4))
+        return QG_ERR_ALIGN;
+    qg::ProbeArgs a{static_cast<const uint4 *>(buf), static_cast<int64_t>(bytes / 16), sink};
+    hipError_t e = qg::launch_kernel(reinterpret_cast<const void *>(&qg::read_probe_kernel), dim3(wgs), dim3(256),
+                                     0, static_cast<hipStream_t>(stream), a);
+    return e == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
+}

@@ -1,0 +1,240 @@
+"""GPU parity: the HIP GEMV / dequant kernels against the CPU oracle.
+
+Acceptance per output element: finite and |y - y_ref| <= 1e-3 * s + 1e-6 with
+s = sum_k |w_k x_k| (fp32 sums of exact products are far inside this);
+dequantized weights bit-exact.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import seeded_inputs as si
+from gpu_util import Q4_0, Q8_0, acts, assert_within, pack_both, qg, sample_rows, to_dev, torch_cuda, weights
+
+pytestmark = pytest.mark.gpu
+
+FMTS = [Q4_0, Q8_0]
+FNAME = {Q4_0: "q4_0", Q8_0: "q8_0"}
+
+
+def _gemv(fmt, Wd, xd, N, K):
+    q = qg()
+    y = (q.qgemv_q4_0 if fmt == Q4_0 else q.qgemv_q8_0)(Wd, xd, N, K)
+    torch_cuda().cuda.synchronize()
+    return y.cpu().numpy()
+
+
+# Shapes that span several lane/row tiles and ragged tails: K/32 below,
+# at and above 64 and not a multiple of 64; N not a multiple of the row group.
+SMALL_SHAPES = [(1, 32), (3, 64), (5, 96), (65, 640), (130, 2048), (257, 2560), (33, 4096), (70, 6144),
+                (19, 14336), (9, 16384), (11, 4128)]
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FNAME[f])
+@pytest.mark.parametrize("N,K", SMALL_SHAPES)
+def test_dequant_bit_exact(fmt, N, K):
+    torch = torch_cuda()
+    q = qg()
+    w = weights(N, K, seed=N + K)
+    pb, po = pack_both(fmt, w)
+    Wd = to_dev(pb)
+    deq = q.qdequant_q4_0 if fmt == Q4_0 else q.qdequant_q8_0
+    f32 = deq(Wd, N, K, fp16=False)
+    f16 = deq(Wd, N, K, fp16=True)
+    torch.cuda.synchronize()
+    o = oracle.get()
+    assert np.array_equal(f32.cpu().numpy().view(np.uint32), o.dequant(fmt, po, N, K, "f32").view(np.uint32))
+    assert np.array_equal(f16.cpu().numpy().view(np.uint16), o.dequant(fmt, po, N, K, "f16").view(np.uint16))
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FNAME[f])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("N,K", SMALL_SHAPES)
+def test_gemv_small_parity(fmt, M, N, K):
+    q = qg()
+    limit = 16384 * min(8 // M, 7 if fmt == Q4_0 else 4)
+    w = weights(N, K, seed=3 * N + K)
+    x = acts(M, K, seed=M + K)
+    pb, po = pack_both(fmt, w)
+    if K > limit:
+        with pytest.raises(q.QGError):
+            _gemv(fmt, to_dev(pb), to_dev(x), N, K)
+        return
+    y = _gemv(fmt, to_dev(pb), to_dev(x), N, K)
+    y_ref, s = oracle.get().gemv(fmt, po, N, K, x)
+    assert_within(y, y_ref, s, f"{FNAME[fmt]} {N}x{K} M={M}")
+
+
+def test_gemv_q4_0_2048_seed0():
+    """Q4_0 GEMV, N=2048 out x K=2048 in, one token, seed 0: every output."""
+    N = K = 2048
+    w = si.weights(N, K, seed=0)
+    x = si.activations(1, K, seed=0)
+    pb, po = pack_both(Q4_0, w)
+    y = _gemv(Q4_0, to_dev(pb), to_dev(x), N, K)
+    y_ref, s = oracle.get().gemv(Q4_0, po, N, K, x)
+    assert_within(y, y_ref, s, "2048x2048")
+
+
+@pytest.mark.parametrize("N,K", si.LLAMA3_8B_SHAPES)
+def test_gemv_q4_0_llama3_8b_full_size(N, K):
+    """Full-size Llama-3-8B projection shapes at one token, in the launch
+    configuration the bench times, checked on sampled rows."""
+    w = si.weights(N, K, seed=0)
+    x = si.activations(1, K, seed=0)
+    pb, po = pack_both(Q4_0, w)
+    del w
+    y = _gemv(Q4_0, to_dev(pb), to_dev(x), N, K)
+    rows = sample_rows(N)
+    y_ref, s = oracle.get().gemv_rows(Q4_0, po, N, K, x, rows)
+    assert_within(y[:, rows], y_ref, s, f"{N}x{K}")
+    assert np.isfinite(y).all()
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FNAME[f])
+@pytest.mark.parametrize("N,K", si.SMALL_BATCH_SHAPES)
+@pytest.mark.parametrize("M", [1, 2, 4, 8])
+def test_small_batch_decode(fmt, N, K, M):
+    """Small-batch decode shapes, every output against the oracle."""
+    w = si.weights(N, K, seed=0)
+    x = si.activations(M, K, seed=0)
+    pb, po = pack_both(fmt, w)
+    y = _gemv(fmt, to_dev(pb), to_dev(x), N, K)
+    y_ref, s = oracle.get().gemv(fmt, po, N, K, x)
+    assert_within(y, y_ref, s, f"{FNAME[fmt]} {N}x{K} M={M}")
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FNAME[f])
+def test_one_hot_columns_are_exact(fmt):
+    """x = e_k returns column k of the dequantized matrix bit-exactly (pins the
+    nibble order and block indexing on the GPU)."""
+    N, K = 96, 4096
+    w = weights(N, K, seed=12)
+    pb, po = pack_both(fmt, w)
+    Wd = to_dev(pb)
+    cols = [0, 1, 5, 15, 16, 17, 31, 32, 2047, 2048 + 20, 4095]
+    x = np.zeros((len(cols), K), np.float16)
+    for i, k in enumerate(cols):
+        x[i, k] = 1.0
+    wh = oracle.get().dequant(fmt, po, N, K, "f32")
+    for lo in range(0, len(cols), 8):
+        y = _gemv(fmt, Wd, to_dev(x[lo:lo + 8]), N, K)
+        for i, k in enumerate(cols[lo:lo + 8]):
+            assert np.array_equal(y[i], wh[:, k]), f"column {k}"
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FNAME[f])
+@pytest.mark.parametrize("kind", ["large", "tiny"])
+def test_stress_activations(fmt, kind):
+    """Planted large (+-20000..60000) and tiny activations, as the pages'
+    precision stress; fp32 accumulation must stay inside the bound."""
+    N, K = 300, 6144
+    w = weights(N, K, seed=21)
+    x = si.stress_activations(4, K, seed=21, kind=kind)
+    pb, po = pack_both(fmt, w)
+    y = _gemv(fmt, to_dev(pb), to_dev(x), N, K)
+    y_ref, s = oracle.get().gemv(fmt, po, N, K, x)
+    assert_within(y, y_ref, s, f"{FNAME[fmt]} stress {kind}")
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FNAME[f])
+def test_zero_and_degenerate_blocks(fmt):
+    """All-zero blocks (scale 0), subnormal scales, a single non-zero weight."""
+    N, K = 40, 2560
+    w = weights(N, K, seed=5)
+    w[0, :] = 0.0
+    w[1, 32:64] = 0.0
+    w[2, :] *= np.float32(1e-6)          # subnormal binary16 scales
+    w[3, :] = 0.0
+    w[3, 100] = np.float32(0.5)
+    x = acts(3, K, seed=5)
+    pb, po = pack_both(fmt, w)
+    y = _gemv(fmt, to_dev(pb), to_dev(x), N, K)
+    y_ref, s = oracle.get().gemv(fmt, po, N, K, x)
+    assert_within(y, y_ref, s, "degenerate")
+    assert (y[:, 0] == 0).all()
+    y0 = _gemv(fmt, to_dev(pb), to_dev(np.zeros((2, K), np.float16)), N, K)
+    assert (y0 == 0).all()
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FNAME[f])
+def test_deterministic_and_copy_invariant(fmt):
+    """Same bytes at two addresses, two calls each: bitwise-equal outputs."""
+    torch = torch_cuda()
+    N, K = 6144, 4096
+    w = weights(N, K, seed=8)
+    x = acts(2, K, seed=8)
+    pb, _ = pack_both(fmt, w)
+    A, B = to_dev(pb), to_dev(pb)
+    xd = to_dev(x)
+    q = qg()
+    f = q.qgemv_q4_0 if fmt == Q4_0 else q.qgemv_q8_0
+    ys = [f(A, xd, N, K), f(B, xd, N, K), f(A, xd, N, K)]
+    torch.cuda.synchronize()
+    assert torch.equal(ys[0], ys[1]) and torch.equal(ys[0], ys[2])
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FNAME[f])
+def test_sabotaged_weights_fail_every_check(fmt):
+    """Corrupt the device copy (code bytes XOR 0x11, scale signs flipped); the
+    oracle keeps the clean bytes, so every packed-kernel check must fail
+    [volta-kernel-bakeoff, "Making it fair"]."""
+    torch = torch_cuda()
+    o = oracle.get()
+    failed = checks = 0
+    for (N, K, M) in ((64, 2048, 1), (130, 2560, 4), (257, 4096, 8)):
+        w = weights(N, K, seed=N)
+        x = acts(M, K, seed=N)
+        pb, po = pack_both(fmt, w)
+        bad = pb.copy()
+        nb = N * K // 32
+        cb = 16 if fmt == Q4_0 else 32
+        bad[:nb * cb] ^= 0x11
+        s0 = (nb * cb + 255) // 256 * 256
+        bad[s0 + 1:s0 + 2 * nb:2] ^= 0x80
+        y = _gemv(fmt, to_dev(bad), to_dev(x), N, K)
+        y_ref, s = o.gemv(fmt, po, N, K, x)
+        checks += 1
+        failed += int(not oracle.within_bound(y, y_ref, s).all())
+        deq = (qg().qdequant_q4_0 if fmt == Q4_0 else qg().qdequant_q8_0)(to_dev(bad), N, K)
+        torch.cuda.synchronize()
+        checks += 1
+        failed += int(not np.array_equal(deq.cpu().numpy(), o.dequant(fmt, po, N, K, "f32")))
+    assert failed == checks
+
+
+def test_abi_errors_are_reported_before_launch():
+    torch = torch_cuda()
+    q = qg()
+    L = q.lib()
+    N, K = 64, 256
+    W = torch.zeros(q.qpacked_bytes_q4_0(N, K) + 256, dtype=torch.uint8, device="cuda")
+    x = torch.zeros((9, K), dtype=torch.float16, device="cuda")
+    y = torch.zeros((9, N), dtype=torch.float32, device="cuda")
+    s = q._stream()
+    p = W.data_ptr
+    assert L.qgemv_q4_0(None, x.data_ptr(), y.data_ptr(), 1, N, K, s) == 1
+    assert L.qgemv_q4_0(p(), x.data_ptr(), y.data_ptr(), 9, N, K, s) == 2        # M > 8
+    assert L.qgemv_q4_0(p(), x.data_ptr(), y.data_ptr(), 0, N, K, s) == 2        # M < 1
+    assert L.qgemv_q4_0(p(), x.data_ptr(), y.data_ptr(), 1, N, 48, s) == 2       # K % 32
+    assert L.qgemv_q4_0(p(), x.data_ptr(), y.data_ptr(), 1, 0, K, s) == 2        # N < 1
+    assert L.qgemv_q4_0(p() + 16, x.data_ptr(), y.data_ptr(), 1, N, K, s) == 3   # W alignment
+    assert L.qgemv_q4_0(p(), x.data_ptr() + 2, y.data_ptr(), 1, N, K, s) == 3    # x alignment
+    assert L.qdequant_q4_0(p(), N, 40, 0, y.data_ptr(), s) == 2
+    torch.cuda.synchronize()
+    assert (y == 0).all()   # nothing was launched
+
+
+def test_outputs_stay_in_bounds():
+    """Canary elements around y are untouched for ragged shapes."""
+    torch = torch_cuda()
+    q = qg()
+    for fmt in FMTS:
+        for (N, K, M) in ((1, 32, 1), (7, 2560, 3), (131, 4096, 8), (4099, 2048, 2)):
+            pb, _ = pack_both(fmt, weights(N, K, seed=N))
+            x = to_dev(acts(M, K, seed=1))
+            buf = torch.full((M * N + 128,), 7.0, dtype=torch.float32, device="cuda")
+            y = buf[64:64 + M * N].view(M, N)
+            (q.qgemv_q4_0 if fmt == Q4_0 else q.qgemv_q8_0)(to_dev(pb), x, N, K, y)
+            torch.cuda.synchronize()
+            assert (buf[:64] == 7.0).all() and (buf[64 + M * N:] == 7.0).all()
