@@ -46,6 +46,21 @@ def algorithmic_bytes(N: int, K: int, M: int = 1) -> int:
     return N * K // 32 * 18 + 2 * M * K + 4 * M * N
 
 
+def measured_traffic():
+    """HBM bytes per step from the committed rocprofv3 counter summary, if it
+    was taken on the GEMV sources as they are now; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "gemv_q4_0_llama3_8b_m1_traffic.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+        from quantized_weight_gemv_amd.profiling import gemv_source_hash
+        if d.get("gemv_source_sha256") != gemv_source_hash():
+            return None
+        return int(d["traffic_bytes_per_step"])
+    except (OSError, ValueError, KeyError):
+        return None
+
+
 def log(msg: str):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -67,21 +82,22 @@ def build_workload(qg, torch):
         del first
         x = torch.from_numpy(si.activations(1, K, seed=0)).to("cuda")
         y = torch.empty((1, N), dtype=torch.float32, device="cuda")
-        work.append(dict(N=N, K=K, nb=nb, copies=copies, buf=buf, x=x, y=y, next=0,
+        # one validated call per copy: the timed loop only enqueues kernels
+        calls = [qg.PreparedGemv(qg.Q4_0, buf[c * nb:(c + 1) * nb], x, y, N, K) for c in range(copies)]
+        work.append(dict(N=N, K=K, nb=nb, copies=copies, buf=buf, x=x, y=y, next=0, calls=calls,
                          bytes=algorithmic_bytes(N, K)))
         log(f"shape {N}x{K}: {copies} copies x {nb} B ({time.perf_counter() - t0:.1f} s)")
     torch.cuda.synchronize()
     return work
 
 
-def run_step(qg, work, timer=None):
+def run_step(work, timer=None):
     for w in work:
         c = w["next"]
         w["next"] = (c + 1) % w["copies"]
-        nb = w["nb"]
         if timer is not None:
             timer.arm()
-        qg.qgemv_q4_0(w["buf"][c * nb:(c + 1) * nb], w["x"], w["N"], w["K"], w["y"])
+        w["calls"][c]()
 
 
 def hbm_probe(qg, torch, gib: int = 4, reps: int = 5) -> float:
@@ -130,6 +146,126 @@ def cpu_baseline(seconds: float) -> dict:
                       f"{seconds:.0f} s in total: " + ", ".join(sample)}
 
 
+# ------------------------------------------------------------------- suite
+def _copies(torch, packed: np.ndarray, min_bytes: int = COPY_BYTES):
+    nb = packed.size
+    copies = max(2, math.ceil(min_bytes / nb))
+    buf = torch.empty(copies * nb, dtype=torch.uint8, device="cuda")
+    first = torch.from_numpy(packed).to("cuda")
+    for c in range(copies):
+        buf[c * nb:(c + 1) * nb].copy_(first)
+    return buf, nb, copies
+
+
+def _time_calls(qg, torch, calls, reps: int, warm: int = 5):
+    """Median / mean kernel time (us) of `reps` calls, rotating through `calls`,
+    from the HIP events each launch records."""
+    for i in range(warm):
+        calls[i % len(calls)]()
+    timer = qg.KernelTimer(reps)
+    for i in range(reps):
+        timer.arm()
+        calls[(i + warm) % len(calls)]()
+    ms = np.array(timer.elapsed_ms())
+    timer.close()
+    return float(np.median(ms) * 1e3), float(ms.mean() * 1e3)
+
+
+def _time_wall(torch, fns, reps: int, warm: int = 5):
+    """Per-call time (us) from torch events around each call on the current
+    stream (includes every kernel a call launches and the gaps between them)."""
+    for i in range(warm):
+        fns[i % len(fns)]()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(reps):
+        ev[i][0].record()
+        fns[(i + warm) % len(fns)]()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    return float(np.median(ms) * 1e3), float(ms.mean() * 1e3)
+
+
+def suite(qg, torch, reps: int):
+    """Every workload of the library, one JSON record each."""
+    out = []
+    cus = qg.qg_device_cus()
+
+    def rec(**kw):
+        out.append(kw)
+        log(json.dumps(kw))
+
+    # GEMV: 2048x2048 seed 0 and the small-batch shapes, both formats, M = 1, 2, 4, 8
+    gemv_cases = [(qg.Q4_0, 2048, 2048, 1)]
+    for fmt in (qg.Q4_0, qg.Q8_0):
+        for (N, K) in si.SMALL_BATCH_SHAPES:
+            for M in (1, 2, 4, 8):
+                gemv_cases.append((fmt, N, K, M))
+    packed_cache = {}
+    for fmt, N, K, M in gemv_cases:
+        key = (fmt, N, K)
+        if key not in packed_cache:
+            packed_cache.clear()
+            w = si.weights(N, K, seed=0)
+            packed_cache[key] = _copies(torch, qg.qquantize_q4_0(w) if fmt == qg.Q4_0 else qg.qquantize_q8_0(w))
+        buf, nb, copies = packed_cache[key]
+        x = torch.from_numpy(si.activations(M, K, seed=0)).to("cuda")
+        y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        calls = [qg.PreparedGemv(fmt, buf[c * nb:(c + 1) * nb], x, y, N, K) for c in range(copies)]
+        med, mean = _time_calls(qg, torch, calls, reps)
+        b = N * K // 32 * (18 if fmt == qg.Q4_0 else 34) + 2 * M * K + 4 * M * N
+        rec(kind="gemv", fmt="q4_0" if fmt == qg.Q4_0 else "q8_0", N=N, K=K, M=M, us_median=round(med, 3),
+            us_mean=round(mean, 3), GBps=round(b / med / 1e3, 1), pct_of_8TBps=round(b / med / 1e3 / 80, 2),
+            algorithmic_bytes=b, copies=copies)
+    packed_cache.clear()
+
+    # MoE: a pool of P experts replicated to >= 1 GiB; fresh distinct indices per call
+    for (P, E, N, K) in si.MOE_CONFIGS:
+        pw = si.expert_pool(P, N, K, seed=0)
+        pool = np.concatenate([qg.qquantize_q4_0(pw[j]) for j in range(P)])
+        del pw
+        buf, nb, copies = _copies(torch, pool)
+        ncalls = 64
+        idx = torch.from_numpy(np.stack([si.expert_indices(P, E, seed=0, call=c) for c in range(ncalls)])).cuda()
+        x = torch.from_numpy(si.activations(E, K, seed=0)).to("cuda")
+        y = torch.empty((E, N), dtype=torch.float32, device="cuda")
+        fns = []
+        for c in range(max(copies, ncalls)):
+            pool_c = buf[(c % copies) * nb:(c % copies + 1) * nb]
+            fns.append(lambda pc=pool_c, ic=idx[c % ncalls]: qg.qmoe_gemv_q4_0(pc, P, ic, x, N, K, y))
+        med, mean = _time_calls(qg, torch, fns, reps)
+        b = E * (N * K // 32 * 18 + 2 * K + 4 * N)
+        rec(kind="moe", fmt="q4_0", P=P, E=E, N=N, K=K, us_median=round(med, 3), us_mean=round(mean, 3),
+            GBps=round(b / med / 1e3, 1), pct_of_8TBps=round(b / med / 1e3 / 80, 2), algorithmic_bytes=b,
+            pool_copies=copies)
+        del buf
+
+    # prefill, and the dense fp16 GEMM on pre-dequantized weights beside it
+    for (N, K) in si.PREFILL_SHAPES:
+        w = si.weights(N, K, seed=0)
+        buf, nb, copies = _copies(torch, qg.qquantize_q4_0(w))
+        del w
+        w16 = [qg.qdequant_q4_0(buf[c * nb:(c + 1) * nb], N, K, fp16=True).t().contiguous()
+               for c in range(max(2, math.ceil(COPY_BYTES / (2 * N * K))))]
+        for M in si.PREFILL_TOKENS:
+            X = torch.from_numpy(si.activations(M, K, seed=0)).to("cuda")
+            Y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+            fns = [lambda c=c: qg.qgemm_q4_0_prefill(buf[c * nb:(c + 1) * nb], X, N, K, Y) for c in range(copies)]
+            kmed, _ = _time_calls(qg, torch, fns, reps)
+            med, mean = _time_wall(torch, fns, reps)
+            dense = [lambda c=c: torch.matmul(X, w16[c]) for c in range(len(w16))]
+            dmed, _ = _time_wall(torch, dense, reps)
+            flops = 2 * M * N * K
+            b = N * K // 32 * 18 + 2 * M * K + 4 * M * N
+            rec(kind="prefill", fmt="q4_0", N=N, K=K, M=M, us_median=round(med, 3), us_mean=round(mean, 3),
+                gemm_kernel_us_median=round(kmed, 3), TFLOPs=round(flops / med / 1e6, 1),
+                pct_of_2500TF=round(flops / med / 1e6 / 25, 2), GBps=round(b / med / 1e3, 1),
+                dense_fp16_us_median=round(dmed, 3), speedup_vs_dense=round(dmed / med, 3), copies=copies)
+        del buf, w16
+        torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -138,6 +274,10 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--suite", default=None, metavar="FILE",
+                    help="instead of the headline step, time every workload (GEMV both formats and M = 1..8, "
+                         "MoE, prefill with its dense fp16 comparator) and write one JSON record per line to FILE")
+    ap.add_argument("--reps", type=int, default=100)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the GEMV path runs on a single MI355X (no collectives); "
@@ -151,18 +291,25 @@ def main() -> int:
     import quantized_weight_gemv_amd as qg
     qg.lib()
 
+    if args.suite:
+        recs = suite(qg, torch, args.reps)
+        with open(args.suite, "w") as f:
+            for r in recs:
+                f.write(json.dumps(r) + "\n")
+        return 0
+
     work = build_workload(qg, torch)
     step_bytes = sum(w["bytes"] for w in work)
 
     for _ in range(args.warmup):
-        run_step(qg, work)
+        run_step(work)
     torch.cuda.synchronize()
 
     timer = qg.KernelTimer(args.steps * len(work))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        run_step(qg, work, timer)
+        run_step(work, timer)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = np.array(timer.elapsed_ms()).reshape(args.steps, len(work))
@@ -202,10 +349,12 @@ def main() -> int:
                    "step": "one qgemv_q4_0 call per shape"},
         "pct_of_8TBps": round(value / PEAK_GBPS * 100, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_GBPS, 4), "traffic": measured_traffic(),
+                     "algorithmic_bytes": step_bytes,
                      "kernel": "qg::gemv_kernel (Q4_0, M=1)",
-                     "note": "algorithmic bytes of the six calls / sum of their kernel times (HIP events "
-                             "recorded by each launch)"},
+                     "note": "per step of six launches: achieved = algorithmic bytes / sum of their kernel "
+                             "times (HIP events recorded by each launch); traffic = HBM bytes of the six launches "
+                             "from rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated on copies of known size"},
         "per_shape": per_shape,
         "hbm_probe_GBps": probe,
     }

@@ -17,7 +17,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libqgemv.so")
+# QGEMV_LIB points the binding at another build of the library (for example
+# a variant compiled for an experiment); default: the in-tree build.
+LIB_PATH = os.environ.get("QGEMV_LIB") or os.path.join(_HERE, "libqgemv.so")
 
 QG_STATUS = {0: "ok", 1: "null pointer", 2: "shape out of range", 3: "misaligned pointer",
              4: "non-finite weight or scale overflow", 5: "buffer too small", 6: "kernel launch failed",
@@ -167,6 +169,30 @@ def _gemv(fn: str, fmt: int, Wp, x, N: int, K: int, y=None):
     yp = _dev(y, torch.float32, "y", M * N)
     _check(fn, getattr(lib(), fn)(wp, xp, yp, M, N, K, _stream()))
     return y
+
+
+class PreparedGemv:
+    """A qgemv_* call validated once, for launch-bound loops: calling it only
+    enqueues the kernel (ctypes call with the stored raw pointers) on the
+    stream that was current when it was prepared.  The tensors must stay
+    alive and unmoved while the object is used."""
+
+    def __init__(self, fmt: int, Wp, x, y, N: int, K: int):
+        torch = _torch()
+        if x.dim() != 2 or x.shape[1] != K or y.shape != (x.shape[0], N):
+            raise ValueError("x must be [M][K] and y [M][N]")
+        self._keep = (Wp, x, y)
+        self._fn = lib().qgemv_q4_0 if fmt == Q4_0 else lib().qgemv_q8_0
+        self._name = "qgemv_q4_0" if fmt == Q4_0 else "qgemv_q8_0"
+        self._args = (_dev(Wp, torch.uint8, "Wp", packed_bytes(fmt, N, K)).value,
+                      _dev(_x16(x), torch.int16, "x", x.shape[0] * K).value,
+                      _dev(y, torch.float32, "y", x.shape[0] * N).value,
+                      int(x.shape[0]), int(N), int(K), _stream().value)
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st:
+            raise QGError(self._name, st)
 
 
 def qgemv_q4_0(Wp, x, N: int, K: int, y=None):

@@ -83,10 +83,16 @@ bool choose_shape(int fmt, int M, int64_t N, int64_t K, int items, int cus, Gemv
         return false;
     int J = static_cast<int>((KB + 64LL * ksplit - 1) / (64LL * ksplit));
     const int rj = (fmt == kQ4_0) ? 8 : 4;   // R * J budget of the kernel table
-    int R = (4 * J <= rj) ? 4 : (2 * J <= rj ? 2 : 1);
-    if (M > 2 && R > 2)
+    // Per-shape choice, from launch sweeps on MI355X (256 CUs): one row per
+    // group for up to 64K rows, two beyond; 8-wave workgroups; about 8, 16 or
+    // 64 teams per CU over the call (more teams than fit at once: the
+    // hardware dispatcher balances the tail better than a persistent loop).
+    int R = (N > 65536) ? 2 : 1;
+    if (M >= 4)
         R = 2;
-    int teams_per_wg = (ksplit == 1) ? 4 : 1;
+    while (R * J > rj && R > 1)
+        R /= 2;
+    int teams_per_wg = (ksplit == 1) ? (N > 65536 ? 4 : 8) : 1;
     if (o_J) {
         J = o_J;
         ksplit = static_cast<int>((KB + 64LL * J - 1) / (64LL * J));
@@ -107,8 +113,8 @@ bool choose_shape(int fmt, int M, int64_t N, int64_t K, int items, int cus, Gemv
     if (teams_per_wg * ksplit > kMaxWavesPerWg)
         teams_per_wg = std::max(1, kMaxWavesPerWg / ksplit);
     const int64_t ngroups = (N + R - 1) / R;
-    // persistent grid: about 8 waves per compute unit over the whole call
-    int64_t teams = std::max<int64_t>(1, static_cast<int64_t>(cus) * 8 / ksplit / std::max(1, items));
+    const int per_cu = (N <= 4096) ? 8 : (N <= 65536 ? 16 : 64);
+    int64_t teams = std::max<int64_t>(1, static_cast<int64_t>(cus) * per_cu / ksplit / std::max(1, items));
     if (o_teams)
         teams = o_teams;
     teams = std::min(teams, ngroups);

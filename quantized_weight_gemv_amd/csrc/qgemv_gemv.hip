@@ -178,6 +178,34 @@ struct Group {
 // entries get a zero scale (and zero activations) in compute_group, so they
 // add nothing.  Each row's base address is wave-uniform (scalar registers);
 // lanes add a 32-bit offset.
+#ifndef QG_NT_LOADS
+#define QG_NT_LOADS 1
+#endif
+
+// Weight bytes are read once per call: they are loaded non-temporal so the
+// stream does not displace the activations from the caches (measured on
+// MI355X: 6.5 TB/s against 6.0 TB/s with plain loads on the 296 MB
+// 128256 x 4096 matrix).
+__device__ __forceinline__ uint4 stream_load16(const uint8_t *p)
+{
+#if QG_NT_LOADS
+    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+    const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+#else
+    return *reinterpret_cast<const uint4 *>(p);
+#endif
+}
+
+__device__ __forceinline__ uint16_t stream_load2(const uint8_t *p)
+{
+#if QG_NT_LOADS
+    return __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(p));
+#else
+    return *reinterpret_cast<const uint16_t *>(p);
+#endif
+}
+
 template <int FMT, int J, int R>
 __device__ __forceinline__ void load_group(Group<FMT, J, R> &g, const uint8_t *__restrict__ W,
                                            const uint16_t *__restrict__ S, int64_t row0, int N, int KB,
@@ -193,12 +221,12 @@ __device__ __forceinline__ void load_group(Group<FMT, J, R> &g, const uint8_t *_
         for (int j = 0; j < J; ++j) {
             // scalar row base + unsigned 32-bit lane offset
             if constexpr (FMT == kQ4_0) {
-                g.code[i][j].c = *reinterpret_cast<const uint4 *>(crow + (uint64_t)(boff[j] * 16u));
+                g.code[i][j].c = stream_load16(crow + (uint64_t)(boff[j] * 16u));
             } else {
-                g.code[i][j].c0 = *reinterpret_cast<const uint4 *>(crow + (uint64_t)(boff[j] * 32u));
-                g.code[i][j].c1 = *reinterpret_cast<const uint4 *>(crow + (uint64_t)(boff[j] * 32u + 16u));
+                g.code[i][j].c0 = stream_load16(crow + (uint64_t)(boff[j] * 32u));
+                g.code[i][j].c1 = stream_load16(crow + (uint64_t)(boff[j] * 32u + 16u));
             }
-            g.scale[i][j] = *reinterpret_cast<const uint16_t *>(srow + (uint64_t)(boff[j] * 2u));
+            g.scale[i][j] = stream_load2(srow + (uint64_t)(boff[j] * 2u));
         }
     }
 }

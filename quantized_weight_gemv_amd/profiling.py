@@ -1,0 +1,127 @@
+"""Turn rocprofv3 CSV output of bench.py runs into the short summaries kept
+under profiles/.
+
+    python -m quantized_weight_gemv_amd.profiling stats <kernel_stats.csv> <kernel_trace.csv> <out.md> <command>
+    python -m quantized_weight_gemv_amd.profiling traffic <fetch_counter_collection.csv>
+           <write_counter_collection.csv> <out.json> <command-fetch> <command-write>
+
+Traffic calibration: the bench's own weight-copy kernels (__amd_rocclr_copyBuffer
+of known sizes, dispatched while it builds its workload) give the factor each
+counter reads per real byte; kernel counters are divided by it.
+"""
+from __future__ import annotations
+
+import csv
+import hashlib
+import json
+import os
+import statistics
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+# the files that determine the GEMV kernel and its launch shapes
+GEMV_SOURCES = ["csrc/qgemv_gemv.hip", "csrc/qgemv_capi.hip", "csrc/qgemv_internal.h"]
+
+LLAMA_SHAPES = [(4096, 4096), (6144, 4096), (14336, 4096), (4096, 14336), (28672, 4096), (128256, 4096)]
+
+
+def gemv_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in GEMV_SOURCES:
+        with open(os.path.join(HERE, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def algorithmic_bytes(N, K, M=1):
+    return N * K // 32 * 18 + 2 * M * K + 4 * M * N
+
+
+def packed_bytes(N, K):
+    nb = N * K // 32
+    s0 = (nb * 16 + 255) // 256 * 256
+    return (s0 + 2 * nb + 255) // 256 * 256
+
+
+def _rows(path, counter):
+    rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    return rows
+
+
+def _copy_sizes():
+    out = []
+    for N, K in LLAMA_SHAPES:
+        nb = packed_bytes(N, K)
+        out += [nb] * max(2, -(-(1 << 30) // nb))
+    return out
+
+
+def traffic(fetch_csv, write_csv, out_json, cmd_f, cmd_w):
+    F = _rows(fetch_csv, "FETCH_SIZE")
+    W = _rows(write_csv, "WRITE_SIZE")
+    sizes = _copy_sizes()
+    cf = [r for r in F if "copyBuffer" in r["Kernel_Name"] and int(r["Grid_Size"]) >= 65536]
+    cw = [r for r in W if "copyBuffer" in r["Kernel_Name"] and int(r["Grid_Size"]) >= 65536]
+    assert len(cf) == len(sizes) == len(cw), (len(cf), len(cw), len(sizes))
+    ff = statistics.median(float(r["Counter_Value"]) * 1024 / nb for r, nb in zip(cf, sizes))
+    fw = statistics.median(float(r["Counter_Value"]) * 1024 / nb for r, nb in zip(cw, sizes))
+    gf = [r for r in F if "gemv_kernel" in r["Kernel_Name"]]
+    gw = [r for r in W if "gemv_kernel" in r["Kernel_Name"]]
+    assert len(gf) == len(gw) and len(gf) % len(LLAMA_SHAPES) == 0
+    per = {}
+    for i, (N, K) in enumerate(LLAMA_SHAPES):
+        fv = [float(r["Counter_Value"]) * 1024 / ff for r in gf[i::len(LLAMA_SHAPES)]]
+        wv = [float(r["Counter_Value"]) * 1024 / fw for r in gw[i::len(LLAMA_SHAPES)]]
+        t = statistics.median(fv) + statistics.median(wv)
+        per[f"{N}x{K}"] = {"fetch_bytes": round(statistics.median(fv)), "write_bytes": round(statistics.median(wv)),
+                           "traffic_bytes": round(t), "algorithmic_bytes": algorithmic_bytes(N, K),
+                           "traffic_over_algorithmic": round(t / algorithmic_bytes(N, K), 4),
+                           "kernel": gf[i]["Kernel_Name"]}
+    total = sum(v["traffic_bytes"] for v in per.values())
+    out = {"what": "HBM traffic of qgemv_q4_0 (M=1) per launch on the Llama-3-8B shapes, from rocprofv3 "
+                   "FETCH_SIZE and WRITE_SIZE (KiB per dispatch) divided by the factor each counter reads for a "
+                   "plain copy of known size",
+           "gemv_source_sha256": gemv_source_hash(),
+           "fetch_factor": round(ff, 5), "write_factor": round(fw, 5),
+           "traffic_bytes_per_step": total,
+           "algorithmic_bytes_per_step": sum(algorithmic_bytes(N, K) for N, K in LLAMA_SHAPES),
+           "per_shape": per, "commands": [cmd_f, cmd_w]}
+    with open(out_json, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def stats(stats_csv, trace_csv, out_md, cmd):
+    rows = list(csv.DictReader(open(stats_csv)))
+    trace = list(csv.DictReader(open(trace_csv)))
+    g = sorted([r for r in trace if "gemv_kernel" in r["Kernel_Name"]], key=lambda r: int(r["Start_Timestamp"]))
+    lines = [f"# rocprofv3 kernel statistics: {os.path.basename(out_md)[:-3]}", "", "Command:", "", "```", cmd, "```",
+             "", "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| `{r['Name'][:70]}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} |")
+    by = {}
+    for r in g:
+        key = (r["Kernel_Name"], r["Grid_Size_X"])
+        by.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    lines += ["", "GEMV dispatches by launch (grid threads): average / median duration", "",
+              "| kernel | grid threads | calls | average us | median us |", "|---|---|---|---|---|"]
+    for (name, grid), v in by.items():
+        lines.append(f"| `{name[:60]}` | {grid} | {len(v)} | {statistics.mean(v) / 1e3:.3f} | "
+                     f"{statistics.median(v) / 1e3:.3f} |")
+    gaps = [int(b["Start_Timestamp"]) - int(a["End_Timestamp"]) for a, b in zip(g, g[1:])]
+    if gaps:
+        lines += ["", f"Gap between consecutive GEMV dispatches: median {statistics.median(gaps) / 1e3:.2f} us "
+                      f"(host launch path included)."]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+if __name__ == "__main__":
+    if sys.argv[1] == "stats":
+        stats(*sys.argv[2:6])
+    elif sys.argv[1] == "traffic":
+        traffic(*sys.argv[2:7])
+    else:
+        raise SystemExit(__doc__)
