@@ -66,10 +66,11 @@ inline int64_t scale_offset(int fmt, int64_t N, int64_t K)
 struct GemvShape {
     int J, R, ksplit, teams_per_wg;
     int64_t teams;   // teams per batch item
+    bool xl;         // one token: activations staged in LDS, not registers
 };
 
 // Caller-set override for tuning sweeps (thread-local, zeros = heuristic).
-thread_local int o_J = 0, o_R = 0, o_ksplit = 0, o_teams_per_wg = 0;
+thread_local int o_J = 0, o_R = 0, o_ksplit = 0, o_teams_per_wg = 0, o_xl = -1;
 thread_local int64_t o_teams = 0;
 
 bool choose_shape(int fmt, int M, int64_t N, int64_t K, int items, int cus, GemvShape &s)
@@ -77,7 +78,11 @@ bool choose_shape(int fmt, int M, int64_t N, int64_t K, int items, int cus, Gemv
     const int64_t KB = K / 32;
     // resident activations: J * M <= 8 blocks per lane; Q8_0 code words are
     // twice as wide, so it keeps J <= 4
-    const int jmax = std::min(8 / M, fmt == kQ4_0 ? 7 : 4);
+    // one token with long rows: activations staged in LDS (no register cost)
+    bool xl = (M == 1 && fmt == kQ4_0 && KB > 256 && KB <= 512);
+    if (o_xl >= 0)
+        xl = (o_xl == 1);
+    const int jmax = xl ? 8 : std::min(8 / M, fmt == kQ4_0 ? 7 : 4);
     int ksplit = static_cast<int>((KB + 64 * jmax - 1) / (64 * jmax));
     if (ksplit > kMaxWavesPerWg)
         return false;
@@ -108,6 +113,8 @@ bool choose_shape(int fmt, int M, int64_t N, int64_t K, int items, int cus, Gemv
         R = o_R;
     if (o_teams_per_wg)
         teams_per_wg = o_teams_per_wg;
+    if (xl && (ksplit > 1 || M != 1 || KB > 1023))
+        return false;
     if (ksplit > 1)
         teams_per_wg = 1;   // a workgroup's waves must walk the same row groups
     if (teams_per_wg * ksplit > kMaxWavesPerWg)
@@ -118,7 +125,7 @@ bool choose_shape(int fmt, int M, int64_t N, int64_t K, int items, int cus, Gemv
     if (o_teams)
         teams = o_teams;
     teams = std::min(teams, ngroups);
-    s = GemvShape{J, R, ksplit, teams_per_wg, teams};
+    s = GemvShape{J, R, ksplit, teams_per_wg, teams, xl};
     return true;
 }
 
@@ -153,7 +160,7 @@ qg_status run_gemv(int fmt, const void *Wp, const int32_t *idx, int64_t P, const
     const int64_t wgs = (s.teams + s.teams_per_wg - 1) / s.teams_per_wg;
     dim3 grid(static_cast<unsigned>(wgs), static_cast<unsigned>(items), 1);
     dim3 block(64 * s.ksplit * s.teams_per_wg, 1, 1);
-    hipError_t e = launch_gemv(fmt, M, s.J, s.R, p, grid, block, static_cast<hipStream_t>(stream));
+    hipError_t e = launch_gemv(fmt, M, s.J, s.R, s.xl, p, grid, block, static_cast<hipStream_t>(stream));
     if (e == hipErrorInvalidValue)
         return QG_ERR_SHAPE;
     return e == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
@@ -302,11 +309,13 @@ qg_status qg_device_cus(int device, int *cus)
 }
 
 // Tuning knob for launch-shape sweeps: fixes J (blocks per lane), R (rows per
-// group), ksplit (waves along K), teams per workgroup and total teams for the
-// GEMV / MoE calls made afterwards from the calling thread.  Zero keeps the
-// built-in choice for that field.
-void qg_set_gemv_shape(int J, int R, int ksplit, int teams_per_wg, int64_t teams)
+// group), ksplit (waves along K), teams per workgroup, total teams and the
+// activation staging (xl: -1 built-in, 0 registers, 1 LDS) for the GEMV / MoE
+// calls made afterwards from the calling thread.  Zero keeps the built-in
+// choice for the other fields.
+void qg_set_gemv_shape(int J, int R, int ksplit, int teams_per_wg, int64_t teams, int xl)
 {
+    qg::o_xl = xl;
     qg::o_J = J;
     qg::o_R = R;
     qg::o_ksplit = ksplit;

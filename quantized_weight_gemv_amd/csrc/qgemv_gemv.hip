@@ -231,9 +231,14 @@ __device__ __forceinline__ void load_group(Group<FMT, J, R> &g, const uint8_t *_
     }
 }
 
-template <int FMT, int M, int J, int R>
-__device__ __forceinline__ void compute_group(const Group<FMT, J, R> &g, const uint32_t (&X)[M][J][16],
-                                              const bool (&ok)[J], int64_t row0, int N, float (&acc)[R][M])
+// Activations come either from registers (X, loaded once per team) or, with
+// XL, from the workgroup's LDS copy (one token; xs holds every block of x in
+// pair order plus one zero block that padding lanes read).
+template <int FMT, int M, int J, int R, bool XL>
+__device__ __forceinline__ void compute_group(const Group<FMT, J, R> &g,
+                                              const uint32_t (&X)[XL ? 1 : M][XL ? 1 : J][16],
+                                              const uint4 *xs, const uint32_t (&xoff)[J], const bool (&ok)[J],
+                                              int64_t row0, int N, float (&acc)[R][M])
 {
 #pragma unroll
     for (int i = 0; i < R; ++i) {
@@ -252,11 +257,27 @@ __device__ __forceinline__ void compute_group(const Group<FMT, J, R> &g, const u
             const float d = (float)dh;
 #pragma unroll
             for (int m = 0; m < M; ++m) {
+                uint32_t xw[16];
+                if constexpr (XL) {
+                    const uint4 *q = xs + xoff[j] * 4;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const uint4 t = q[u];
+                        xw[4 * u + 0] = t.x;
+                        xw[4 * u + 1] = t.y;
+                        xw[4 * u + 2] = t.z;
+                        xw[4 * u + 3] = t.w;
+                    }
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 16; ++t)
+                        xw[t] = X[m][j][t];
+                }
                 float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
                 for (int t = 0; t < 16; t += 2) {
-                    s0 = dot2(v[t], as_h2(X[m][j][t]), s0);
-                    s1 = dot2(v[t + 1], as_h2(X[m][j][t + 1]), s1);
+                    s0 = dot2(v[t], as_h2(xw[t]), s0);
+                    s1 = dot2(v[t + 1], as_h2(xw[t + 1]), s1);
                 }
                 acc[i][m] = __builtin_fmaf(d, s0 + s1, acc[i][m]);
             }
@@ -309,9 +330,10 @@ __device__ __forceinline__ void finish_group(const float (&acc)[R][M], float *__
     }
 }
 
-template <int FMT, int M, int J, int R>
+template <int FMT, int M, int J, int R, bool XL>
 __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
 {
+    static_assert(!XL || M == 1, "LDS-staged activations are for one token");
     const int lane = threadIdx.x & 63;
     // wave-uniform: everything derived from it (rows, addresses) stays scalar
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -331,13 +353,14 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
     const int KB = p.K >> 5;
     const int bbeg = kw * 64 * J;
     const int bend = min(KB, bbeg + 64 * J);
-    uint32_t blk[J];
+    uint32_t blk[J], xoff[J];
     bool ok[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
         const int b = bbeg + lane + 64 * j;
         ok[j] = b < bend;
         blk[j] = (uint32_t)(ok[j] ? b : bend - 1);
+        xoff[j] = (uint32_t)(ok[j] ? b : KB);   // LDS block KB is all zeros
     }
 
     const int64_t ngroups = ((int64_t)p.N + R - 1) / R;
@@ -348,18 +371,37 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
         load_group<FMT, J, R>(ga, W, S, g * R, p.N, KB, blk);
 
     // activations of this lane's blocks, all M tokens, kept for every row
-    uint32_t X[M][J][16];
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-#pragma unroll
-        for (int j = 0; j < J; ++j) {
-            load_x_block<FMT>(x + (int64_t)m * p.K + (int64_t)blk[j] * 32, X[m][j]);
-            if (!ok[j]) {
+    uint32_t X[XL ? 1 : M][XL ? 1 : J][16];
+    extern __shared__ uint4 xs_dyn[];
+    if constexpr (XL) {
+        // the workgroup stages x once, in pair order, plus a zero block
+        for (int b = threadIdx.x; b <= KB; b += blockDim.x) {
+            uint32_t w16[16];
+            if (b < KB) {
+                load_x_block<FMT>(x + (int64_t)b * 32, w16);
+            } else {
 #pragma unroll
                 for (int t = 0; t < 16; ++t)
-                    X[m][j][t] = 0u;
+                    w16[t] = 0u;
             }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                xs_dyn[b * 4 + u] = make_uint4(w16[4 * u], w16[4 * u + 1], w16[4 * u + 2], w16[4 * u + 3]);
         }
+        __syncthreads();
+    } else {
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                load_x_block<FMT>(x + (int64_t)m * p.K + (int64_t)blk[j] * 32, X[m][j]);
+                if (!ok[j]) {
+#pragma unroll
+                    for (int t = 0; t < 16; ++t)
+                        X[m][j][t] = 0u;
+                }
+            }
+    }
 
     __shared__ float red[2][kMaxWavesPerWg][kMaxRM];
     int buf = 0;
@@ -371,7 +413,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
         int64_t gn = g + teams_total;
         if (gn < ngroups)
             load_group<FMT, J, R>(gb, W, S, gn * R, p.N, KB, blk);
-        compute_group<FMT, M, J, R>(ga, X, ok, g * R, p.N, acc);
+        compute_group<FMT, M, J, R, XL>(ga, X, xs_dyn, xoff, ok, g * R, p.N, acc);
         finish_group<M, R>(acc, y, g * R, p.N, lane, wave, team, kw, p.ksplit, red, buf);
         g = gn;
         if (g >= ngroups)
@@ -379,7 +421,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
         gn = g + teams_total;
         if (gn < ngroups)
             load_group<FMT, J, R>(ga, W, S, gn * R, p.N, KB, blk);
-        compute_group<FMT, M, J, R>(gb, X, ok, g * R, p.N, acc);
+        compute_group<FMT, M, J, R, XL>(gb, X, xs_dyn, xoff, ok, g * R, p.N, acc);
         finish_group<M, R>(acc, y, g * R, p.N, lane, wave, team, kw, p.ksplit, red, buf);
         g = gn;
     }
@@ -387,77 +429,89 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
 
 // ---------------------------------------------------------------- dispatch
 
-template <int FMT, int M, int J, int R>
-static hipError_t launch_one(const GemvParams &p, dim3 grid, dim3 block, hipStream_t stream)
+template <int FMT, int M, int J, int R, bool XL>
+static hipError_t launch_one(const GemvParams &p, dim3 grid, dim3 block, size_t shmem, hipStream_t stream)
 {
-    return launch_kernel(reinterpret_cast<const void *>(&gemv_kernel<FMT, M, J, R>), grid, block, 0, stream, p);
+    return launch_kernel(reinterpret_cast<const void *>(&gemv_kernel<FMT, M, J, R, XL>), grid, block, shmem, stream,
+                         p);
 }
 
-// Register budget: R * J code words in flight twice (ping-pong) plus J * M
-// resident activation blocks.  R * J <= 8 (Q4_0) / 4 (Q8_0) and J <= 7 keep
-// every instantiation within 256 registers without spilling.
-template <int FMT, int J, int R>
-constexpr bool fits() { return R * J <= (FMT == kQ4_0 ? 8 : 4) && J <= 7; }
+// Register budget: R * J code words in flight twice (ping-pong) plus, without
+// XL, J * M resident activation blocks.  R * J <= 8 (Q4_0) / 4 (Q8_0) and
+// J <= 7 (8 with XL) keep every instantiation within 256 registers without
+// spilling.
+template <int FMT, int J, int R, bool XL>
+constexpr bool fits() { return R * J <= (FMT == kQ4_0 ? 8 : 4) && J <= (XL ? 8 : 7); }
 
-template <int FMT, int M, int J>
-static hipError_t launch_r(int R, const GemvParams &p, dim3 grid, dim3 block, hipStream_t stream)
+template <int FMT, int M, int J, bool XL>
+static hipError_t launch_r(int R, const GemvParams &p, dim3 grid, dim3 block, size_t shmem, hipStream_t stream)
 {
-    if constexpr (fits<FMT, J, 1>())
-        if (R == 1) return launch_one<FMT, M, J, 1>(p, grid, block, stream);
-    if constexpr (fits<FMT, J, 2>())
-        if (R == 2) return launch_one<FMT, M, J, 2>(p, grid, block, stream);
-    if constexpr (fits<FMT, J, 4>())
-        if (R == 4) return launch_one<FMT, M, J, 4>(p, grid, block, stream);
+    if constexpr (fits<FMT, J, 1, XL>())
+        if (R == 1) return launch_one<FMT, M, J, 1, XL>(p, grid, block, shmem, stream);
+    if constexpr (fits<FMT, J, 2, XL>())
+        if (R == 2) return launch_one<FMT, M, J, 2, XL>(p, grid, block, shmem, stream);
+    if constexpr (fits<FMT, J, 4, XL>())
+        if (R == 4) return launch_one<FMT, M, J, 4, XL>(p, grid, block, shmem, stream);
     return hipErrorInvalidValue;
 }
 
-template <int FMT, int M>
-static hipError_t launch_j(int J, int R, const GemvParams &p, dim3 grid, dim3 block, hipStream_t stream)
+template <int FMT, int M, bool XL>
+static hipError_t launch_j(int J, int R, const GemvParams &p, dim3 grid, dim3 block, size_t shmem,
+                           hipStream_t stream)
 {
-    // J * M <= 8 keeps the resident activations at <= 128 registers
+    // J * M <= 8 keeps resident activations at <= 128 registers
     if constexpr (M == 1) {
         switch (J) {
-        case 1: return launch_r<FMT, 1, 1>(R, p, grid, block, stream);
-        case 2: return launch_r<FMT, 1, 2>(R, p, grid, block, stream);
-        case 3: return launch_r<FMT, 1, 3>(R, p, grid, block, stream);
-        case 4: return launch_r<FMT, 1, 4>(R, p, grid, block, stream);
-        case 5: return launch_r<FMT, 1, 5>(R, p, grid, block, stream);
-        case 6: return launch_r<FMT, 1, 6>(R, p, grid, block, stream);
-        case 7: return launch_r<FMT, 1, 7>(R, p, grid, block, stream);
-        case 8: return launch_r<FMT, 1, 8>(R, p, grid, block, stream);
+        case 1: return launch_r<FMT, 1, 1, XL>(R, p, grid, block, shmem, stream);
+        case 2: return launch_r<FMT, 1, 2, XL>(R, p, grid, block, shmem, stream);
+        case 3: return launch_r<FMT, 1, 3, XL>(R, p, grid, block, shmem, stream);
+        case 4: return launch_r<FMT, 1, 4, XL>(R, p, grid, block, shmem, stream);
+        case 5: return launch_r<FMT, 1, 5, XL>(R, p, grid, block, shmem, stream);
+        case 6: return launch_r<FMT, 1, 6, XL>(R, p, grid, block, shmem, stream);
+        case 7: return launch_r<FMT, 1, 7, XL>(R, p, grid, block, shmem, stream);
+        case 8: return launch_r<FMT, 1, 8, XL>(R, p, grid, block, shmem, stream);
         }
     } else if constexpr (M == 2) {
         switch (J) {
-        case 1: return launch_r<FMT, 2, 1>(R, p, grid, block, stream);
-        case 2: return launch_r<FMT, 2, 2>(R, p, grid, block, stream);
-        case 3: return launch_r<FMT, 2, 3>(R, p, grid, block, stream);
-        case 4: return launch_r<FMT, 2, 4>(R, p, grid, block, stream);
+        case 1: return launch_r<FMT, 2, 1, false>(R, p, grid, block, shmem, stream);
+        case 2: return launch_r<FMT, 2, 2, false>(R, p, grid, block, shmem, stream);
+        case 3: return launch_r<FMT, 2, 3, false>(R, p, grid, block, shmem, stream);
+        case 4: return launch_r<FMT, 2, 4, false>(R, p, grid, block, shmem, stream);
         }
     } else if constexpr (M <= 4) {
         switch (J) {
-        case 1: return launch_r<FMT, M, 1>(R, p, grid, block, stream);
-        case 2: return launch_r<FMT, M, 2>(R, p, grid, block, stream);
+        case 1: return launch_r<FMT, M, 1, false>(R, p, grid, block, shmem, stream);
+        case 2: return launch_r<FMT, M, 2, false>(R, p, grid, block, shmem, stream);
         }
     } else {
         if (J == 1)
-            return launch_r<FMT, M, 1>(R, p, grid, block, stream);
+            return launch_r<FMT, M, 1, false>(R, p, grid, block, shmem, stream);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemv(int fmt, int M, int J, int R, const GemvParams &p, dim3 grid, dim3 block,
+hipError_t launch_gemv(int fmt, int M, int J, int R, bool xl, const GemvParams &p, dim3 grid, dim3 block,
                        hipStream_t stream)
 {
-#define QG_CASE_M(FMT)                                                        \
-    switch (M) {                                                              \
-    case 1: return launch_j<FMT, 1>(J, R, p, grid, block, stream);            \
-    case 2: return launch_j<FMT, 2>(J, R, p, grid, block, stream);            \
-    case 3: return launch_j<FMT, 3>(J, R, p, grid, block, stream);            \
-    case 4: return launch_j<FMT, 4>(J, R, p, grid, block, stream);            \
-    case 5: return launch_j<FMT, 5>(J, R, p, grid, block, stream);            \
-    case 6: return launch_j<FMT, 6>(J, R, p, grid, block, stream);            \
-    case 7: return launch_j<FMT, 7>(J, R, p, grid, block, stream);            \
-    case 8: return launch_j<FMT, 8>(J, R, p, grid, block, stream);            \
+    // XL: one token, one wave per row group, activations staged in LDS
+    // (K/32 blocks of 64 bytes plus one zero block)
+    const size_t shmem = xl ? (size_t)(p.K / 32 + 1) * 64 : 0;
+    if (xl) {
+        if (M != 1 || p.ksplit != 1)
+            return hipErrorInvalidValue;
+        return fmt == kQ4_0 ? launch_j<kQ4_0, 1, true>(J, R, p, grid, block, shmem, stream)
+                            : launch_j<kQ8_0, 1, true>(J, R, p, grid, block, shmem, stream);
+    }
+#define QG_CASE_M(FMT)                                                                \
+    switch (M) {                                                                      \
+    case 1: return launch_j<FMT, 1, false>(J, R, p, grid, block, 0, stream);          \
+    case 2: return launch_j<FMT, 2, false>(J, R, p, grid, block, 0, stream);          \
+    case 3: return launch_j<FMT, 3, false>(J, R, p, grid, block, 0, stream);          \
+    case 4: return launch_j<FMT, 4, false>(J, R, p, grid, block, 0, stream);          \
+    case 5: return launch_j<FMT, 5, false>(J, R, p, grid, block, 0, stream);          \
+    case 6: return launch_j<FMT, 6, false>(J, R, p, grid, block, 0, stream);          \
+    case 7: return launch_j<FMT, 7, false>(J, R, p, grid, block, 0, stream);          \
+    case 8: return launch_j<FMT, 8, false>(J, R, p, grid, block, 0, stream);          \
     }
     if (fmt == kQ4_0) {
         QG_CASE_M(kQ4_0)

@@ -42,7 +42,7 @@ inline hipError_t launch_kernel(const void *fn, dim3 grid, dim3 block, size_t sh
     return launch_raw(fn, grid, block, a, shmem, stream);
 }
 
-hipError_t launch_gemv(int fmt, int M, int J, int R, const GemvParams &p, dim3 grid, dim3 block,
+hipError_t launch_gemv(int fmt, int M, int J, int R, bool xl, const GemvParams &p, dim3 grid, dim3 block,
                        hipStream_t stream);
 
 }  // namespace qg

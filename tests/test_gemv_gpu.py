@@ -238,3 +238,33 @@ def test_outputs_stay_in_bounds():
             (q.qgemv_q4_0 if fmt == Q4_0 else q.qgemv_q8_0)(to_dev(pb), x, N, K, y)
             torch.cuda.synchronize()
             assert (buf[:64] == 7.0).all() and (buf[64 + M * N:] == 7.0).all()
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FNAME[f])
+@pytest.mark.parametrize("N,K,M", [(257, 4096, 1), (100, 14336, 1), (33, 2560, 1), (70, 6144, 2), (130, 2048, 8)])
+def test_gemv_every_launch_shape(fmt, N, K, M):
+    """Parity for the launch shapes the tuning knob can select (rows per
+    group, teams, workgroup size, K split, LDS-staged activations)."""
+    q = qg()
+    w = weights(N, K, seed=N)
+    x = acts(M, K, seed=K)
+    pb, po = pack_both(fmt, w)
+    Wd, xd = to_dev(pb), to_dev(x)
+    y_ref, s = oracle.get().gemv(fmt, po, N, K, x)
+    tried = 0
+    try:
+        for R in (1, 2, 4):
+            for tpw in (1, 2, 8):
+                for teams in (1, 7, 100000):
+                    for ks in (0, 2, 3):
+                        for xl in (-1, 0, 1):
+                            q.qg_set_gemv_shape(0, R, ks, tpw, teams, xl)
+                            try:
+                                y = _gemv(fmt, Wd, xd, N, K)
+                            except q.QGError:
+                                continue
+                            tried += 1
+                            assert_within(y, y_ref, s, f"R{R} tpw{tpw} teams{teams} ks{ks} xl{xl}")
+    finally:
+        q.qg_set_gemv_shape(0, 0, 0, 0, 0, -1)
+    assert tried >= 10
