@@ -149,12 +149,13 @@ qg_status qg_device_cus(int device, int *cus);
 /* Tuning knob for launch-shape sweeps of qgemv_* / qmoe_gemv_q4_0: fixes J
  * (blocks per lane per row, J * M <= 8), R (rows per group: 1, 2 or 4),
  * ksplit (waves sharing a row along K), teams per workgroup, the total
- * number of teams, and xl (activations of a one-token call staged in LDS: 1,
- * kept in registers: 0, built-in choice: -1) for later calls from the calling
- * thread.  A zero (or -1 for xl) keeps the built-in per-shape choice for that
- * field.  An impossible combination makes the later calls return
- * QG_ERR_SHAPE. */
-void qg_set_gemv_shape(int J, int R, int ksplit, int teams_per_wg, int64_t teams, int xl);
+ * number of teams, xl (activations of a one-token call staged in LDS: 1,
+ * kept in registers: 0) and engine (vector-ALU kernel: 0; matrix-core kernel
+ * for 2..8 tokens and rows of at most 256 blocks: 1, where ksplit is its
+ * number of waves along K) for later calls from the calling thread.  A zero
+ * (-1 for xl and engine) keeps the built-in per-shape choice for that field.
+ * An impossible combination makes the later calls return QG_ERR_SHAPE. */
+void qg_set_gemv_shape(int J, int R, int ksplit, int teams_per_wg, int64_t teams, int xl, int engine);
 
 /* Memory-bandwidth probe: a streaming 16-byte read of `bytes` (rounded down
  * to a multiple of 16) of device memory at `buf` by `wgs` workgroups of 256

@@ -70,7 +70,7 @@ struct GemvShape {
 };
 
 // Caller-set override for tuning sweeps (thread-local, zeros = heuristic).
-thread_local int o_J = 0, o_R = 0, o_ksplit = 0, o_teams_per_wg = 0, o_xl = -1;
+thread_local int o_J = 0, o_R = 0, o_ksplit = 0, o_teams_per_wg = 0, o_xl = -1, o_engine = -1;
 thread_local int64_t o_teams = 0;
 
 bool choose_shape(int fmt, int M, int64_t N, int64_t K, int items, int cus, GemvShape &s)
@@ -142,6 +142,27 @@ qg_status run_gemv(int fmt, const void *Wp, const int32_t *idx, int64_t P, const
     const int cus = device_cus();
     if (cus <= 0)
         return QG_ERR_DEVICE;
+    // Four or more tokens (plain GEMV, rows up to 256 blocks long): the
+    // matrix-core kernel, whose unpack cost per block does not grow with M
+    // (measured on MI355X: 6144 x 2048 at 8 tokens 7.1 us against 15.3 us on
+    // the vector path; at 2 tokens the vector path is faster, 4.8 vs 6.4 us).
+    const int64_t KB = K / 32;
+    bool mfma = (idx == nullptr && M >= 4 && KB <= 256);
+    if (o_engine >= 0)
+        mfma = (o_engine == 1);
+    if (mfma) {
+        if (idx != nullptr || KB > 256 || N > INT32_MAX)
+            return QG_ERR_SHAPE;
+        int waves = static_cast<int>(std::min<int64_t>(8, std::max<int64_t>(1, (KB + 7) / 8)));
+        if (o_ksplit)
+            waves = o_ksplit;
+        hipError_t e = launch_gemv_mfma(fmt, static_cast<const uint8_t *>(Wp), scale_offset(fmt, N, K), x, y, M,
+                                        static_cast<int>(N), static_cast<int>(K), waves,
+                                        static_cast<hipStream_t>(stream));
+        if (e == hipErrorInvalidValue)
+            return QG_ERR_SHAPE;
+        return e == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
+    }
     GemvShape s;
     if (!choose_shape(fmt, M, N, K, items, cus, s))
         return QG_ERR_SHAPE;
@@ -310,12 +331,14 @@ qg_status qg_device_cus(int device, int *cus)
 
 // Tuning knob for launch-shape sweeps: fixes J (blocks per lane), R (rows per
 // group), ksplit (waves along K), teams per workgroup, total teams and the
-// activation staging (xl: -1 built-in, 0 registers, 1 LDS) for the GEMV / MoE
-// calls made afterwards from the calling thread.  Zero keeps the built-in
-// choice for the other fields.
-void qg_set_gemv_shape(int J, int R, int ksplit, int teams_per_wg, int64_t teams, int xl)
+// activation staging (xl: -1 built-in, 0 registers, 1 LDS) and the engine
+// (-1 built-in, 0 vector ALU, 1 matrix cores; with the matrix cores ksplit is
+// the number of waves along K) for the GEMV / MoE calls made afterwards from
+// the calling thread.  Zero keeps the built-in choice for the other fields.
+void qg_set_gemv_shape(int J, int R, int ksplit, int teams_per_wg, int64_t teams, int xl, int engine)
 {
     qg::o_xl = xl;
+    qg::o_engine = engine;
     qg::o_J = J;
     qg::o_R = R;
     qg::o_ksplit = ksplit;

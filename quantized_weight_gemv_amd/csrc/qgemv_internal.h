@@ -45,4 +45,8 @@ inline hipError_t launch_kernel(const void *fn, dim3 grid, dim3 block, size_t sh
 hipError_t launch_gemv(int fmt, int M, int J, int R, bool xl, const GemvParams &p, dim3 grid, dim3 block,
                        hipStream_t stream);
 
+// Few-token GEMV on the matrix cores (qgemv_mfma.hip): `waves` waves split K.
+hipError_t launch_gemv_mfma(int fmt, const uint8_t *W, int64_t scale_offset, const uint16_t *x, float *y, int M,
+                            int N, int K, int waves, hipStream_t stream);
+
 }  // namespace qg

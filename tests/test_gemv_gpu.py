@@ -258,7 +258,7 @@ def test_gemv_every_launch_shape(fmt, N, K, M):
                 for teams in (1, 7, 100000):
                     for ks in (0, 2, 3):
                         for xl in (-1, 0, 1):
-                            q.qg_set_gemv_shape(0, R, ks, tpw, teams, xl)
+                            q.qg_set_gemv_shape(0, R, ks, tpw, teams, xl, 0)
                             try:
                                 y = _gemv(fmt, Wd, xd, N, K)
                             except q.QGError:
@@ -266,5 +266,42 @@ def test_gemv_every_launch_shape(fmt, N, K, M):
                             tried += 1
                             assert_within(y, y_ref, s, f"R{R} tpw{tpw} teams{teams} ks{ks} xl{xl}")
     finally:
-        q.qg_set_gemv_shape(0, 0, 0, 0, 0, -1)
+        q.qg_set_gemv_shape(0, 0, 0, 0, 0, -1, -1)
     assert tried >= 10
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FNAME[f])
+@pytest.mark.parametrize("N,K,M", [(17, 32, 2), (257, 4096, 8), (100, 2560, 3), (33, 6144, 5), (130, 8192, 1),
+                                   (64, 96, 8), (4099, 2048, 2)])
+def test_gemv_matrix_core_engine(fmt, N, K, M):
+    """The matrix-core few-token kernel, every wave count along K, against the
+    oracle; one-hot columns stay exact on it (exact (q-8) operands, scale
+    applied in fp32)."""
+    q = qg()
+    w = weights(N, K, seed=N + 1)
+    x = acts(M, K, seed=K + 1)
+    pb, po = pack_both(fmt, w)
+    Wd, xd = to_dev(pb), to_dev(x)
+    y_ref, s = oracle.get().gemv(fmt, po, N, K, x)
+    tried = 0
+    try:
+        for ks in (0, 1, 2, 3, 4, 6, 7, 8):
+            q.qg_set_gemv_shape(0, 0, ks, 0, 0, -1, 1)
+            try:
+                y = _gemv(fmt, Wd, xd, N, K)
+            except q.QGError:
+                continue
+            tried += 1
+            assert_within(y, y_ref, s, f"mfma waves={ks}")
+        q.qg_set_gemv_shape(0, 0, 0, 0, 0, -1, 1)
+        cols = [0, 5, 16, 31, K - 1]
+        xo = np.zeros((len(cols), K), np.float16)
+        for i, k in enumerate(cols):
+            xo[i, k] = 1.0
+        y = _gemv(fmt, Wd, to_dev(xo), N, K)
+        wh = oracle.get().dequant(fmt, po, N, K, "f32")
+        for i, k in enumerate(cols):
+            assert np.array_equal(y[i], wh[:, k]), f"one-hot column {k}"
+    finally:
+        q.qg_set_gemv_shape(0, 0, 0, 0, 0, -1, -1)
+    assert tried >= 2   # long rows admit only the larger wave counts (<= 32 blocks per wave)
