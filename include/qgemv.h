@@ -157,6 +157,12 @@ qg_status qg_device_cus(int device, int *cus);
  * An impossible combination makes the later calls return QG_ERR_SHAPE. */
 void qg_set_gemv_shape(int J, int R, int ksplit, int teams_per_wg, int64_t teams, int xl, int engine);
 
+/* Tuning knob for sweeps of qgemm_q4_0_prefill: fixes the number of
+ * workgroups sharing one output tile along K (splits; more than one adds fp32
+ * partial tiles atomically into a zero-filled Y) and the token tile (bm: 64 or
+ * 128) for later calls from the calling thread.  0 keeps the built-in choice. */
+void qg_set_prefill_shape(int splits, int bm);
+
 /* Memory-bandwidth probe: a streaming 16-byte read of `bytes` (rounded down
  * to a multiple of 16) of device memory at `buf` by `wgs` workgroups of 256
  * threads; workgroup g writes one word to sink[g] (device, >= wgs words) so

@@ -68,6 +68,7 @@ def lib() -> ctypes.CDLL:
         "qg_device_cus": (c_int, [c_int, ctypes.POINTER(c_int)]),
         "qg_set_gemv_shape": (None, [c_int, c_int, c_int, c_int, i64, c_int, c_int]),
         "qg_read_probe": (c_int, [vp, sz, vp, c_int, vp]),
+        "qg_set_prefill_shape": (None, [c_int, c_int]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -80,7 +81,7 @@ def lib() -> ctypes.CDLL:
 def exported_symbols() -> list[str]:
     return ["qg_status_str", "qpacked_bytes_q4_0", "qpacked_bytes_q8_0", "qquantize_q4_0", "qquantize_q8_0",
             "qgemv_q4_0", "qgemv_q8_0", "qmoe_gemv_q4_0", "qgemm_q4_0_prefill", "qdequant_q4_0",
-            "qdequant_q8_0", "qg_time_next_launch", "qg_device_cus", "qg_set_gemv_shape", "qg_read_probe"]
+            "qdequant_q8_0", "qg_time_next_launch", "qg_device_cus", "qg_set_gemv_shape", "qg_read_probe", "qg_set_prefill_shape"]
 
 
 def _check(fn: str, st: int):
@@ -267,6 +268,10 @@ def qg_read_probe(buf, sink, wgs: int):
     bp = _dev(buf, torch.uint8, "buf")
     sp = _dev(sink, torch.int32, "sink", wgs)
     _check("qg_read_probe", lib().qg_read_probe(bp, buf.numel(), sp, wgs, _stream()))
+
+
+def qg_set_prefill_shape(splits: int = 0, bm: int = 0):
+    lib().qg_set_prefill_shape(splits, bm)
 
 
 def qg_device_cus(device: int = 0) -> int:

@@ -10,9 +10,9 @@
 // tile to shared memory, then matrix-core multiply) and "Stage 3" (unpack
 // inside the multiply instead of dequantize-to-fp16 followed by a dense GEMM)].
 //
-// Pipeline per 64-wide K step: the global loads of step s+1 are issued into
-// registers before the MFMAs of step s run out of the other LDS buffer, so one
-// barrier per step suffices.  Both tiles are stored in the same permuted
+// Pipeline per 64-wide K step: the global loads of the next three steps are in
+// flight in registers; the MFMAs of step s run out of one of two LDS buffers
+// while the next step is dequantized into the other, one barrier per step.  Both tiles are stored in the same permuted
 // k order within each 32-element block (the order the nibble unpack produces),
 // which leaves the contraction unchanged.  When the output tiles are too few
 // to occupy the chip, K is split across workgroups that add their partial
@@ -33,6 +33,7 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f16x_t __attribute__((ext_vector_type(16)));
 
 constexpr int kBK = 64;          // K per pipeline step: two Q4_0 blocks
+constexpr int kDepth = 3;        // K steps of global loads in flight
 constexpr int kLdsStride = 72;   // halves per LDS tile row: 64 + 8 padding
 
 __device__ __forceinline__ h2_t as_h2(uint32_t u) { return __builtin_bit_cast(h2_t, u); }
@@ -210,31 +211,54 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p)
             for (int r = 0; r < 16; ++r)
                 acc[i][j][r] = 0.0f;
 
-    Stage<BM, BN> st;
-    if (s_beg < s_end)
-        load_stage<BM, BN>(st, p, m0, n0, s_beg);
+    // A ring of kDepth register stages keeps the global loads of the next
+    // kDepth K steps in flight.  Each iteration first issues the MFMAs of
+    // step s (reading LDS buffer s & 1), then unpacks and stores step s + 1
+    // into the other buffer, so the vector-ALU dequantization runs while the
+    // matrix cores work; one barrier per step.  The buffer written in
+    // iteration s was last read in iteration s - 1, before its barrier.
+    Stage<BM, BN> st[kDepth];
+#pragma unroll
+    for (int q = 0; q < kDepth; ++q)
+        if (s_beg + q < s_end)
+            load_stage<BM, BN>(st[q], p, m0, n0, s_beg + q);
+    if (s_beg < s_end) {
+        store_stage<BM, BN>(st[0], p, m0, n0, s_beg, Xs[0], Ws[0]);
+        if (s_beg + kDepth < s_end)
+            load_stage<BM, BN>(st[0], p, m0, n0, s_beg + kDepth);
+    }
+    __syncthreads();
 
-    for (int s = s_beg; s < s_end; ++s) {
-        const int buf = (s - s_beg) & 1;
-        store_stage<BM, BN>(st, p, m0, n0, s, Xs[buf], Ws[buf]);
-        __syncthreads();
-        if (s + 1 < s_end)
-            load_stage<BM, BN>(st, p, m0, n0, s + 1);
+    for (int s0 = s_beg; s0 < s_end; s0 += kDepth) {
 #pragma unroll
-        for (int kk = 0; kk < kBK / 16; ++kk) {
-            const int col = kk * 16 + (lane >> 5) * 8;
-            half8_t a[TM], b[TN];
+        for (int q = 0; q < kDepth; ++q) {
+            const int s = s0 + q;
+            if (s < s_end) {
+                const int buf = (s - s_beg) & 1;
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
-                a[i] = *reinterpret_cast<const half8_t *>(&Xs[buf][wm * (BM / 2) + 32 * i + (lane & 31)][col]);
+                for (int kk = 0; kk < kBK / 16; ++kk) {
+                    const int col = kk * 16 + (lane >> 5) * 8;
+                    half8_t a[TM], b[TN];
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-                b[j] = *reinterpret_cast<const half8_t *>(&Ws[buf][wn * (BN / 2) + 32 * j + (lane & 31)][col]);
+                    for (int i = 0; i < TM; ++i)
+                        a[i] = *reinterpret_cast<const half8_t *>(&Xs[buf][wm * (BM / 2) + 32 * i + (lane & 31)][col]);
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
+                    for (int j = 0; j < TN; ++j)
+                        b[j] = *reinterpret_cast<const half8_t *>(&Ws[buf][wn * (BN / 2) + 32 * j + (lane & 31)][col]);
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+                    for (int i = 0; i < TM; ++i)
+#pragma unroll
+                        for (int j = 0; j < TN; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+                }
+                const int qn = (q + 1) % kDepth;   // ring slot of step s + 1 (static once unrolled)
+                if (s + 1 < s_end) {
+                    store_stage<BM, BN>(st[qn], p, m0, n0, s + 1, Xs[buf ^ 1], Ws[buf ^ 1]);
+                    if (s + 1 + kDepth < s_end)
+                        load_stage<BM, BN>(st[qn], p, m0, n0, s + 1 + kDepth);
+                }
+                __syncthreads();
+            }
         }
     }
 
@@ -272,6 +296,8 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(FillParams f)
 
 inline bool aligned(const void *ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0; }
 
+thread_local int o_splits = 0, o_bm = 0;   // tuning override (0: built-in)
+
 template <int BM, int BN>
 hipError_t launch_prefill(PrefillParams p, int cus, hipStream_t stream)
 {
@@ -280,11 +306,17 @@ hipError_t launch_prefill(PrefillParams p, int cus, hipStream_t stream)
     const int nsteps = (p.K / 32 + 1) / 2;
     int splits = 1;
     const int64_t tiles = tiles_n * tiles_m;
-    if (tiles < cus) {
-        // split K so that about two workgroups per CU exist, each with >= 4 steps
-        splits = (int)std::min<int64_t>((2 * cus + tiles - 1) / tiles, std::max(1, nsteps / 4));
-        splits = std::max(1, std::min(splits, 32));
+    if (tiles < (int64_t)cus * 5 / 8) {
+        // Too few output tiles to occupy the chip: split K, about one
+        // workgroup per CU in total.  Each extra split adds an fp32 atomic per
+        // output element and needs a zero-filled Y, so splits stay few
+        // (sweeps on MI355X: 6144 x 2048 at 512 tokens 38.6 us unsplit
+        // against 47.0 us with 2 splits; 2560 x 6144 at 512 tokens best at 3).
+        splits = (int)std::min<int64_t>((cus + tiles / 2) / tiles, std::max(1, nsteps / 4));
+        splits = std::max(1, std::min(splits, 16));
     }
+    if (o_splits > 0)
+        splits = std::min(o_splits, nsteps);
     p.steps_per_split = (nsteps + splits - 1) / splits;
     splits = (nsteps + p.steps_per_split - 1) / p.steps_per_split;
     p.atomic = splits > 1;
@@ -332,8 +364,18 @@ extern "C" qg_status qgemm_q4_0_prefill(const void *Wp, const uint16_t *X, float
     p.steps_per_split = 0;
     p.atomic = 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = (M <= 64) ? launch_prefill<64, 128>(p, cus, s) : launch_prefill<128, 128>(p, cus, s);
+    const bool small = o_bm ? (o_bm == 64) : (M <= 64);
+    hipError_t e = small ? launch_prefill<64, 128>(p, cus, s) : launch_prefill<128, 128>(p, cus, s);
     if (e == hipErrorInvalidValue)
         return QG_ERR_SHAPE;
     return e == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
+}
+
+// Tuning knob for sweeps: fixes the K split count and the token tile (64 or
+// 128) of later qgemm_q4_0_prefill calls from the calling thread; 0 keeps the
+// built-in choice.
+extern "C" void qg_set_prefill_shape(int splits, int bm)
+{
+    qg::o_splits = splits;
+    qg::o_bm = bm;
 }
