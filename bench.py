@@ -11,7 +11,9 @@ call streams its weights from HBM and not from the 256 MB last-level cache
 reads from memory].
 
 value    = algorithmic bytes of all K timed steps / wall time of the K steps
-           (inputs resident in HBM; launch gaps included; plain launches).
+           (inputs resident in HBM; launch gaps included), the K steps
+           replayed as one captured HIP graph (eager launch time reported
+           beside it; --no-graph times value eagerly).
 roofline = the GEMV kernel's own time, from HIP events recorded by each
            launch (hipExtLaunchKernel) over a second pass of K steps, against
            8 TB/s; algorithmic bytes per call = N*K/32*18 (codes + scales) +
@@ -275,6 +277,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time value with eager launches instead of a graph")
     ap.add_argument("--suite", default=None, metavar="FILE",
                     help="instead of the headline step, time every workload (GEMV both formats and M = 1..8, "
                          "MoE, prefill with its dense fp16 comparator) and write one JSON record per line to FILE")
@@ -306,18 +309,46 @@ def main() -> int:
         run_step(work)
     torch.cuda.synchronize()
 
-    # Timed region 1 (value): K steps of plain launches, bracketed by
-    # synchronizations, plus stream events for the GPU-side span.
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
-        run_step(work)
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_span = ev0.elapsed_time(ev1) * 1e-3
+    # Timed region 1 (value): K steps, captured once into a HIP graph and
+    # replayed (the launch-bound loop as a graph; the copy rotation continues
+    # exactly as eager launches would, so every call still reads cold copies),
+    # bracketed by synchronizations.  The same K steps launched eagerly are
+    # timed too and reported beside it.
+    def timed_eager():
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(args.steps):
+            run_step(work)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t
+
+    eager_wall = timed_eager()
+    wall = eager_wall
+    graph_used = False
+    if not args.no_graph:
+        nexts = [w["next"] for w in work]
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            gcalls = [[qg.PreparedGemv(qg.Q4_0, w["buf"][c * w["nb"]:(c + 1) * w["nb"]], w["x"], w["y"], w["N"],
+                                       w["K"]) for c in range(w["copies"])] for w in work]
+            with torch.cuda.graph(graph, stream=cap):
+                for _ in range(args.steps):
+                    for w, calls in zip(work, gcalls):
+                        c = w["next"]
+                        w["next"] = (c + 1) % w["copies"]
+                        calls[c]()
+        torch.cuda.synchronize()
+        for w, n in zip(work, nexts):   # warm the graph on the same copies, then time it
+            w["next"] = n
+        graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        graph.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        graph_used = True
 
     # Timed region 2 (roofline): the same K steps, every launch recording its
     # own start and end (hipExtLaunchKernel events).  The event path costs
@@ -352,7 +383,9 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(wall / args.steps * 1e3, 4),
-        "gpu_ms_per_step": round(gpu_span / args.steps * 1e3, 4),
+        "launch": "hip graph of the K steps" if graph_used else "eager",
+        "eager_ms_per_step": round(eager_wall / args.steps * 1e3, 4),
+        "eager_value": round(step_bytes * args.steps / eager_wall / 1e9, 1),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
