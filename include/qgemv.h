@@ -34,9 +34,16 @@
  *   - Alignment: packed weights 256 B, fp16 activations 16 B, fp32 outputs
  *     4 B (QG_ERR_ALIGN otherwise).
  *   - Outputs are fp32, accumulated in fp32 from exactly dequantized weights
- *     and fp16 activations (products are exact; only the sums round).
- *   - Kernels use no atomics; for a fixed shape and launch the results are
- *     bitwise reproducible.
+ *     and fp16 activations (products are exact; only the sums round).  The
+ *     vector-ALU GEMV forms each block sum from the biased codes (1024 + q
+ *     as fp16) and subtracts the bias times the block's activation sum, so
+ *     its fp32 rounding is relative to about 1152 * sum |x| per block, far
+ *     inside the 1e-3 * sum |w x| tolerance; a one-hot activation still
+ *     returns a weight column exactly.  A block with a non-finite scale makes
+ *     its row non-finite (inf or NaN).
+ *   - The GEMV / MoE kernels use no atomics: for a fixed shape and launch
+ *     their results are bitwise reproducible.  The prefill adds split-K
+ *     partial tiles atomically (last-bit differences between runs).
  */
 #ifndef QGEMV_H
 #define QGEMV_H
@@ -147,15 +154,18 @@ void qg_time_next_launch(void *start, void *stop);
 qg_status qg_device_cus(int device, int *cus);
 
 /* Tuning knob for launch-shape sweeps of qgemv_* / qmoe_gemv_q4_0: fixes J
- * (blocks per lane per row, J * M <= 8), R (rows per group: 1, 2 or 4),
+ * (blocks per lane per row, J * M <= 8), R (row sets per group: 1, 2 or 4),
  * ksplit (waves sharing a row along K), teams per workgroup, the total
  * number of teams, xl (activations of a one-token call staged in LDS: 1,
- * kept in registers: 0) and engine (vector-ALU kernel: 0; matrix-core kernel
+ * kept in registers: 0), engine (vector-ALU kernel: 0; matrix-core kernel
  * for 2..8 tokens and rows of at most 256 blocks: 1, where ksplit is its
- * number of waves along K) for later calls from the calling thread.  A zero
- * (-1 for xl and engine) keeps the built-in per-shape choice for that field.
- * An impossible combination makes the later calls return QG_ERR_SHAPE. */
-void qg_set_gemv_shape(int J, int R, int ksplit, int teams_per_wg, int64_t teams, int xl, int engine);
+ * number of waves along K) and lanes_per_row (lanes of a wave that share one
+ * row in the vector-ALU kernel: 16, 32 or 64; below 64 one token only) for
+ * later calls from the calling thread.  A zero (-1 for xl and engine) keeps
+ * the built-in per-shape choice for that field.  An impossible combination
+ * makes the later calls return QG_ERR_SHAPE. */
+void qg_set_gemv_shape(int J, int R, int ksplit, int teams_per_wg, int64_t teams, int xl, int engine,
+                       int lanes_per_row);
 
 /* Tuning knob for sweeps of qgemm_q4_0_prefill: fixes the number of
  * workgroups sharing one output tile along K (splits; more than one adds fp32

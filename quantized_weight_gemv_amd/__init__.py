@@ -66,7 +66,7 @@ def lib() -> ctypes.CDLL:
         "qdequant_q8_0": (c_int, [vp, i64, i64, c_int, vp, vp]),
         "qg_time_next_launch": (None, [vp, vp]),
         "qg_device_cus": (c_int, [c_int, ctypes.POINTER(c_int)]),
-        "qg_set_gemv_shape": (None, [c_int, c_int, c_int, c_int, i64, c_int, c_int]),
+        "qg_set_gemv_shape": (None, [c_int, c_int, c_int, c_int, i64, c_int, c_int, c_int]),
         "qg_read_probe": (c_int, [vp, sz, vp, c_int, vp]),
         "qg_set_prefill_shape": (None, [c_int, c_int]),
     }
@@ -258,8 +258,8 @@ def qdequant_q8_0(Wp, N: int, K: int, fp16: bool = False, out=None):
 
 # --------------------------------------------------------------- measurement
 def qg_set_gemv_shape(J: int = 0, R: int = 0, ksplit: int = 0, teams_per_wg: int = 0, teams: int = 0,
-                      xl: int = -1, engine: int = -1):
-    lib().qg_set_gemv_shape(J, R, ksplit, teams_per_wg, teams, xl, engine)
+                      xl: int = -1, engine: int = -1, lanes: int = 0):
+    lib().qg_set_gemv_shape(J, R, ksplit, teams_per_wg, teams, xl, engine, lanes)
 
 
 def qg_read_probe(buf, sink, wgs: int):

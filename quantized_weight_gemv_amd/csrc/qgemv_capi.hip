@@ -64,68 +64,99 @@ inline int64_t scale_offset(int fmt, int64_t N, int64_t K)
 
 // Launch shape for one GEMV / MoE call.
 struct GemvShape {
-    int J, R, ksplit, teams_per_wg;
+    int G, J, R, ksplit, teams_per_wg;
     int64_t teams;   // teams per batch item
     bool xl;         // one token: activations staged in LDS, not registers
 };
 
 // Caller-set override for tuning sweeps (thread-local, zeros = heuristic).
-thread_local int o_J = 0, o_R = 0, o_ksplit = 0, o_teams_per_wg = 0, o_xl = -1, o_engine = -1;
+thread_local int o_G = 0, o_J = 0, o_R = 0, o_ksplit = 0, o_teams_per_wg = 0, o_xl = -1, o_engine = -1;
 thread_local int64_t o_teams = 0;
 
 bool choose_shape(int fmt, int M, int64_t N, int64_t K, int items, int cus, GemvShape &s)
 {
     const int64_t KB = K / 32;
-    // resident activations: J * M <= 8 blocks per lane; Q8_0 code words are
-    // twice as wide, so it keeps J <= 4
-    // one token with long rows: activations staged in LDS (no register cost)
-    bool xl = (M == 1 && fmt == kQ4_0 && KB > 256 && KB <= 512);
+    // Activations staged in LDS (one token) stay a tuning option: one block
+    // per lane with K split over several waves measured faster on MI355X.
+    bool xl = false;
     if (o_xl >= 0)
         xl = (o_xl == 1);
-    const int jmax = xl ? 8 : std::min(8 / M, fmt == kQ4_0 ? 7 : 4);
-    int ksplit = static_cast<int>((KB + 64 * jmax - 1) / (64 * jmax));
-    if (ksplit > kMaxWavesPerWg)
+    // Lanes per row: one token with rows of 65..128 blocks spreads a row over
+    // 16 (up to 4096 rows) or 32 lanes (up to 64K rows), so a wave reduces
+    // several rows at once; shorter rows take one wave each.
+    int G = 64;
+    if (M == 1 && !xl && KB > 64 && KB <= 128) {
+        if (N <= 4096 && N >= 4)
+            G = 16;
+        else if (N <= 65536 && N >= 2)
+            G = 32;
+    }
+    if (o_G)
+        G = o_G;
+    if (G != 16 && G != 32 && G != 64)
         return false;
-    int J = static_cast<int>((KB + 64LL * ksplit - 1) / (64LL * ksplit));
+    const int P = 64 / G;
+    if (N < P)
+        return false;
+    // One block per lane per row, K split over up to 8 waves; longer rows
+    // take more blocks per lane (with XL: one wave per row).
+    int J = static_cast<int>(std::max<int64_t>(1, (KB + 8LL * G - 1) / (8LL * G)));
+    if (xl)
+        J = static_cast<int>((KB + G - 1) / G);
+    int ksplit = static_cast<int>((KB + static_cast<int64_t>(G) * J - 1) / (static_cast<int64_t>(G) * J));
     const int rj = (fmt == kQ4_0) ? 8 : 4;   // R * J budget of the kernel table
-    // Per-shape choice, from launch sweeps on MI355X (256 CUs): one row per
-    // group for up to 64K rows, two beyond; 8-wave workgroups; about 8, 16 or
-    // 64 teams per CU over the call (more teams than fit at once: the
-    // hardware dispatcher balances the tail better than a persistent loop).
-    int R = (N > 65536) ? 2 : 1;
-    if (M >= 4)
-        R = 2;
+    // Two row sets per group, four for full-wave rows beyond 64K rows
+    // (launch sweeps on MI355X, 256 CUs).
+    int R = (N > 65536 && G == 64) ? 4 : 2;
     while (R * J > rj && R > 1)
         R /= 2;
-    int teams_per_wg = (ksplit == 1) ? (N > 65536 ? 4 : 8) : 1;
+    // stay within the instantiated kernels (register budget): fewer row sets,
+    // then more waves along K
+    while (R > 1 && !gemv_fits(fmt, M, G, J, R, xl))
+        R /= 2;
+    while (!xl && !gemv_fits(fmt, M, G, J, R, xl) && ksplit < kMaxWavesPerWg && J > 1) {
+        --J;
+        ksplit = static_cast<int>((KB + static_cast<int64_t>(G) * J - 1) / (static_cast<int64_t>(G) * J));
+    }
+    if (ksplit > kMaxWavesPerWg)
+        return false;
+    int teams_per_wg = 1;
     if (o_J) {
         J = o_J;
-        ksplit = static_cast<int>((KB + 64LL * J - 1) / (64LL * J));
-        if (J * M > 8 || ksplit > kMaxWavesPerWg)
+        ksplit = static_cast<int>((KB + static_cast<int64_t>(G) * J - 1) / (static_cast<int64_t>(G) * J));
+        if (ksplit > kMaxWavesPerWg)
             return false;
     }
     if (o_ksplit) {
         ksplit = o_ksplit;
-        if (static_cast<int64_t>(ksplit) * 64 * J < KB || ksplit > kMaxWavesPerWg)
+        if (static_cast<int64_t>(ksplit) * G * J < KB || ksplit > kMaxWavesPerWg)
             return false;
     }
     if (o_R)
         R = o_R;
     if (o_teams_per_wg)
         teams_per_wg = o_teams_per_wg;
-    if (xl && (ksplit > 1 || M != 1 || KB > 1023))
+    if (xl && (ksplit > 1 || M != 1 || gemv_xl_lds_bytes(static_cast<int>(K)) > 65536))
+        return false;
+    if (!gemv_fits(fmt, M, G, J, R, xl))
         return false;
     if (ksplit > 1)
         teams_per_wg = 1;   // a workgroup's waves must walk the same row groups
     if (teams_per_wg * ksplit > kMaxWavesPerWg)
         teams_per_wg = std::max(1, kMaxWavesPerWg / ksplit);
-    const int64_t ngroups = (N + R - 1) / R;
-    const int per_cu = (N <= 4096) ? 8 : (N <= 65536 ? 16 : 64);
-    int64_t teams = std::max<int64_t>(1, static_cast<int64_t>(cus) * per_cu / ksplit / std::max(1, items));
+    const int64_t ngroups = (N + static_cast<int64_t>(R) * P - 1) / (static_cast<int64_t>(R) * P);
+    // Teams per CU (launch sweeps on MI355X): 8 for one-wave rows; with K
+    // split, about 16 waves per CU for one token and 8 for several; beyond
+    // 64K rows 64 teams per CU, more than fit at once (the hardware
+    // dispatcher then balances the tail).
+    int per_cu = (ksplit == 1) ? 8 : (M == 1 ? std::max(4, 16 / ksplit) : std::max(2, 8 / ksplit));
+    if (N > 65536 && M == 1)
+        per_cu = 64;
+    int64_t teams = std::max<int64_t>(1, static_cast<int64_t>(cus) * per_cu / std::max(1, items));
     if (o_teams)
         teams = o_teams;
     teams = std::min(teams, ngroups);
-    s = GemvShape{J, R, ksplit, teams_per_wg, teams, xl};
+    s = GemvShape{G, J, R, ksplit, teams_per_wg, teams, xl};
     return true;
 }
 
@@ -181,7 +212,7 @@ qg_status run_gemv(int fmt, const void *Wp, const int32_t *idx, int64_t P, const
     const int64_t wgs = (s.teams + s.teams_per_wg - 1) / s.teams_per_wg;
     dim3 grid(static_cast<unsigned>(wgs), static_cast<unsigned>(items), 1);
     dim3 block(64 * s.ksplit * s.teams_per_wg, 1, 1);
-    hipError_t e = launch_gemv(fmt, M, s.J, s.R, s.xl, p, grid, block, static_cast<hipStream_t>(stream));
+    hipError_t e = launch_gemv(fmt, M, s.G, s.J, s.R, s.xl, p, grid, block, static_cast<hipStream_t>(stream));
     if (e == hipErrorInvalidValue)
         return QG_ERR_SHAPE;
     return e == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
@@ -329,13 +360,15 @@ qg_status qg_device_cus(int device, int *cus)
     return QG_OK;
 }
 
-// Tuning knob for launch-shape sweeps: fixes J (blocks per lane), R (rows per
-// group), ksplit (waves along K), teams per workgroup, total teams and the
-// activation staging (xl: -1 built-in, 0 registers, 1 LDS) and the engine
-// (-1 built-in, 0 vector ALU, 1 matrix cores; with the matrix cores ksplit is
-// the number of waves along K) for the GEMV / MoE calls made afterwards from
-// the calling thread.  Zero keeps the built-in choice for the other fields.
-void qg_set_gemv_shape(int J, int R, int ksplit, int teams_per_wg, int64_t teams, int xl, int engine)
+// Tuning knob for launch-shape sweeps: fixes J (blocks per lane), R (row sets
+// per group), ksplit (waves along K), teams per workgroup, total teams, the
+// activation staging (xl: -1 built-in, 0 registers, 1 LDS), the engine (-1
+// built-in, 0 vector ALU, 1 matrix cores; with the matrix cores ksplit is the
+// number of waves along K) and the lanes per row (16, 32 or 64) for the GEMV /
+// MoE calls made afterwards from the calling thread.  Zero keeps the built-in
+// choice for the other fields.
+void qg_set_gemv_shape(int J, int R, int ksplit, int teams_per_wg, int64_t teams, int xl, int engine,
+                       int lanes_per_row)
 {
     qg::o_xl = xl;
     qg::o_engine = engine;
@@ -344,6 +377,7 @@ void qg_set_gemv_shape(int J, int R, int ksplit, int teams_per_wg, int64_t teams
     qg::o_ksplit = ksplit;
     qg::o_teams_per_wg = teams_per_wg;
     qg::o_teams = teams;
+    qg::o_G = lanes_per_row;
 }
 
 }  // extern "C"

@@ -1,37 +1,49 @@
 // Fused dequantize-and-multiply GEMV kernels (Q4_0, Q8_0, and the one-launch
-// MoE variant) for gfx950.
+// MoE variant) for gfx950: the vector-ALU path (1..8 tokens; the library uses
+// it for 1..3 tokens and for rows too long for the matrix-core kernel).
 //
 // The work is bound by streaming the packed weights from HBM once per call
 // [volta-kernel-bakeoff, "Why the V100 is interesting here";
 //  H100-KERNEL-5X-ROADMAP, "Why the decode gap is bandwidth"], so the design
 // goals are: every weight byte read exactly once with 16-byte coalesced loads,
 // enough bytes in flight per compute unit to cover HBM latency, and an unpack
-// cheap enough that the vector ALUs keep pace with the memory stream.
+// cheap enough that the vector ALUs keep pace with the memory stream.  On
+// MI355X the last point is the hard one: at ~7 TB/s a compute unit receives a
+// 32-weight block every ~3 cycles, and a wave64 vector instruction occupies
+// its SIMD for 4 cycles, so the per-block instruction count decides whether
+// the kernel is memory- or ALU-bound.
 //
 // Mapping (one wave64 = 64 lanes):
-//   * A "team" of `ksplit` waves owns a group of R consecutive rows at a time.
-//     Wave w of the team covers blocks [w*64J, (w+1)*64J) of every row; lane
-//     l of that wave owns blocks w*64J + l + 64j (j < J).  Consecutive lanes
-//     read consecutive 16-byte code words: every load instruction of a wave
-//     touches one contiguous 1 KiB span (Q4_0).
+//   * A row is spread over G lanes (G = 16, 32 or 64), so a wave works on
+//     P = 64 / G rows at once (a "row set").  Lane l serves row l / G of the
+//     set and, of that row, the blocks b0 + l % G + G j (j < J), where b0 is
+//     the start of the wave's K chunk.  Lanes of one row read consecutive
+//     16-byte code words: a load instruction touches P contiguous spans of
+//     16 G bytes.
+//   * A "team" of `ksplit` waves owns a group of R row sets at a time (wave w
+//     of the team covers K chunk w); teams stride over the groups.
 //   * Each lane keeps the activations of its blocks in registers for all M
 //     tokens, loaded once per team and reused for every row the team visits
 //     (one activation load serves many rows [volta-kernel-bakeoff, "Results",
-//     the few-tokens bullet]).  J*M <= 8 bounds that register cost.
-//   * Teams stride over row groups (a persistent grid sized to the chip) and
-//     prefetch the next group's codes and scales before computing the current
-//     one, so each wave always has a full group of loads in flight.
+//     the few-tokens bullet]), or, with XL (one token, long rows), reads them
+//     from the workgroup's LDS copy.
+//   * Two register sets in ping-pong: the next group's loads are in flight
+//     while the current group is unpacked and multiplied.
 //   * Unpack: a nibble n OR-ed into the binary16 pattern 0x6400 is the half
 //     1024 + n exactly [volta-kernel-bakeoff, "What's in the race", the
-//     fused_q4_v2 bit trick]; subtracting 1032 gives n - 8 exactly, two
-//     weights per packed-half instruction.  Nibbles in bits 4..7 give
-//     1024 + 16 n, and (1024 + 16 n) / 16 - 72 = n - 8, also exact, which
-//     saves the shift.  Products with the activations go through
-//     v_dot2_f32_f16 (two fp16 products, exact, summed into fp32).  The block
-//     scale multiplies the 32-term block sum once.
-//   * Reduction of a row's 64 lane partials: DPP within 16-lane rows, then
-//     the four row sums are read out with readlane; waves of a team (ksplit
-//     > 1) combine through LDS.  No atomics: results are reproducible.
+//     fused_q4_v2 bit trick]; a high nibble left in place gives 1024 + 16 n.
+//     One v_and_or_b32 makes two such halves.  The bias is not subtracted per
+//     weight: products with the activations go through v_dot2_f32_f16 (two
+//     exact fp16 products summed into fp32), and each block's two dot chains
+//     start from -1032 * (sum of its low-nibble activations) and -1152 * (sum
+//     of its high-nibble activations), constants computed once per team.  Then
+//     low chain + high chain / 16 = sum (q - 8) x exactly up to fp32 rounding
+//     of the chains.  Q8_0: (q + 128) | 0x6400 = q + 1152, placed with one
+//     v_perm_b32 per pair, chains start from -1152 * (sum of activations).
+//     The block scale multiplies the block sum once.
+//   * Reduction over a row's G lanes: DPP within 16-lane rows, then
+//     v_permlane16_swap / v_permlane32_swap across them; waves of a team
+//     (ksplit > 1) combine through LDS.  No atomics: results are reproducible.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -49,17 +61,23 @@ __device__ __forceinline__ float dot2(h2_t a, h2_t b, float c)
     return __builtin_amdgcn_fdot2(a, b, c, false);
 }
 
+// The first product of a chain that starts from a value still needed later
+// (a loop-invariant bias term): the three-operand encoding writes a fresh
+// register, where the compiler's two-operand form would first copy c.
+__device__ __forceinline__ float dot2_from(h2_t a, h2_t b, float c)
+{
+    float d;
+    asm("v_dot2_f32_f16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+    return d;
+}
+
 // ---------------------------------------------------------------- unpacking
 //
-// Both formats unpack a block into 16 half pairs v[0..15] whose activation
-// partners are the pairs X[0..15] built by load_x_block<FMT>.
+// Both formats unpack a block into 16 half pairs whose activation partners
+// are the pairs X[0..15] built by load_x_block<FMT>.
 
-// Q4_0: word t holds bytes 4t..4t+3 = elements 4t..4t+3 (low nibbles) and
-// 16+4t..19+4t (high nibbles).
-//   v[4t+0] = (e[4t],    e[4t+2])      v[4t+2] = (e[4t+1],  e[4t+3])
-//   v[4t+1] = (e[16+4t], e[18+4t])     v[4t+3] = (e[17+4t], e[19+4t])
-// The magic constant is pinned in a vector register: with the mask in a scalar
-// register, (w & mask) | magic is then a single v_and_or_b32.
+// The magic constant is pinned in a vector register (once per kernel): with the
+// mask in a scalar register, (w & mask) | magic is then a single v_and_or_b32.
 __device__ __forceinline__ uint32_t magic_reg()
 {
     uint32_t m;
@@ -67,37 +85,40 @@ __device__ __forceinline__ uint32_t magic_reg()
     return m;
 }
 
-__device__ __forceinline__ void unpack_q4(const uint4 c, h2_t (&v)[16])
+// Q4_0: word t holds bytes 4t..4t+3 = elements 4t..4t+3 (low nibbles) and
+// 16+4t..19+4t (high nibbles).
+//   lo[2t]   = 1024 + (e[4t],    e[4t+2])        partner X[4t+0]
+//   lo[2t+1] = 1024 + (e[4t+1],  e[4t+3])        partner X[4t+2]
+//   hi[2t]   = 1024 + 16 (e[16+4t], e[18+4t])    partner X[4t+1]
+//   hi[2t+1] = 1024 + 16 (e[17+4t], e[19+4t])    partner X[4t+3]
+__device__ __forceinline__ void unpack_q4(const uint4 c, uint32_t kMagic, h2_t (&lo)[8], h2_t (&hi)[8])
 {
-    const uint32_t kMagic = magic_reg();
-    const h2_t kOffLo = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-    const h2_t kScaleHi = {(_Float16)0.0625f, (_Float16)0.0625f};
-    const h2_t kOffHi = {(_Float16)-72.0f, (_Float16)-72.0f};
     const uint32_t w[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const uint32_t a = w[t];
         const uint32_t b = w[t] >> 8;
-        v[4 * t + 0] = as_h2((a & 0x000F000Fu) | kMagic) + kOffLo;
-        v[4 * t + 1] = as_h2((a & 0x00F000F0u) | kMagic) * kScaleHi + kOffHi;
-        v[4 * t + 2] = as_h2((b & 0x000F000Fu) | kMagic) + kOffLo;
-        v[4 * t + 3] = as_h2((b & 0x00F000F0u) | kMagic) * kScaleHi + kOffHi;
+        lo[2 * t + 0] = as_h2((a & 0x000F000Fu) | kMagic);
+        hi[2 * t + 0] = as_h2((a & 0x00F000F0u) | kMagic);
+        lo[2 * t + 1] = as_h2((b & 0x000F000Fu) | kMagic);
+        hi[2 * t + 1] = as_h2((b & 0x00F000F0u) | kMagic);
     }
 }
 
 // Q8_0: word t holds int8 elements 4t..4t+3.  Flipping the sign bits gives
-// u = q + 128 in 1..255; 0x6400 | u is 1024 + u; minus 1152 is q, exactly.
-//   v[2t] = (e[4t], e[4t+2])   v[2t+1] = (e[4t+1], e[4t+3])
-__device__ __forceinline__ void unpack_q8(const uint4 c0, const uint4 c1, h2_t (&v)[16])
+// u = q + 128 in 0..255; with 0x64 as the high byte, u is the half 1024 + u =
+// q + 1152 exactly.  v_perm_b32 takes bytes 0 and 2 (1 and 3) of u and the
+// 0x64 bytes of the magic word in one instruction.
+//   v[2t] = 1152 + (e[4t], e[4t+2])   v[2t+1] = 1152 + (e[4t+1], e[4t+3])
+__device__ __forceinline__ void unpack_q8(const uint4 c0, const uint4 c1, uint32_t kMagic, h2_t (&v)[16])
 {
-    const uint32_t kMagic = magic_reg();
-    const h2_t kOff = {(_Float16)-1152.0f, (_Float16)-1152.0f};
     const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
         const uint32_t u = w[t] ^ 0x80808080u;
-        v[2 * t + 0] = as_h2((u & 0x00FF00FFu) | kMagic) + kOff;
-        v[2 * t + 1] = as_h2(((u >> 8) & 0x00FF00FFu) | kMagic) + kOff;
+        // selector bytes: 0-3 pick bytes of u, 4-7 bytes of the magic word
+        v[2 * t + 0] = as_h2(__builtin_amdgcn_perm(kMagic, u, 0x07020500u));
+        v[2 * t + 1] = as_h2(__builtin_amdgcn_perm(kMagic, u, 0x07030501u));
     }
 }
 
@@ -131,6 +152,36 @@ __device__ __forceinline__ void load_x_block(const uint16_t *p, uint32_t (&X)[16
     }
 }
 
+// Starting values of a block's two dot chains: minus the bias times the
+// activations each chain sees.  Q4_0: chain 0 takes the low nibbles (bias
+// 1032 = 1024 + 8), chain 1 the high nibbles at 16x scale (bias 1152 =
+// 16 * 72); Q8_0: chain 0 takes pairs 0..7, chain 1 pairs 8..15 (bias 1152).
+template <int FMT>
+__device__ __forceinline__ void bias_terms(const uint32_t (&X)[16], float (&c)[2])
+{
+    float a = 0.0f, b = 0.0f;
+    if constexpr (FMT == kQ4_0) {
+        const h2_t kLo = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+        const h2_t kHi = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            a = dot2(kLo, as_h2(X[4 * t + 0]), a);
+            a = dot2(kLo, as_h2(X[4 * t + 2]), a);
+            b = dot2(kHi, as_h2(X[4 * t + 1]), b);
+            b = dot2(kHi, as_h2(X[4 * t + 3]), b);
+        }
+    } else {
+        const h2_t k = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            a = dot2(k, as_h2(X[t]), a);
+            b = dot2(k, as_h2(X[8 + t]), b);
+        }
+    }
+    c[0] = a;
+    c[1] = b;
+}
+
 // ---------------------------------------------------------------- reduction
 
 template <int CTRL>
@@ -139,19 +190,29 @@ __device__ __forceinline__ float dpp(float v)
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 
-// Sum over the 64 lanes of a wave; the result is wave-uniform.
-__device__ __forceinline__ float wave_sum(float v)
+// Sum over each G-lane segment of the wave; every lane of a segment receives
+// its sum.  With 16-lane rows r0..r3: v_permlane16_swap(A, B) gives
+// A = [A.r0, B.r0, A.r2, B.r2], B = [A.r1, B.r1, A.r3, B.r3] and
+// v_permlane32_swap(A, B) gives A = [A.r0, A.r1, B.r0, B.r1],
+// B = [A.r2, A.r3, B.r2, B.r3].
+template <int G>
+__device__ __forceinline__ float seg_sum(float v)
 {
     v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
     v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
     v += dpp<0x141>(v);   // row_half_mirror
     v += dpp<0x140>(v);   // row_mirror: every lane holds its 16-lane row's sum
-    const int b = __builtin_bit_cast(int, v);
-    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
-    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
-    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
-    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
-    return (r0 + r1) + (r2 + r3);
+    if constexpr (G >= 32) {
+        const uint32_t u = __builtin_bit_cast(uint32_t, v);
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        v = __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+    }
+    if constexpr (G == 64) {
+        const uint32_t u = __builtin_bit_cast(uint32_t, v);
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        v = __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+    }
+    return v;
 }
 
 // ---------------------------------------------------------------- the kernel
@@ -173,91 +234,101 @@ struct Group {
     uint16_t scale[R][J];
 };
 
-// Issue the loads of one row group.  Addresses are always in bounds: rows past
-// N are clamped to N - 1 and padding lanes to their chunk's last block; such
-// entries get a zero scale (and zero activations) in compute_group, so they
-// add nothing.  Each row's base address is wave-uniform (scalar registers);
-// lanes add a 32-bit offset.
-#ifndef QG_NT_LOADS
-#define QG_NT_LOADS 1
-#endif
-
 // Weight bytes are read once per call: they are loaded non-temporal so the
 // stream does not displace the activations from the caches (measured on
 // MI355X: 6.5 TB/s against 6.0 TB/s with plain loads on the 296 MB
-// 128256 x 4096 matrix).
-__device__ __forceinline__ uint4 stream_load16(const uint8_t *p)
+// 128256 x 4096 matrix).  The loads are buffer loads: the row set's base
+// address and extent live in a scalar resource descriptor, each lane adds a
+// loop-invariant 32-bit offset, so no vector instruction is spent on
+// addresses, and the hardware range check returns zeros rather than reading
+// past the matrix.
+constexpr int kNtAux = 2;                     // cache policy: non-temporal
+constexpr int kRsrcWord3 = 0x00020000;        // raw (untyped) buffer, gfx9 family
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t *base, int64_t bytes)
 {
-#if QG_NT_LOADS
-    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-    const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p));
-    return make_uint4(t.x, t.y, t.z, t.w);
-#else
-    return *reinterpret_cast<const uint4 *>(p);
-#endif
+    const int n = (int)min(bytes, (int64_t)0x7FFFFFFF);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), (short)0, n, kRsrcWord3);
 }
 
-__device__ __forceinline__ uint16_t stream_load2(const uint8_t *p)
+__device__ __forceinline__ uint4 stream_load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
-#if QG_NT_LOADS
-    return __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(p));
-#else
-    return *reinterpret_cast<const uint16_t *>(p);
-#endif
+    const auto t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNtAux);
+    return make_uint4(t[0], t[1], t[2], t[3]);
 }
 
-template <int FMT, int J, int R>
+__device__ __forceinline__ uint16_t stream_load2(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kNtAux);
+}
+
+// Issue the loads of one group (R row sets from row rs0).  Each row set's
+// first row is wave-uniform and clamped to rmax = N - P, so every lane's row
+// rbase + l / G stays inside the matrix; lanes add a 32-bit offset (coff,
+// soff: row within the set and block).  Padding lanes of a short K chunk read
+// their chunk's last block (their block index is clamped) and have zero
+// activations, so they add nothing.
+template <int FMT, int G, int J, int R>
 __device__ __forceinline__ void load_group(Group<FMT, J, R> &g, const uint8_t *__restrict__ W,
-                                           const uint16_t *__restrict__ S, int64_t row0, int N, int KB,
-                                           const uint32_t (&boff)[J])
+                                           const uint8_t *__restrict__ S, int64_t rs0, int64_t rmax, int KB,
+                                           int64_t nblocks, const uint32_t (&coff)[J], const uint32_t (&soff)[J])
 {
+    constexpr int P = 64 / G;
+    constexpr int CB = (FMT == kQ4_0) ? 16 : 32;   // code bytes per block
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-        const int64_t row = min(row0 + i, (int64_t)N - 1);
-        const int64_t base = row * KB;   // first block of the row
-        const uint8_t *__restrict__ srow = reinterpret_cast<const uint8_t *>(S + base);
-        const uint8_t *__restrict__ crow = W + base * (FMT == kQ4_0 ? 16 : 32);
+        const int64_t rbase = min(rs0 + i * P, rmax);
+        const int64_t base = rbase * KB;   // first block of the row set
+        const auto rc = make_rsrc(W + base * CB, (nblocks - base) * CB);
+        const auto rs = make_rsrc(S + base * 2, (nblocks - base) * 2);
 #pragma unroll
         for (int j = 0; j < J; ++j) {
-            // scalar row base + unsigned 32-bit lane offset
             if constexpr (FMT == kQ4_0) {
-                g.code[i][j].c = stream_load16(crow + (uint64_t)(boff[j] * 16u));
+                g.code[i][j].c = stream_load16(rc, coff[j]);
             } else {
-                g.code[i][j].c0 = stream_load16(crow + (uint64_t)(boff[j] * 32u));
-                g.code[i][j].c1 = stream_load16(crow + (uint64_t)(boff[j] * 32u + 16u));
+                g.code[i][j].c0 = stream_load16(rc, coff[j]);
+                g.code[i][j].c1 = stream_load16(rc, coff[j] + 16u);
             }
-            g.scale[i][j] = stream_load2(srow + (uint64_t)(boff[j] * 2u));
+            g.scale[i][j] = stream_load2(rs, soff[j]);
         }
     }
 }
 
-// Activations come either from registers (X, loaded once per team) or, with
-// XL, from the workgroup's LDS copy (one token; xs holds every block of x in
-// pair order plus one zero block that padding lanes read).
+// Activations come either from registers (X and their bias terms XC, loaded
+// once per team) or, with XL, from the workgroup's LDS copy (one token; xs
+// holds every block of x in pair order plus one zero block that padding
+// lanes read, xc the blocks' bias terms).
 template <int FMT, int M, int J, int R, bool XL>
 __device__ __forceinline__ void compute_group(const Group<FMT, J, R> &g,
                                               const uint32_t (&X)[XL ? 1 : M][XL ? 1 : J][16],
-                                              const uint4 *xs, const uint32_t (&xoff)[J], const bool (&ok)[J],
-                                              int64_t row0, int N, float (&acc)[R][M])
+                                              const float (&XC)[XL ? 1 : M][XL ? 1 : J][2],
+                                              const uint4 *xs, const float2 *xc, const uint32_t (&xoff)[J],
+                                              uint32_t magic, float (&acc)[R][M])
 {
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-        const bool rok = row0 + i < N;
 #pragma unroll
         for (int m = 0; m < M; ++m)
             acc[i][m] = 0.0f;
 #pragma unroll
         for (int j = 0; j < J; ++j) {
-            h2_t v[16];
-            if constexpr (FMT == kQ4_0)
-                unpack_q4(g.code[i][j].c, v);
-            else
-                unpack_q8(g.code[i][j].c0, g.code[i][j].c1, v);
-            const _Float16 dh = __builtin_bit_cast(_Float16, (uint16_t)((rok && ok[j]) ? g.scale[i][j] : 0));
-            const float d = (float)dh;
+            const float d = (float)__builtin_bit_cast(_Float16, g.scale[i][j]);
+            h2_t v0[8], v1[8];   // the pairs of chain 0 and chain 1
+            if constexpr (FMT == kQ4_0) {
+                unpack_q4(g.code[i][j].c, magic, v0, v1);
+            } else {
+                h2_t v[16];
+                unpack_q8(g.code[i][j].c0, g.code[i][j].c1, magic, v);
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    v0[t] = v[t];
+                    v1[t] = v[8 + t];
+                }
+            }
 #pragma unroll
             for (int m = 0; m < M; ++m) {
                 uint32_t xw[16];
+                float c0, c1;
                 if constexpr (XL) {
                     const uint4 *q = xs + xoff[j] * 4;
 #pragma unroll
@@ -268,72 +339,118 @@ __device__ __forceinline__ void compute_group(const Group<FMT, J, R> &g,
                         xw[4 * u + 2] = t.z;
                         xw[4 * u + 3] = t.w;
                     }
+                    const float2 cc = xc[xoff[j]];
+                    c0 = cc.x;
+                    c1 = cc.y;
                 } else {
 #pragma unroll
                     for (int t = 0; t < 16; ++t)
                         xw[t] = X[m][j][t];
+                    c0 = XC[m][j][0];
+                    c1 = XC[m][j][1];
                 }
-                float s0 = 0.0f, s1 = 0.0f;
+                float blk;
+                if constexpr (FMT == kQ4_0) {
+                    c0 = dot2_from(v0[0], as_h2(xw[0]), c0);
+                    c1 = dot2_from(v1[0], as_h2(xw[1]), c1);
+                    c0 = dot2(v0[1], as_h2(xw[2]), c0);
+                    c1 = dot2(v1[1], as_h2(xw[3]), c1);
 #pragma unroll
-                for (int t = 0; t < 16; t += 2) {
-                    s0 = dot2(v[t], as_h2(xw[t]), s0);
-                    s1 = dot2(v[t + 1], as_h2(xw[t + 1]), s1);
+                    for (int t = 1; t < 4; ++t) {
+                        c0 = dot2(v0[2 * t], as_h2(xw[4 * t + 0]), c0);
+                        c1 = dot2(v1[2 * t], as_h2(xw[4 * t + 1]), c1);
+                        c0 = dot2(v0[2 * t + 1], as_h2(xw[4 * t + 2]), c0);
+                        c1 = dot2(v1[2 * t + 1], as_h2(xw[4 * t + 3]), c1);
+                    }
+                    blk = __builtin_fmaf(c1, 0.0625f, c0);
+                } else {
+                    c0 = dot2_from(v0[0], as_h2(xw[0]), c0);
+                    c1 = dot2_from(v1[0], as_h2(xw[8]), c1);
+#pragma unroll
+                    for (int t = 1; t < 8; ++t) {
+                        c0 = dot2(v0[t], as_h2(xw[t]), c0);
+                        c1 = dot2(v1[t], as_h2(xw[8 + t]), c1);
+                    }
+                    blk = c0 + c1;
                 }
-                acc[i][m] = __builtin_fmaf(d, s0 + s1, acc[i][m]);
+                acc[i][m] = __builtin_fmaf(d, blk, acc[i][m]);
             }
         }
     }
 }
 
 // Reduce one group's partials and store y (ksplit == 1), or combine the
-// team's waves through LDS first (ksplit > 1).
-template <int M, int R>
-__device__ __forceinline__ void finish_group(const float (&acc)[R][M], float *__restrict__ y, int64_t row0, int N,
-                                             int lane, int wave, int team, int kw, int ksplit,
+// team's waves through LDS first (ksplit > 1).  A row set whose first row
+// was clamped (at the matrix's tail) also holds rows below rs0 + i P that an
+// earlier row set stores: only rows in [rs0 + i P, N) are written.
+template <int G, int M, int R>
+__device__ __forceinline__ void finish_group(const float (&acc)[R][M], float *__restrict__ y, int64_t rs0,
+                                             int64_t rmax, int N, int lane, int wave, int team, int kw, int ksplit,
                                              float (&red)[2][kMaxWavesPerWg][kMaxRM], int &buf)
 {
-    float tot[R * M];
+    constexpr int P = 64 / G;
+    float tot[R][M];
 #pragma unroll
     for (int i = 0; i < R; ++i)
 #pragma unroll
         for (int m = 0; m < M; ++m)
-            tot[i * M + m] = wave_sum(acc[i][m]);
+            tot[i][m] = seg_sum<G>(acc[i][m]);
 
-    if (ksplit == 1) {
-        float out = 0.0f;
+    // rows of row set i: first = min(want, rmax) + lr; stored if first + lr
+    // lies in [want, N), i.e. lo <= lr < hi with small uniform bounds
+    const int lr = lane / G;
+    int lo[R], hi[R];
 #pragma unroll
-        for (int t = 0; t < R * M; ++t)
-            out = (lane == t) ? tot[t] : out;
-        if (lane < R * M) {
-            const int i = lane / M, m = lane % M;
-            const int64_t row = row0 + i;
-            if (row < N)
-                y[(int64_t)m * N + row] = out;
+    for (int i = 0; i < R; ++i) {
+        const int64_t want = rs0 + i * P;
+        const int64_t first = min(want, rmax);
+        lo[i] = (int)(want - first);
+        hi[i] = (int)min((int64_t)N - first, (int64_t)P);
+    }
+    if (ksplit == 1) {
+        if (lane % G == 0) {
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                if (lr >= lo[i] && lr < hi[i]) {
+                    const int64_t row = min(rs0 + i * P, rmax) + lr;
+#pragma unroll
+                    for (int m = 0; m < M; ++m)
+                        y[(int64_t)m * N + row] = tot[i][m];
+                }
+            }
         }
     } else {
-        if (lane == 0) {
+        if (lane % G == 0) {
 #pragma unroll
-            for (int t = 0; t < R * M; ++t)
-                red[buf][wave][t] = tot[t];
+            for (int i = 0; i < R; ++i)
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+                    red[buf][wave][(i * M + m) * P + lr] = tot[i][m];
         }
         __syncthreads();
-        if (kw == 0 && lane < R * M) {
+        if (kw == 0 && lane < R * M * P) {
             float s = 0.0f;
             for (int w = 0; w < ksplit; ++w)
                 s += red[buf][team * ksplit + w][lane];
-            const int i = lane / M, m = lane % M;
-            const int64_t row = row0 + i;
-            if (row < N)
-                y[(int64_t)m * N + row] = s;
+            const int i = lane / (M * P), m = (lane / P) % M, r = lane % P;
+            int loi = 0, hii = 0;
+#pragma unroll
+            for (int t = 0; t < R; ++t) {
+                loi = (i == t) ? lo[t] : loi;
+                hii = (i == t) ? hi[t] : hii;
+            }
+            if (r >= loi && r < hii)
+                y[(int64_t)m * N + min(rs0 + i * P, rmax) + r] = s;
         }
         buf ^= 1;
     }
 }
 
-template <int FMT, int M, int J, int R, bool XL>
+template <int FMT, int M, int G, int J, int R, bool XL>
 __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
 {
     static_assert(!XL || M == 1, "LDS-staged activations are for one token");
+    constexpr int P = 64 / G;
     const int lane = threadIdx.x & 63;
     // wave-uniform: everything derived from it (rows, addresses) stays scalar
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -346,35 +463,48 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
     const uint8_t *__restrict__ W = p.W;
     if (p.idx)
         W += (int64_t)p.idx[item] * p.matrix_stride;
-    const uint16_t *__restrict__ S = reinterpret_cast<const uint16_t *>(W + p.scale_offset);
+    const uint8_t *__restrict__ S = W + p.scale_offset;
     const uint16_t *__restrict__ x = p.x + (int64_t)item * M * p.K;
     float *__restrict__ y = p.y + (int64_t)item * M * p.N;
 
     const int KB = p.K >> 5;
-    const int bbeg = kw * 64 * J;
-    const int bend = min(KB, bbeg + 64 * J);
-    uint32_t blk[J], xoff[J];
+    const int lr = lane / G;
+    const int bbeg = kw * G * J;
+    const int bend = min(KB, bbeg + G * J);
+    uint32_t blk[J], xoff[J], coff[J], soff[J];
     bool ok[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-        const int b = bbeg + lane + 64 * j;
+        const int b = bbeg + lane % G + G * j;
         ok[j] = b < bend;
         blk[j] = (uint32_t)(ok[j] ? b : bend - 1);
         xoff[j] = (uint32_t)(ok[j] ? b : KB);   // LDS block KB is all zeros
+        const uint32_t e = (uint32_t)lr * (uint32_t)KB + blk[j];   // block offset from the row set
+        coff[j] = e * (FMT == kQ4_0 ? 16u : 32u);
+        soff[j] = e * 2u;
     }
 
-    const int64_t ngroups = ((int64_t)p.N + R - 1) / R;
+    // groups of R row sets; a row set's first row is clamped to rmax = N - P
+    // (the launcher ensures N >= P)
+    const int64_t rows_per_group = (int64_t)R * P;
+    const int64_t ngroups = ((int64_t)p.N + rows_per_group - 1) / rows_per_group;
+    const int64_t rmax = (int64_t)p.N - P;
+    const int64_t nblocks = (int64_t)p.N * KB;
     int64_t g = team_id;
 
     Group<FMT, J, R> ga, gb;
     if (g < ngroups)
-        load_group<FMT, J, R>(ga, W, S, g * R, p.N, KB, blk);
+        load_group<FMT, G, J, R>(ga, W, S, g * rows_per_group, rmax, KB, nblocks, coff, soff);
 
     // activations of this lane's blocks, all M tokens, kept for every row
     uint32_t X[XL ? 1 : M][XL ? 1 : J][16];
+    float XC[XL ? 1 : M][XL ? 1 : J][2];
     extern __shared__ uint4 xs_dyn[];
+    const float2 *xc_lds = reinterpret_cast<const float2 *>(xs_dyn + (XL ? (KB + 1) * 4 : 0));
     if constexpr (XL) {
-        // the workgroup stages x once, in pair order, plus a zero block
+        // the workgroup stages x once, in pair order, plus a zero block, and
+        // the bias terms of every block
+        float2 *xcw = reinterpret_cast<float2 *>(xs_dyn + (KB + 1) * 4);
         for (int b = threadIdx.x; b <= KB; b += blockDim.x) {
             uint32_t w16[16];
             if (b < KB) {
@@ -384,9 +514,12 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
                 for (int t = 0; t < 16; ++t)
                     w16[t] = 0u;
             }
+            float c[2];
+            bias_terms<FMT>(w16, c);
 #pragma unroll
             for (int u = 0; u < 4; ++u)
                 xs_dyn[b * 4 + u] = make_uint4(w16[4 * u], w16[4 * u + 1], w16[4 * u + 2], w16[4 * u + 3]);
+            xcw[b] = make_float2(c[0], c[1]);
         }
         __syncthreads();
     } else {
@@ -400,118 +533,127 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
                     for (int t = 0; t < 16; ++t)
                         X[m][j][t] = 0u;
                 }
+                bias_terms<FMT>(X[m][j], XC[m][j]);
             }
     }
 
     __shared__ float red[2][kMaxWavesPerWg][kMaxRM];
     int buf = 0;
+    const uint32_t magic = magic_reg();
 
-    // two register sets in ping-pong: the next group's loads are in flight
-    // while the current group is unpacked and multiplied
-    while (g < ngroups) {
+    // Groups g, g + T, g + 2T, ... (T = teams_total), n of them.  The loop
+    // body computes two groups and prefetches the next two; the last one or
+    // two groups are peeled off after it, so no load is ever conditional: on
+    // every path the compiler's wait before a compute then covers exactly
+    // that group's loads (with a conditional prefetch it also waits for the
+    // prefetch, which serializes the two).
+    const int64_t n = (g < ngroups) ? (ngroups - g + teams_total - 1) / teams_total : 0;
+    int64_t k = 0;
+    for (; k + 2 < n; k += 2) {
         float acc[R][M];
-        int64_t gn = g + teams_total;
-        if (gn < ngroups)
-            load_group<FMT, J, R>(gb, W, S, gn * R, p.N, KB, blk);
-        compute_group<FMT, M, J, R, XL>(ga, X, xs_dyn, xoff, ok, g * R, p.N, acc);
-        finish_group<M, R>(acc, y, g * R, p.N, lane, wave, team, kw, p.ksplit, red, buf);
-        g = gn;
-        if (g >= ngroups)
-            break;
-        gn = g + teams_total;
-        if (gn < ngroups)
-            load_group<FMT, J, R>(ga, W, S, gn * R, p.N, KB, blk);
-        compute_group<FMT, M, J, R, XL>(gb, X, xs_dyn, xoff, ok, g * R, p.N, acc);
-        finish_group<M, R>(acc, y, g * R, p.N, lane, wave, team, kw, p.ksplit, red, buf);
-        g = gn;
+        load_group<FMT, G, J, R>(gb, W, S, (g + teams_total) * rows_per_group, rmax, KB, nblocks, coff, soff);
+        __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the compute
+        compute_group<FMT, M, J, R, XL>(ga, X, XC, xs_dyn, xc_lds, xoff, magic, acc);
+        finish_group<G, M, R>(acc, y, g * rows_per_group, rmax, p.N, lane, wave, team, kw, p.ksplit, red, buf);
+        g += teams_total;
+        load_group<FMT, G, J, R>(ga, W, S, (g + teams_total) * rows_per_group, rmax, KB, nblocks, coff, soff);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_group<FMT, M, J, R, XL>(gb, X, XC, xs_dyn, xc_lds, xoff, magic, acc);
+        finish_group<G, M, R>(acc, y, g * rows_per_group, rmax, p.N, lane, wave, team, kw, p.ksplit, red, buf);
+        g += teams_total;
+    }
+    if (n - k == 2) {
+        float acc[R][M];
+        load_group<FMT, G, J, R>(gb, W, S, (g + teams_total) * rows_per_group, rmax, KB, nblocks, coff, soff);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_group<FMT, M, J, R, XL>(ga, X, XC, xs_dyn, xc_lds, xoff, magic, acc);
+        finish_group<G, M, R>(acc, y, g * rows_per_group, rmax, p.N, lane, wave, team, kw, p.ksplit, red, buf);
+        g += teams_total;
+        compute_group<FMT, M, J, R, XL>(gb, X, XC, xs_dyn, xc_lds, xoff, magic, acc);
+        finish_group<G, M, R>(acc, y, g * rows_per_group, rmax, p.N, lane, wave, team, kw, p.ksplit, red, buf);
+    } else if (n - k == 1) {
+        float acc[R][M];
+        compute_group<FMT, M, J, R, XL>(ga, X, XC, xs_dyn, xc_lds, xoff, magic, acc);
+        finish_group<G, M, R>(acc, y, g * rows_per_group, rmax, p.N, lane, wave, team, kw, p.ksplit, red, buf);
     }
 }
 
 // ---------------------------------------------------------------- dispatch
 
-template <int FMT, int M, int J, int R, bool XL>
+template <int FMT, int M, int G, int J, int R, bool XL>
 static hipError_t launch_one(const GemvParams &p, dim3 grid, dim3 block, size_t shmem, hipStream_t stream)
 {
-    return launch_kernel(reinterpret_cast<const void *>(&gemv_kernel<FMT, M, J, R, XL>), grid, block, shmem, stream,
-                         p);
+    return launch_kernel(reinterpret_cast<const void *>(&gemv_kernel<FMT, M, G, J, R, XL>), grid, block, shmem,
+                         stream, p);
 }
 
-// Register budget: R * J code words in flight twice (ping-pong) plus, without
-// XL, J * M resident activation blocks.  R * J <= 8 (Q4_0) / 4 (Q8_0) and
-// J <= 7 (8 with XL) keep every instantiation within 256 registers without
-// spilling.
-template <int FMT, int J, int R, bool XL>
-constexpr bool fits() { return R * J <= (FMT == kQ4_0 ? 8 : 4) && J <= (XL ? 8 : 7); }
-
-template <int FMT, int M, int J, bool XL>
+template <int FMT, int M, int G, int J, bool XL>
 static hipError_t launch_r(int R, const GemvParams &p, dim3 grid, dim3 block, size_t shmem, hipStream_t stream)
 {
-    if constexpr (fits<FMT, J, 1, XL>())
-        if (R == 1) return launch_one<FMT, M, J, 1, XL>(p, grid, block, shmem, stream);
-    if constexpr (fits<FMT, J, 2, XL>())
-        if (R == 2) return launch_one<FMT, M, J, 2, XL>(p, grid, block, shmem, stream);
-    if constexpr (fits<FMT, J, 4, XL>())
-        if (R == 4) return launch_one<FMT, M, J, 4, XL>(p, grid, block, shmem, stream);
+    if constexpr (gemv_fits(FMT, M, G, J, 1, XL))
+        if (R == 1) return launch_one<FMT, M, G, J, 1, XL>(p, grid, block, shmem, stream);
+    if constexpr (gemv_fits(FMT, M, G, J, 2, XL))
+        if (R == 2) return launch_one<FMT, M, G, J, 2, XL>(p, grid, block, shmem, stream);
+    if constexpr (gemv_fits(FMT, M, G, J, 4, XL))
+        if (R == 4) return launch_one<FMT, M, G, J, 4, XL>(p, grid, block, shmem, stream);
+    return hipErrorInvalidValue;
+}
+
+template <int FMT, int M, int G, bool XL>
+static hipError_t launch_j(int J, int R, const GemvParams &p, dim3 grid, dim3 block, size_t shmem,
+                           hipStream_t stream)
+{
+    switch (J) {
+    case 1: return launch_r<FMT, M, G, 1, XL>(R, p, grid, block, shmem, stream);
+    case 2: return launch_r<FMT, M, G, 2, XL>(R, p, grid, block, shmem, stream);
+    case 3: return launch_r<FMT, M, G, 3, XL>(R, p, grid, block, shmem, stream);
+    case 4: return launch_r<FMT, M, G, 4, XL>(R, p, grid, block, shmem, stream);
+    case 5: return launch_r<FMT, M, G, 5, XL>(R, p, grid, block, shmem, stream);
+    case 6: return launch_r<FMT, M, G, 6, XL>(R, p, grid, block, shmem, stream);
+    case 7: return launch_r<FMT, M, G, 7, XL>(R, p, grid, block, shmem, stream);
+    case 8: return launch_r<FMT, M, G, 8, XL>(R, p, grid, block, shmem, stream);
+    }
     return hipErrorInvalidValue;
 }
 
 template <int FMT, int M, bool XL>
-static hipError_t launch_j(int J, int R, const GemvParams &p, dim3 grid, dim3 block, size_t shmem,
+static hipError_t launch_g(int G, int J, int R, const GemvParams &p, dim3 grid, dim3 block, size_t shmem,
                            hipStream_t stream)
 {
-    // J * M <= 8 keeps resident activations at <= 128 registers
+    // narrow row segments only for one token (the register cost of resident
+    // activations grows with M)
     if constexpr (M == 1) {
-        switch (J) {
-        case 1: return launch_r<FMT, 1, 1, XL>(R, p, grid, block, shmem, stream);
-        case 2: return launch_r<FMT, 1, 2, XL>(R, p, grid, block, shmem, stream);
-        case 3: return launch_r<FMT, 1, 3, XL>(R, p, grid, block, shmem, stream);
-        case 4: return launch_r<FMT, 1, 4, XL>(R, p, grid, block, shmem, stream);
-        case 5: return launch_r<FMT, 1, 5, XL>(R, p, grid, block, shmem, stream);
-        case 6: return launch_r<FMT, 1, 6, XL>(R, p, grid, block, shmem, stream);
-        case 7: return launch_r<FMT, 1, 7, XL>(R, p, grid, block, shmem, stream);
-        case 8: return launch_r<FMT, 1, 8, XL>(R, p, grid, block, shmem, stream);
-        }
-    } else if constexpr (M == 2) {
-        switch (J) {
-        case 1: return launch_r<FMT, 2, 1, false>(R, p, grid, block, shmem, stream);
-        case 2: return launch_r<FMT, 2, 2, false>(R, p, grid, block, shmem, stream);
-        case 3: return launch_r<FMT, 2, 3, false>(R, p, grid, block, shmem, stream);
-        case 4: return launch_r<FMT, 2, 4, false>(R, p, grid, block, shmem, stream);
-        }
-    } else if constexpr (M <= 4) {
-        switch (J) {
-        case 1: return launch_r<FMT, M, 1, false>(R, p, grid, block, shmem, stream);
-        case 2: return launch_r<FMT, M, 2, false>(R, p, grid, block, shmem, stream);
-        }
-    } else {
-        if (J == 1)
-            return launch_r<FMT, M, 1, false>(R, p, grid, block, shmem, stream);
+        if (G == 16) return launch_j<FMT, M, 16, XL>(J, R, p, grid, block, shmem, stream);
+        if (G == 32) return launch_j<FMT, M, 32, XL>(J, R, p, grid, block, shmem, stream);
     }
+    if (G == 64) return launch_j<FMT, M, 64, XL>(J, R, p, grid, block, shmem, stream);
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemv(int fmt, int M, int J, int R, bool xl, const GemvParams &p, dim3 grid, dim3 block,
+size_t gemv_xl_lds_bytes(int K) { return (size_t)(K / 32 + 1) * 72; }
+
+hipError_t launch_gemv(int fmt, int M, int G, int J, int R, bool xl, const GemvParams &p, dim3 grid, dim3 block,
                        hipStream_t stream)
 {
-    // XL: one token, one wave per row group, activations staged in LDS
-    // (K/32 blocks of 64 bytes plus one zero block)
-    const size_t shmem = xl ? (size_t)(p.K / 32 + 1) * 64 : 0;
+    // XL: one token, activations and their bias terms staged in LDS (K/32
+    // blocks of 64 + 8 bytes plus a zero block)
     if (xl) {
         if (M != 1 || p.ksplit != 1)
             return hipErrorInvalidValue;
-        return fmt == kQ4_0 ? launch_j<kQ4_0, 1, true>(J, R, p, grid, block, shmem, stream)
-                            : launch_j<kQ8_0, 1, true>(J, R, p, grid, block, shmem, stream);
+        const size_t shmem = gemv_xl_lds_bytes(p.K);
+        return fmt == kQ4_0 ? launch_g<kQ4_0, 1, true>(G, J, R, p, grid, block, shmem, stream)
+                            : launch_g<kQ8_0, 1, true>(G, J, R, p, grid, block, shmem, stream);
     }
-#define QG_CASE_M(FMT)                                                                \
-    switch (M) {                                                                      \
-    case 1: return launch_j<FMT, 1, false>(J, R, p, grid, block, 0, stream);          \
-    case 2: return launch_j<FMT, 2, false>(J, R, p, grid, block, 0, stream);          \
-    case 3: return launch_j<FMT, 3, false>(J, R, p, grid, block, 0, stream);          \
-    case 4: return launch_j<FMT, 4, false>(J, R, p, grid, block, 0, stream);          \
-    case 5: return launch_j<FMT, 5, false>(J, R, p, grid, block, 0, stream);          \
-    case 6: return launch_j<FMT, 6, false>(J, R, p, grid, block, 0, stream);          \
-    case 7: return launch_j<FMT, 7, false>(J, R, p, grid, block, 0, stream);          \
-    case 8: return launch_j<FMT, 8, false>(J, R, p, grid, block, 0, stream);          \
+#define QG_CASE_M(FMT)                                                                   \
+    switch (M) {                                                                         \
+    case 1: return launch_g<FMT, 1, false>(G, J, R, p, grid, block, 0, stream);          \
+    case 2: return launch_g<FMT, 2, false>(G, J, R, p, grid, block, 0, stream);          \
+    case 3: return launch_g<FMT, 3, false>(G, J, R, p, grid, block, 0, stream);          \
+    case 4: return launch_g<FMT, 4, false>(G, J, R, p, grid, block, 0, stream);          \
+    case 5: return launch_g<FMT, 5, false>(G, J, R, p, grid, block, 0, stream);          \
+    case 6: return launch_g<FMT, 6, false>(G, J, R, p, grid, block, 0, stream);          \
+    case 7: return launch_g<FMT, 7, false>(G, J, R, p, grid, block, 0, stream);          \
+    case 8: return launch_g<FMT, 8, false>(G, J, R, p, grid, block, 0, stream);          \
     }
     if (fmt == kQ4_0) {
         QG_CASE_M(kQ4_0)

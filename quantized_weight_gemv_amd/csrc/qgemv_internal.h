@@ -42,7 +42,32 @@ inline hipError_t launch_kernel(const void *fn, dim3 grid, dim3 block, size_t sh
     return launch_raw(fn, grid, block, a, shmem, stream);
 }
 
-hipError_t launch_gemv(int fmt, int M, int J, int R, bool xl, const GemvParams &p, dim3 grid, dim3 block,
+// Which vector-ALU GEMV instantiations exist (G lanes per row, J blocks per
+// lane, R row sets per group, xl: activations in LDS).  Register estimate: R *
+// J code words and scales in flight twice (ping-pong; 5 registers per Q4_0
+// block, 9 per Q8_0 block), without XL J * M resident activation blocks of 16
+// registers plus 2 bias terms, R * M sums and ~36 temporaries; keeping it
+// within 256 (and R * J <= 8 / 4, J <= 7, 8 with XL, J * M <= 8) leaves every
+// instantiation free of spills.  Rows narrower than a wave (G < 64) and XL are
+// for one token; XL uses G = 64.
+constexpr bool gemv_fits(int fmt, int M, int G, int J, int R, bool xl)
+{
+    if (G != 16 && G != 32 && G != 64)
+        return false;
+    if (M != 1 && (G != 64 || xl))
+        return false;
+    if (xl && G != 64)
+        return false;
+    if (R * J > (fmt == kQ4_0 ? 8 : 4) || J > (xl ? 8 : 7) || (!xl && J * M > 8))
+        return false;
+    const int regs = 2 * R * J * (fmt == kQ4_0 ? 5 : 9) + (xl ? 0 : J * M * 18) + R * M + 36;
+    return regs <= 256 && R * M * (64 / G) <= kMaxRM;
+}
+
+// LDS bytes of the XL activation copy for a row of K weights.
+size_t gemv_xl_lds_bytes(int K);
+
+hipError_t launch_gemv(int fmt, int M, int G, int J, int R, bool xl, const GemvParams &p, dim3 grid, dim3 block,
                        hipStream_t stream);
 
 // Few-token GEMV on the matrix cores (qgemv_mfma.hip): `waves` waves split K.

@@ -241,33 +241,36 @@ def test_outputs_stay_in_bounds():
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FNAME[f])
-@pytest.mark.parametrize("N,K,M", [(257, 4096, 1), (100, 14336, 1), (33, 2560, 1), (70, 6144, 2), (130, 2048, 8)])
+@pytest.mark.parametrize("N,K,M", [(257, 4096, 1), (100, 14336, 1), (33, 2560, 1), (70, 6144, 2), (130, 2048, 8),
+                                   (5, 512, 1), (3, 1024, 1), (1, 64, 1)])
 def test_gemv_every_launch_shape(fmt, N, K, M):
-    """Parity for the launch shapes the tuning knob can select (rows per
-    group, teams, workgroup size, K split, LDS-staged activations)."""
+    """Parity for the launch shapes the tuning knob can select (lanes per row,
+    blocks per lane, row sets per group, teams, workgroup size, K split,
+    LDS-staged activations), including row sets clamped at the matrix tail."""
     q = qg()
     w = weights(N, K, seed=N)
     x = acts(M, K, seed=K)
     pb, po = pack_both(fmt, w)
     Wd, xd = to_dev(pb), to_dev(x)
     y_ref, s = oracle.get().gemv(fmt, po, N, K, x)
-    tried = 0
+    tried = set()
     try:
-        for R in (1, 2, 4):
-            for tpw in (1, 2, 8):
-                for teams in (1, 7, 100000):
-                    for ks in (0, 2, 3):
-                        for xl in (-1, 0, 1):
-                            q.qg_set_gemv_shape(0, R, ks, tpw, teams, xl, 0)
-                            try:
-                                y = _gemv(fmt, Wd, xd, N, K)
-                            except q.QGError:
-                                continue
-                            tried += 1
-                            assert_within(y, y_ref, s, f"R{R} tpw{tpw} teams{teams} ks{ks} xl{xl}")
+        for lanes in (0, 16, 32, 64):
+            for J in (0, 1, 2, 3, 5, 7):
+                for R in (1, 2, 4):
+                    for ks in (0, 2):
+                        for tpw, teams in ((1, 1), (2, 7), (8, 100000)):
+                            for xl in (-1, 0, 1):
+                                q.qg_set_gemv_shape(J, R, ks, tpw, teams, xl, 0, lanes)
+                                try:
+                                    y = _gemv(fmt, Wd, xd, N, K)
+                                except q.QGError:
+                                    continue
+                                tried.add((lanes, J, R, ks, xl))
+                                assert_within(y, y_ref, s, f"G{lanes} J{J} R{R} tpw{tpw} teams{teams} ks{ks} xl{xl}")
     finally:
-        q.qg_set_gemv_shape(0, 0, 0, 0, 0, -1, -1)
-    assert tried >= 10
+        q.qg_set_gemv_shape(0, 0, 0, 0, 0, -1, -1, 0)
+    assert len(tried) >= 10
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FNAME[f])
@@ -286,14 +289,14 @@ def test_gemv_matrix_core_engine(fmt, N, K, M):
     tried = 0
     try:
         for ks in (0, 1, 2, 3, 4, 6, 7, 8):
-            q.qg_set_gemv_shape(0, 0, ks, 0, 0, -1, 1)
+            q.qg_set_gemv_shape(0, 0, ks, 0, 0, -1, 1, 0)
             try:
                 y = _gemv(fmt, Wd, xd, N, K)
             except q.QGError:
                 continue
             tried += 1
             assert_within(y, y_ref, s, f"mfma waves={ks}")
-        q.qg_set_gemv_shape(0, 0, 0, 0, 0, -1, 1)
+        q.qg_set_gemv_shape(0, 0, 0, 0, 0, -1, 1, 0)
         cols = [0, 5, 16, 31, K - 1]
         xo = np.zeros((len(cols), K), np.float16)
         for i, k in enumerate(cols):
@@ -303,5 +306,5 @@ def test_gemv_matrix_core_engine(fmt, N, K, M):
         for i, k in enumerate(cols):
             assert np.array_equal(y[i], wh[:, k]), f"one-hot column {k}"
     finally:
-        q.qg_set_gemv_shape(0, 0, 0, 0, 0, -1, -1)
+        q.qg_set_gemv_shape(0, 0, 0, 0, 0, -1, -1, 0)
     assert tried >= 2   # long rows admit only the larger wave counts (<= 32 blocks per wave)
