@@ -125,15 +125,13 @@ __device__ __forceinline__ void unpack_q8(const uint4 c0, const uint4 c1, uint32
 __device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
 __device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
 
-// The 32 fp16 activations of one block (64 bytes at p) as the 16 pairs that
-// match unpack_q4 / unpack_q8.
+// The 32 fp16 activations of one block (64 bytes, raw words r) as the 16
+// pairs that match unpack_q4 / unpack_q8.
 template <int FMT>
-__device__ __forceinline__ void load_x_block(const uint16_t *p, uint32_t (&X)[16])
+__device__ __forceinline__ void pair_x_block(const uint4 (&r)[4], uint32_t (&X)[16])
 {
-    const uint4 *q = reinterpret_cast<const uint4 *>(p);
-    const uint4 r0 = q[0], r1 = q[1], r2 = q[2], r3 = q[3];
-    const uint32_t d[16] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w,
-                            r2.x, r2.y, r2.z, r2.w, r3.x, r3.y, r3.z, r3.w};
+    const uint32_t d[16] = {r[0].x, r[0].y, r[0].z, r[0].w, r[1].x, r[1].y, r[1].z, r[1].w,
+                            r[2].x, r[2].y, r[2].z, r[2].w, r[3].x, r[3].y, r[3].z, r[3].w};
     // d[i] = (x[2i], x[2i+1])
     if constexpr (FMT == kQ4_0) {
 #pragma unroll
@@ -150,6 +148,22 @@ __device__ __forceinline__ void load_x_block(const uint16_t *p, uint32_t (&X)[16
             X[2 * t + 1] = pair_hi(d[2 * t], d[2 * t + 1]);
         }
     }
+}
+
+__device__ __forceinline__ void load_x_raw(const uint16_t *p, uint4 (&r)[4])
+{
+    const uint4 *q = reinterpret_cast<const uint4 *>(p);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+        r[u] = q[u];
+}
+
+template <int FMT>
+__device__ __forceinline__ void load_x_block(const uint16_t *p, uint32_t (&X)[16])
+{
+    uint4 r[4];
+    load_x_raw(p, r);
+    pair_x_block<FMT>(r, X);
 }
 
 // Starting values of a block's two dot chains: minus the bias times the
@@ -493,14 +507,29 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
     int64_t g = team_id;
 
     Group<FMT, J, R> ga, gb;
-    if (g < ngroups)
-        load_group<FMT, G, J, R>(ga, W, S, g * rows_per_group, rmax, KB, nblocks, coff, soff);
 
-    // activations of this lane's blocks, all M tokens, kept for every row
+    // Activations of this lane's blocks, all M tokens, kept for every row.
+    // Their loads are issued before the first weight loads: they hit in the
+    // cache after the first waves, and queued behind a full round of weight
+    // requests they would hold up every wave's first compute.
     uint32_t X[XL ? 1 : M][XL ? 1 : J][16];
     float XC[XL ? 1 : M][XL ? 1 : J][2];
     extern __shared__ uint4 xs_dyn[];
     const float2 *xc_lds = reinterpret_cast<const float2 *>(xs_dyn + (XL ? (KB + 1) * 4 : 0));
+    uint4 XR[XL ? 1 : M][XL ? 1 : J][4];   // raw activation words, paired below
+    if constexpr (!XL) {
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int j = 0; j < J; ++j)
+                load_x_raw(x + (int64_t)m * p.K + (int64_t)blk[j] * 32, XR[m][j]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // unconditional (a team without groups re-reads a clamped, in-bounds row
+    // set): with a conditional load the wait for the activations below would
+    // also cover these weights
+    load_group<FMT, G, J, R>(ga, W, S, g * rows_per_group, rmax, KB, nblocks, coff, soff);
+    __builtin_amdgcn_sched_barrier(0);
     if constexpr (XL) {
         // the workgroup stages x once, in pair order, plus a zero block, and
         // the bias terms of every block
@@ -527,7 +556,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
         for (int m = 0; m < M; ++m)
 #pragma unroll
             for (int j = 0; j < J; ++j) {
-                load_x_block<FMT>(x + (int64_t)m * p.K + (int64_t)blk[j] * 32, X[m][j]);
+                pair_x_block<FMT>(XR[m][j], X[m][j]);
                 if (!ok[j]) {
 #pragma unroll
                     for (int t = 0; t < 16; ++t)
