@@ -103,6 +103,35 @@ def run_step(work, timer=None):
         w["calls"][c]()
 
 
+def per_shape_graph_us(qg, torch, work, calls_per_shape: int = 64) -> dict:
+    """Microseconds per call of each shape launched back to back: one captured
+    graph of `calls_per_shape` consecutive calls (cycling the copies), replayed
+    once and timed with stream events around the replay.  Unlike per-launch
+    events this includes the dispatch gap between calls and nothing else."""
+    out = {}
+    for w in work:
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            calls = [qg.PreparedGemv(qg.Q4_0, w["buf"][c * w["nb"]:(c + 1) * w["nb"]], w["x"], w["y"], w["N"],
+                                     w["K"]) for c in range(w["copies"])]
+            with torch.cuda.graph(g, stream=cap):
+                for i in range(calls_per_shape):
+                    calls[i % w["copies"]]()
+        torch.cuda.synchronize()
+        g.replay()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record()
+        g.replay()
+        e.record()
+        torch.cuda.synchronize()
+        out[f"{w['N']}x{w['K']}"] = s.elapsed_time(e) * 1e3 / calls_per_shape
+        del g
+    return out
+
+
 def hbm_probe(qg, torch, gib: int = 4, reps: int = 5) -> float:
     buf = torch.empty(gib << 30, dtype=torch.uint8, device="cuda")
     buf.fill_(1)
@@ -372,6 +401,12 @@ def main() -> int:
                                            "algorithmic_bytes": w["bytes"], "copies": w["copies"]}
     kernel_s_per_step = ms.sum(axis=1).mean() * 1e-3
     achieved = step_bytes / kernel_s_per_step / 1e9
+
+    b2b = per_shape_graph_us(qg, torch, work)
+    for key, us in b2b.items():
+        rec = per_shape[key]
+        rec["us_per_call_back_to_back"] = round(us, 3)
+        rec["GBps_back_to_back"] = round(rec["algorithmic_bytes"] / (us * 1e-6) / 1e9, 1)
 
     probe = None if args.no_probe else round(hbm_probe(qg, torch), 1)
 
