@@ -307,6 +307,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time value with eager launches instead of a graph")
+    ap.add_argument("--no-back-to-back", action="store_true",
+                    help="skip the per-shape back-to-back pass (profiler runs: only interleaved steps)")
     ap.add_argument("--suite", default=None, metavar="FILE",
                     help="instead of the headline step, time every workload (GEMV both formats and M = 1..8, "
                          "MoE, prefill with its dense fp16 comparator) and write one JSON record per line to FILE")
@@ -402,7 +404,7 @@ def main() -> int:
     kernel_s_per_step = ms.sum(axis=1).mean() * 1e-3
     achieved = step_bytes / kernel_s_per_step / 1e9
 
-    b2b = per_shape_graph_us(qg, torch, work)
+    b2b = {} if args.no_back_to_back else per_shape_graph_us(qg, torch, work)
     for key, us in b2b.items():
         rec = per_shape[key]
         rec["us_per_call_back_to_back"] = round(us, 3)

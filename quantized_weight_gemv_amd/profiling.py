@@ -4,6 +4,7 @@ under profiles/.
     python -m quantized_weight_gemv_amd.profiling stats <kernel_stats.csv> <kernel_trace.csv> <out.md> <command>
     python -m quantized_weight_gemv_amd.profiling traffic <fetch_counter_collection.csv>
            <write_counter_collection.csv> <out.json> <command-fetch> <command-write>
+    python -m quantized_weight_gemv_amd.profiling suite <kernel_stats.csv> <suite.jsonl> <out.md> <command>
 
 Traffic calibration: the bench's own weight-copy kernels (__amd_rocclr_copyBuffer
 of known sizes, dispatched while it builds its workload) give the factor each
@@ -68,6 +69,8 @@ def traffic(fetch_csv, write_csv, out_json, cmd_f, cmd_w):
     fw = statistics.median(float(r["Counter_Value"]) * 1024 / nb for r, nb in zip(cw, sizes))
     gf = [r for r in F if "gemv_kernel" in r["Kernel_Name"]]
     gw = [r for r in W if "gemv_kernel" in r["Kernel_Name"]]
+    # bench.py --no-back-to-back: every GEMV dispatch belongs to an interleaved
+    # step of the six shapes
     assert len(gf) == len(gw) and len(gf) % len(LLAMA_SHAPES) == 0
     per = {}
     for i, (N, K) in enumerate(LLAMA_SHAPES):
@@ -100,19 +103,51 @@ def stats(stats_csv, trace_csv, out_md, cmd):
              "", "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
     for r in rows:
         lines.append(f"| `{r['Name'][:70]}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} |")
-    by = {}
-    for r in g:
-        key = (r["Kernel_Name"], r["Grid_Size_X"])
-        by.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-    lines += ["", "GEMV dispatches by launch (grid threads): average / median duration", "",
-              "| kernel | grid threads | calls | average us | median us |", "|---|---|---|---|---|"]
-    for (name, grid), v in by.items():
-        lines.append(f"| `{name[:60]}` | {grid} | {len(v)} | {statistics.mean(v) / 1e3:.3f} | "
-                     f"{statistics.median(v) / 1e3:.3f} |")
+    # bench.py --no-back-to-back launches the six shapes in step order
+    assert len(g) % len(LLAMA_SHAPES) == 0, len(g)
+    lines += ["", "GEMV dispatches per shape (every step launches the six shapes in this order): average / median "
+                  "duration", "", "| shape N x K | kernel | grid threads | calls | average us | median us |",
+              "|---|---|---|---|---|---|"]
+    for i, (N, K) in enumerate(LLAMA_SHAPES):
+        rs = g[i::len(LLAMA_SHAPES)]
+        v = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rs]
+        lines.append(f"| {N}x{K} | `{rs[0]['Kernel_Name'][:60]}` | {rs[0]['Grid_Size_X']} | {len(v)} | "
+                     f"{statistics.mean(v) / 1e3:.3f} | {statistics.median(v) / 1e3:.3f} |")
     gaps = [int(b["Start_Timestamp"]) - int(a["End_Timestamp"]) for a, b in zip(g, g[1:])]
     if gaps:
         lines += ["", f"Gap between consecutive GEMV dispatches: median {statistics.median(gaps) / 1e3:.2f} us "
                       f"(host launch path included)."]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def suite(stats_csv, suite_jsonl, out_md, cmd):
+    """Kernel statistics of a rocprofv3 run of `bench.py --suite` plus the
+    per-workload medians of a plain (unprofiled) suite run."""
+    rows = list(csv.DictReader(open(stats_csv)))
+    recs = [json.loads(l) for l in open(suite_jsonl) if l.strip()]
+    lines = ["# rocprofv3 kernel statistics: every workload of bench.py --suite", "",
+             "GEMV Q4_0 2048x2048; small-batch GEMV Q4_0/Q8_0 at 1, 2, 4, 8 tokens on 6144x2048, 2048x6144, "
+             "8192x2048;", "one-launch MoE (10 of 128 experts 640x2560, 8 of 256 experts 512x2048); Q4_0 prefill "
+             "at 64 and 512 tokens", "on 12288x2560, 2560x6144, 6144x2048 with the dense fp16 GEMM on "
+             "pre-dequantized weights beside it.", "", "Command:", "", "```", cmd, "```", "",
+             "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| `{r['Name'][:80]}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | "
+                     f"{r['MaxNs']} |")
+    lines += ["", "Per-workload medians of a separate, unprofiled `bench.py --suite` run (kernel events; prefill: "
+                  "whole call incl. the zero fill of split-K launches):", "",
+              "| workload | median us | GB/s or TFLOP/s |", "|---|---|---|"]
+    for r in recs:
+        if r["kind"] == "gemv":
+            lines.append(f"| GEMV {r['fmt']} {r['N']}x{r['K']} M={r['M']} | {r['us_median']} | {r['GBps']} GB/s |")
+        elif r["kind"] == "moe":
+            lines.append(f"| MoE {r['fmt']} {r['E']} of {r['P']} x {r['N']}x{r['K']} | {r['us_median']} | "
+                         f"{r['GBps']} GB/s |")
+        else:
+            lines.append(f"| prefill {r['fmt']} {r['N']}x{r['K']} M={r['M']} | {r['us_median']} (dense fp16 "
+                         f"{r['dense_fp16_us_median']}) | {r['TFLOPs']} TFLOP/s |")
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -123,5 +158,7 @@ if __name__ == "__main__":
         stats(*sys.argv[2:6])
     elif sys.argv[1] == "traffic":
         traffic(*sys.argv[2:7])
+    elif sys.argv[1] == "suite":
+        suite(*sys.argv[2:6])
     else:
         raise SystemExit(__doc__)
