@@ -103,11 +103,25 @@ bool choose_shape(int fmt, int M, int64_t N, int64_t K, int items, int cus, Gemv
     int J = static_cast<int>(std::max<int64_t>(1, (KB + 8LL * G - 1) / (8LL * G)));
     if (xl)
         J = static_cast<int>((KB + G - 1) / G);
+    // Two to four tokens: two blocks per lane where that halves the waves
+    // along K without leaving half of the last wave idle (rows a multiple of
+    // 128 blocks, or longer than 384).  Measured on MI355X, Q4_0 at two
+    // tokens: 4096 x 4096 4.6 against 5.0 us, 14336 x 4096 8.7 against
+    // 10.7 us; 2048 x 6144 (192 blocks) stays faster with one block per lane.
+    if (M >= 2 && M <= 4 && !xl && J == 1 && KB > 64 && (KB % 128 == 0 || KB > 384))
+        J = 2;
     int ksplit = static_cast<int>((KB + static_cast<int64_t>(G) * J - 1) / (static_cast<int64_t>(G) * J));
     const int rj = (fmt == kQ4_0) ? 8 : 4;   // R * J budget of the kernel table
-    // Two row sets per group, four for full-wave rows beyond 64K rows
-    // (launch sweeps on MI355X, 256 CUs).
+    // Two row sets per group, four for full-wave rows beyond 64K rows, and
+    // four for several tokens with K split over waves (launch sweeps on
+    // MI355X, 256 CUs: Q4_0 2048 x 6144 at six tokens 7.9 against 8.5 us).
+    // Q8_0 holds twice the code registers per row set: there four pay only
+    // where one group per team then covers all rows (Q8_0 4096 x 14336 at
+    // six tokens: 26.0 us with four, 25.2 with two).
     int R = (N > 65536 && G == 64) ? 4 : 2;
+    if (M >= 2 && J == 1 && ksplit > 1 &&
+        (fmt == kQ4_0 || N <= 4LL * cus * std::max(2, 8 / ksplit)))
+        R = 4;
     while (R * J > rj && R > 1)
         R /= 2;
     // stay within the instantiated kernels (register budget): fewer row sets,
@@ -153,6 +167,13 @@ bool choose_shape(int fmt, int M, int64_t N, int64_t K, int items, int cus, Gemv
     if (N > 65536 && M == 1)
         per_cu = 64;
     int64_t teams = std::max<int64_t>(1, static_cast<int64_t>(cus) * per_cu / std::max(1, items));
+    // Several tokens, two blocks per lane, whole rows per wave: at least two
+    // groups per team, so the prefetch of the next group overlaps the current
+    // one (4096 x 4096 at two tokens: 1024 teams 4.6 us, 2048 teams 5.1;
+    // with one block per lane, 6144 x 2048 prefers 2048 teams, 4.1 against
+    // 4.6 us).
+    if (M >= 2 && J >= 2 && ksplit == 1 && items == 1)
+        teams = std::min(teams, std::max<int64_t>(1, (ngroups + 1) / 2));
     if (o_teams)
         teams = o_teams;
     teams = std::min(teams, ngroups);
@@ -173,12 +194,17 @@ qg_status run_gemv(int fmt, const void *Wp, const int32_t *idx, int64_t P, const
     const int cus = device_cus();
     if (cus <= 0)
         return QG_ERR_DEVICE;
-    // Four or more tokens (plain GEMV, rows up to 256 blocks long): the
-    // matrix-core kernel, whose unpack cost per block does not grow with M
-    // (measured on MI355X: 6144 x 2048 at 8 tokens 7.1 us against 15.3 us on
-    // the vector path; at 2 tokens the vector path is faster, 4.8 vs 6.4 us).
+    // Many tokens on short rows (plain GEMV): the matrix-core kernel, whose
+    // unpack cost per block does not grow with M.  It needs at least one
+    // 16-row tile per CU, and the vector kernel stays faster below five tokens
+    // for Q4_0 and seven for Q8_0, and on longer rows (measured on MI355X:
+    // Q4_0 8192 x 2048 at 8 tokens 7.3 against 9.6 us, at 4 tokens 6.6
+    // against 6.3; Q8_0 14336 x 4096 at 8 tokens 29.3 against 25.0 us;
+    // 2048 x 6144 is faster on the vector kernel at every token count).
     const int64_t KB = K / 32;
-    bool mfma = (idx == nullptr && M >= 4 && KB <= 256);
+    const bool tiles_fill = N >= 16LL * cus;
+    bool mfma = idx == nullptr && tiles_fill &&
+                ((fmt == kQ4_0 && M >= 5 && KB <= 128) || (fmt == kQ8_0 && M >= 7 && KB <= 64));
     if (o_engine >= 0)
         mfma = (o_engine == 1);
     if (mfma) {
