@@ -159,7 +159,8 @@ qg_status qg_device_cus(int device, int *cus);
  * number of teams, xl (activations of a one-token call staged in LDS: 1,
  * kept in registers: 0), engine (vector-ALU kernel: 0; matrix-core kernel
  * for 2..8 tokens and rows of at most 256 blocks: 1, where ksplit is its
- * number of waves along K) and lanes_per_row (lanes of a wave that share one
+ * number of waves along K and teams its number of persistent workgroups)
+ * and lanes_per_row (lanes of a wave that share one
  * row in the vector-ALU kernel: 16, 32 or 64; below 64 one token only) for
  * later calls from the calling thread.  A zero (-1 for xl and engine) keeps
  * the built-in per-shape choice for that field.  An impossible combination

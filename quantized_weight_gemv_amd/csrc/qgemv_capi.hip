@@ -194,27 +194,32 @@ qg_status run_gemv(int fmt, const void *Wp, const int32_t *idx, int64_t P, const
     const int cus = device_cus();
     if (cus <= 0)
         return QG_ERR_DEVICE;
-    // Many tokens on short rows (plain GEMV): the matrix-core kernel, whose
-    // unpack cost per block does not grow with M.  It needs at least one
-    // 16-row tile per CU, and the vector kernel stays faster below five tokens
-    // for Q4_0 and seven for Q8_0, and on longer rows (measured on MI355X:
-    // Q4_0 8192 x 2048 at 8 tokens 7.3 against 9.6 us, at 4 tokens 6.6
-    // against 6.3; Q8_0 14336 x 4096 at 8 tokens 29.3 against 25.0 us;
-    // 2048 x 6144 is faster on the vector kernel at every token count).
+    // Several tokens on short rows (plain GEMV): the matrix-core kernel,
+    // whose unpack cost per block does not grow with M.  It wants at least
+    // one 16-row tile per CU; the vector kernel stays faster below four
+    // tokens, and for Q8_0 (whose vector unpack is cheaper) below six on rows
+    // of 128 blocks.  Measured on MI355X: Q4_0 8192 x 2048 at 4 tokens 5.5
+    // against 6.3 us, at 8 tokens 5.9 against 9.6; Q8_0 14336 x 4096 at 4
+    // tokens 19.0 against 16.3, at 8 tokens 19.9 against 25.0.  With 2048 rows
+    // half the chip idles and only Q4_0 at 8 tokens gains (2048 x 6144: 9.0
+    // against 9.6 us; at 6 tokens 8.9 against 7.9).
     const int64_t KB = K / 32;
     const bool tiles_fill = N >= 16LL * cus;
-    bool mfma = idx == nullptr && tiles_fill &&
-                ((fmt == kQ4_0 && M >= 5 && KB <= 128) || (fmt == kQ8_0 && M >= 7 && KB <= 64));
+    bool mfma = idx == nullptr &&
+                ((tiles_fill && fmt == kQ4_0 && M >= 4 && KB <= 128) ||
+                 (tiles_fill && fmt == kQ8_0 && ((M >= 4 && KB <= 64) || (M >= 6 && KB <= 128))) ||
+                 (N >= 8LL * cus && fmt == kQ4_0 && M == 8 && KB <= 256));
     if (o_engine >= 0)
         mfma = (o_engine == 1);
     if (mfma) {
         if (idx != nullptr || KB > 256 || N > INT32_MAX)
             return QG_ERR_SHAPE;
-        int waves = static_cast<int>(std::min<int64_t>(8, std::max<int64_t>(1, (KB + 7) / 8)));
+        // about 16 blocks per wave (sweeps: 4 waves for K = 2048, 8 for 4096)
+        int waves = static_cast<int>(std::min<int64_t>(8, std::max<int64_t>(1, (KB + 15) / 16)));
         if (o_ksplit)
             waves = o_ksplit;
         hipError_t e = launch_gemv_mfma(fmt, static_cast<const uint8_t *>(Wp), scale_offset(fmt, N, K), x, y, M,
-                                        static_cast<int>(N), static_cast<int>(K), waves,
+                                        static_cast<int>(N), static_cast<int>(K), waves, o_teams, cus,
                                         static_cast<hipStream_t>(stream));
         if (e == hipErrorInvalidValue)
             return QG_ERR_SHAPE;

@@ -248,34 +248,6 @@ struct Group {
     uint16_t scale[R][J];
 };
 
-// Weight bytes are read once per call: they are loaded non-temporal so the
-// stream does not displace the activations from the caches (measured on
-// MI355X: 6.5 TB/s against 6.0 TB/s with plain loads on the 296 MB
-// 128256 x 4096 matrix).  The loads are buffer loads: the row set's base
-// address and extent live in a scalar resource descriptor, each lane adds a
-// loop-invariant 32-bit offset, so no vector instruction is spent on
-// addresses, and the hardware range check returns zeros rather than reading
-// past the matrix.
-constexpr int kNtAux = 2;                     // cache policy: non-temporal
-constexpr int kRsrcWord3 = 0x00020000;        // raw (untyped) buffer, gfx9 family
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t *base, int64_t bytes)
-{
-    const int n = (int)min(bytes, (int64_t)0x7FFFFFFF);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), (short)0, n, kRsrcWord3);
-}
-
-__device__ __forceinline__ uint4 stream_load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
-{
-    const auto t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNtAux);
-    return make_uint4(t[0], t[1], t[2], t[3]);
-}
-
-__device__ __forceinline__ uint16_t stream_load2(__amdgpu_buffer_rsrc_t r, uint32_t off)
-{
-    return (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kNtAux);
-}
-
 // Issue the loads of one group (R row sets from row rs0).  Each row set's
 // first row is wave-uniform and clamped to rmax = N - P, so every lane's row
 // rbase + l / G stays inside the matrix; lanes add a 32-bit offset (coff,

@@ -12,22 +12,25 @@
 // as fp16, each MFMA sums the 32 exact products of one block into fp32, and
 // the block's scale multiplies that sum in fp32 afterwards.
 //
-// Mapping: a workgroup owns 16 consecutive rows; its `ksplit` waves split K.
-// Per step a lane loads 16 code bytes with one 16-byte load: lane l reads row
+// Mapping: a workgroup walks 16-row tiles (tiles w, w + grid, ...: a
+// persistent grid, so each workgroup stages its activations once); its
+// `ksplit` waves split K.  Per step a lane loads 16 code bytes with one 16-byte load: lane l reads row
 // n0 + l%16, block b0 + l/16 (Q4_0; four blocks of the 16 rows per
 // instruction, 64 contiguous bytes per row).  The 16x16x32 B operand wants
 // lane group g to hold word g of one block, so the four words are transposed
 // across the four 16-lane groups with v_permlane32_swap and v_permlane16_swap
 // (Q8_0 blocks are 32 bytes: two blocks per load, one swap stage, and the k
 // order inside a block is permuted the same way in the activations, which
-// leaves the contraction unchanged).  Each wave issues all of its code and
-// scale loads (one scale per lane per step, broadcast to the row's lane groups
-// with the same swaps) before the first MFMA, and stages its activation slice
-// in LDS with coalesced 16-byte loads, already in operand order, so an A
-// operand is one ds_read_b128.  Partial 16x16 tiles of the waves are summed
+// leaves the contraction unchanged).  Each wave issues all of a tile's code
+// and scale loads (one scale per lane per step, broadcast to the row's lane
+// groups with the same swaps) before that tile's first MFMA, and the next
+// tile's while it multiplies the current one.  It stages its activation slice
+// in LDS once, with coalesced 16-byte loads, already in operand order, so an
+// A operand is one ds_read_b128.  Partial 16x16 tiles of the waves are summed
 // through LDS in a fixed order: results are reproducible.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "qgemv_internal.h"
@@ -146,99 +149,123 @@ __device__ __forceinline__ void permute_x(const uint4 (&r)[4], uint4 (&o)[4])
         o[q] = make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
 }
 
-template <int FMT, int KWMAX>
-__global__ __launch_bounds__(512) void gemv_mfma_kernel(MfmaParams p)
-{
-    constexpr int kBlocksPerLoad = (FMT == kQ4_0) ? 4 : 2;   // blocks of 16 rows per 16-byte load step
-    constexpr int kSteps = KWMAX / kBlocksPerLoad;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int nwaves = blockDim.x >> 6;
-    const int g = lane >> 4;          // lane group
-    const int c = lane & 15;          // row within the tile / token of the A operand
-    const int n0 = blockIdx.x * 16;
-    const int KB = p.K >> 5;
-    const int kbeg = wave * p.kw;
-    const int kend = min(KB, kbeg + p.kw);
-    const int nblk = max(0, kend - kbeg);
-    const int nsteps = (nblk + kBlocksPerLoad - 1) / kBlocksPerLoad;
-
-    const int row = min(n0 + c, p.N - 1);
-    const uint8_t *__restrict__ crow = p.W + (int64_t)row * KB * (FMT == kQ4_0 ? 16 : 32);
-    const uint16_t *__restrict__ srow = reinterpret_cast<const uint16_t *>(p.W + p.scale_offset) + (int64_t)row * KB;
-
-    // 1. this wave's activations (M tokens x its blocks, 64 bytes each) with
-    //    coalesced 16-byte loads.  They are issued first: loads retire in
-    //    order, and these come from cache while the codes come from HBM.
-    constexpr int kXPer = 8 * KWMAX / 64;    // (token, block) pairs per lane, M <= 8
-    uint4 xr[kXPer][4];
-#pragma unroll
-    for (int t = 0; t < kXPer; ++t) {
-        const int i = lane + 64 * t;
-        if (i < p.M * nblk) {
-            const int m = i / nblk, b = i - m * nblk;
-            const uint4 *src = reinterpret_cast<const uint4 *>(p.x + (int64_t)m * p.K + (int64_t)(kbeg + b) * 32);
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                xr[t][q] = src[q];
-        }
-    }
-
-    // 2. this wave's code and scale loads: one 16-byte code load and one
-    //    scale per lane per step (lane group g: block b0 + g, Q4_0; block
-    //    b0 + g/2, Q8_0)
+// One 16-row tile's codes and scales for a wave's K slice (KW blocks per
+// wave at most).  Codes: per step one 16-byte load per lane (lane group g:
+// block b0 + g, Q4_0; block b0 + g/2, Q8_0).  Scales, WS (rows of an even
+// number of blocks, so every row's scales are 4-byte aligned): one load per
+// lane per tile of the KW/4 scales of row c starting at block kbeg + g*KW/4
+// (16 rows x KW*2 bytes per instruction rather than one instruction per step,
+// a quarter of the cache requests); otherwise one 2-byte scale per lane per
+// step (lane group g: the block its code load covers).
+template <int FMT, int KW, bool WS>
+struct TileRegs {
+    static constexpr int kSteps = KW / ((FMT == kQ4_0) ? 4 : 2);
+    static constexpr int kScaleRegs = WS ? KW / 8 : kSteps;
     uint4 code[kSteps];
-    uint16_t scl[kSteps];
+    uint32_t scl[kScaleRegs];
+};
+
+// Issue one tile's loads at the lane's 32-bit offsets coff / soff from the
+// tile's first block.  Every load is issued, so the compiler waits for
+// exactly one tile's loads while the next tile's are in flight: blocks past
+// the wave's slice read neighbouring blocks of the matrix and rows past N
+// read zeros (the descriptors end at the matrix), and `compute_tile` drops
+// both.  A tile past the last one (the prefetch after a workgroup's final
+// tile) gets empty descriptors: its loads return zeros without touching
+// memory.
+template <int FMT, int KW, bool WS>
+__device__ __forceinline__ void load_tile(const MfmaParams &p, int tile, int ntiles, int KB, uint32_t coff,
+                                          uint32_t soff, TileRegs<FMT, KW, WS> &t)
+{
+    constexpr int kBlocksPerLoad = (FMT == kQ4_0) ? 4 : 2;
+    constexpr int CB = (FMT == kQ4_0) ? 16 : 32;   // code bytes per block
+    const int64_t nblocks = (int64_t)p.N * KB;
+    const bool real = tile < ntiles;
+    const int64_t base = (int64_t)(real ? tile : 0) * 16 * KB;
+    const int64_t left = real ? nblocks - base : 0;
+    const auto rc = make_rsrc(p.W + base * CB, left * CB);
+    const auto rs = make_rsrc(p.W + p.scale_offset + base * 2, left * 2);
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-        if (s < nsteps) {
-            const int b0 = kbeg + s * kBlocksPerLoad;
-            const int bl = (FMT == kQ4_0) ? min(b0 + g, KB - 1) : min(b0 + (g >> 1), KB - 1);
-            const int off = (FMT == kQ4_0) ? bl * 16 : bl * 32 + (g & 1) * 16;
-            typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-            const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(crow + (uint32_t)off));
-            code[s] = make_uint4(t.x, t.y, t.z, t.w);
-            scl[s] = srow[bl];
+    for (int s = 0; s < TileRegs<FMT, KW, WS>::kSteps; ++s)
+        t.code[s] = stream_load16(rc, coff + s * kBlocksPerLoad * CB);
+    if constexpr (WS) {
+        if constexpr (KW == 8) {
+            t.scl[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, soff, 0, kNtAux);
+        } else if constexpr (KW == 16) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, soff, 0, kNtAux);
+            t.scl[0] = v[0];
+            t.scl[1] = v[1];
+        } else {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, soff, 0, kNtAux);
+            t.scl[0] = v[0];
+            t.scl[1] = v[1];
+            t.scl[2] = v[2];
+            t.scl[3] = v[3];
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < TileRegs<FMT, KW, WS>::kSteps; ++s)
+            t.scl[s] = stream_load2(rs, soff + s * kBlocksPerLoad * 2);
+    }
+}
+
+__device__ __forceinline__ float half_lo(uint32_t u) { return (float)__builtin_bit_cast(_Float16, (uint16_t)u); }
+__device__ __forceinline__ float half_hi(uint32_t u)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16));
+}
+
+// The tile's partial 16 x 16 product over this wave's K slice:
+// D layout lane l, register r -> token 4(l/16) + r, row l%16 of the tile.
+// Lanes whose A row is past the tokens (c >= M) read token `cm` = min(c,
+// M - 1): row i of D depends only on row i of A, so those rows are never
+// stored and need no masking.  Blocks past the slice (only in the last step)
+// are skipped with a wave-uniform branch; rows past N carry zero scales (the
+// descriptor returns zeros) and are not stored.
+template <int FMT, int KW, bool WS>
+__device__ __forceinline__ f4_t compute_tile(TileRegs<FMT, KW, WS> &t, const uint4 *xs, int M, int cm, int xq,
+                                             int kbeg, int kend, int nsteps, uint32_t magic)
+{
+    constexpr int kBlocksPerLoad = (FMT == kQ4_0) ? 4 : 2;
+    constexpr int kSteps = TileRegs<FMT, KW, WS>::kSteps;
+    // WS: every lane group's scale words to all four groups: bc[d][src] is
+    // word d of lane group src (scales of blocks kbeg + src*KW/4 + 2d, +1)
+    uint32_t bc[WS ? KW / 8 : 1][4];
+    if constexpr (WS) {
+#pragma unroll
+        for (int d = 0; d < KW / 8; ++d) {
+            uint32_t lo = t.scl[d], hi = t.scl[d];
+            swap32(lo, hi);                    // lo = [r0 r1 r0 r1], hi = [r2 r3 r2 r3]
+            uint32_t lo2 = lo, hi2 = hi;
+            swap16(lo, lo2);                   // lo = [r0 x4], lo2 = [r1 x4]
+            swap16(hi, hi2);                   // hi = [r2 x4], hi2 = [r3 x4]
+            bc[d][0] = lo;
+            bc[d][1] = lo2;
+            bc[d][2] = hi;
+            bc[d][3] = hi2;
         }
     }
-
-    // 3. the activations into this wave's own LDS area, in MFMA operand
-    //    order; layout [block][token][64 bytes]
-    extern __shared__ uint4 xs_dyn[];
-    uint4 *xs = xs_dyn + (int64_t)wave * p.kw * p.M * 4;
-#pragma unroll
-    for (int t = 0; t < kXPer; ++t) {
-        const int i = lane + 64 * t;
-        if (i < p.M * nblk) {
-            const int m = i / nblk, b = i - m * nblk;
-            uint4 o[4];
-            permute_x<FMT>(xr[t], o);
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                xs[(b * p.M + m) * 4 + q] = o[q];
-        }
-    }
-    // the reads below are this wave's own writes: LDS keeps a wave's order
-
-    const uint32_t magic = magic_reg();
     f4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    const bool rok = n0 + c < p.N;
-    const bool live = c < p.M;
-    const int xq = (FMT == kQ4_0) ? g : (((g & 1) << 1) | (g >> 1));
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
         if (s < nsteps) {
             const int b0 = kbeg + s * kBlocksPerLoad;
-            uint32_t w0 = code[s].x, w1 = code[s].y, w2 = code[s].z, w3 = code[s].w;
-            // scale of (row, block b0 + j) to every lane group of the row
-            uint32_t sa = scl[s], sb = scl[s];
-            swap32(sa, sb);                      // Q4_0: sa = [s0 s1 s0 s1], sb = [s2 s3 s2 s3]
-            uint32_t sc[4];
+            uint32_t w0 = t.code[s].x, w1 = t.code[s].y, w2 = t.code[s].z, w3 = t.code[s].w;
+            uint32_t sc[4] = {0u, 0u, 0u, 0u};
+            if constexpr (!WS) {
+                // scale of (row, block b0 + j) to every lane group of the row
+                uint32_t sa = t.scl[s], sb = t.scl[s];
+                swap32(sa, sb);                      // Q4_0: sa = [s0 s1 s0 s1], sb = [s2 s3 s2 s3]
+                if constexpr (FMT == kQ4_0) {
+                    uint32_t sa2 = sa, sb2 = sb;
+                    swap16(sa, sa2);
+                    swap16(sb, sb2);
+                    sc[0] = sa; sc[1] = sa2; sc[2] = sb; sc[3] = sb2;
+                } else {
+                    sc[0] = sa; sc[1] = sb;          // Q8_0: [s0 s0 s0 s0], [s1 s1 s1 s1]
+                }
+            }
             if constexpr (FMT == kQ4_0) {
-                uint32_t sa2 = sa, sb2 = sb;
-                swap16(sa, sa2);
-                swap16(sb, sb2);
-                sc[0] = sa; sc[1] = sa2; sc[2] = sb; sc[3] = sb2;
                 // 4 x 4 transpose across lane groups: afterwards register j
                 // of lane group g holds word g of block b0 + j
                 swap32(w0, w2);
@@ -246,7 +273,6 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(MfmaParams p)
                 swap16(w0, w1);
                 swap16(w2, w3);
             } else {
-                sc[0] = sa; sc[1] = sb; sc[2] = 0; sc[3] = 0;   // Q8_0: [s0 s0 s0 s0], [s1 s1 s1 s1]
                 // afterwards (w0, w1) hold block b0 and (w2, w3) block b0 + 1:
                 // lane group g has code words 2p, 2p + 1, p = {0, 2, 1, 3}[g]
                 swap32(w0, w2);
@@ -255,53 +281,167 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(MfmaParams p)
 #pragma unroll
             for (int j = 0; j < kBlocksPerLoad; ++j) {
                 const int b = b0 + j;
-                const bool bok = b < kend;
-                half8_t bop;
-                if constexpr (FMT == kQ4_0)
-                    bop = q4_operand(j == 0 ? w0 : j == 1 ? w1 : j == 2 ? w2 : w3, magic);
-                else
-                    bop = (j == 0) ? q8_operand(w0, w1, magic) : q8_operand(w2, w3, magic);
-                half8_t aop = pack8(0u, 0u, 0u, 0u);
-                if (live && bok) {
-                    const uint4 v = xs[((b - kbeg) * p.M + c) * 4 + xq];
-                    aop = pack8(v.x, v.y, v.z, v.w);
-                }
-                const f4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
-                const f4_t d = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, zero, 0, 0, 0);
-                // D layout: lane l, register r -> token 4(l/16) + r, row n0 + l%16
-                const float scv = (bok && rok) ? (float)__builtin_bit_cast(_Float16, (uint16_t)sc[j]) : 0.0f;
+                if (b < kend) {
+                    half8_t bop;
+                    if constexpr (FMT == kQ4_0)
+                        bop = q4_operand(j == 0 ? w0 : j == 1 ? w1 : j == 2 ? w2 : w3, magic);
+                    else
+                        bop = (j == 0) ? q8_operand(w0, w1, magic) : q8_operand(w2, w3, magic);
+                    const uint4 v = xs[((b - kbeg) * M + cm) * 4 + (xq ^ ((b - kbeg) & 3))];
+                    const half8_t aop = pack8(v.x, v.y, v.z, v.w);
+                    const f4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+                    const f4_t d = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, zero, 0, 0, 0);
+                    float scv;
+                    if constexpr (WS) {
+                        constexpr int kPer = KW / 4;          // scales per lane group
+                        const int rb = s * kBlocksPerLoad + j;   // block within the slice
+                        const uint32_t wsc = bc[(rb % kPer) / 2][rb / kPer];
+                        scv = (rb & 1) ? half_hi(wsc) : half_lo(wsc);
+                    } else {
+                        scv = half_lo(sc[j]);
+                    }
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    acc[r] = __builtin_fmaf(scv, d[r], acc[r]);
+                    for (int r = 0; r < 4; ++r)
+                        acc[r] = __builtin_fmaf(scv, d[r], acc[r]);
+                }
             }
         }
     }
+    return acc;
+}
 
-    // combine the waves' partial tiles in a fixed order and store
-    __shared__ f4_t red[kMaxWavesPerWg][64];
-    red[wave][lane] = acc;
+// Sum the waves' partial tiles in a fixed order (wave 0 first) and store.
+// `red` is double-buffered by tile parity: tile i writes red[i & 1] and one
+// barrier per tile separates every write from the reads of the same buffer.
+// The reducing wave rotates with the tile so no wave carries all stores.
+__device__ __forceinline__ void reduce_store(const MfmaParams &p, f4_t acc, f4_t (*red)[kMaxWavesPerWg][64], int it,
+                                             int tile, int wave, int nwaves, int lane, int g, int c)
+{
+    const int par = it & 1;
+    red[par][wave][lane] = acc;
     __syncthreads();
-    if (wave == 0) {
-        f4_t s = red[0][lane];
+    if (wave == it % nwaves) {
+        f4_t s = red[par][0][lane];
         for (int w = 1; w < nwaves; ++w) {
-            const f4_t t = red[w][lane];
+            const f4_t t = red[par][w][lane];
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 s[r] += t[r];
         }
+        const int n = tile * 16 + c;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int m = 4 * g + r;
-            if (m < p.M && rok)
-                p.y[(int64_t)m * p.N + n0 + c] = s[r];
+            if (m < p.M && n < p.N)
+                p.y[(int64_t)m * p.N + n] = s[r];
         }
     }
 }
 
-template <int FMT, int KWMAX>
-hipError_t launch_kw(const MfmaParams &p, int waves, hipStream_t stream)
+// Persistent over 16-row tiles: workgroup w takes tiles w, w + grid, ...;
+// its waves split K, stage their activation slices in LDS once, and prefetch
+// the next tile's codes and scales while the current tile is multiplied.
+// Persistent over 16-row tiles: workgroup w takes tiles w, w + grid, ...;
+// its waves split K, stage their activation slices in LDS once, and prefetch
+// the next tile's codes and scales while the current tile is multiplied.
+template <int FMT, int KWMAX, bool WS>
+__global__ __launch_bounds__(512) void gemv_mfma_kernel(MfmaParams p)
 {
-    const void *fn = reinterpret_cast<const void *>(&gemv_mfma_kernel<FMT, KWMAX>);
+    constexpr int kBlocksPerLoad = (FMT == kQ4_0) ? 4 : 2;   // blocks of 16 rows per 16-byte load step
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nwaves = blockDim.x >> 6;
+    const int g = lane >> 4;          // lane group
+    const int c = lane & 15;          // row within the tile / token of the A operand
+    const int KB = p.K >> 5;
+    const int ntiles = (p.N + 15) >> 4;
+    const int kbeg = wave * p.kw;
+    const int kend = min(KB, kbeg + p.kw);
+    const int nblk = max(0, kend - kbeg);
+    const int nsteps = (nblk + kBlocksPerLoad - 1) / kBlocksPerLoad;
+
+    // 1. this wave's activations (M tokens x its blocks, 64 bytes each) with
+    //    coalesced 16-byte loads, issued first (they come from cache; loads
+    //    retire in order).  Pair i is (token i / nblk, block i % nblk); pairs
+    //    past the slice re-read a valid block.
+    constexpr int kXPer = 8 * KWMAX / 64;    // (token, block) pairs per lane, M <= 8
+    const int npairs = p.M * nblk;
+    uint4 xr[kXPer][4];
+#pragma unroll
+    for (int t = 0; t < kXPer; ++t) {
+        const int i = min(lane + 64 * t, max(npairs, 1) - 1);
+        const int m = i / max(nblk, 1), b = i - m * max(nblk, 1);
+        const int blk = min(kbeg + b, KB - 1);
+        const uint4 *src = reinterpret_cast<const uint4 *>(p.x + (int64_t)m * p.K + (int64_t)blk * 32);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            xr[t][q] = src[q];
+    }
+
+    // 2. the first tile's codes and scales; lane offsets from a tile's first
+    //    block (row c of the tile, this wave's first block, lane group g)
+    const int gb = (FMT == kQ4_0) ? g : (g >> 1);
+    const uint32_t coff = (uint32_t)(c * KB + kbeg + gb) * (FMT == kQ4_0 ? 16u : 32u) +
+                          ((FMT == kQ4_0) ? 0u : (uint32_t)(g & 1) * 16u);
+    const uint32_t soff = WS ? (uint32_t)(c * KB + kbeg + g * (KWMAX / 4)) * 2u : (uint32_t)(c * KB + kbeg + gb) * 2u;
+    int tile = blockIdx.x;
+    TileRegs<FMT, KWMAX, WS> ta, tb;
+    load_tile<FMT, KWMAX, WS>(p, tile, ntiles, KB, coff, soff, ta);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 3. the activations into this wave's own LDS area, in MFMA operand
+    //    order; layout [block][token][64 bytes], 16-byte chunk q of (block b,
+    //    token m) at position q ^ (b & 3) of its slot: consecutive lanes hold
+    //    consecutive blocks, whose slots are M * 64 bytes apart (the same
+    //    banks for M a multiple of 4), and the swizzle spreads four of them
+    //    over different banks.  The reads below are this wave's own writes:
+    //    LDS keeps a wave's order.
+    extern __shared__ uint4 xs_dyn[];
+    uint4 *xs = xs_dyn + (int64_t)wave * p.kw * p.M * 4;
+#pragma unroll
+    for (int t = 0; t < kXPer; ++t) {
+        const int i = lane + 64 * t;
+        if (i < npairs) {
+            const int m = i / max(nblk, 1), b = i - m * max(nblk, 1);
+            uint4 o[4];
+            permute_x<FMT>(xr[t], o);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                xs[(b * p.M + m) * 4 + (q ^ (b & 3))] = o[q];
+        }
+    }
+
+    __shared__ f4_t red[2][kMaxWavesPerWg][64];
+    const uint32_t magic = magic_reg();
+    const int cm = min(c, p.M - 1);
+    const int xq = (FMT == kQ4_0) ? g : (((g & 1) << 1) | (g >> 1));
+    const int step = gridDim.x;
+    const int last = ntiles - 1;
+    for (int it = 0;; it += 2) {
+        // tile in `ta`; prefetch the next into `tb` (past the end: empty
+        // loads, never used)
+        const int t1 = tile + step;
+        load_tile<FMT, KWMAX, WS>(p, t1, ntiles, KB, coff, soff, tb);
+        __builtin_amdgcn_sched_barrier(0);
+        f4_t acc = compute_tile<FMT, KWMAX, WS>(ta, xs, p.M, cm, xq, kbeg, kend, nsteps, magic);
+        reduce_store(p, acc, red, it, tile, wave, nwaves, lane, g, c);
+        if (t1 > last)
+            break;
+        const int t2 = t1 + step;
+        load_tile<FMT, KWMAX, WS>(p, t2, ntiles, KB, coff, soff, ta);
+        __builtin_amdgcn_sched_barrier(0);
+        acc = compute_tile<FMT, KWMAX, WS>(tb, xs, p.M, cm, xq, kbeg, kend, nsteps, magic);
+        reduce_store(p, acc, red, it + 1, t1, wave, nwaves, lane, g, c);
+        if (t2 > last)
+            break;
+        tile = t2;
+    }
+}
+
+template <int FMT, int KWMAX, bool WS>
+hipError_t launch_kw(const MfmaParams &p, int waves, int64_t wgs, int cus, hipStream_t stream)
+{
+    const void *fn = reinterpret_cast<const void *>(&gemv_mfma_kernel<FMT, KWMAX, WS>);
     // every wave stages M x kw blocks of activations (64 bytes each)
     const size_t shmem = (size_t)waves * p.kw * p.M * 64;
     if (shmem > kMaxLds)
@@ -312,17 +452,30 @@ hipError_t launch_kw(const MfmaParams &p, int waves, hipStream_t stream)
             return hipErrorInvalidValue;
         raised = true;
     }
-    const dim3 grid((unsigned)((p.N + 15) / 16)), block(64 * waves);
+    const int64_t ntiles = (p.N + 15) / 16;
+    if (wgs <= 0) {
+        // workgroups per CU that fit in LDS (160 KB, 16 KB of it for the
+        // partial tiles) and in the wave slots (32 per CU), at most 2
+        const size_t per_wg = shmem + 2 * kMaxWavesPerWg * 64 * 16;
+        const int64_t fit = std::max<int64_t>(1, std::min<int64_t>((160 * 1024) / per_wg, 32 / waves));
+        wgs = (int64_t)cus * std::min<int64_t>(2, fit);
+    }
+    wgs = std::min(wgs, ntiles);
+    const dim3 grid((unsigned)wgs), block(64 * waves);
     return launch_kernel(fn, grid, block, shmem, stream, p);
 }
 
 template <int FMT>
-hipError_t launch_fmt(const MfmaParams &p, int kwmax, int waves, hipStream_t stream)
+hipError_t launch_fmt(const MfmaParams &p, int kwmax, int waves, int64_t wgs, int cus, hipStream_t stream)
 {
+    const bool ws = (p.K / 32) % 2 == 0;   // every row's scales 4-byte aligned
     switch (kwmax) {
-    case 8: return launch_kw<FMT, 8>(p, waves, stream);
-    case 16: return launch_kw<FMT, 16>(p, waves, stream);
-    case 32: return launch_kw<FMT, 32>(p, waves, stream);
+    case 8: return ws ? launch_kw<FMT, 8, true>(p, waves, wgs, cus, stream)
+                      : launch_kw<FMT, 8, false>(p, waves, wgs, cus, stream);
+    case 16: return ws ? launch_kw<FMT, 16, true>(p, waves, wgs, cus, stream)
+                       : launch_kw<FMT, 16, false>(p, waves, wgs, cus, stream);
+    case 32: return ws ? launch_kw<FMT, 32, true>(p, waves, wgs, cus, stream)
+                       : launch_kw<FMT, 32, false>(p, waves, wgs, cus, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -330,9 +483,10 @@ hipError_t launch_fmt(const MfmaParams &p, int kwmax, int waves, hipStream_t str
 }  // namespace
 
 // Launch the matrix-core GEMV: `waves` (1..8) split K; each wave takes
-// kw = ceil(K/32 / waves) blocks rounded up to 4, at most 32.
+// kw = ceil(K/32 / waves) blocks rounded up to 4, at most 32; `wgs`
+// persistent workgroups walk the 16-row tiles (0: the built-in count).
 hipError_t launch_gemv_mfma(int fmt, const uint8_t *W, int64_t scale_offset, const uint16_t *x, float *y, int M,
-                            int N, int K, int waves, hipStream_t stream)
+                            int N, int K, int waves, int64_t wgs, int cus, hipStream_t stream)
 {
     const int KB = K / 32;
     if (M < 1 || M > 8 || waves < 1 || waves > kMaxWavesPerWg)
@@ -343,7 +497,8 @@ hipError_t launch_gemv_mfma(int fmt, const uint8_t *W, int64_t scale_offset, con
         return hipErrorInvalidValue;
     const int kwmax = kw <= 8 ? 8 : (kw <= 16 ? 16 : 32);
     MfmaParams p{W, x, y, scale_offset, M, N, K, kw};
-    return fmt == kQ4_0 ? launch_fmt<kQ4_0>(p, kwmax, waves, stream) : launch_fmt<kQ8_0>(p, kwmax, waves, stream);
+    return fmt == kQ4_0 ? launch_fmt<kQ4_0>(p, kwmax, waves, wgs, cus, stream)
+                        : launch_fmt<kQ8_0>(p, kwmax, waves, wgs, cus, stream);
 }
 
 }  // namespace qg
