@@ -113,32 +113,31 @@ __device__ __forceinline__ void load_stage(Stage<BM, BN> &st, const PrefillParam
 {
     const int tid = threadIdx.x;
     const int KB = p.K >> 5;
+    // Every thread issues every load (threads past the tile repeat its last
+    // chunk): with no load under a condition the compiler can wait for
+    // exactly the stage it needs while the later stages stay in flight.
 #pragma unroll
     for (int c = 0; c < Stage<BM, BN>::kXChunks; ++c) {
-        const int idx = tid + 256 * c;     // chunk index within the BM x 2 tile
+        const int idx = min(tid + 256 * c, BM * 2 - 1);   // chunk index within the BM x 2 tile
         const int r = idx >> 1, b = idx & 1;
-        if (idx < BM * 2) {
-            const int m = min(m0 + r, p.M - 1);
-            const int kb = min(step * 2 + b, KB - 1);
-            const uint4 *src = reinterpret_cast<const uint4 *>(p.X + (int64_t)m * p.K + (int64_t)kb * 32);
+        const int m = min(m0 + r, p.M - 1);
+        const int kb = min(step * 2 + b, KB - 1);
+        const uint4 *src = reinterpret_cast<const uint4 *>(p.X + (int64_t)m * p.K + (int64_t)kb * 32);
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                st.x[c][q] = src[q];
-        }
+        for (int q = 0; q < 4; ++q)
+            st.x[c][q] = src[q];
     }
 #pragma unroll
     for (int c = 0; c < Stage<BM, BN>::kWBlocks; ++c) {
-        const int idx = tid + 256 * c;
+        const int idx = min(tid + 256 * c, BN * 2 - 1);
         const int r = idx >> 1, b = idx & 1;
-        if (idx < BN * 2) {
-            const int64_t n = min(n0 + r, p.N - 1);
-            const int kb = min(step * 2 + b, KB - 1);
-            const int64_t bi = n * KB + kb;
-            typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-            const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p.W + bi * 16));
-            st.code[c] = make_uint4(t.x, t.y, t.z, t.w);
-            st.scale[c] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(p.W + p.scale_offset) + bi);
-        }
+        const int64_t n = min(n0 + r, p.N - 1);
+        const int kb = min(step * 2 + b, KB - 1);
+        const int64_t bi = n * KB + kb;
+        typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+        const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p.W + bi * 16));
+        st.code[c] = make_uint4(t.x, t.y, t.z, t.w);
+        st.scale[c] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(p.W + p.scale_offset) + bi);
     }
 }
 
@@ -148,11 +147,13 @@ __device__ __forceinline__ void store_stage(const Stage<BM, BN> &st, const Prefi
 {
     const int tid = threadIdx.x;
     const int KB = p.K >> 5;
+    // Threads past the tile store a repeat of its last chunk: the same bytes
+    // to the same place, so no store needs a condition either.
 #pragma unroll
     for (int c = 0; c < Stage<BM, BN>::kXChunks; ++c) {
-        const int idx = tid + 256 * c;
+        const int idx = min(tid + 256 * c, BM * 2 - 1);
         const int r = idx >> 1, b = idx & 1;
-        if (idx < BM * 2) {
+        {
             const bool ok = (m0 + r < p.M) && (step * 2 + b < KB);
             uint32_t d[16], o[16];
 #pragma unroll
@@ -171,9 +172,9 @@ __device__ __forceinline__ void store_stage(const Stage<BM, BN> &st, const Prefi
     }
 #pragma unroll
     for (int c = 0; c < Stage<BM, BN>::kWBlocks; ++c) {
-        const int idx = tid + 256 * c;
+        const int idx = min(tid + 256 * c, BN * 2 - 1);
         const int r = idx >> 1, b = idx & 1;
-        if (idx < BN * 2) {
+        {
             const bool ok = (n0 + r < p.N) && (step * 2 + b < KB);
             uint32_t o[16];
             dequant_block_f16(st.code[c], ok ? st.scale[c] : (uint16_t)0, o);
@@ -217,48 +218,64 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p)
     // into the other buffer, so the vector-ALU dequantization runs while the
     // matrix cores work; one barrier per step.  The buffer written in
     // iteration s was last read in iteration s - 1, before its barrier.
+    //
+    // Every stage load is issued unconditionally, also past the workgroup's
+    // last step (load_stage clamps to valid blocks; such stages are never
+    // multiplied): with the same load order on every path into the loop the
+    // compiler waits only for the stage a step consumes, while the later
+    // stages stay in flight.
     Stage<BM, BN> st[kDepth];
 #pragma unroll
     for (int q = 0; q < kDepth; ++q)
-        if (s_beg + q < s_end)
-            load_stage<BM, BN>(st[q], p, m0, n0, s_beg + q);
-    if (s_beg < s_end) {
-        store_stage<BM, BN>(st[0], p, m0, n0, s_beg, Xs[0], Ws[0]);
-        if (s_beg + kDepth < s_end)
-            load_stage<BM, BN>(st[0], p, m0, n0, s_beg + kDepth);
-    }
+        load_stage<BM, BN>(st[q], p, m0, n0, s_beg + q);
+    store_stage<BM, BN>(st[0], p, m0, n0, s_beg, Xs[0], Ws[0]);
+    load_stage<BM, BN>(st[0], p, m0, n0, s_beg + kDepth);
     __syncthreads();
 
-    for (int s0 = s_beg; s0 < s_end; s0 += kDepth) {
+    auto multiply = [&](int buf) {
+#pragma unroll
+        for (int kk = 0; kk < kBK / 16; ++kk) {
+            const int col = kk * 16 + (lane >> 5) * 8;
+            half8_t a[TM], b[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                a[i] = *reinterpret_cast<const half8_t *>(&Xs[buf][wm * (BM / 2) + 32 * i + (lane & 31)][col]);
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                b[j] = *reinterpret_cast<const half8_t *>(&Ws[buf][wn * (BN / 2) + 32 * j + (lane & 31)][col]);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+    };
+
+    // Steps s0 .. s0 + kDepth - 1 per iteration, ring slot (s - s_beg) %
+    // kDepth static once unrolled.  Staging step s + 1 = s_end (last step
+    // of the last iteration) fills the unused buffer with data never read.
+    int s0 = s_beg;
+    for (; s0 + kDepth <= s_end; s0 += kDepth) {
 #pragma unroll
         for (int q = 0; q < kDepth; ++q) {
             const int s = s0 + q;
-            if (s < s_end) {
-                const int buf = (s - s_beg) & 1;
+            const int buf = (s - s_beg) & 1;
+            multiply(buf);
+            const int qn = (q + 1) % kDepth;
+            store_stage<BM, BN>(st[qn], p, m0, n0, s + 1, Xs[buf ^ 1], Ws[buf ^ 1]);
+            load_stage<BM, BN>(st[qn], p, m0, n0, s + 1 + kDepth);
+            __syncthreads();
+        }
+    }
 #pragma unroll
-                for (int kk = 0; kk < kBK / 16; ++kk) {
-                    const int col = kk * 16 + (lane >> 5) * 8;
-                    half8_t a[TM], b[TN];
-#pragma unroll
-                    for (int i = 0; i < TM; ++i)
-                        a[i] = *reinterpret_cast<const half8_t *>(&Xs[buf][wm * (BM / 2) + 32 * i + (lane & 31)][col]);
-#pragma unroll
-                    for (int j = 0; j < TN; ++j)
-                        b[j] = *reinterpret_cast<const half8_t *>(&Ws[buf][wn * (BN / 2) + 32 * j + (lane & 31)][col]);
-#pragma unroll
-                    for (int i = 0; i < TM; ++i)
-#pragma unroll
-                        for (int j = 0; j < TN; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
-                }
-                const int qn = (q + 1) % kDepth;   // ring slot of step s + 1 (static once unrolled)
-                if (s + 1 < s_end) {
-                    store_stage<BM, BN>(st[qn], p, m0, n0, s + 1, Xs[buf ^ 1], Ws[buf ^ 1]);
-                    if (s + 1 + kDepth < s_end)
-                        load_stage<BM, BN>(st[qn], p, m0, n0, s + 1 + kDepth);
-                }
-                __syncthreads();
-            }
+    for (int q = 0; q < kDepth - 1; ++q) {
+        const int s = s0 + q;
+        if (s < s_end) {
+            const int buf = (s - s_beg) & 1;
+            multiply(buf);
+            if (s + 1 < s_end)
+                store_stage<BM, BN>(st[(q + 1) % kDepth], p, m0, n0, s + 1, Xs[buf ^ 1], Ws[buf ^ 1]);
+            __syncthreads();
         }
     }
 
@@ -365,7 +382,16 @@ extern "C" qg_status qgemm_q4_0_prefill(const void *Wp, const uint16_t *X, float
     p.atomic = 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool small = o_bm ? (o_bm == 64) : (M <= 64);
-    hipError_t e = small ? launch_prefill<64, 128>(p, cus, s) : launch_prefill<128, 128>(p, cus, s);
+    // 128 x 192 tiles where they give every CU exactly one workgroup while
+    // 128 x 128 tiles would leave some CUs with two (MI355X: 12288 x 2560 at
+    // 512 tokens 79 against 86 us); elsewhere 128 x 128 (with fewer tiles
+    // than CUs the wider tile needs more K splits and loses).
+    const int64_t tiles_m = (M + 127) / 128;
+    const int64_t t128 = (N + 127) / 128 * tiles_m, t192 = (N + 191) / 192 * tiles_m;
+    const bool wide = !small && o_bm == 0 && t128 > cus && t192 <= cus && t192 * 8 >= (int64_t)cus * 7;
+    hipError_t e = small  ? launch_prefill<64, 128>(p, cus, s)
+                   : wide ? launch_prefill<128, 192>(p, cus, s)
+                          : launch_prefill<128, 128>(p, cus, s);
     if (e == hipErrorInvalidValue)
         return QG_ERR_SHAPE;
     return e == hipSuccess ? QG_OK : QG_ERR_LAUNCH;

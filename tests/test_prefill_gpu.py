@@ -65,6 +65,25 @@ def test_prefill_m512_sampled(N, K):
     assert_within(Yd[np.ix_(toks, cols)], y_ref, s, "dense fp16 comparator")
 
 
+def test_prefill_wide_tile_full():
+    """The 128 x 192 tile the launcher picks when it gives every CU exactly
+    one workgroup (384 tokens x 16000 rows on 256 CUs): every output against
+    the oracle, with a ragged last tile along N and an odd block count along
+    K (the last K step holds one block)."""
+    M, N, K = 384, 16000, 96
+    cus = qg().qg_device_cus()
+    t128 = -(-N // 128) * 3
+    t192 = -(-N // 192) * 3
+    if not (t128 > cus and t192 <= cus and t192 * 8 >= cus * 7):
+        pytest.skip(f"the wide tile is not chosen on {cus} CUs")
+    w = si.weights(N, K, seed=7)
+    X = si.activations(M, K, seed=7)
+    pb, po = pack_both(Q4_0, w)
+    Y = _prefill(to_dev(pb), X, N, K)
+    Y_ref, S = oracle.get().prefill(po, N, K, X)
+    assert_within(Y, Y_ref, S, f"prefill wide tile M={M} {N}x{K}")
+
+
 def test_prefill_one_hot_is_the_fp16_dequant_column():
     """X = e_k returns fp16-rounded column k bit-exactly (pins the tile layout
     and the permuted k order)."""
