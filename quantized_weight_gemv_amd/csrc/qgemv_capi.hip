@@ -82,13 +82,14 @@ bool choose_shape(int fmt, int M, int64_t N, int64_t K, int items, int cus, Gemv
     if (o_xl >= 0)
         xl = (o_xl == 1);
     // Lanes per row: one token with rows of 65..128 blocks spreads a row over
-    // 16 (up to 4096 rows) or 32 lanes (up to 64K rows), so a wave reduces
-    // several rows at once; shorter rows take one wave each.
+    // 16 (up to 4096 rows) or 32 lanes (up to 64K rows; Q4_0 GEMV: up to 8192),
+    // so a wave reduces several rows at once; shorter rows take one wave each.
+    const bool q4_one = fmt == kQ4_0 && M == 1 && items == 1 && !xl;
     int G = 64;
     if (M == 1 && !xl && KB > 64 && KB <= 128) {
         if (N <= 4096 && N >= 4)
             G = 16;
-        else if (N <= 65536 && N >= 2)
+        else if (N <= (q4_one ? 8192 : 65536) && N >= 2)
             G = 32;
     }
     if (o_G)
@@ -110,6 +111,14 @@ bool choose_shape(int fmt, int M, int64_t N, int64_t K, int items, int cus, Gemv
     // 10.7 us; 2048 x 6144 (192 blocks) stays faster with one block per lane.
     if (M >= 2 && M <= 4 && !xl && J == 1 && KB > 64 && (KB % 128 == 0 || KB > 384))
         J = 2;
+    // One token, Q4_0, full-wave rows: a whole row per wave, no K split and
+    // no cross-wave reduction (two blocks per lane for 65..128 blocks, up to
+    // seven for 257..448).  Timed as back-to-back graph replay on MI355X:
+    // 28672 x 4096 12.4 against 13.5 us with K split over four waves,
+    // 14336 x 4096 7.6 against 8.0, 4096 x 14336 7.95 against 8.6,
+    // 128256 x 4096 45.1 against 46.9.
+    if (q4_one && o_G == 0 && G == 64 && ((KB > 64 && KB <= 128) || (KB > 256 && KB <= 448)))
+        J = static_cast<int>((KB + 63) / 64);
     int ksplit = static_cast<int>((KB + static_cast<int64_t>(G) * J - 1) / (static_cast<int64_t>(G) * J));
     const int rj = (fmt == kQ4_0) ? 8 : 4;   // R * J budget of the kernel table
     // Two row sets per group, four for full-wave rows beyond 64K rows, and
@@ -119,6 +128,8 @@ bool choose_shape(int fmt, int M, int64_t N, int64_t K, int items, int cus, Gemv
     // where one group per team then covers all rows (Q8_0 4096 x 14336 at
     // six tokens: 26.0 us with four, 25.2 with two).
     int R = (N > 65536 && G == 64) ? 4 : 2;
+    if (q4_one && G == 16)
+        R = 4;   // 4096 x 4096: 3.95 against 4.10 us back to back
     if (M >= 2 && J == 1 && ksplit > 1 &&
         (fmt == kQ4_0 || N <= 4LL * cus * std::max(2, 8 / ksplit)))
         R = 4;
@@ -164,6 +175,8 @@ bool choose_shape(int fmt, int M, int64_t N, int64_t K, int items, int cus, Gemv
     // 64K rows 64 teams per CU, more than fit at once (the hardware
     // dispatcher then balances the tail).
     int per_cu = (ksplit == 1) ? 8 : (M == 1 ? std::max(4, 16 / ksplit) : std::max(2, 8 / ksplit));
+    if (M == 1 && ksplit == 1 && J > 2)
+        per_cu = 4;   // long whole rows per wave: 4096 x 14336 7.95 us at 4, 8.9 at 8
     if (N > 65536 && M == 1)
         per_cu = 64;
     int64_t teams = std::max<int64_t>(1, static_cast<int64_t>(cus) * per_cu / std::max(1, items));
