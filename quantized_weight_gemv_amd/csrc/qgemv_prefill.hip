@@ -148,13 +148,16 @@ __device__ __forceinline__ void store_stage(const Stage<BM, BN> &st, const Prefi
     const int tid = threadIdx.x;
     const int KB = p.K >> 5;
     // Threads past the tile store a repeat of its last chunk: the same bytes
-    // to the same place, so no store needs a condition either.
+    // to the same place, so no store needs a condition either.  Activation
+    // rows past M and blocks past K hold clamped copies of real activations
+    // and are stored as they are: rows past M only reach output rows that are
+    // never written, and blocks past K meet weights whose scale is zeroed
+    // below.  (With no select the step body is one basic block.)
 #pragma unroll
     for (int c = 0; c < Stage<BM, BN>::kXChunks; ++c) {
         const int idx = min(tid + 256 * c, BM * 2 - 1);
         const int r = idx >> 1, b = idx & 1;
         {
-            const bool ok = (m0 + r < p.M) && (step * 2 + b < KB);
             uint32_t d[16], o[16];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -167,7 +170,7 @@ __device__ __forceinline__ void store_stage(const Stage<BM, BN> &st, const Prefi
             uint4 *dst = reinterpret_cast<uint4 *>(&Xs[r][b * 32]);
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                dst[q] = ok ? make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]) : make_uint4(0, 0, 0, 0);
+                dst[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
         }
     }
 #pragma unroll
