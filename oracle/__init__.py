@@ -83,6 +83,12 @@ class Oracle:
         L.orc_moe.restype = None
         L.orc_moe.argtypes = [ctypes.c_int, u8p, i64, ctypes.POINTER(ctypes.c_int32), i64,
                               u16p, i64, i64, f64p, f64p]
+        L.orc_floats_to_half.restype = None
+        L.orc_floats_to_half.argtypes = [f32p, i64, u16p]
+        L.orc_silu.restype = ctypes.c_double
+        L.orc_silu.argtypes = [ctypes.c_double]
+        L.orc_swiglu.restype = None
+        L.orc_swiglu.argtypes = [f64p, f64p, i64, f64p]
 
     # -- helpers ---------------------------------------------------------
     @staticmethod
@@ -189,12 +195,56 @@ class Oracle:
         """Q4_0 prefill GEMM: the GEMV definition over M token rows (fp64, exact weights)."""
         return self.gemv(Q4_0, packed, N, K, X)
 
+    # -- fp32 activations, SwiGLU ------------------------------------------
+    def floats_to_half(self, x: np.ndarray) -> np.ndarray:
+        """fp32 activations rounded to binary16 bits (oracle.c's codec)."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        out = np.empty(x.shape, np.uint16)
+        self._L.orc_floats_to_half(self._p(x, ctypes.c_float), x.size, self._p(out, ctypes.c_uint16))
+        return out
+
+    def gemv_f32in(self, fmt: int, packed: np.ndarray, N: int, K: int, x32: np.ndarray):
+        """(y, s) of the GEMV on fp32 activations rounded to binary16."""
+        return self.gemv(fmt, packed, N, K, self.floats_to_half(x32))
+
+    def silu(self, v: float) -> float:
+        return float(self._L.orc_silu(float(v)))
+
+    def swiglu(self, packed: np.ndarray, N: int, K: int, x32: np.ndarray):
+        """Q4_0 stacked gate + up table (2N x K): (y, g, u, sg, su) with
+        y = silu(g) * u, g and u the GEMVs of rows 0..N-1 and N..2N-1 on the
+        fp32 activations rounded to binary16, sg and su their sums of |w x|."""
+        y2, s2 = self.gemv_f32in(Q4_0, packed, 2 * N, K, x32)
+        g = np.ascontiguousarray(y2[:, :N])
+        u = np.ascontiguousarray(y2[:, N:])
+        y = np.empty_like(g)
+        self._L.orc_swiglu(self._p(g, ctypes.c_double), self._p(u, ctypes.c_double), g.size,
+                           self._p(y, ctypes.c_double))
+        return y, g, u, np.ascontiguousarray(s2[:, :N]), np.ascontiguousarray(s2[:, N:])
+
 
 def within_bound(y, y_ref, s, rel: float = 1e-3, abs_: float = 1e-6):
     """Acceptance bound per element: finite and |y - y_ref| <= rel * s + abs."""
     y = np.asarray(y, dtype=np.float64)
     ok = np.isfinite(y) & (np.abs(y - y_ref) <= rel * s + abs_)
     return ok
+
+
+def swiglu_within_bound(y, y_ref, g, u, sg, su, rel: float = 1e-3, abs_: float = 1e-6):
+    """Acceptance bound of silu(g) u per element, carried from the GEMV bound.
+
+    The kernel's g' and u' satisfy |g' - g| <= eg = rel sg + abs and
+    |u' - u| <= eu = rel su + abs.  With L = max |silu'| < 1.1 and
+    |silu(g)| <= |g|,
+      |silu(g') u' - silu(g) u| <= L eg (|u| + eu) + |g| eu,
+    and the fp32 evaluation of silu(g') u' (an exponential, a division and a
+    product) adds at most a few units in the last place: 1e-5 |y_ref| + abs.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    eg = rel * sg + abs_
+    eu = rel * su + abs_
+    bound = 1.1 * eg * (np.abs(u) + eu) + np.abs(g) * eu + 1e-5 * np.abs(y_ref) + abs_
+    return np.isfinite(y) & (np.abs(y - y_ref) <= bound)
 
 
 _default = None

@@ -14,7 +14,8 @@
  * ORC_PLANT_* macros build deliberately broken copies for the tests that show
  * the pins catch plausible mistakes (a swapped nibble order, a dropped offset,
  * the wrong tie rule or divisor, a shifted index, a dropped term, a codec
- * slip).  The default build defines none of them.
+ * slip, a sign slip in silu, gate and up swapped).  The default build defines
+ * none of them.
  *
  * What is computed, and where it is defined:
  *  - Q4_0 block: 32 weights share one binary16 scale d and carry 4-bit codes
@@ -36,6 +37,17 @@
  *  - MoE: expert e uses pool matrix idx[e] and its own token x[e]
  *    [volta-kernel-bakeoff, "What's in the race" (moe_*) and "Making it fair"].
  *  - Prefill: the GEMV definition for M token rows (same sums).
+ *  - fp32 activations: each is rounded to binary16 (nearest, ties to even,
+ *    overflow to infinity) and the GEMV definition applies to the rounded
+ *    values [volta-kernel-bakeoff, "Results", the like-for-like bullets:
+ *    fp32 activations in, their conversion counted; values beyond binary16's
+ *    range become infinity].
+ *  - SwiGLU on a stacked table: rows 0..N-1 of one packed 2N x K matrix are
+ *    the gate rows, rows N..2N-1 the up rows; the output is silu(g) * u with
+ *    g, u the two GEMVs and silu(v) = v / (1 + e^-v) [volta-kernel-bakeoff,
+ *    "Results", the few-tokens bullet: gate and up stacked into one table,
+ *    the activations converted once; the FFN fusion step of the CUDA-kernel
+ *    diary: gate, up and SwiGLU in one kernel, the activations read once].
  *
  * Packed buffer layout (one N x K matrix, K % 32 == 0, blocks along K, block
  * index i = n * (K / 32) + b):
@@ -341,4 +353,34 @@ void orc_moe(int fmt, const uint8_t *pool, int64_t P, const int32_t *idx, int64_
         }
         orc_gemv(fmt, pool + (size_t)j * stride, N, K, x + e * K, 1, y + e * N, s + e * N);
     }
+}
+
+/* ------------------------------------------------ fp32 input and SwiGLU */
+
+/* Round n fp32 activations to binary16 bits (the codec above). */
+void orc_floats_to_half(const float *x, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = orc_float_to_half(x[i]);
+}
+
+/* silu(v) = v * sigmoid(v) = v / (1 + e^-v). */
+double orc_silu(double v)
+{
+#if defined(ORC_PLANT_SILU)
+    return v / (1.0 + exp(v));
+#else
+    return v / (1.0 + exp(-v));
+#endif
+}
+
+/* y[i] = silu(g[i]) * u[i] for the gate and up halves of a stacked GEMV. */
+void orc_swiglu(const double *g, const double *u, int64_t n, double *y)
+{
+    for (int64_t i = 0; i < n; ++i)
+#if defined(ORC_PLANT_GLU)
+        y[i] = orc_silu(u[i]) * g[i];
+#else
+        y[i] = orc_silu(g[i]) * u[i];
+#endif
 }

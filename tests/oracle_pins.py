@@ -20,6 +20,16 @@ What each pin rests on:
                gives zero, linearity, M tokens == M single-token calls.
   moe          reduces to independent GEMVs of the chosen experts.
   prefill      equals a float64 matmul (numpy) on the dequantized weights.
+  f32in        fp32 -> binary16 against numpy's float16 cast (a library
+               routine) on random, overflow, tie and subnormal values; the
+               GEMV on fp32 input equals the GEMV on numpy's cast, bitwise.
+  silu         closed forms and published constants: silu(0) = 0,
+               silu(ln 3) = (3/4) ln 3, silu(40) = 40 and silu(-40) ~ 0 in
+               fp64, the minimum -0.2784645 near -1.2784645, and
+               silu(v) - silu(-v) = v.
+  swiglu       the stacked table's halves are the separately quantized gate
+               and up GEMVs, bitwise; a zero gate gives zero; a large gate
+               (silu(g) = g in fp64) gives g * u.
 """
 from __future__ import annotations
 
@@ -360,5 +370,89 @@ def pin_prefill(orc) -> list:
     return fails
 
 
+def pin_f32in(orc) -> list:
+    fails = []
+    g = np.random.default_rng(11)
+    vals = np.concatenate([
+        g.standard_normal(4096).astype(np.float32) * np.float32(3),
+        np.array([0.0, -0.0, 1.0, 65504.0, 65519.99, 65520.0, 70000.0, -1e6, 1e-7, 5.96e-8, 2.98e-8,
+                  2.9802322e-08, 6.1035156e-05, 6.1e-05, 1.0 + 2 ** -11, 1.0 + 3 * 2 ** -11, -(1.0 + 2 ** -11),
+                  2048.0 + 1.0, 2048.0 + 3.0, 1e-10, -3e-8], np.float32),
+        (g.standard_normal(512) * 30000).astype(np.float32),
+        (g.standard_normal(512) * 1e-6).astype(np.float32)])
+    ours = orc.floats_to_half(vals)
+    with np.errstate(over="ignore"):                 # 70000 and -1e6 overflow on purpose
+        ref = vals.astype(np.float16).view(np.uint16)
+    bad = np.flatnonzero(ours != ref)
+    if bad.size:
+        i = bad[0]
+        fails.append(f"f32 -> f16 of {vals[i]!r}: {ours[i]:#06x} vs numpy {ref[i]:#06x} ({bad.size} differ)")
+    nan = orc.floats_to_half(np.array([np.nan], np.float32))[0]
+    if not ((nan & 0x7c00) == 0x7c00 and (nan & 0x3ff)):
+        fails.append("f32 -> f16 of NaN is not a NaN")
+    for fmt in (Q4_0, Q8_0):
+        N, K, M = 12, 128, 3
+        p = orc.quantize(fmt, si.weights(N, K, seed=6))
+        x32 = (g.standard_normal((M, K)) * 4).astype(np.float32)
+        y, s_ = orc.gemv_f32in(fmt, p, N, K, x32)
+        y2, s2 = orc.gemv(fmt, p, N, K, x32.astype(np.float16))
+        if not (np.array_equal(y, y2) and np.array_equal(s_, s2)):
+            fails.append(f"fmt{fmt}: GEMV on fp32 input differs from the GEMV on numpy's float16 cast")
+    return fails
+
+
+def pin_silu(orc) -> list:
+    fails = []
+    ln3 = float(np.log(3.0))
+    checks = [(0.0, 0.0, 0.0), (ln3, 0.75 * ln3, 1e-15), (40.0, 40.0, 1e-15)]
+    for v, want, rel in checks:
+        got = orc.silu(v)
+        if abs(got - want) > rel * abs(want):
+            fails.append(f"silu({v}) = {got!r}, want {want!r}")
+    if abs(orc.silu(-40.0)) > 1e-15:
+        fails.append(f"silu(-40) = {orc.silu(-40.0)!r} is not ~0")
+    vmin = orc.silu(-1.2784645)
+    if abs(vmin + 0.2784645) > 1e-7:
+        fails.append(f"silu at its minimum -1.2784645 is {vmin!r}, not -0.2784645")
+    if orc.silu(-1.2784645 - 0.01) < vmin or orc.silu(-1.2784645 + 0.01) < vmin:
+        fails.append("silu's minimum is not near -1.2784645")
+    for v in np.random.default_rng(12).standard_normal(64) * 5:
+        d = orc.silu(v) - orc.silu(-v)
+        if abs(d - v) > 1e-14 * abs(v):
+            fails.append(f"silu({v}) - silu({-v}) = {d!r} is not {v!r}")
+            break
+    return fails
+
+
+def pin_swiglu(orc) -> list:
+    fails = []
+    N, K, M = 10, 96, 2
+    wg = si.weights(N, K, seed=21)
+    wu = si.weights(N, K, seed=22)
+    stacked = orc.quantize(Q4_0, np.concatenate([wg, wu]))
+    x32 = (np.random.default_rng(23).standard_normal((M, K)) * 2).astype(np.float32)
+    y, g, u, sg, su = orc.swiglu(stacked, N, K, x32)
+    g1, sg1 = orc.gemv_f32in(Q4_0, orc.quantize(Q4_0, wg), N, K, x32)
+    u1, su1 = orc.gemv_f32in(Q4_0, orc.quantize(Q4_0, wu), N, K, x32)
+    if not (np.array_equal(g, g1) and np.array_equal(sg, sg1)):
+        fails.append("swiglu: gate half is not the gate table's GEMV")
+    if not (np.array_equal(u, u1) and np.array_equal(su, su1)):
+        fails.append("swiglu: up half is not the up table's GEMV")
+    # a zero gate table: silu(0) = 0 whatever the up rows give
+    yz, gz, uz, _, _ = orc.swiglu(orc.quantize(Q4_0, np.concatenate([np.zeros_like(wg), wu])), N, K, x32)
+    if (yz != 0).any() or (uz == 0).all():
+        fails.append("swiglu: a zero gate table does not give zero")
+    # a large gate (every gate weight 0.875, activations 2: g = 56, silu(g) = g
+    # in fp64) gives g * u
+    big = np.full((N, K), 0.875, np.float32)
+    xb = np.full((M, K), 2.0, np.float32)
+    yb, gb, ub, _, _ = orc.swiglu(orc.quantize(Q4_0, np.concatenate([big, wu])), N, K, xb)
+    if not (gb == 0.875 * 2.0 * K).all():
+        fails.append(f"swiglu: gate of constant rows is {gb[0, 0]!r}, not {0.875 * 2.0 * K}")
+    if not (np.abs(yb - gb * ub) <= 1e-12 * np.abs(gb * ub)).all():
+        fails.append("swiglu: a large gate does not give gate * up")
+    return fails
+
+
 ALL_PINS = [pin_codec, pin_golden, pin_nearest, pin_invariants, pin_exact_gemv, pin_special, pin_moe,
-            pin_prefill]
+            pin_prefill, pin_f32in, pin_silu, pin_swiglu]

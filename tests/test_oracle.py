@@ -26,6 +26,8 @@ PLANTS = {
     "xindex": [pins.pin_exact_gemv],      # activation index slip (k ^ 1)
     "drop": [pins.pin_exact_gemv],        # last block of each row dropped from the sum
     "scaleidx": [pins.pin_prefill],       # scale of the next block used
+    "silu": [pins.pin_silu],              # e^v instead of e^-v in silu
+    "glu": [pins.pin_swiglu],             # silu applied to the up half, not the gate
 }
 
 
