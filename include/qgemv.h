@@ -109,6 +109,34 @@ qg_status qgemv_q4_0(const void *Wp, const uint16_t *x, float *y, int M, int64_t
 qg_status qgemv_q8_0(const void *Wp, const uint16_t *x, float *y, int M, int64_t N, int64_t K,
                      void *stream);
 
+/* Q4_0 GEMV on fp32 activations, 1 <= M <= 4 tokens: each activation is
+ * rounded to binary16 inside the kernel (nearest, ties to even; a magnitude
+ * above 65504 becomes infinity, and so does its outputs' sum), then
+ *   y[m][n] = sum_k w[n][k] * fp16(x[m][k])
+ * with the conventions of qgemv_q4_0.  x: fp32 [M][K] row-major (device,
+ * 16-byte aligned); Wp, y and the other limits as for qgemv_q4_0, with
+ * K <= 16384 * min(floor(4 / M), 4).  The conversion is done once per
+ * activation block by each team that reads it, not in a separate pass.
+ * [volta-kernel-bakeoff, "Results", the like-for-like bullets: fp32
+ *  activations in, the conversion counted, inside the kernel at 1 token and
+ *  at up to 4 tokens on expert-sized tables] */
+qg_status qgemv_q4_0_f32in(const void *Wp, const float *x, float *y, int M, int64_t N, int64_t K, void *stream);
+
+/* Gate, up and SwiGLU in one launch, Q4_0, fp32 activations, 1 <= M <= 4:
+ * Wp is ONE packed table of 2N rows (the layout above for 2N x K): rows
+ * 0..N-1 are the gate rows, rows N..2N-1 the up rows.  With g and u the two
+ * GEMVs on fp16(x) (as qgemv_q4_0_f32in),
+ *   y[m][n] = silu(g[m][n]) * u[m][n],   silu(v) = v / (1 + e^-v),
+ * evaluated in fp32 on the fp32 sums; only y is written.  y: fp32 [M][N].
+ * 1 <= N <= 2^30 - 1; K as for qgemv_q4_0_f32in.  Accuracy: g and u meet
+ * the GEMV bound, and y is within 1.1 eg (|u| + eu) + |g| eu + 1e-5 |y| of
+ * the exact silu(g) u (eg, eu: the GEMV bounds of g and u).
+ * [volta-kernel-bakeoff, "Results", the few-tokens bullet: gate and up
+ *  stacked into one table, the activations converted once; the FFN fusion
+ *  step of the CUDA-kernel diary: gate, up and SwiGLU in one kernel] */
+qg_status qgemv_q4_0_swiglu_f32in(const void *Wp, const float *x, float *y, int M, int64_t N, int64_t K,
+                                  void *stream);
+
 /* Mixture-of-experts GEMV in one launch, Q4_0: expert slot e (0 <= e < E)
  * multiplies pool matrix idx[e] by its own token x[e]:
  *   y[e][n] = sum_k w_{idx[e]}[n][k] * x[e][k]

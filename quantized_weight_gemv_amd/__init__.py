@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
         "qquantize_q8_0": (c_int, [vp, i64, i64, vp, sz]),
         "qgemv_q4_0": (c_int, [vp, vp, vp, c_int, i64, i64, vp]),
         "qgemv_q8_0": (c_int, [vp, vp, vp, c_int, i64, i64, vp]),
+        "qgemv_q4_0_f32in": (c_int, [vp, vp, vp, c_int, i64, i64, vp]),
+        "qgemv_q4_0_swiglu_f32in": (c_int, [vp, vp, vp, c_int, i64, i64, vp]),
         "qmoe_gemv_q4_0": (c_int, [vp, i64, vp, vp, vp, c_int, i64, i64, vp]),
         "qgemm_q4_0_prefill": (c_int, [vp, vp, vp, i64, i64, i64, vp]),
         "qdequant_q4_0": (c_int, [vp, i64, i64, c_int, vp, vp]),
@@ -80,7 +82,8 @@ def lib() -> ctypes.CDLL:
 
 def exported_symbols() -> list[str]:
     return ["qg_status_str", "qpacked_bytes_q4_0", "qpacked_bytes_q8_0", "qquantize_q4_0", "qquantize_q8_0",
-            "qgemv_q4_0", "qgemv_q8_0", "qmoe_gemv_q4_0", "qgemm_q4_0_prefill", "qdequant_q4_0",
+            "qgemv_q4_0", "qgemv_q8_0", "qgemv_q4_0_f32in", "qgemv_q4_0_swiglu_f32in", "qmoe_gemv_q4_0",
+            "qgemm_q4_0_prefill", "qdequant_q4_0",
             "qdequant_q8_0", "qg_time_next_launch", "qg_device_cus", "qg_set_gemv_shape", "qg_read_probe", "qg_set_prefill_shape"]
 
 
@@ -204,6 +207,30 @@ def qgemv_q4_0(Wp, x, N: int, K: int, y=None):
 def qgemv_q8_0(Wp, x, N: int, K: int, y=None):
     """y[M][N] (fp32) = dequant(Wp) @ x[M][K]^T; Wp uint8 packed Q8_0, x fp16, 1 <= M <= 8."""
     return _gemv("qgemv_q8_0", Q8_0, Wp, x, N, K, y)
+
+
+def _f32in(fn: str, Wp, x, N: int, K: int, y, rows: int):
+    torch = _torch()
+    if x.dim() != 2 or x.shape[1] != K or x.dtype != torch.float32:
+        raise ValueError(f"x must be float32 [M][{K}]")
+    M = x.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    wp = _dev(Wp, torch.uint8, "Wp", qpacked_bytes_q4_0(rows, K))
+    xp = _dev(x, torch.float32, "x", M * K)
+    yp = _dev(y, torch.float32, "y", M * N)
+    _check(fn, getattr(lib(), fn)(wp, xp, yp, M, N, K, _stream()))
+    return y
+
+
+def qgemv_q4_0_f32in(Wp, x, N: int, K: int, y=None):
+    """y[M][N] = dequant(Wp) @ fp16(x)^T with fp32 x rounded inside the kernel."""
+    return _f32in("qgemv_q4_0_f32in", Wp, x, N, K, y, N)
+
+
+def qgemv_q4_0_swiglu_f32in(Wp, x, N: int, K: int, y=None):
+    """y[M][N] = silu(gate) * up; Wp packs the 2N x K table [gate rows; up rows]."""
+    return _f32in("qgemv_q4_0_swiglu_f32in", Wp, x, N, K, y, 2 * N)
 
 
 def qmoe_gemv_q4_0(pool, P: int, idx, x, N: int, K: int, y=None):

@@ -73,8 +73,9 @@ struct GemvShape {
 thread_local int o_G = 0, o_J = 0, o_R = 0, o_ksplit = 0, o_teams_per_wg = 0, o_xl = -1, o_engine = -1;
 thread_local int64_t o_teams = 0;
 
-bool choose_shape(int fmt, int M, int64_t N, int64_t K, int items, int cus, GemvShape &s)
+bool choose_shape(int fmt, int M, int64_t N, int64_t K, int items, int cus, int mode, GemvShape &s)
 {
+    const bool glu = mode == kModeGlu;
     const int64_t KB = K / 32;
     // Activations staged in LDS (one token) stay a tuning option: one block
     // per lane with K split over several waves measured faster on MI355X.
@@ -130,16 +131,22 @@ bool choose_shape(int fmt, int M, int64_t N, int64_t K, int items, int cus, Gemv
     int R = (N > 65536 && G == 64) ? 4 : 2;
     if (q4_one && G == 16)
         R = 4;   // 4096 x 4096: 3.95 against 4.10 us back to back
-    if (M >= 2 && J == 1 && ksplit > 1 &&
+    if (glu)
+        R = 2;   // SwiGLU: one gate and one up row set per group
+    if (M >= 2 && J == 1 && ksplit > 1 && !glu &&
         (fmt == kQ4_0 || N <= 4LL * cus * std::max(2, 8 / ksplit)))
         R = 4;
-    while (R * J > rj && R > 1)
+    while (R * J > rj && R > (glu ? 2 : 1))
         R /= 2;
     // stay within the instantiated kernels (register budget): fewer row sets,
     // then more waves along K
-    while (R > 1 && !gemv_fits(fmt, M, G, J, R, xl))
+    while (R > (glu ? 2 : 1) && !gemv_fits(fmt, M, G, J, R, xl, mode))
         R /= 2;
-    while (!xl && !gemv_fits(fmt, M, G, J, R, xl) && ksplit < kMaxWavesPerWg && J > 1) {
+    while (glu && R * J > rj && J > 1) {
+        --J;
+        ksplit = static_cast<int>((KB + static_cast<int64_t>(G) * J - 1) / (static_cast<int64_t>(G) * J));
+    }
+    while (!xl && !gemv_fits(fmt, M, G, J, R, xl, mode) && ksplit < kMaxWavesPerWg && J > 1) {
         --J;
         ksplit = static_cast<int>((KB + static_cast<int64_t>(G) * J - 1) / (static_cast<int64_t>(G) * J));
     }
@@ -157,19 +164,20 @@ bool choose_shape(int fmt, int M, int64_t N, int64_t K, int items, int cus, Gemv
         if (static_cast<int64_t>(ksplit) * G * J < KB || ksplit > kMaxWavesPerWg)
             return false;
     }
-    if (o_R)
+    if (o_R && !glu)
         R = o_R;
     if (o_teams_per_wg)
         teams_per_wg = o_teams_per_wg;
     if (xl && (ksplit > 1 || M != 1 || gemv_xl_lds_bytes(static_cast<int>(K)) > 65536))
         return false;
-    if (!gemv_fits(fmt, M, G, J, R, xl))
+    if (!gemv_fits(fmt, M, G, J, R, xl, mode))
         return false;
     if (ksplit > 1)
         teams_per_wg = 1;   // a workgroup's waves must walk the same row groups
     if (teams_per_wg * ksplit > kMaxWavesPerWg)
         teams_per_wg = std::max(1, kMaxWavesPerWg / ksplit);
-    const int64_t ngroups = (N + static_cast<int64_t>(R) * P - 1) / (static_cast<int64_t>(R) * P);
+    const int64_t rows_per_group = glu ? P : static_cast<int64_t>(R) * P;   // output rows per group
+    const int64_t ngroups = (N + rows_per_group - 1) / rows_per_group;
     // Teams per CU (launch sweeps on MI355X): 8 for one-wave rows; with K
     // split, about 16 waves per CU for one token and 8 for several; beyond
     // 64K rows 64 teams per CU, more than fit at once (the hardware
@@ -195,14 +203,19 @@ bool choose_shape(int fmt, int M, int64_t N, int64_t K, int items, int cus, Gemv
 }
 
 qg_status run_gemv(int fmt, const void *Wp, const int32_t *idx, int64_t P, const uint16_t *x, float *y, int M,
-                   int items, int64_t N, int64_t K, void *stream)
+                   int items, int64_t N, int64_t K, void *stream, int mode = kModeF16, const float *xf = nullptr)
 {
-    if (!Wp || !x || !y)
+    const void *xa = (mode == kModeF16) ? static_cast<const void *>(x) : static_cast<const void *>(xf);
+    if (!Wp || !xa || !y)
         return QG_ERR_NULL;
-    if (M < 1 || M > 8 || N < 1 || N > INT32_MAX || K < 32 || K % 32 != 0 || K > (1 << 20) || items < 1 ||
+    const int64_t nmax = (mode == kModeGlu) ? INT32_MAX / 2 : INT32_MAX;   // SwiGLU reads 2N rows
+    // fp32 activations: up to 4 tokens (their raw words stay in registers
+    // until converted)
+    const int mmax = (mode == kModeF16) ? 8 : 4;
+    if (M < 1 || M > mmax || N < 1 || N > nmax || K < 32 || K % 32 != 0 || K > (1 << 20) || items < 1 ||
         items > 65535)
         return QG_ERR_SHAPE;
-    if (!aligned(Wp, 256) || !aligned(x, 16) || !aligned(y, 4))
+    if (!aligned(Wp, 256) || !aligned(xa, 16) || !aligned(y, 4))
         return QG_ERR_ALIGN;
     const int cus = device_cus();
     if (cus <= 0)
@@ -218,12 +231,14 @@ qg_status run_gemv(int fmt, const void *Wp, const int32_t *idx, int64_t P, const
     // against 9.6 us; at 6 tokens 8.9 against 7.9).
     const int64_t KB = K / 32;
     const bool tiles_fill = N >= 16LL * cus;
-    bool mfma = idx == nullptr &&
+    bool mfma = idx == nullptr && mode == kModeF16 &&
                 ((tiles_fill && fmt == kQ4_0 && M >= 4 && KB <= 128) ||
                  (tiles_fill && fmt == kQ8_0 && ((M >= 4 && KB <= 64) || (M >= 6 && KB <= 128))) ||
                  (N >= 8LL * cus && fmt == kQ4_0 && M == 8 && KB <= 256));
     if (o_engine >= 0)
         mfma = (o_engine == 1);
+    if (mfma && mode != kModeF16)
+        return QG_ERR_SHAPE;   // the matrix-core kernel reads fp16 activations
     if (mfma) {
         if (idx != nullptr || KB > 256 || N > INT32_MAX)
             return QG_ERR_SHAPE;
@@ -239,15 +254,17 @@ qg_status run_gemv(int fmt, const void *Wp, const int32_t *idx, int64_t P, const
         return e == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
     }
     GemvShape s;
-    if (!choose_shape(fmt, M, N, K, items, cus, s))
+    if (!choose_shape(fmt, M, N, K, items, cus, mode, s))
         return QG_ERR_SHAPE;
+    const int64_t rows = (mode == kModeGlu) ? 2 * N : N;   // rows of the packed table
     GemvParams p;
     p.W = static_cast<const uint8_t *>(Wp);
     p.idx = idx;
     p.x = x;
+    p.xf = xf;
     p.y = y;
-    p.matrix_stride = static_cast<int64_t>(fmt == kQ4_0 ? qpacked_bytes_q4_0(N, K) : qpacked_bytes_q8_0(N, K));
-    p.scale_offset = scale_offset(fmt, N, K);
+    p.matrix_stride = static_cast<int64_t>(fmt == kQ4_0 ? qpacked_bytes_q4_0(rows, K) : qpacked_bytes_q8_0(rows, K));
+    p.scale_offset = scale_offset(fmt, rows, K);
     p.N = static_cast<int>(N);
     p.K = static_cast<int>(K);
     p.ksplit = s.ksplit;
@@ -256,7 +273,7 @@ qg_status run_gemv(int fmt, const void *Wp, const int32_t *idx, int64_t P, const
     const int64_t wgs = (s.teams + s.teams_per_wg - 1) / s.teams_per_wg;
     dim3 grid(static_cast<unsigned>(wgs), static_cast<unsigned>(items), 1);
     dim3 block(64 * s.ksplit * s.teams_per_wg, 1, 1);
-    hipError_t e = launch_gemv(fmt, M, s.G, s.J, s.R, s.xl, p, grid, block, static_cast<hipStream_t>(stream));
+    hipError_t e = launch_gemv(fmt, M, s.G, s.J, s.R, s.xl, mode, p, grid, block, static_cast<hipStream_t>(stream));
     if (e == hipErrorInvalidValue)
         return QG_ERR_SHAPE;
     return e == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
@@ -363,6 +380,17 @@ qg_status qgemv_q4_0(const void *Wp, const uint16_t *x, float *y, int M, int64_t
 qg_status qgemv_q8_0(const void *Wp, const uint16_t *x, float *y, int M, int64_t N, int64_t K, void *stream)
 {
     return qg::run_gemv(qg::kQ8_0, Wp, nullptr, 1, x, y, M, 1, N, K, stream);
+}
+
+qg_status qgemv_q4_0_f32in(const void *Wp, const float *x, float *y, int M, int64_t N, int64_t K, void *stream)
+{
+    return qg::run_gemv(qg::kQ4_0, Wp, nullptr, 1, nullptr, y, M, 1, N, K, stream, qg::kModeF32, x);
+}
+
+qg_status qgemv_q4_0_swiglu_f32in(const void *Wp, const float *x, float *y, int M, int64_t N, int64_t K,
+                                  void *stream)
+{
+    return qg::run_gemv(qg::kQ4_0, Wp, nullptr, 1, nullptr, y, M, 1, N, K, stream, qg::kModeGlu, x);
 }
 
 qg_status qmoe_gemv_q4_0(const void *pool, int64_t P, const int32_t *idx, const uint16_t *x, float *y, int E,

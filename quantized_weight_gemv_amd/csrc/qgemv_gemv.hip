@@ -32,15 +32,16 @@
 //   * Unpack: a nibble n OR-ed into the binary16 pattern 0x6400 is the half
 //     1024 + n exactly [volta-kernel-bakeoff, "What's in the race", the
 //     fused_q4_v2 bit trick]; a high nibble left in place gives 1024 + 16 n.
-//     One v_and_or_b32 makes two such halves.  The bias is not subtracted per
-//     weight: products with the activations go through v_dot2_f32_f16 (two
-//     exact fp16 products summed into fp32), and each block's two dot chains
-//     start from -1032 * (sum of its low-nibble activations) and -1152 * (sum
-//     of its high-nibble activations), constants computed once per team.  Then
-//     low chain + high chain / 16 = sum (q - 8) x exactly up to fp32 rounding
-//     of the chains.  Q8_0: (q + 128) | 0x6400 = q + 1152, placed with one
-//     v_perm_b32 per pair, chains start from -1152 * (sum of activations).
-//     The block scale multiplies the block sum once.
+//     One v_and_or_b32 makes two such halves and one v_pk_add_f16 removes the
+//     bias from both, exactly: n - 8 and 16 (n - 8).  Q8_0: (q + 128) | 0x6400
+//     = q + 1152, placed with one v_perm_b32 per pair, minus 1152 gives q.
+//     Products with the activations go through v_dot2_f32_f16 (two exact fp16
+//     products summed into fp32) in two chains per block, low + high / 16 =
+//     sum (q - 8) x; the block scale multiplies the block sum once.  (Leaving
+//     the bias in and starting the chains from -1032 * sum x saves the
+//     subtraction, but the chains then run at 1032 |x|: one activation near
+//     the binary16 limit against a zero weight rounds them by more than the
+//     1e-3 sum |w x| accuracy of the result.)
 //   * Reduction over a row's G lanes: DPP within 16-lane rows, then
 //     v_permlane16_swap / v_permlane32_swap across them; waves of a team
 //     (ksplit > 1) combine through LDS.  No atomics: results are reproducible.
@@ -61,13 +62,13 @@ __device__ __forceinline__ float dot2(h2_t a, h2_t b, float c)
     return __builtin_amdgcn_fdot2(a, b, c, false);
 }
 
-// The first product of a chain that starts from a value still needed later
-// (a loop-invariant bias term): the three-operand encoding writes a fresh
-// register, where the compiler's two-operand form would first copy c.
-__device__ __forceinline__ float dot2_from(h2_t a, h2_t b, float c)
+// The first product of a chain: the three-operand encoding with an inline
+// zero writes a fresh register, where the compiler zeroes one with a move and
+// then accumulates into it.
+__device__ __forceinline__ float dot2_first(h2_t a, h2_t b)
 {
     float d;
-    asm("v_dot2_f32_f16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+    asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(d) : "v"(a), "v"(b));
     return d;
 }
 
@@ -86,22 +87,24 @@ __device__ __forceinline__ uint32_t magic_reg()
 }
 
 // Q4_0: word t holds bytes 4t..4t+3 = elements 4t..4t+3 (low nibbles) and
-// 16+4t..19+4t (high nibbles).
-//   lo[2t]   = 1024 + (e[4t],    e[4t+2])        partner X[4t+0]
-//   lo[2t+1] = 1024 + (e[4t+1],  e[4t+3])        partner X[4t+2]
-//   hi[2t]   = 1024 + 16 (e[16+4t], e[18+4t])    partner X[4t+1]
-//   hi[2t+1] = 1024 + 16 (e[17+4t], e[19+4t])    partner X[4t+3]
+// 16+4t..19+4t (high nibbles); with q' = q - 8:
+//   lo[2t]   = (q'[4t],    q'[4t+2])          partner X[4t+0]
+//   lo[2t+1] = (q'[4t+1],  q'[4t+3])          partner X[4t+2]
+//   hi[2t]   = 16 (q'[16+4t], q'[18+4t])      partner X[4t+1]
+//   hi[2t+1] = 16 (q'[17+4t], q'[19+4t])      partner X[4t+3]
 __device__ __forceinline__ void unpack_q4(const uint4 c, uint32_t kMagic, h2_t (&lo)[8], h2_t (&hi)[8])
 {
     const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    const h2_t kLo = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    const h2_t kHi = {(_Float16)-1152.0f, (_Float16)-1152.0f};
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const uint32_t a = w[t];
         const uint32_t b = w[t] >> 8;
-        lo[2 * t + 0] = as_h2((a & 0x000F000Fu) | kMagic);
-        hi[2 * t + 0] = as_h2((a & 0x00F000F0u) | kMagic);
-        lo[2 * t + 1] = as_h2((b & 0x000F000Fu) | kMagic);
-        hi[2 * t + 1] = as_h2((b & 0x00F000F0u) | kMagic);
+        lo[2 * t + 0] = as_h2((a & 0x000F000Fu) | kMagic) + kLo;
+        hi[2 * t + 0] = as_h2((a & 0x00F000F0u) | kMagic) + kHi;
+        lo[2 * t + 1] = as_h2((b & 0x000F000Fu) | kMagic) + kLo;
+        hi[2 * t + 1] = as_h2((b & 0x00F000F0u) | kMagic) + kHi;
     }
 }
 
@@ -109,16 +112,18 @@ __device__ __forceinline__ void unpack_q4(const uint4 c, uint32_t kMagic, h2_t (
 // u = q + 128 in 0..255; with 0x64 as the high byte, u is the half 1024 + u =
 // q + 1152 exactly.  v_perm_b32 takes bytes 0 and 2 (1 and 3) of u and the
 // 0x64 bytes of the magic word in one instruction.
-//   v[2t] = 1152 + (e[4t], e[4t+2])   v[2t+1] = 1152 + (e[4t+1], e[4t+3])
+// Subtracting 1152 leaves the codes:
+//   v[2t] = (q[4t], q[4t+2])   v[2t+1] = (q[4t+1], q[4t+3])
 __device__ __forceinline__ void unpack_q8(const uint4 c0, const uint4 c1, uint32_t kMagic, h2_t (&v)[16])
 {
     const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    const h2_t kBias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
         const uint32_t u = w[t] ^ 0x80808080u;
         // selector bytes: 0-3 pick bytes of u, 4-7 bytes of the magic word
-        v[2 * t + 0] = as_h2(__builtin_amdgcn_perm(kMagic, u, 0x07020500u));
-        v[2 * t + 1] = as_h2(__builtin_amdgcn_perm(kMagic, u, 0x07030501u));
+        v[2 * t + 0] = as_h2(__builtin_amdgcn_perm(kMagic, u, 0x07020500u)) + kBias;
+        v[2 * t + 1] = as_h2(__builtin_amdgcn_perm(kMagic, u, 0x07030501u)) + kBias;
     }
 }
 
@@ -158,42 +163,36 @@ __device__ __forceinline__ void load_x_raw(const uint16_t *p, uint4 (&r)[4])
         r[u] = q[u];
 }
 
+// 32 fp32 activations rounded to binary16 (nearest, ties to even, the
+// conversion's default mode; beyond binary16's range: infinity), in the same
+// natural-order words load_x_raw returns [volta-kernel-bakeoff, "Results":
+// fp32 activations in, the conversion inside the kernel].
+__device__ __forceinline__ uint32_t pack_half2(float a, float b)
+{
+    const uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)a);
+    const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)b);
+    return lo | (hi << 16);
+}
+
+__device__ __forceinline__ void load_x_raw_f32(const float *p, uint4 (&r)[4])
+{
+    const float4 *q = reinterpret_cast<const float4 *>(p);
+    float4 f[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+        f[u] = q[u];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+        r[u] = make_uint4(pack_half2(f[2 * u].x, f[2 * u].y), pack_half2(f[2 * u].z, f[2 * u].w),
+                          pack_half2(f[2 * u + 1].x, f[2 * u + 1].y), pack_half2(f[2 * u + 1].z, f[2 * u + 1].w));
+}
+
 template <int FMT>
 __device__ __forceinline__ void load_x_block(const uint16_t *p, uint32_t (&X)[16])
 {
     uint4 r[4];
     load_x_raw(p, r);
     pair_x_block<FMT>(r, X);
-}
-
-// Starting values of a block's two dot chains: minus the bias times the
-// activations each chain sees.  Q4_0: chain 0 takes the low nibbles (bias
-// 1032 = 1024 + 8), chain 1 the high nibbles at 16x scale (bias 1152 =
-// 16 * 72); Q8_0: chain 0 takes pairs 0..7, chain 1 pairs 8..15 (bias 1152).
-template <int FMT>
-__device__ __forceinline__ void bias_terms(const uint32_t (&X)[16], float (&c)[2])
-{
-    float a = 0.0f, b = 0.0f;
-    if constexpr (FMT == kQ4_0) {
-        const h2_t kLo = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-        const h2_t kHi = {(_Float16)-1152.0f, (_Float16)-1152.0f};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            a = dot2(kLo, as_h2(X[4 * t + 0]), a);
-            a = dot2(kLo, as_h2(X[4 * t + 2]), a);
-            b = dot2(kHi, as_h2(X[4 * t + 1]), b);
-            b = dot2(kHi, as_h2(X[4 * t + 3]), b);
-        }
-    } else {
-        const h2_t k = {(_Float16)-1152.0f, (_Float16)-1152.0f};
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            a = dot2(k, as_h2(X[t]), a);
-            b = dot2(k, as_h2(X[8 + t]), b);
-        }
-    }
-    c[0] = a;
-    c[1] = b;
 }
 
 // ---------------------------------------------------------------- reduction
@@ -254,16 +253,18 @@ struct Group {
 // soff: row within the set and block).  Padding lanes of a short K chunk read
 // their chunk's last block (their block index is clamped) and have zero
 // activations, so they add nothing.
-template <int FMT, int G, int J, int R>
+template <int FMT, int G, int J, int R, bool GLU>
 __device__ __forceinline__ void load_group(Group<FMT, J, R> &g, const uint8_t *__restrict__ W,
                                            const uint8_t *__restrict__ S, int64_t rs0, int64_t rmax, int KB,
-                                           int64_t nblocks, const uint32_t (&coff)[J], const uint32_t (&soff)[J])
+                                           int64_t nblocks, const uint32_t (&coff)[J], const uint32_t (&soff)[J],
+                                           int64_t N)
 {
     constexpr int P = 64 / G;
     constexpr int CB = (FMT == kQ4_0) ? 16 : 32;   // code bytes per block
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-        const int64_t rbase = min(rs0 + i * P, rmax);
+        // GLU: row set 0 holds gate rows, row set 1 the up rows N further
+        const int64_t rbase = GLU ? min(rs0, rmax) + i * N : min(rs0 + i * P, rmax);
         const int64_t base = rbase * KB;   // first block of the row set
         const auto rc = make_rsrc(W + base * CB, (nblocks - base) * CB);
         const auto rs = make_rsrc(S + base * 2, (nblocks - base) * 2);
@@ -280,16 +281,14 @@ __device__ __forceinline__ void load_group(Group<FMT, J, R> &g, const uint8_t *_
     }
 }
 
-// Activations come either from registers (X and their bias terms XC, loaded
-// once per team) or, with XL, from the workgroup's LDS copy (one token; xs
-// holds every block of x in pair order plus one zero block that padding
-// lanes read, xc the blocks' bias terms).
+// Activations come either from registers (X, loaded once per team) or, with
+// XL, from the workgroup's LDS copy (one token; xs holds every block of x in
+// pair order plus one zero block that padding lanes read).
 template <int FMT, int M, int J, int R, bool XL>
 __device__ __forceinline__ void compute_group(const Group<FMT, J, R> &g,
                                               const uint32_t (&X)[XL ? 1 : M][XL ? 1 : J][16],
-                                              const float (&XC)[XL ? 1 : M][XL ? 1 : J][2],
-                                              const uint4 *xs, const float2 *xc, const uint32_t (&xoff)[J],
-                                              uint32_t magic, float (&acc)[R][M])
+                                              const uint4 *xs, const uint32_t (&xoff)[J], uint32_t magic,
+                                              float (&acc)[R][M])
 {
 #pragma unroll
     for (int i = 0; i < R; ++i) {
@@ -314,7 +313,6 @@ __device__ __forceinline__ void compute_group(const Group<FMT, J, R> &g,
 #pragma unroll
             for (int m = 0; m < M; ++m) {
                 uint32_t xw[16];
-                float c0, c1;
                 if constexpr (XL) {
                     const uint4 *q = xs + xoff[j] * 4;
 #pragma unroll
@@ -325,20 +323,15 @@ __device__ __forceinline__ void compute_group(const Group<FMT, J, R> &g,
                         xw[4 * u + 2] = t.z;
                         xw[4 * u + 3] = t.w;
                     }
-                    const float2 cc = xc[xoff[j]];
-                    c0 = cc.x;
-                    c1 = cc.y;
                 } else {
 #pragma unroll
                     for (int t = 0; t < 16; ++t)
                         xw[t] = X[m][j][t];
-                    c0 = XC[m][j][0];
-                    c1 = XC[m][j][1];
                 }
                 float blk;
                 if constexpr (FMT == kQ4_0) {
-                    c0 = dot2_from(v0[0], as_h2(xw[0]), c0);
-                    c1 = dot2_from(v1[0], as_h2(xw[1]), c1);
+                    float c0 = dot2_first(v0[0], as_h2(xw[0]));
+                    float c1 = dot2_first(v1[0], as_h2(xw[1]));
                     c0 = dot2(v0[1], as_h2(xw[2]), c0);
                     c1 = dot2(v1[1], as_h2(xw[3]), c1);
 #pragma unroll
@@ -350,8 +343,8 @@ __device__ __forceinline__ void compute_group(const Group<FMT, J, R> &g,
                     }
                     blk = __builtin_fmaf(c1, 0.0625f, c0);
                 } else {
-                    c0 = dot2_from(v0[0], as_h2(xw[0]), c0);
-                    c1 = dot2_from(v1[0], as_h2(xw[8]), c1);
+                    float c0 = dot2_first(v0[0], as_h2(xw[0]));
+                    float c1 = dot2_first(v1[0], as_h2(xw[8]));
 #pragma unroll
                     for (int t = 1; t < 8; ++t) {
                         c0 = dot2(v0[t], as_h2(xw[t]), c0);
@@ -432,10 +425,75 @@ __device__ __forceinline__ void finish_group(const float (&acc)[R][M], float *__
     }
 }
 
-template <int FMT, int M, int G, int J, int R, bool XL>
+// SwiGLU epilogue: silu(gate) * up, evaluated in fp32 on the two row sets'
+// reduced sums (gate rows of the group, and the up rows N further)
+// [the CUDA-kernel diary's FFN fusion step: gate, up and SwiGLU in one kernel,
+// only the final product written].
+__device__ __forceinline__ float swiglu(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+template <int G, int M>
+__device__ __forceinline__ void finish_group_glu(const float (&acc)[2][M], float *__restrict__ y, int64_t rs0,
+                                                 int64_t rmax, int N, int lane, int wave, int team, int kw,
+                                                 int ksplit, float (&red)[2][kMaxWavesPerWg][kMaxRM], int &buf)
+{
+    constexpr int P = 64 / G;
+    float tot[2][M];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+            tot[i][m] = seg_sum<G>(acc[i][m]);
+    const int lr = lane / G;
+    const int64_t first = min(rs0, rmax);
+    const int lo = (int)(rs0 - first);
+    const int hi = (int)min((int64_t)N - first, (int64_t)P);
+    if (ksplit == 1) {
+        if (lane % G == 0 && lr >= lo && lr < hi) {
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+                y[(int64_t)m * N + first + lr] = swiglu(tot[0][m], tot[1][m]);
+        }
+    } else {
+        if (lane % G == 0) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+                    red[buf][wave][(i * M + m) * P + lr] = tot[i][m];
+        }
+        __syncthreads();
+        if (kw == 0 && lane < M * P) {
+            const int m = lane / P, r = lane % P;
+            float gs = 0.0f, us = 0.0f;
+            for (int w = 0; w < ksplit; ++w) {
+                gs += red[buf][team * ksplit + w][m * P + r];
+                us += red[buf][team * ksplit + w][(M + m) * P + r];
+            }
+            if (r >= lo && r < hi)
+                y[(int64_t)m * N + first + r] = swiglu(gs, us);
+        }
+        buf ^= 1;
+    }
+}
+
+template <int G, int M, int R, bool GLU>
+__device__ __forceinline__ void finish(const float (&acc)[R][M], float *__restrict__ y, int64_t rs0, int64_t rmax,
+                                       int N, int lane, int wave, int team, int kw, int ksplit,
+                                       float (&red)[2][kMaxWavesPerWg][kMaxRM], int &buf)
+{
+    if constexpr (GLU)
+        finish_group_glu<G, M>(acc, y, rs0, rmax, N, lane, wave, team, kw, ksplit, red, buf);
+    else
+        finish_group<G, M, R>(acc, y, rs0, rmax, N, lane, wave, team, kw, ksplit, red, buf);
+}
+
+template <int FMT, int M, int G, int J, int R, bool XL, int MODE>
 __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
 {
     static_assert(!XL || M == 1, "LDS-staged activations are for one token");
+    static_assert(MODE == kModeF16 || (!XL && FMT == kQ4_0), "fp32 activations: Q4_0, registers");
+    constexpr bool GLU = MODE == kModeGlu;
+    static_assert(!GLU || R == 2, "SwiGLU: one gate and one up row set per group");
     constexpr int P = 64 / G;
     const int lane = threadIdx.x & 63;
     // wave-uniform: everything derived from it (rows, addresses) stays scalar
@@ -451,6 +509,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
         W += (int64_t)p.idx[item] * p.matrix_stride;
     const uint8_t *__restrict__ S = W + p.scale_offset;
     const uint16_t *__restrict__ x = p.x + (int64_t)item * M * p.K;
+    const float *__restrict__ xf = p.xf;
     float *__restrict__ y = p.y + (int64_t)item * M * p.N;
 
     const int KB = p.K >> 5;
@@ -472,10 +531,12 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
 
     // groups of R row sets; a row set's first row is clamped to rmax = N - P
     // (the launcher ensures N >= P)
-    const int64_t rows_per_group = (int64_t)R * P;
+    // (GLU: a group is P output rows, read as P gate rows and P up rows of
+    // the 2N-row table)
+    const int64_t rows_per_group = GLU ? P : (int64_t)R * P;
     const int64_t ngroups = ((int64_t)p.N + rows_per_group - 1) / rows_per_group;
     const int64_t rmax = (int64_t)p.N - P;
-    const int64_t nblocks = (int64_t)p.N * KB;
+    const int64_t nblocks = (int64_t)p.N * KB * (GLU ? 2 : 1);
     int64_t g = team_id;
 
     Group<FMT, J, R> ga, gb;
@@ -485,27 +546,26 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
     // cache after the first waves, and queued behind a full round of weight
     // requests they would hold up every wave's first compute.
     uint32_t X[XL ? 1 : M][XL ? 1 : J][16];
-    float XC[XL ? 1 : M][XL ? 1 : J][2];
     extern __shared__ uint4 xs_dyn[];
-    const float2 *xc_lds = reinterpret_cast<const float2 *>(xs_dyn + (XL ? (KB + 1) * 4 : 0));
     uint4 XR[XL ? 1 : M][XL ? 1 : J][4];   // raw activation words, paired below
     if constexpr (!XL) {
 #pragma unroll
         for (int m = 0; m < M; ++m)
 #pragma unroll
             for (int j = 0; j < J; ++j)
-                load_x_raw(x + (int64_t)m * p.K + (int64_t)blk[j] * 32, XR[m][j]);
+                if constexpr (MODE == kModeF16)
+                    load_x_raw(x + (int64_t)m * p.K + (int64_t)blk[j] * 32, XR[m][j]);
+                else
+                    load_x_raw_f32(xf + (int64_t)m * p.K + (int64_t)blk[j] * 32, XR[m][j]);
     }
     __builtin_amdgcn_sched_barrier(0);
     // unconditional (a team without groups re-reads a clamped, in-bounds row
     // set): with a conditional load the wait for the activations below would
     // also cover these weights
-    load_group<FMT, G, J, R>(ga, W, S, g * rows_per_group, rmax, KB, nblocks, coff, soff);
+    load_group<FMT, G, J, R, GLU>(ga, W, S, g * rows_per_group, rmax, KB, nblocks, coff, soff, p.N);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (XL) {
-        // the workgroup stages x once, in pair order, plus a zero block, and
-        // the bias terms of every block
-        float2 *xcw = reinterpret_cast<float2 *>(xs_dyn + (KB + 1) * 4);
+        // the workgroup stages x once, in pair order, plus a zero block
         for (int b = threadIdx.x; b <= KB; b += blockDim.x) {
             uint32_t w16[16];
             if (b < KB) {
@@ -515,12 +575,9 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
                 for (int t = 0; t < 16; ++t)
                     w16[t] = 0u;
             }
-            float c[2];
-            bias_terms<FMT>(w16, c);
 #pragma unroll
             for (int u = 0; u < 4; ++u)
                 xs_dyn[b * 4 + u] = make_uint4(w16[4 * u], w16[4 * u + 1], w16[4 * u + 2], w16[4 * u + 3]);
-            xcw[b] = make_float2(c[0], c[1]);
         }
         __syncthreads();
     } else {
@@ -534,7 +591,6 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
                     for (int t = 0; t < 16; ++t)
                         X[m][j][t] = 0u;
                 }
-                bias_terms<FMT>(X[m][j], XC[m][j]);
             }
     }
 
@@ -552,90 +608,119 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
     int64_t k = 0;
     for (; k + 2 < n; k += 2) {
         float acc[R][M];
-        load_group<FMT, G, J, R>(gb, W, S, (g + teams_total) * rows_per_group, rmax, KB, nblocks, coff, soff);
+        load_group<FMT, G, J, R, GLU>(gb, W, S, (g + teams_total) * rows_per_group, rmax, KB, nblocks, coff, soff, p.N);
         __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the compute
-        compute_group<FMT, M, J, R, XL>(ga, X, XC, xs_dyn, xc_lds, xoff, magic, acc);
-        finish_group<G, M, R>(acc, y, g * rows_per_group, rmax, p.N, lane, wave, team, kw, p.ksplit, red, buf);
+        compute_group<FMT, M, J, R, XL>(ga, X, xs_dyn, xoff, magic, acc);
+        finish<G, M, R, GLU>(acc, y, g * rows_per_group, rmax, p.N, lane, wave, team, kw, p.ksplit, red, buf);
         g += teams_total;
-        load_group<FMT, G, J, R>(ga, W, S, (g + teams_total) * rows_per_group, rmax, KB, nblocks, coff, soff);
+        load_group<FMT, G, J, R, GLU>(ga, W, S, (g + teams_total) * rows_per_group, rmax, KB, nblocks, coff, soff, p.N);
         __builtin_amdgcn_sched_barrier(0);
-        compute_group<FMT, M, J, R, XL>(gb, X, XC, xs_dyn, xc_lds, xoff, magic, acc);
-        finish_group<G, M, R>(acc, y, g * rows_per_group, rmax, p.N, lane, wave, team, kw, p.ksplit, red, buf);
+        compute_group<FMT, M, J, R, XL>(gb, X, xs_dyn, xoff, magic, acc);
+        finish<G, M, R, GLU>(acc, y, g * rows_per_group, rmax, p.N, lane, wave, team, kw, p.ksplit, red, buf);
         g += teams_total;
     }
     if (n - k == 2) {
         float acc[R][M];
-        load_group<FMT, G, J, R>(gb, W, S, (g + teams_total) * rows_per_group, rmax, KB, nblocks, coff, soff);
+        load_group<FMT, G, J, R, GLU>(gb, W, S, (g + teams_total) * rows_per_group, rmax, KB, nblocks, coff, soff, p.N);
         __builtin_amdgcn_sched_barrier(0);
-        compute_group<FMT, M, J, R, XL>(ga, X, XC, xs_dyn, xc_lds, xoff, magic, acc);
-        finish_group<G, M, R>(acc, y, g * rows_per_group, rmax, p.N, lane, wave, team, kw, p.ksplit, red, buf);
+        compute_group<FMT, M, J, R, XL>(ga, X, xs_dyn, xoff, magic, acc);
+        finish<G, M, R, GLU>(acc, y, g * rows_per_group, rmax, p.N, lane, wave, team, kw, p.ksplit, red, buf);
         g += teams_total;
-        compute_group<FMT, M, J, R, XL>(gb, X, XC, xs_dyn, xc_lds, xoff, magic, acc);
-        finish_group<G, M, R>(acc, y, g * rows_per_group, rmax, p.N, lane, wave, team, kw, p.ksplit, red, buf);
+        compute_group<FMT, M, J, R, XL>(gb, X, xs_dyn, xoff, magic, acc);
+        finish<G, M, R, GLU>(acc, y, g * rows_per_group, rmax, p.N, lane, wave, team, kw, p.ksplit, red, buf);
     } else if (n - k == 1) {
         float acc[R][M];
-        compute_group<FMT, M, J, R, XL>(ga, X, XC, xs_dyn, xc_lds, xoff, magic, acc);
-        finish_group<G, M, R>(acc, y, g * rows_per_group, rmax, p.N, lane, wave, team, kw, p.ksplit, red, buf);
+        compute_group<FMT, M, J, R, XL>(ga, X, xs_dyn, xoff, magic, acc);
+        finish<G, M, R, GLU>(acc, y, g * rows_per_group, rmax, p.N, lane, wave, team, kw, p.ksplit, red, buf);
     }
 }
 
 // ---------------------------------------------------------------- dispatch
 
-template <int FMT, int M, int G, int J, int R, bool XL>
+template <int FMT, int M, int G, int J, int R, bool XL, int MODE>
 static hipError_t launch_one(const GemvParams &p, dim3 grid, dim3 block, size_t shmem, hipStream_t stream)
 {
-    return launch_kernel(reinterpret_cast<const void *>(&gemv_kernel<FMT, M, G, J, R, XL>), grid, block, shmem,
-                         stream, p);
+    return launch_kernel(reinterpret_cast<const void *>(&gemv_kernel<FMT, M, G, J, R, XL, MODE>), grid, block,
+                         shmem, stream, p);
 }
 
-template <int FMT, int M, int G, int J, bool XL>
+template <int FMT, int M, int G, int J, bool XL, int MODE>
 static hipError_t launch_r(int R, const GemvParams &p, dim3 grid, dim3 block, size_t shmem, hipStream_t stream)
 {
-    if constexpr (gemv_fits(FMT, M, G, J, 1, XL))
-        if (R == 1) return launch_one<FMT, M, G, J, 1, XL>(p, grid, block, shmem, stream);
-    if constexpr (gemv_fits(FMT, M, G, J, 2, XL))
-        if (R == 2) return launch_one<FMT, M, G, J, 2, XL>(p, grid, block, shmem, stream);
-    if constexpr (gemv_fits(FMT, M, G, J, 4, XL))
-        if (R == 4) return launch_one<FMT, M, G, J, 4, XL>(p, grid, block, shmem, stream);
-    return hipErrorInvalidValue;
+    if constexpr (MODE == kModeGlu) {
+        if constexpr (gemv_fits(FMT, M, G, J, 2, XL, MODE))
+            if (R == 2) return launch_one<FMT, M, G, J, 2, XL, MODE>(p, grid, block, shmem, stream);
+        return hipErrorInvalidValue;
+    } else {
+        if constexpr (gemv_fits(FMT, M, G, J, 1, XL, MODE))
+            if (R == 1) return launch_one<FMT, M, G, J, 1, XL, MODE>(p, grid, block, shmem, stream);
+        if constexpr (gemv_fits(FMT, M, G, J, 2, XL, MODE))
+            if (R == 2) return launch_one<FMT, M, G, J, 2, XL, MODE>(p, grid, block, shmem, stream);
+        if constexpr (gemv_fits(FMT, M, G, J, 4, XL, MODE))
+            if (R == 4) return launch_one<FMT, M, G, J, 4, XL, MODE>(p, grid, block, shmem, stream);
+        return hipErrorInvalidValue;
+    }
 }
 
-template <int FMT, int M, int G, bool XL>
+template <int FMT, int M, int G, bool XL, int MODE>
 static hipError_t launch_j(int J, int R, const GemvParams &p, dim3 grid, dim3 block, size_t shmem,
                            hipStream_t stream)
 {
     switch (J) {
-    case 1: return launch_r<FMT, M, G, 1, XL>(R, p, grid, block, shmem, stream);
-    case 2: return launch_r<FMT, M, G, 2, XL>(R, p, grid, block, shmem, stream);
-    case 3: return launch_r<FMT, M, G, 3, XL>(R, p, grid, block, shmem, stream);
-    case 4: return launch_r<FMT, M, G, 4, XL>(R, p, grid, block, shmem, stream);
-    case 5: return launch_r<FMT, M, G, 5, XL>(R, p, grid, block, shmem, stream);
-    case 6: return launch_r<FMT, M, G, 6, XL>(R, p, grid, block, shmem, stream);
-    case 7: return launch_r<FMT, M, G, 7, XL>(R, p, grid, block, shmem, stream);
-    case 8: return launch_r<FMT, M, G, 8, XL>(R, p, grid, block, shmem, stream);
+    case 1: return launch_r<FMT, M, G, 1, XL, MODE>(R, p, grid, block, shmem, stream);
+    case 2: return launch_r<FMT, M, G, 2, XL, MODE>(R, p, grid, block, shmem, stream);
+    case 3: return launch_r<FMT, M, G, 3, XL, MODE>(R, p, grid, block, shmem, stream);
+    case 4: return launch_r<FMT, M, G, 4, XL, MODE>(R, p, grid, block, shmem, stream);
+    case 5: return launch_r<FMT, M, G, 5, XL, MODE>(R, p, grid, block, shmem, stream);
+    case 6: return launch_r<FMT, M, G, 6, XL, MODE>(R, p, grid, block, shmem, stream);
+    case 7: return launch_r<FMT, M, G, 7, XL, MODE>(R, p, grid, block, shmem, stream);
+    case 8: return launch_r<FMT, M, G, 8, XL, MODE>(R, p, grid, block, shmem, stream);
     }
     return hipErrorInvalidValue;
 }
 
-template <int FMT, int M, bool XL>
+template <int FMT, int M, bool XL, int MODE = kModeF16>
 static hipError_t launch_g(int G, int J, int R, const GemvParams &p, dim3 grid, dim3 block, size_t shmem,
                            hipStream_t stream)
 {
     // narrow row segments only for one token (the register cost of resident
     // activations grows with M)
     if constexpr (M == 1) {
-        if (G == 16) return launch_j<FMT, M, 16, XL>(J, R, p, grid, block, shmem, stream);
-        if (G == 32) return launch_j<FMT, M, 32, XL>(J, R, p, grid, block, shmem, stream);
+        if (G == 16) return launch_j<FMT, M, 16, XL, MODE>(J, R, p, grid, block, shmem, stream);
+        if (G == 32) return launch_j<FMT, M, 32, XL, MODE>(J, R, p, grid, block, shmem, stream);
     }
-    if (G == 64) return launch_j<FMT, M, 64, XL>(J, R, p, grid, block, shmem, stream);
+    if (G == 64) return launch_j<FMT, M, 64, XL, MODE>(J, R, p, grid, block, shmem, stream);
     return hipErrorInvalidValue;
 }
 
-size_t gemv_xl_lds_bytes(int K) { return (size_t)(K / 32 + 1) * 72; }
+size_t gemv_xl_lds_bytes(int K) { return (size_t)(K / 32 + 1) * 64; }
 
-hipError_t launch_gemv(int fmt, int M, int G, int J, int R, bool xl, const GemvParams &p, dim3 grid, dim3 block,
-                       hipStream_t stream)
+hipError_t launch_gemv(int fmt, int M, int G, int J, int R, bool xl, int mode, const GemvParams &p, dim3 grid,
+                       dim3 block, hipStream_t stream)
 {
+    if (mode != kModeF16) {
+        // fp32 activations (and SwiGLU): Q4_0, activations in registers
+        if (fmt != kQ4_0 || xl)
+            return hipErrorInvalidValue;
+#define QG_CASE_MODE(MODE)                                                                    \
+    switch (M) {                                                                              \
+    case 1: return launch_g<kQ4_0, 1, false, MODE>(G, J, R, p, grid, block, 0, stream);       \
+    case 2: return launch_g<kQ4_0, 2, false, MODE>(G, J, R, p, grid, block, 0, stream);       \
+    case 3: return launch_g<kQ4_0, 3, false, MODE>(G, J, R, p, grid, block, 0, stream);       \
+    case 4: return launch_g<kQ4_0, 4, false, MODE>(G, J, R, p, grid, block, 0, stream);       \
+    case 5: return launch_g<kQ4_0, 5, false, MODE>(G, J, R, p, grid, block, 0, stream);       \
+    case 6: return launch_g<kQ4_0, 6, false, MODE>(G, J, R, p, grid, block, 0, stream);       \
+    case 7: return launch_g<kQ4_0, 7, false, MODE>(G, J, R, p, grid, block, 0, stream);       \
+    case 8: return launch_g<kQ4_0, 8, false, MODE>(G, J, R, p, grid, block, 0, stream);       \
+    }
+        if (mode == kModeF32) {
+            QG_CASE_MODE(kModeF32)
+        } else if (mode == kModeGlu) {
+            QG_CASE_MODE(kModeGlu)
+        }
+#undef QG_CASE_MODE
+        return hipErrorInvalidValue;
+    }
     // XL: one token, activations and their bias terms staged in LDS (K/32
     // blocks of 64 + 8 bytes plus a zero block)
     if (xl) {

@@ -45,6 +45,7 @@ struct GemvParams {
     const uint8_t *W;          // packed matrix, or the expert pool for MoE
     const int32_t *idx;        // MoE: expert index per batch item; nullptr for GEMV
     const uint16_t *x;         // fp16 activations [items][M][K]
+    const float *xf;           // fp32 activations [M][K] (fp32-input modes)
     float *y;                  // fp32 outputs [items][M][N]
     int64_t matrix_stride;     // bytes between pool matrices (MoE)
     int64_t scale_offset;      // byte offset of the scale region in one matrix
@@ -69,15 +70,24 @@ inline hipError_t launch_kernel(const void *fn, dim3 grid, dim3 block, size_t sh
     return launch_raw(fn, grid, block, a, shmem, stream);
 }
 
+// Activation modes of the vector-ALU GEMV kernel: fp16 activations; fp32
+// activations rounded to binary16 as they are loaded (Q4_0); fp32
+// activations and a stacked gate + up table (2N rows) with the SwiGLU
+// epilogue y = silu(gate) * up (Q4_0, two row sets: a gate set and the up
+// set N rows further).
+constexpr int kModeF16 = 0;
+constexpr int kModeF32 = 1;
+constexpr int kModeGlu = 2;
+
 // Which vector-ALU GEMV instantiations exist (G lanes per row, J blocks per
 // lane, R row sets per group, xl: activations in LDS).  Register estimate: R *
 // J code words and scales in flight twice (ping-pong; 5 registers per Q4_0
 // block, 9 per Q8_0 block), without XL J * M resident activation blocks of 16
-// registers plus 2 bias terms, R * M sums and ~36 temporaries; keeping it
+// registers (counted as 18, 2 of slack), R * M sums and ~36 temporaries; keeping it
 // within 256 (and R * J <= 8 / 4, J <= 7, 8 with XL, J * M <= 8) leaves every
 // instantiation free of spills.  Rows narrower than a wave (G < 64) and XL are
 // for one token; XL uses G = 64.
-constexpr bool gemv_fits(int fmt, int M, int G, int J, int R, bool xl)
+constexpr bool gemv_fits(int fmt, int M, int G, int J, int R, bool xl, int mode = 0)
 {
     if (G != 16 && G != 32 && G != 64)
         return false;
@@ -87,15 +97,18 @@ constexpr bool gemv_fits(int fmt, int M, int G, int J, int R, bool xl)
         return false;
     if (R * J > (fmt == kQ4_0 ? 8 : 4) || J > (xl ? 8 : 7) || (!xl && J * M > 8))
         return false;
-    const int regs = 2 * R * J * (fmt == kQ4_0 ? 5 : 9) + (xl ? 0 : J * M * 18) + R * M + 36;
+    // fp32 activations (mode != 0) hold 32 raw words per block until they
+    // are converted, 16 more than fp16 ones
+    const int regs = 2 * R * J * (fmt == kQ4_0 ? 5 : 9) + (xl ? 0 : J * M * (mode ? 34 : 18)) + R * M + 36;
     return regs <= 256 && R * M * (64 / G) <= kMaxRM;
 }
 
 // LDS bytes of the XL activation copy for a row of K weights.
 size_t gemv_xl_lds_bytes(int K);
 
-hipError_t launch_gemv(int fmt, int M, int G, int J, int R, bool xl, const GemvParams &p, dim3 grid, dim3 block,
-                       hipStream_t stream);
+
+hipError_t launch_gemv(int fmt, int M, int G, int J, int R, bool xl, int mode, const GemvParams &p, dim3 grid,
+                       dim3 block, hipStream_t stream);
 
 // Few-token GEMV on the matrix cores (qgemv_mfma.hip): `waves` waves split K;
 // `wgs` persistent workgroups (0: as many as fit, at most 2 per CU of `cus`).

@@ -138,6 +138,39 @@ def test_stress_activations(fmt, kind):
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FNAME[f])
+@pytest.mark.parametrize("K", [32, 96, 640, 4096])
+def test_outliers_on_zero_weights(fmt, K):
+    """Activations near the binary16 limit (+-60000, -30000) on columns whose
+    weights are exactly zero (code 8 / 0), the rest ~N(0, 1): the exact
+    result is the small remainder, and the bound is set by it alone.  Short
+    rows make that remainder a few units; both engines."""
+    q = qg()
+    N, M = 64, 4
+    w = weights(N, K, seed=K + 3)
+    g = np.random.default_rng([K, 61])
+    cols = g.choice(K, 3, replace=False)
+    w[:, cols] = 0.0
+    x = acts(M, K, seed=K + 3)
+    x[:, cols[0]] = 60000.0
+    x[1::2, cols[0]] = -60000.0
+    x[:, cols[1]] = -30000.0
+    x[:, cols[2]] = 65504.0
+    pb, po = pack_both(fmt, w)
+    Wd, xd = to_dev(pb), to_dev(x)
+    y_ref, s = oracle.get().gemv(fmt, po, N, K, x)
+    try:
+        for engine in (-1, 0, 1):
+            q.qg_set_gemv_shape(0, 0, 0, 0, 0, -1, engine, 0)
+            for m in (1, 2, M):
+                if engine == 1 and m < 2:
+                    continue
+                y = _gemv(fmt, Wd, xd[:m], N, K)
+                assert_within(y, y_ref[:m], s[:m], f"{FNAME[fmt]} outliers K={K} M={m} engine={engine}")
+    finally:
+        q.qg_set_gemv_shape(0, 0, 0, 0, 0, -1, -1, 0)
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FNAME[f])
 def test_zero_and_degenerate_blocks(fmt):
     """All-zero blocks (scale 0), subnormal scales, a single non-zero weight."""
     N, K = 40, 2560
