@@ -272,6 +272,50 @@ def suite(qg, torch, reps: int):
             pool_copies=copies)
         del buf
 
+    # fp32 activations rounded inside the kernel, beside the same call on
+    # activations converted by a separate step (torch's .half()) first
+    for (N, K, M) in si.F32IN_CASES:
+        buf, nb, copies = _copies(torch, qg.qquantize_q4_0(si.weights(N, K, seed=0)))
+        x = torch.from_numpy(si.activations32(M, K, seed=0)).to("cuda")
+        y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        fns = [lambda c=c: qg.qgemv_q4_0_f32in(buf[c * nb:(c + 1) * nb], x, N, K, y) for c in range(copies)]
+        med, mean = _time_calls(qg, torch, fns, reps)
+        wmed, _ = _time_wall(torch, fns, reps)
+        two = [lambda c=c: qg.qgemv_q4_0(buf[c * nb:(c + 1) * nb], x.half(), N, K, y) for c in range(copies)]
+        smed, _ = _time_wall(torch, two, reps)
+        b = N * K // 32 * 18 + 4 * M * K + 4 * M * N
+        rec(kind="f32in", fmt="q4_0", N=N, K=K, M=M, us_median=round(med, 3), us_mean=round(mean, 3),
+            GBps=round(b / med / 1e3, 1), pct_of_8TBps=round(b / med / 1e3 / 80, 2), algorithmic_bytes=b,
+            wall_us_median=round(wmed, 3), separate_conversion_wall_us_median=round(smed, 3), copies=copies)
+        del buf
+
+    # gate + up stacked in one 2N-row table with SwiGLU in the epilogue, beside
+    # the unfused steps (conversion, one GEMV over the stacked table, silu * up)
+    for (N, K) in si.SWIGLU_SHAPES:
+        w = np.concatenate([si.weights(N, K, seed=0), si.weights(N, K, seed=1)])
+        buf, nb, copies = _copies(torch, qg.qquantize_q4_0(w))
+        del w
+        for M in si.SWIGLU_TOKENS:
+            x = torch.from_numpy(si.activations32(M, K, seed=0)).to("cuda")
+            y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+            gu = torch.empty((M, 2 * N), dtype=torch.float32, device="cuda")
+            fns = [lambda c=c: qg.qgemv_q4_0_swiglu_f32in(buf[c * nb:(c + 1) * nb], x, N, K, y)
+                   for c in range(copies)]
+            med, mean = _time_calls(qg, torch, fns, reps)
+            wmed, _ = _time_wall(torch, fns, reps)
+
+            def unfused(c):
+                qg.qgemv_q4_0(buf[c * nb:(c + 1) * nb], x.half(), 2 * N, K, gu)
+                torch.mul(torch.nn.functional.silu(gu[:, :N]), gu[:, N:], out=y)
+            ufn = [lambda c=c: unfused(c) for c in range(copies)]
+            umed, _ = _time_wall(torch, ufn, reps)
+            b = 2 * N * K // 32 * 18 + 4 * M * K + 4 * M * N
+            rec(kind="swiglu", fmt="q4_0", N=N, K=K, M=M, us_median=round(med, 3), us_mean=round(mean, 3),
+                GBps=round(b / med / 1e3, 1), pct_of_8TBps=round(b / med / 1e3 / 80, 2), algorithmic_bytes=b,
+                wall_us_median=round(wmed, 3), unfused_wall_us_median=round(umed, 3), copies=copies)
+        del buf
+        torch.cuda.empty_cache()
+
     # prefill, and the dense fp16 GEMM on pre-dequantized weights beside it
     for (N, K) in si.PREFILL_SHAPES:
         w = si.weights(N, K, seed=0)

@@ -115,8 +115,9 @@ qg_status qgemv_q8_0(const void *Wp, const uint16_t *x, float *y, int M, int64_t
  *   y[m][n] = sum_k w[n][k] * fp16(x[m][k])
  * with the conventions of qgemv_q4_0.  x: fp32 [M][K] row-major (device,
  * 16-byte aligned); Wp, y and the other limits as for qgemv_q4_0, with
- * K <= 16384 * min(floor(4 / M), 4).  The conversion is done once per
- * activation block by each team that reads it, not in a separate pass.
+ * K <= 16384 * min(floor(4 / M), 4).  The conversion is done inside the
+ * GEMV launch, not in a separate pass: once per workgroup into LDS on large
+ * tables, by each team for the blocks it reads otherwise.
  * [volta-kernel-bakeoff, "Results", the like-for-like bullets: fp32
  *  activations in, the conversion counted, inside the kernel at 1 token and
  *  at up to 4 tokens on expert-sized tables] */
@@ -184,13 +185,13 @@ qg_status qg_device_cus(int device, int *cus);
 /* Tuning knob for launch-shape sweeps of qgemv_* / qmoe_gemv_q4_0: fixes J
  * (blocks per lane per row, J * M <= 8), R (row sets per group: 1, 2 or 4),
  * ksplit (waves sharing a row along K), teams per workgroup, the total
- * number of teams, xl (activations of a one-token call staged in LDS: 1,
- * kept in registers: 0), engine (vector-ALU kernel: 0; matrix-core kernel
- * for 2..8 tokens and rows of at most 256 blocks: 1, where ksplit is its
- * number of waves along K and teams its number of persistent workgroups)
- * and lanes_per_row (lanes of a wave that share one
- * row in the vector-ALU kernel: 16, 32 or 64; below 64 one token only) for
- * later calls from the calling thread.  A zero (-1 for xl and engine) keeps
+ * number of teams, xl (activations of 1-4 tokens staged once per workgroup
+ * in LDS, whole rows per wave: 1; kept in each lane's registers: 0), engine
+ * (vector-ALU kernel: 0; matrix-core kernel for 2..8 tokens and rows of at
+ * most 256 blocks: 1, where ksplit is its number of waves along K and teams
+ * its number of persistent workgroups) and lanes_per_row (lanes of a wave
+ * that share one row in the vector-ALU kernel: 16, 32 or 64; below 64 one
+ * token only) for later calls from the calling thread.  A zero (-1 for xl and engine) keeps
  * the built-in per-shape choice for that field.  An impossible combination
  * makes the later calls return QG_ERR_SHAPE. */
 void qg_set_gemv_shape(int J, int R, int ksplit, int teams_per_wg, int64_t teams, int xl, int engine,

@@ -77,11 +77,24 @@ bool choose_shape(int fmt, int M, int64_t N, int64_t K, int items, int cus, int 
 {
     const bool glu = mode == kModeGlu;
     const int64_t KB = K / 32;
-    // Activations staged in LDS (one token) stay a tuning option: one block
-    // per lane with K split over several waves measured faster on MI355X.
+    // Activations staged in LDS once per workgroup of 8 teams (XL, whole rows
+    // per wave): the default for fp32 activations on tables of at least four
+    // groups per CU (one-token GEMV: beyond 8192 rows), where every team's own
+    // register copy would read 4 M K bytes (up to ~10x the weight bytes at
+    // four tokens).  Launch sweeps on MI355X: one token 14336 x 4096 8.1
+    // against 10.6 us, four tokens 6144 x 2048 7.3 against 10.4; SwiGLU
+    // 14336 x 4096 13.9 against 16.5 at one token, 25.5 against 32.5 at four.
+    // With fp16 activations (half the bytes), on smaller tables and at one
+    // token up to 8192 rows (4096 x 4096: 5.0 against 4.6 us with 16 lanes per
+    // row) the register copy stays faster.
     bool xl = false;
+    const int xl_r = glu ? 2 : (M == 1 ? 1 : 2);
     if (o_xl >= 0)
         xl = (o_xl == 1);
+    else if (mode != kModeF16 && items == 1)
+        xl = (KB + 63) / 64 * xl_r <= 8 && gemv_xl_lds_bytes(static_cast<int>(K), M) <= 65536 &&
+             N / (glu ? 1 : xl_r) >= 4LL * cus && (M > 1 || glu || N > 8192);
+    const bool xl_auto = xl && o_xl < 0;
     // Lanes per row: one token with rows of 65..128 blocks spreads a row over
     // 16 (up to 4096 rows) or 32 lanes (up to 64K rows; Q4_0 GEMV: up to 8192),
     // so a wave reduces several rows at once; shorter rows take one wave each.
@@ -136,6 +149,8 @@ bool choose_shape(int fmt, int M, int64_t N, int64_t K, int items, int cus, int 
     if (M >= 2 && J == 1 && ksplit > 1 && !glu &&
         (fmt == kQ4_0 || N <= 4LL * cus * std::max(2, 8 / ksplit)))
         R = 4;
+    if (xl_auto)
+        R = xl_r;   // one row set per group at one token, two at 2-4 tokens
     while (R * J > rj && R > (glu ? 2 : 1))
         R /= 2;
     // stay within the instantiated kernels (register budget): fewer row sets,
@@ -152,7 +167,7 @@ bool choose_shape(int fmt, int M, int64_t N, int64_t K, int items, int cus, int 
     }
     if (ksplit > kMaxWavesPerWg)
         return false;
-    int teams_per_wg = 1;
+    int teams_per_wg = xl_auto ? 8 : 1;
     if (o_J) {
         J = o_J;
         ksplit = static_cast<int>((KB + static_cast<int64_t>(G) * J - 1) / (static_cast<int64_t>(G) * J));
@@ -168,7 +183,7 @@ bool choose_shape(int fmt, int M, int64_t N, int64_t K, int items, int cus, int 
         R = o_R;
     if (o_teams_per_wg)
         teams_per_wg = o_teams_per_wg;
-    if (xl && (ksplit > 1 || M != 1 || gemv_xl_lds_bytes(static_cast<int>(K)) > 65536))
+    if (xl && (ksplit > 1 || M > 4 || gemv_xl_lds_bytes(static_cast<int>(K), M) > 65536))
         return false;
     if (!gemv_fits(fmt, M, G, J, R, xl, mode))
         return false;
@@ -187,13 +202,15 @@ bool choose_shape(int fmt, int M, int64_t N, int64_t K, int items, int cus, int 
         per_cu = 4;   // long whole rows per wave: 4096 x 14336 7.95 us at 4, 8.9 at 8
     if (N > 65536 && M == 1)
         per_cu = 64;
+    if (xl_auto)
+        per_cu = (M == 1 && !glu) || (glu && KB <= 64) ? 16 : 8;
     int64_t teams = std::max<int64_t>(1, static_cast<int64_t>(cus) * per_cu / std::max(1, items));
     // Several tokens, two blocks per lane, whole rows per wave: at least two
     // groups per team, so the prefetch of the next group overlaps the current
     // one (4096 x 4096 at two tokens: 1024 teams 4.6 us, 2048 teams 5.1;
     // with one block per lane, 6144 x 2048 prefers 2048 teams, 4.1 against
     // 4.6 us).
-    if (M >= 2 && J >= 2 && ksplit == 1 && items == 1)
+    if (M >= 2 && J >= 2 && ksplit == 1 && items == 1 && !xl)
         teams = std::min(teams, std::max<int64_t>(1, (ngroups + 1) / 2));
     if (o_teams)
         teams = o_teams;

@@ -25,8 +25,9 @@
 //   * Each lane keeps the activations of its blocks in registers for all M
 //     tokens, loaded once per team and reused for every row the team visits
 //     (one activation load serves many rows [volta-kernel-bakeoff, "Results",
-//     the few-tokens bullet]), or, with XL (one token, long rows), reads them
-//     from the workgroup's LDS copy.
+//     the few-tokens bullet]), or, with XL (up to 4 tokens, whole rows per
+//     wave), reads them from the workgroup's LDS copy, staged once for all
+//     the workgroup's teams.
 //   * Two register sets in ping-pong: the next group's loads are in flight
 //     while the current group is unpacked and multiplied.
 //   * Unpack: a nibble n OR-ed into the binary16 pattern 0x6400 is the half
@@ -281,78 +282,107 @@ __device__ __forceinline__ void load_group(Group<FMT, J, R> &g, const uint8_t *_
     }
 }
 
+// One block's unpacked pairs (chain 0 and chain 1, see unpack_q4 / unpack_q8).
+template <int FMT>
+__device__ __forceinline__ void unpack_block(const Codes<FMT> &c, uint32_t magic, h2_t (&v0)[8], h2_t (&v1)[8])
+{
+    if constexpr (FMT == kQ4_0) {
+        unpack_q4(c.c, magic, v0, v1);
+    } else {
+        h2_t v[16];
+        unpack_q8(c.c0, c.c1, magic, v);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            v0[t] = v[t];
+            v1[t] = v[8 + t];
+        }
+    }
+}
+
+// sum (q - 8) x (Q4_0) or sum q x (Q8_0) of one block against one token's 16
+// activation pairs.
+template <int FMT>
+__device__ __forceinline__ float block_dot(const h2_t (&v0)[8], const h2_t (&v1)[8], const uint32_t (&xw)[16])
+{
+    if constexpr (FMT == kQ4_0) {
+        float c0 = dot2_first(v0[0], as_h2(xw[0]));
+        float c1 = dot2_first(v1[0], as_h2(xw[1]));
+        c0 = dot2(v0[1], as_h2(xw[2]), c0);
+        c1 = dot2(v1[1], as_h2(xw[3]), c1);
+#pragma unroll
+        for (int t = 1; t < 4; ++t) {
+            c0 = dot2(v0[2 * t], as_h2(xw[4 * t + 0]), c0);
+            c1 = dot2(v1[2 * t], as_h2(xw[4 * t + 1]), c1);
+            c0 = dot2(v0[2 * t + 1], as_h2(xw[4 * t + 2]), c0);
+            c1 = dot2(v1[2 * t + 1], as_h2(xw[4 * t + 3]), c1);
+        }
+        return __builtin_fmaf(c1, 0.0625f, c0);
+    } else {
+        float c0 = dot2_first(v0[0], as_h2(xw[0]));
+        float c1 = dot2_first(v1[0], as_h2(xw[8]));
+#pragma unroll
+        for (int t = 1; t < 8; ++t) {
+            c0 = dot2(v0[t], as_h2(xw[t]), c0);
+            c1 = dot2(v1[t], as_h2(xw[8 + t]), c1);
+        }
+        return c0 + c1;
+    }
+}
+
 // Activations come either from registers (X, loaded once per team) or, with
-// XL, from the workgroup's LDS copy (one token; xs holds every block of x in
-// pair order plus one zero block that padding lanes read).
+// XL, from the workgroup's LDS copy (xs holds, token after token, every block
+// of x in pair order plus one zero block that padding lanes read; xstride =
+// one token's share in uint4).  With XL a block's activations are read once
+// per group and used by every row set before the next block's are read (read
+// per row set, the compiler keeps them all live across row sets instead).
 template <int FMT, int M, int J, int R, bool XL>
 __device__ __forceinline__ void compute_group(const Group<FMT, J, R> &g,
                                               const uint32_t (&X)[XL ? 1 : M][XL ? 1 : J][16],
-                                              const uint4 *xs, const uint32_t (&xoff)[J], uint32_t magic,
-                                              float (&acc)[R][M])
+                                              const uint4 *xs, uint32_t xstride, const uint32_t (&xoff)[J],
+                                              uint32_t magic, float (&acc)[R][M])
 {
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
+    for (int i = 0; i < R; ++i)
 #pragma unroll
         for (int m = 0; m < M; ++m)
             acc[i][m] = 0.0f;
+    if constexpr (XL) {
 #pragma unroll
         for (int j = 0; j < J; ++j) {
-            const float d = (float)__builtin_bit_cast(_Float16, g.scale[i][j]);
-            h2_t v0[8], v1[8];   // the pairs of chain 0 and chain 1
-            if constexpr (FMT == kQ4_0) {
-                unpack_q4(g.code[i][j].c, magic, v0, v1);
-            } else {
-                h2_t v[16];
-                unpack_q8(g.code[i][j].c0, g.code[i][j].c1, magic, v);
+            uint32_t xw[M][16];
 #pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    v0[t] = v[t];
-                    v1[t] = v[8 + t];
+            for (int m = 0; m < M; ++m) {
+                const uint4 *q = xs + m * xstride + xoff[j] * 4;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const uint4 t = q[u];
+                    xw[m][4 * u + 0] = t.x;
+                    xw[m][4 * u + 1] = t.y;
+                    xw[m][4 * u + 2] = t.z;
+                    xw[m][4 * u + 3] = t.w;
                 }
             }
 #pragma unroll
-            for (int m = 0; m < M; ++m) {
-                uint32_t xw[16];
-                if constexpr (XL) {
-                    const uint4 *q = xs + xoff[j] * 4;
+            for (int i = 0; i < R; ++i) {
+                const float d = (float)__builtin_bit_cast(_Float16, g.scale[i][j]);
+                h2_t v0[8], v1[8];
+                unpack_block<FMT>(g.code[i][j], magic, v0, v1);
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const uint4 t = q[u];
-                        xw[4 * u + 0] = t.x;
-                        xw[4 * u + 1] = t.y;
-                        xw[4 * u + 2] = t.z;
-                        xw[4 * u + 3] = t.w;
-                    }
-                } else {
+                for (int m = 0; m < M; ++m)
+                    acc[i][m] = __builtin_fmaf(d, block_dot<FMT>(v0, v1, xw[m]), acc[i][m]);
+            }
+        }
+    } else {
 #pragma unroll
-                    for (int t = 0; t < 16; ++t)
-                        xw[t] = X[m][j][t];
-                }
-                float blk;
-                if constexpr (FMT == kQ4_0) {
-                    float c0 = dot2_first(v0[0], as_h2(xw[0]));
-                    float c1 = dot2_first(v1[0], as_h2(xw[1]));
-                    c0 = dot2(v0[1], as_h2(xw[2]), c0);
-                    c1 = dot2(v1[1], as_h2(xw[3]), c1);
+        for (int i = 0; i < R; ++i) {
 #pragma unroll
-                    for (int t = 1; t < 4; ++t) {
-                        c0 = dot2(v0[2 * t], as_h2(xw[4 * t + 0]), c0);
-                        c1 = dot2(v1[2 * t], as_h2(xw[4 * t + 1]), c1);
-                        c0 = dot2(v0[2 * t + 1], as_h2(xw[4 * t + 2]), c0);
-                        c1 = dot2(v1[2 * t + 1], as_h2(xw[4 * t + 3]), c1);
-                    }
-                    blk = __builtin_fmaf(c1, 0.0625f, c0);
-                } else {
-                    float c0 = dot2_first(v0[0], as_h2(xw[0]));
-                    float c1 = dot2_first(v1[0], as_h2(xw[8]));
+            for (int j = 0; j < J; ++j) {
+                const float d = (float)__builtin_bit_cast(_Float16, g.scale[i][j]);
+                h2_t v0[8], v1[8];
+                unpack_block<FMT>(g.code[i][j], magic, v0, v1);
 #pragma unroll
-                    for (int t = 1; t < 8; ++t) {
-                        c0 = dot2(v0[t], as_h2(xw[t]), c0);
-                        c1 = dot2(v1[t], as_h2(xw[8 + t]), c1);
-                    }
-                    blk = c0 + c1;
-                }
-                acc[i][m] = __builtin_fmaf(d, blk, acc[i][m]);
+                for (int m = 0; m < M; ++m)
+                    acc[i][m] = __builtin_fmaf(d, block_dot<FMT>(v0, v1, X[m][j]), acc[i][m]);
             }
         }
     }
@@ -490,8 +520,8 @@ __device__ __forceinline__ void finish(const float (&acc)[R][M], float *__restri
 template <int FMT, int M, int G, int J, int R, bool XL, int MODE>
 __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
 {
-    static_assert(!XL || M == 1, "LDS-staged activations are for one token");
-    static_assert(MODE == kModeF16 || (!XL && FMT == kQ4_0), "fp32 activations: Q4_0, registers");
+    static_assert(!XL || M <= 4, "LDS-staged activations: up to 4 tokens");
+    static_assert(MODE == kModeF16 || FMT == kQ4_0, "fp32 activations: Q4_0");
     constexpr bool GLU = MODE == kModeGlu;
     static_assert(!GLU || R == 2, "SwiGLU: one gate and one up row set per group");
     constexpr int P = 64 / G;
@@ -509,7 +539,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
         W += (int64_t)p.idx[item] * p.matrix_stride;
     const uint8_t *__restrict__ S = W + p.scale_offset;
     const uint16_t *__restrict__ x = p.x + (int64_t)item * M * p.K;
-    const float *__restrict__ xf = p.xf;
+    const float *__restrict__ xf = p.xf + (int64_t)item * M * p.K;
     float *__restrict__ y = p.y + (int64_t)item * M * p.N;
 
     const int KB = p.K >> 5;
@@ -564,12 +594,21 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
     // also cover these weights
     load_group<FMT, G, J, R, GLU>(ga, W, S, g * rows_per_group, rmax, KB, nblocks, coff, soff, p.N);
     __builtin_amdgcn_sched_barrier(0);
+    const uint32_t xstride = (uint32_t)(KB + 1) * 4u;
     if constexpr (XL) {
-        // the workgroup stages x once, in pair order, plus a zero block
-        for (int b = threadIdx.x; b <= KB; b += blockDim.x) {
+        // the workgroup stages x once, token after token, in pair order, each
+        // token followed by a zero block (fp32 input: rounded here)
+        for (int i = threadIdx.x; i < M * (KB + 1); i += blockDim.x) {
+            const int m = i / (KB + 1);
+            const int b = i - m * (KB + 1);
             uint32_t w16[16];
             if (b < KB) {
-                load_x_block<FMT>(x + (int64_t)b * 32, w16);
+                uint4 r[4];
+                if constexpr (MODE == kModeF16)
+                    load_x_raw(x + (int64_t)m * p.K + (int64_t)b * 32, r);
+                else
+                    load_x_raw_f32(xf + (int64_t)m * p.K + (int64_t)b * 32, r);
+                pair_x_block<FMT>(r, w16);
             } else {
 #pragma unroll
                 for (int t = 0; t < 16; ++t)
@@ -577,7 +616,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u)
-                xs_dyn[b * 4 + u] = make_uint4(w16[4 * u], w16[4 * u + 1], w16[4 * u + 2], w16[4 * u + 3]);
+                xs_dyn[i * 4 + u] = make_uint4(w16[4 * u], w16[4 * u + 1], w16[4 * u + 2], w16[4 * u + 3]);
         }
         __syncthreads();
     } else {
@@ -610,12 +649,12 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
         float acc[R][M];
         load_group<FMT, G, J, R, GLU>(gb, W, S, (g + teams_total) * rows_per_group, rmax, KB, nblocks, coff, soff, p.N);
         __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the compute
-        compute_group<FMT, M, J, R, XL>(ga, X, xs_dyn, xoff, magic, acc);
+        compute_group<FMT, M, J, R, XL>(ga, X, xs_dyn, xstride, xoff, magic, acc);
         finish<G, M, R, GLU>(acc, y, g * rows_per_group, rmax, p.N, lane, wave, team, kw, p.ksplit, red, buf);
         g += teams_total;
         load_group<FMT, G, J, R, GLU>(ga, W, S, (g + teams_total) * rows_per_group, rmax, KB, nblocks, coff, soff, p.N);
         __builtin_amdgcn_sched_barrier(0);
-        compute_group<FMT, M, J, R, XL>(gb, X, xs_dyn, xoff, magic, acc);
+        compute_group<FMT, M, J, R, XL>(gb, X, xs_dyn, xstride, xoff, magic, acc);
         finish<G, M, R, GLU>(acc, y, g * rows_per_group, rmax, p.N, lane, wave, team, kw, p.ksplit, red, buf);
         g += teams_total;
     }
@@ -623,14 +662,14 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
         float acc[R][M];
         load_group<FMT, G, J, R, GLU>(gb, W, S, (g + teams_total) * rows_per_group, rmax, KB, nblocks, coff, soff, p.N);
         __builtin_amdgcn_sched_barrier(0);
-        compute_group<FMT, M, J, R, XL>(ga, X, xs_dyn, xoff, magic, acc);
+        compute_group<FMT, M, J, R, XL>(ga, X, xs_dyn, xstride, xoff, magic, acc);
         finish<G, M, R, GLU>(acc, y, g * rows_per_group, rmax, p.N, lane, wave, team, kw, p.ksplit, red, buf);
         g += teams_total;
-        compute_group<FMT, M, J, R, XL>(gb, X, xs_dyn, xoff, magic, acc);
+        compute_group<FMT, M, J, R, XL>(gb, X, xs_dyn, xstride, xoff, magic, acc);
         finish<G, M, R, GLU>(acc, y, g * rows_per_group, rmax, p.N, lane, wave, team, kw, p.ksplit, red, buf);
     } else if (n - k == 1) {
         float acc[R][M];
-        compute_group<FMT, M, J, R, XL>(ga, X, xs_dyn, xoff, magic, acc);
+        compute_group<FMT, M, J, R, XL>(ga, X, xs_dyn, xstride, xoff, magic, acc);
         finish<G, M, R, GLU>(acc, y, g * rows_per_group, rmax, p.N, lane, wave, team, kw, p.ksplit, red, buf);
     }
 }
@@ -693,58 +732,58 @@ static hipError_t launch_g(int G, int J, int R, const GemvParams &p, dim3 grid, 
     return hipErrorInvalidValue;
 }
 
-size_t gemv_xl_lds_bytes(int K) { return (size_t)(K / 32 + 1) * 64; }
+size_t gemv_xl_lds_bytes(int K, int M) { return (size_t)M * (K / 32 + 1) * 64; }
 
 hipError_t launch_gemv(int fmt, int M, int G, int J, int R, bool xl, int mode, const GemvParams &p, dim3 grid,
                        dim3 block, hipStream_t stream)
 {
-    if (mode != kModeF16) {
-        // fp32 activations (and SwiGLU): Q4_0, activations in registers
-        if (fmt != kQ4_0 || xl)
+    // fp32 activations (and SwiGLU): Q4_0 only
+    if (mode != kModeF16 && fmt != kQ4_0)
+        return hipErrorInvalidValue;
+    // XL: up to 4 tokens with whole rows per wave, activations staged in LDS
+    // (per token K/32 blocks of 64 bytes plus a zero block)
+    if (xl) {
+        if (M > 4 || p.ksplit != 1)
             return hipErrorInvalidValue;
-#define QG_CASE_MODE(MODE)                                                                    \
-    switch (M) {                                                                              \
-    case 1: return launch_g<kQ4_0, 1, false, MODE>(G, J, R, p, grid, block, 0, stream);       \
-    case 2: return launch_g<kQ4_0, 2, false, MODE>(G, J, R, p, grid, block, 0, stream);       \
-    case 3: return launch_g<kQ4_0, 3, false, MODE>(G, J, R, p, grid, block, 0, stream);       \
-    case 4: return launch_g<kQ4_0, 4, false, MODE>(G, J, R, p, grid, block, 0, stream);       \
-    case 5: return launch_g<kQ4_0, 5, false, MODE>(G, J, R, p, grid, block, 0, stream);       \
-    case 6: return launch_g<kQ4_0, 6, false, MODE>(G, J, R, p, grid, block, 0, stream);       \
-    case 7: return launch_g<kQ4_0, 7, false, MODE>(G, J, R, p, grid, block, 0, stream);       \
-    case 8: return launch_g<kQ4_0, 8, false, MODE>(G, J, R, p, grid, block, 0, stream);       \
+        const size_t shmem = gemv_xl_lds_bytes(p.K, M);
+#define QG_CASE_XL(FMT, MODE)                                                                  \
+    switch (M) {                                                                               \
+    case 1: return launch_g<FMT, 1, true, MODE>(G, J, R, p, grid, block, shmem, stream);       \
+    case 2: return launch_g<FMT, 2, true, MODE>(G, J, R, p, grid, block, shmem, stream);       \
+    case 3: return launch_g<FMT, 3, true, MODE>(G, J, R, p, grid, block, shmem, stream);       \
+    case 4: return launch_g<FMT, 4, true, MODE>(G, J, R, p, grid, block, shmem, stream);       \
     }
         if (mode == kModeF32) {
-            QG_CASE_MODE(kModeF32)
+            QG_CASE_XL(kQ4_0, kModeF32)
         } else if (mode == kModeGlu) {
-            QG_CASE_MODE(kModeGlu)
+            QG_CASE_XL(kQ4_0, kModeGlu)
+        } else if (fmt == kQ4_0) {
+            QG_CASE_XL(kQ4_0, kModeF16)
+        } else {
+            QG_CASE_XL(kQ8_0, kModeF16)
         }
-#undef QG_CASE_MODE
+#undef QG_CASE_XL
         return hipErrorInvalidValue;
     }
-    // XL: one token, activations and their bias terms staged in LDS (K/32
-    // blocks of 64 + 8 bytes plus a zero block)
-    if (xl) {
-        if (M != 1 || p.ksplit != 1)
-            return hipErrorInvalidValue;
-        const size_t shmem = gemv_xl_lds_bytes(p.K);
-        return fmt == kQ4_0 ? launch_g<kQ4_0, 1, true>(G, J, R, p, grid, block, shmem, stream)
-                            : launch_g<kQ8_0, 1, true>(G, J, R, p, grid, block, shmem, stream);
+#define QG_CASE_M(FMT, MODE)                                                                  \
+    switch (M) {                                                                              \
+    case 1: return launch_g<FMT, 1, false, MODE>(G, J, R, p, grid, block, 0, stream);         \
+    case 2: return launch_g<FMT, 2, false, MODE>(G, J, R, p, grid, block, 0, stream);         \
+    case 3: return launch_g<FMT, 3, false, MODE>(G, J, R, p, grid, block, 0, stream);         \
+    case 4: return launch_g<FMT, 4, false, MODE>(G, J, R, p, grid, block, 0, stream);         \
+    case 5: return launch_g<FMT, 5, false, MODE>(G, J, R, p, grid, block, 0, stream);         \
+    case 6: return launch_g<FMT, 6, false, MODE>(G, J, R, p, grid, block, 0, stream);         \
+    case 7: return launch_g<FMT, 7, false, MODE>(G, J, R, p, grid, block, 0, stream);         \
+    case 8: return launch_g<FMT, 8, false, MODE>(G, J, R, p, grid, block, 0, stream);         \
     }
-#define QG_CASE_M(FMT)                                                                   \
-    switch (M) {                                                                         \
-    case 1: return launch_g<FMT, 1, false>(G, J, R, p, grid, block, 0, stream);          \
-    case 2: return launch_g<FMT, 2, false>(G, J, R, p, grid, block, 0, stream);          \
-    case 3: return launch_g<FMT, 3, false>(G, J, R, p, grid, block, 0, stream);          \
-    case 4: return launch_g<FMT, 4, false>(G, J, R, p, grid, block, 0, stream);          \
-    case 5: return launch_g<FMT, 5, false>(G, J, R, p, grid, block, 0, stream);          \
-    case 6: return launch_g<FMT, 6, false>(G, J, R, p, grid, block, 0, stream);          \
-    case 7: return launch_g<FMT, 7, false>(G, J, R, p, grid, block, 0, stream);          \
-    case 8: return launch_g<FMT, 8, false>(G, J, R, p, grid, block, 0, stream);          \
-    }
-    if (fmt == kQ4_0) {
-        QG_CASE_M(kQ4_0)
+    if (mode == kModeF32) {
+        QG_CASE_M(kQ4_0, kModeF32)
+    } else if (mode == kModeGlu) {
+        QG_CASE_M(kQ4_0, kModeGlu)
+    } else if (fmt == kQ4_0) {
+        QG_CASE_M(kQ4_0, kModeF16)
     } else {
-        QG_CASE_M(kQ8_0)
+        QG_CASE_M(kQ8_0, kModeF16)
     }
 #undef QG_CASE_M
     return hipErrorInvalidValue;

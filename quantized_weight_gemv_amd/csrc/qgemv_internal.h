@@ -85,15 +85,15 @@ constexpr int kModeGlu = 2;
 // block, 9 per Q8_0 block), without XL J * M resident activation blocks of 16
 // registers (counted as 18, 2 of slack), R * M sums and ~36 temporaries; keeping it
 // within 256 (and R * J <= 8 / 4, J <= 7, 8 with XL, J * M <= 8) leaves every
-// instantiation free of spills.  Rows narrower than a wave (G < 64) and XL are
-// for one token; XL uses G = 64.
+// instantiation free of spills.  Rows narrower than a wave (G < 64) are for
+// one token; XL uses G = 64 and up to 4 tokens.
 constexpr bool gemv_fits(int fmt, int M, int G, int J, int R, bool xl, int mode = 0)
 {
     if (G != 16 && G != 32 && G != 64)
         return false;
-    if (M != 1 && (G != 64 || xl))
+    if (M != 1 && G != 64)
         return false;
-    if (xl && G != 64)
+    if (xl && (G != 64 || M > 4))
         return false;
     if (R * J > (fmt == kQ4_0 ? 8 : 4) || J > (xl ? 8 : 7) || (!xl && J * M > 8))
         return false;
@@ -103,8 +103,8 @@ constexpr bool gemv_fits(int fmt, int M, int G, int J, int R, bool xl, int mode 
     return regs <= 256 && R * M * (64 / G) <= kMaxRM;
 }
 
-// LDS bytes of the XL activation copy for a row of K weights.
-size_t gemv_xl_lds_bytes(int K);
+// LDS bytes of the XL activation copy of M tokens for rows of K weights.
+size_t gemv_xl_lds_bytes(int K, int M);
 
 
 hipError_t launch_gemv(int fmt, int M, int G, int J, int R, bool xl, int mode, const GemvParams &p, dim3 grid,

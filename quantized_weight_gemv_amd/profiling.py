@@ -131,7 +131,8 @@ def suite(stats_csv, suite_jsonl, out_md, cmd):
              "GEMV Q4_0 2048x2048; small-batch GEMV Q4_0/Q8_0 at 1, 2, 4, 8 tokens on 6144x2048, 2048x6144, "
              "8192x2048;", "one-launch MoE (10 of 128 experts 640x2560, 8 of 256 experts 512x2048); Q4_0 prefill "
              "at 64 and 512 tokens", "on 12288x2560, 2560x6144, 6144x2048 with the dense fp16 GEMM on "
-             "pre-dequantized weights beside it.", "", "Command:", "", "```", cmd, "```", "",
+             "pre-dequantized weights beside it; fp32-activation GEMV and stacked gate+up+SwiGLU with",
+             "their unfused steps beside them.", "", "Command:", "", "```", cmd, "```", "",
              "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
     for r in rows:
         lines.append(f"| `{r['Name'][:80]}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | "
@@ -142,6 +143,13 @@ def suite(stats_csv, suite_jsonl, out_md, cmd):
     for r in recs:
         if r["kind"] == "gemv":
             lines.append(f"| GEMV {r['fmt']} {r['N']}x{r['K']} M={r['M']} | {r['us_median']} | {r['GBps']} GB/s |")
+        elif r["kind"] == "f32in":
+            lines.append(f"| GEMV {r['fmt']} fp32 activations in {r['N']}x{r['K']} M={r['M']} | {r['us_median']} "
+                         f"(wall {r['wall_us_median']}; with a separate conversion "
+                         f"{r['separate_conversion_wall_us_median']}) | {r['GBps']} GB/s |")
+        elif r["kind"] == "swiglu":
+            lines.append(f"| gate+up+SwiGLU {r['fmt']} fp32 in, 2x{r['N']}x{r['K']} M={r['M']} | {r['us_median']} "
+                         f"(wall {r['wall_us_median']}; unfused {r['unfused_wall_us_median']}) | {r['GBps']} GB/s |")
         elif r["kind"] == "moe":
             lines.append(f"| MoE {r['fmt']} {r['E']} of {r['P']} x {r['N']}x{r['K']} | {r['us_median']} | "
                          f"{r['GBps']} GB/s |")

@@ -20,7 +20,7 @@ from __future__ import annotations
 import numpy as np
 
 # purpose tags: one independent stream per kind of input
-_W, _X, _IDX, _POOL, _STRESS = 0, 1, 2, 3, 4
+_W, _X, _IDX, _POOL, _STRESS, _X32 = 0, 1, 2, 3, 4, 5
 
 
 def _rng(seed: int, tag: int, *dims: int) -> np.random.Generator:
@@ -39,6 +39,13 @@ def activations(M: int, K: int, seed: int = 0) -> np.ndarray:
     """fp16 [M][K] activations ~ N(0, 1), rounded from fp64 to binary16 (RNE)."""
     g = _rng(seed, _X, M, K)
     return g.standard_normal((M, K)).astype(np.float16)
+
+
+def activations32(M: int, K: int, seed: int = 0) -> np.ndarray:
+    """fp32 [M][K] activations ~ N(0, 1), not rounded to binary16 (the input of
+    the fp32-activation entry points, which round them themselves)."""
+    g = _rng(seed, _X32, M, K)
+    return g.standard_normal((M, K)).astype(np.float32)
 
 
 def expert_pool(P: int, N: int, K: int, seed: int = 0) -> np.ndarray:
@@ -92,3 +99,11 @@ MOE_CONFIGS = [  # (pool P, experts per call E, N, K)
 ]
 PREFILL_SHAPES = [(12288, 2560), (2560, 6144), (6144, 2048)]
 PREFILL_TOKENS = [64, 512]
+# fp32 activations in: one token on Llama-3-8B tables, up to 4 tokens on
+# expert-sized ones [volta-kernel-bakeoff, "Results", the like-for-like bullets]
+F32IN_CASES = [(4096, 4096, 1), (14336, 4096, 1), (640, 2560, 1), (640, 2560, 4), (6144, 2048, 4)]
+# gate + up (N rows each, stacked) + SwiGLU: Qwen3-1.7B's MLP (6144 x 2048)
+# [volta-kernel-bakeoff, "Results"], Llama-3-8B's (14336 x 4096) and an
+# expert's gate / up (640 x 2560)
+SWIGLU_SHAPES = [(6144, 2048), (14336, 4096), (640, 2560)]
+SWIGLU_TOKENS = [1, 2, 4]

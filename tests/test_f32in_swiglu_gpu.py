@@ -68,6 +68,43 @@ def test_f32in_matches_fp16_path_bitwise():
     assert_within(y32, y_ref, s, "f32in 28672x4096")
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 257, 4096), (2, 70, 6144), (3, 33, 2560), (4, 130, 2048), (4, 9, 14336)])
+def test_f32in_every_launch_shape(M, N, K):
+    """fp32 input through the launch shapes the tuning knob can select, with
+    the activations in registers and staged once per workgroup in LDS."""
+    q = qg()
+    torch = torch_cuda()
+    w = si.weights(N, K, seed=N)
+    x = _x32(M, K, seed=K)
+    pb, po = pack_both(Q4_0, w)
+    Wd, xd = to_dev(pb), to_dev(x)
+    y_ref, s = oracle.get().gemv_f32in(Q4_0, po, N, K, x)
+    buf = torch.full((M * N + 128,), 7.0, dtype=torch.float32, device="cuda")
+    yv = buf[64:64 + M * N].view(M, N)
+    tried = set()
+    try:
+        for lanes in (0, 16, 32, 64):
+            for J in (0, 1, 2, 3, 5, 7):
+                for R in (1, 2, 4):
+                    for ks in (0, 2):
+                        for tpw, teams in ((1, 1), (2, 7), (8, 100000)):
+                            for xl in (-1, 0, 1):
+                                q.qg_set_gemv_shape(J, R, ks, tpw, teams, xl, 0, lanes)
+                                try:
+                                    q.qgemv_q4_0_f32in(Wd, xd, N, K, yv)
+                                except q.QGError:
+                                    continue
+                                torch.cuda.synchronize()
+                                tried.add((lanes, J, R, ks, xl))
+                                what = f"f32in M={M} G{lanes} J{J} R{R} ks{ks} tpw{tpw} teams{teams} xl{xl}"
+                                assert_within(yv.cpu().numpy(), y_ref, s, what)
+                                assert (buf[:64] == 7.0).all() and (buf[64 + M * N:] == 7.0).all(), what
+    finally:
+        q.qg_set_gemv_shape(0, 0, 0, 0, 0, -1, -1, 0)
+    xl_fits = M * (K // 32 + 1) * 64 <= 65536    # the LDS copy of M tokens
+    assert len(tried) >= 6 and any(t[4] == 1 for t in tried) == xl_fits
+
+
 def test_f32in_overflow_is_non_finite_like_the_oracle():
     """|x| > 65504 becomes infinity in binary16: every row with a nonzero
     weight there comes out non-finite, as in the oracle; the rest finite."""
@@ -147,19 +184,21 @@ def test_swiglu_saturation_and_every_launch_shape(M):
             for J in (0, 1, 2, 3):
                 for ks in (0, 1, 2, 4, 8):
                     for tpw, teams in ((1, 1), (2, 7), (8, 100000)):
-                        q.qg_set_gemv_shape(J, 0, ks, tpw, teams, -1, 0, lanes)
-                        try:
-                            q.qgemv_q4_0_swiglu_f32in(Wd, xd, N, K, yv)
-                        except q.QGError:
-                            continue
-                        torch.cuda.synchronize()
-                        tried.add((lanes, J, ks))
-                        what = f"swiglu M={M} lanes={lanes} J={J} ks={ks} tpw={tpw} teams={teams}"
-                        _check_swiglu(yv.cpu().numpy(), ref, what)
-                        assert (buf[:64] == 7.0).all() and (buf[64 + M * N:] == 7.0).all(), what
+                        for xl in (-1, 1):
+                            q.qg_set_gemv_shape(J, 0, ks, tpw, teams, xl, 0, lanes)
+                            try:
+                                q.qgemv_q4_0_swiglu_f32in(Wd, xd, N, K, yv)
+                            except q.QGError:
+                                continue
+                            torch.cuda.synchronize()
+                            tried.add((lanes, J, ks, xl))
+                            what = f"swiglu M={M} lanes={lanes} J={J} ks={ks} tpw={tpw} teams={teams} xl={xl}"
+                            _check_swiglu(yv.cpu().numpy(), ref, what)
+                            assert (buf[:64] == 7.0).all() and (buf[64 + M * N:] == 7.0).all(), what
     finally:
         q.qg_set_gemv_shape(0, 0, 0, 0, 0, -1, -1, 0)
     assert len(tried) >= (8 if M == 1 else 4)
+    assert any(t[3] == 1 for t in tried)
 
 
 def test_swiglu_one_token_narrow_rows():

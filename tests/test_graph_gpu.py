@@ -94,3 +94,20 @@ def test_prefill_split_k_graph_replay_within_bound():
         assert_within(rep, y_ref, s, f"prefill graph replay {r}")
 
     _replays_match(lambda: q.qgemm_q4_0_prefill(Wd, Xd, N, K, Y), Y, check)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 6144, 2048), (4, 640, 2560)])
+def test_f32in_and_swiglu_graph_replay_is_bitwise_eager(M, N, K):
+    q = qg()
+    torch = torch_cuda()
+    x = to_dev(si.activations32(M, K, seed=7))
+    w1 = si.weights(N, K, seed=7)
+    w2 = np.concatenate([w1, si.weights(N, K, seed=8)])
+    Wd1, Wd2 = to_dev(q.qquantize_q4_0(w1)), to_dev(q.qquantize_q4_0(w2))
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+
+    def check(rep, eager, r):
+        assert np.array_equal(rep.view(np.uint32), eager.view(np.uint32)), f"replay {r} differs from eager"
+
+    _replays_match(lambda: q.qgemv_q4_0_f32in(Wd1, x, N, K, y), y, check)
+    _replays_match(lambda: q.qgemv_q4_0_swiglu_f32in(Wd2, x, N, K, y), y, check)
