@@ -89,6 +89,11 @@ class Oracle:
         L.orc_silu.argtypes = [ctypes.c_double]
         L.orc_swiglu.restype = None
         L.orc_swiglu.argtypes = [f64p, f64p, i64, f64p]
+        i8p = ctypes.POINTER(ctypes.c_int8)
+        L.orc_quantize_act8.restype = None
+        L.orc_quantize_act8.argtypes = [u16p, i64, i64, i8p, f32p]
+        L.orc_gemv_q8act.restype = None
+        L.orc_gemv_q8act.argtypes = [u8p, i64, i64, i8p, f32p, i64, f64p, f64p]
 
     # -- helpers ---------------------------------------------------------
     @staticmethod
@@ -221,6 +226,40 @@ class Oracle:
         self._L.orc_swiglu(self._p(g, ctypes.c_double), self._p(u, ctypes.c_double), g.size,
                            self._p(y, ctypes.c_double))
         return y, g, u, np.ascontiguousarray(s2[:, :N]), np.ascontiguousarray(s2[:, N:])
+
+
+    # -- 8-bit activations --------------------------------------------------
+    def quantize_act8(self, x: np.ndarray):
+        """fp16 activations [M][K] -> (qx int8 [M][K], dx float32 [M][K/32])
+        per 32-block (oracle.c: amax / 127, rint(x * 127 / amax), binary32)."""
+        x = self._x16(x)
+        if x.ndim == 1:
+            x = x[None, :]
+        M, K = x.shape
+        qx = np.empty((M, K), np.int8)
+        dx = np.empty((M, K // 32), np.float32)
+        self._L.orc_quantize_act8(self._p(x, ctypes.c_uint16), M, K, self._p(qx, ctypes.c_int8),
+                                  self._p(dx, ctypes.c_float))
+        return qx, dx
+
+    def gemv_q8act_codes(self, packed: np.ndarray, N: int, K: int, qx: np.ndarray, dx: np.ndarray):
+        """(y, s) of Q4_0 weights against given 8-bit activations (qx, dx)."""
+        packed = np.ascontiguousarray(packed, dtype=np.uint8)
+        qx = np.ascontiguousarray(qx, dtype=np.int8)
+        dx = np.ascontiguousarray(dx, dtype=np.float32)
+        M = qx.shape[0]
+        assert qx.shape == (M, K) and dx.shape == (M, K // 32)
+        y = np.empty((M, N), np.float64)
+        s = np.empty((M, N), np.float64)
+        self._L.orc_gemv_q8act(self._p(packed, ctypes.c_uint8), N, K, self._p(qx, ctypes.c_int8),
+                               self._p(dx, ctypes.c_float), M, self._p(y, ctypes.c_double),
+                               self._p(s, ctypes.c_double))
+        return y, s
+
+    def gemv_q8act(self, packed: np.ndarray, N: int, K: int, x: np.ndarray):
+        """(y, s): the activations quantized to 8-bit blocks, then the GEMV."""
+        qx, dx = self.quantize_act8(x)
+        return self.gemv_q8act_codes(packed, N, K, qx, dx)
 
 
 def within_bound(y, y_ref, s, rel: float = 1e-3, abs_: float = 1e-6):

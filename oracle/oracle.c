@@ -14,8 +14,9 @@
  * ORC_PLANT_* macros build deliberately broken copies for the tests that show
  * the pins catch plausible mistakes (a swapped nibble order, a dropped offset,
  * the wrong tie rule or divisor, a shifted index, a dropped term, a codec
- * slip, a sign slip in silu, gate and up swapped).  The default build defines
- * none of them.
+ * slip, a sign slip in silu, gate and up swapped, the activation quantizer's
+ * tie rule, a shifted activation scale).  The default build defines none of
+ * them.
  *
  * What is computed, and where it is defined:
  *  - Q4_0 block: 32 weights share one binary16 scale d and carry 4-bit codes
@@ -48,6 +49,16 @@
  *    "Results", the few-tokens bullet: gate and up stacked into one table,
  *    the activations converted once; the FFN fusion step of the CUDA-kernel
  *    diary: gate, up and SwiGLU in one kernel, the activations read once].
+ *  - 8-bit activations: each 32-block of a token's fp16 activations becomes
+ *    int8 codes qx with one binary32 scale dx: amax = the block's largest
+ *    |x|, dx = amax / 127 and inv = 127 / amax (binary32 divisions),
+ *    qx = rint(x * inv) with a binary32 product and ties to even (an
+ *    all-zero block: qx = 0, dx = 0).  The GEMV then takes, per block, the
+ *    exact integer sum of (q - 8) * qx times dw * dx [sm8x-bench, "our
+ *    kernel": the activations quantized to 8-bit blocks once, then an int8
+ *    dot with 4-way multiply-accumulate; the pages fix neither the rounding
+ *    nor the precision of that quantizer, so both are this reading's, taken
+ *    in binary32 as the kernel takes them].
  *
  * Packed buffer layout (one N x K matrix, K % 32 == 0, blocks along K, block
  * index i = n * (K / 32) + b):
@@ -383,4 +394,82 @@ void orc_swiglu(const double *g, const double *u, int64_t n, double *y)
 #else
         y[i] = orc_silu(g[i]) * u[i];
 #endif
+}
+
+/* ------------------------------------------------------ 8-bit activations */
+
+/* Quantize M x K fp16 activations (bits) per 32-block: qx int8 [M][K],
+ * dx binary32 [M][K / 32] (the definition in the header).  Every step is one
+ * IEEE binary32 operation, as written. */
+void orc_quantize_act8(const uint16_t *x, int64_t M, int64_t K, int8_t *qx, float *dx)
+{
+    const int64_t KB = K / 32;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t b = 0; b < KB; ++b) {
+            const uint16_t *xb = x + m * K + b * 32;
+            float v[32];
+            float amax = 0.0f;
+            for (int k = 0; k < 32; ++k) {
+                v[k] = (float)orc_half_to_double(xb[k]);   /* exact */
+                float a = fabsf(v[k]);
+                if (a > amax)
+                    amax = a;
+            }
+            float d = 0.0f, inv = 0.0f;
+            if (amax > 0.0f) {
+                d = amax / 127.0f;
+                inv = 127.0f / amax;
+            }
+            for (int k = 0; k < 32; ++k) {
+                float t = v[k] * inv;
+#if defined(ORC_PLANT_ACTROUND)
+                float r = roundf(t);
+#else
+                float r = rintf(t);
+#endif
+                if (r > 127.0f)
+                    r = 127.0f;
+                if (r < -127.0f)
+                    r = -127.0f;
+                qx[m * K + b * 32 + k] = (int8_t)r;
+            }
+            dx[m * KB + b] = d;
+        }
+}
+
+/* Q4_0 weights against 8-bit activations (qx, dx from orc_quantize_act8):
+ *   y[m][n] = sum_b dw[n][b] * dx[m][b] * sum_k (q - 8) * qx   (fp64)
+ *   s[m][n] = sum_b |dw dx| * sum_k |(q - 8) qx|
+ * The integer sums are exact; the products of the three factors are exact
+ * in fp64 (11 + 24 + 16 significant bits), so y is the exact value up to
+ * the fp64 rounding of the sum over blocks. */
+void orc_gemv_q8act(const uint8_t *p, int64_t N, int64_t K, const int8_t *qx, const float *dx, int64_t M,
+                    double *y, double *s)
+{
+    const int64_t KB = K / 32;
+    for (int64_t m = 0; m < M; ++m) {
+#pragma omp parallel for schedule(static)
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0, sabs = 0.0;
+            for (int64_t b = 0; b < KB; ++b) {
+                size_t i = (size_t)(n * KB + b);
+                double dw = scale_value(ORC_Q4_0, p, N, K, i);
+#if defined(ORC_PLANT_ACTSCALE)
+                double d = (double)dx[m * KB + (b + 1) % KB];
+#else
+                double d = (double)dx[m * KB + b];
+#endif
+                int64_t isum = 0, iabs = 0;
+                for (int k = 0; k < 32; ++k) {
+                    int64_t t = (int64_t)code_value(ORC_Q4_0, p, i, k) * (int64_t)qx[m * K + b * 32 + k];
+                    isum += t;
+                    iabs += t < 0 ? -t : t;
+                }
+                acc += dw * d * (double)isum;
+                sabs += fabs(dw * d) * (double)iabs;
+            }
+            y[m * N + n] = acc;
+            s[m * N + n] = sabs;
+        }
+    }
 }

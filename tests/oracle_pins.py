@@ -454,5 +454,83 @@ def pin_swiglu(orc) -> list:
     return fails
 
 
+def pin_act8(orc) -> list:
+    """8-bit activation quantizer and the GEMV on its codes."""
+    fails = []
+    # hand-derived worked example (ties to even, the all-zero block, fl32(1/127))
+    g = load_golden("act8_we5.txt")
+    K = int(g["K"])
+    x = np.concatenate([np.array([float(v) for v in g[f"x{b}"].split()]) for b in range(K // 32)])
+    x16 = x.astype(np.float16)
+    assert np.array_equal(x16.astype(np.float64), x), "WE5 inputs must be exact binary16 values"
+    qx, dx = orc.quantize_act8(x16[None, :])
+    want_q = np.concatenate([np.array([int(v) for v in g[f"q{b}"].split()]) for b in range(K // 32)])
+    if not np.array_equal(qx[0].astype(np.int64), want_q):
+        i = int(np.flatnonzero(qx[0] != want_q)[0])
+        fails.append(f"act8 WE5: code {i} of x = {x[i]} is {qx[0, i]}, want {want_q[i]}")
+    want_d = np.array([int(v, 16) for v in g["dx_bits"].split()], np.uint32)
+    if not np.array_equal(dx[0].view(np.uint32), want_d):
+        fails.append(f"act8 WE5: scales {[hex(v) for v in dx[0].view(np.uint32)]} vs {list(g['dx_bits'].split())}")
+    # blocks whose amax is 127 * 2^e: dx = 2^e, inv = 2^-e exactly, so the
+    # codes are numpy's round-half-even of x / 2^e (an exact division)
+    rng = np.random.default_rng(31)
+    for e in (-12, -3, 0, 2, 7):
+        xb = (rng.uniform(-1, 1, (3, 64)) * 127 * 2.0 ** e).astype(np.float16)
+        xb[:, 5] = 127 * 2.0 ** e
+        xb[:, 40] = -127 * 2.0 ** e
+        xb[1, 7] = 2.5 * 2.0 ** e                     # ties
+        xb[2, 50] = -0.5 * 2.0 ** e
+        q, d = orc.quantize_act8(xb)
+        if not (d == np.float32(2.0 ** e)).all():
+            fails.append(f"act8: amax 127*2^{e} gives scales {np.unique(d)}")
+        want = np.rint(xb.astype(np.float64) / 2.0 ** e)
+        if not np.array_equal(q.astype(np.float64), want):
+            fails.append(f"act8: amax 127*2^{e}: codes differ from round-half-even of x / 2^{e}")
+    # invariants on wide-range data: |q| <= 127, the block's largest |x| maps
+    # to +-127, reconstruction within half a step
+    xr = (rng.standard_normal((4, 512)) * np.exp(rng.uniform(-8, 8, (4, 1)))).astype(np.float16)
+    xr[0, :32] = 0
+    xr[1, 32:64] = np.float16(3e4) * np.sign(rng.standard_normal(32)).astype(np.float16)
+    q, d = orc.quantize_act8(xr)
+    xf = xr.astype(np.float64).reshape(4, -1, 32)
+    qb = q.astype(np.float64).reshape(4, -1, 32)
+    if (np.abs(qb) > 127).any():
+        fails.append("act8: a code beyond +-127")
+    amax_at = np.abs(xf).argmax(axis=2)
+    top = np.take_along_axis(qb, amax_at[..., None], axis=2)[..., 0]
+    nz = np.abs(xf).max(axis=2) > 0
+    if not (np.abs(top[nz]) == 127).all():
+        fails.append("act8: the largest |x| of a block does not map to +-127")
+    if (qb[~nz] != 0).any() or (d[~nz] != 0).any():
+        fails.append("act8: an all-zero block does not give codes 0 and scale 0")
+    err = np.abs(xf - qb * d.astype(np.float64)[..., None])
+    if (err > 0.5 * d.astype(np.float64)[..., None] * (1 + 1e-5)).any():
+        fails.append("act8: reconstruction error above half a step")
+    # the GEMV on the codes equals numpy's fp64 matmul of the exactly
+    # dequantized weights with the dequantized activations qx * dx
+    N, K, M = 9, 160, 3
+    p = orc.quantize(Q4_0, si.weights(N, K, seed=41))
+    xa = (rng.standard_normal((M, K)) * 2).astype(np.float16)
+    q, d = orc.quantize_act8(xa)
+    y, s_ = orc.gemv_q8act_codes(p, N, K, q, d)
+    W = orc.dequant(Q4_0, p, N, K, "f64")
+    A = q.astype(np.float64) * np.repeat(d.astype(np.float64), 32, axis=1)
+    yr = A @ W.T
+    sr = np.abs(A) @ np.abs(W).T
+    if not (np.abs(y - yr) <= 1e-12 * sr).all():
+        fails.append("act8 GEMV differs from the matmul of dequantized weights and activations")
+    if not (np.abs(s_ - sr) <= 1e-12 * sr).all():
+        fails.append("act8 GEMV: sum |w x| differs from the matmul of the absolute values")
+    y2, _ = orc.gemv_q8act(p, N, K, xa)
+    if not np.array_equal(y, y2):
+        fails.append("act8: gemv_q8act is not quantize_act8 then the GEMV on the codes")
+    # within the activation rounding of the exact fp16 GEMV
+    ye, _ = orc.gemv(Q4_0, p, N, K, xa)
+    bound = np.abs(W) @ (0.5 * np.repeat(d.astype(np.float64), 32, axis=1) * (1 + 1e-5)).T
+    if not (np.abs(y - ye) <= bound.T + 1e-12).all():
+        fails.append("act8 GEMV further from the fp16 GEMV than the activation rounding allows")
+    return fails
+
+
 ALL_PINS = [pin_codec, pin_golden, pin_nearest, pin_invariants, pin_exact_gemv, pin_special, pin_moe,
-            pin_prefill, pin_f32in, pin_silu, pin_swiglu]
+            pin_prefill, pin_f32in, pin_silu, pin_swiglu, pin_act8]

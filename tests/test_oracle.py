@@ -28,6 +28,8 @@ PLANTS = {
     "scaleidx": [pins.pin_prefill],       # scale of the next block used
     "silu": [pins.pin_silu],              # e^v instead of e^-v in silu
     "glu": [pins.pin_swiglu],             # silu applied to the up half, not the gate
+    "actround": [pins.pin_act8],          # activation codes rounded half away from zero
+    "actscale": [pins.pin_act8],          # the next block's activation scale used
 }
 
 
