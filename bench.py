@@ -272,6 +272,24 @@ def suite(qg, torch, reps: int):
             pool_copies=copies)
         del buf
 
+    # activations quantized to 8-bit blocks inside the launch (int8 dot
+    # products), beside the fp16-activation GEMV on the same weights
+    q8_cases = [(N, K, 1) for (N, K) in si.LLAMA3_8B_SHAPES] + \
+        [(N, K, M) for (N, K) in si.SMALL_BATCH_SHAPES for M in (1, 2, 4)]
+    for (N, K, M) in q8_cases:
+        buf, nb, copies = _copies(torch, qg.qquantize_q4_0(si.weights(N, K, seed=0)))
+        x = torch.from_numpy(si.activations(M, K, seed=0)).to("cuda")
+        y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        fns = [lambda c=c: qg.qgemv_q4_0_q8act(buf[c * nb:(c + 1) * nb], x, N, K, y) for c in range(copies)]
+        med, mean = _time_calls(qg, torch, fns, reps)
+        f16 = [qg.PreparedGemv(qg.Q4_0, buf[c * nb:(c + 1) * nb], x, y, N, K) for c in range(copies)]
+        fmed, _ = _time_calls(qg, torch, f16, reps)
+        b = N * K // 32 * 18 + 2 * M * K + 4 * M * N
+        rec(kind="q8act", fmt="q4_0", N=N, K=K, M=M, us_median=round(med, 3), us_mean=round(mean, 3),
+            GBps=round(b / med / 1e3, 1), pct_of_8TBps=round(b / med / 1e3 / 80, 2), algorithmic_bytes=b,
+            fp16_activations_us_median=round(fmed, 3), copies=copies)
+        del buf
+
     # fp32 activations rounded inside the kernel, beside the same call on
     # activations converted by a separate step (torch's .half()) first
     for (N, K, M) in si.F32IN_CASES:

@@ -138,6 +138,27 @@ qg_status qgemv_q4_0_f32in(const void *Wp, const float *x, float *y, int M, int6
 qg_status qgemv_q4_0_swiglu_f32in(const void *Wp, const float *x, float *y, int M, int64_t N, int64_t K,
                                   void *stream);
 
+/* Q4_0 GEMV on activations quantized to 8-bit blocks, 1 <= M <= 4: every
+ * 32-block of each token's fp16 activations becomes int8 codes qx and one
+ * binary32 scale dx (amax = the block's largest |x|; dx = amax / 127 and
+ * inv = 127 / amax, correctly rounded binary32 divisions; qx = rint(x * inv),
+ * a binary32 product rounded to nearest, ties to even; an all-zero block has
+ * qx = 0, dx = 0), once per workgroup inside the launch; then
+ *   y[m][n] = sum_b d[n][b] * dx[m][b] * sum_{k in b} (q - 8) * qx
+ * with exact int8 dot products for the block sums.  This is a different
+ * result from qgemv_q4_0: the activations are rounded to 8 bits, so y is
+ * within sum_k |w[n][k]| * dx / 2 of the fp16 GEMV; against its own
+ * definition above it is within 1e-3 * sum_b |d dx| * sum |(q - 8) qx|.
+ * x: fp16 bits [M][K], finite (device, 16-byte aligned); Wp, y and N as for
+ * qgemv_q4_0; K <= 16384 and M * (K / 32 + 1) * 48 <= 65536 (the LDS copy).
+ * [sm8x-bench, "our kernel": the activations quantized to 8-bit blocks
+ *  once, then a 4-way int8 multiply-accumulate dot with the nibbles unpacked
+ *  by a 0x0F0F0F0F mask; volta-kernel-bakeoff, "Results", the 2-bit bullet:
+ *  activations converted to 8-bit integers once, four weights multiplied per
+ *  instruction] */
+qg_status qgemv_q4_0_q8act(const void *Wp, const uint16_t *x, float *y, int M, int64_t N, int64_t K,
+                           void *stream);
+
 /* Mixture-of-experts GEMV in one launch, Q4_0: expert slot e (0 <= e < E)
  * multiplies pool matrix idx[e] by its own token x[e]:
  *   y[e][n] = sum_k w_{idx[e]}[n][k] * x[e][k]

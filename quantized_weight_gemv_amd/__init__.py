@@ -62,6 +62,7 @@ def lib() -> ctypes.CDLL:
         "qgemv_q8_0": (c_int, [vp, vp, vp, c_int, i64, i64, vp]),
         "qgemv_q4_0_f32in": (c_int, [vp, vp, vp, c_int, i64, i64, vp]),
         "qgemv_q4_0_swiglu_f32in": (c_int, [vp, vp, vp, c_int, i64, i64, vp]),
+        "qgemv_q4_0_q8act": (c_int, [vp, vp, vp, c_int, i64, i64, vp]),
         "qmoe_gemv_q4_0": (c_int, [vp, i64, vp, vp, vp, c_int, i64, i64, vp]),
         "qgemm_q4_0_prefill": (c_int, [vp, vp, vp, i64, i64, i64, vp]),
         "qdequant_q4_0": (c_int, [vp, i64, i64, c_int, vp, vp]),
@@ -82,7 +83,8 @@ def lib() -> ctypes.CDLL:
 
 def exported_symbols() -> list[str]:
     return ["qg_status_str", "qpacked_bytes_q4_0", "qpacked_bytes_q8_0", "qquantize_q4_0", "qquantize_q8_0",
-            "qgemv_q4_0", "qgemv_q8_0", "qgemv_q4_0_f32in", "qgemv_q4_0_swiglu_f32in", "qmoe_gemv_q4_0",
+            "qgemv_q4_0", "qgemv_q8_0", "qgemv_q4_0_f32in", "qgemv_q4_0_swiglu_f32in", "qgemv_q4_0_q8act",
+            "qmoe_gemv_q4_0",
             "qgemm_q4_0_prefill", "qdequant_q4_0",
             "qdequant_q8_0", "qg_time_next_launch", "qg_device_cus", "qg_set_gemv_shape", "qg_read_probe", "qg_set_prefill_shape"]
 
@@ -207,6 +209,12 @@ def qgemv_q4_0(Wp, x, N: int, K: int, y=None):
 def qgemv_q8_0(Wp, x, N: int, K: int, y=None):
     """y[M][N] (fp32) = dequant(Wp) @ x[M][K]^T; Wp uint8 packed Q8_0, x fp16, 1 <= M <= 8."""
     return _gemv("qgemv_q8_0", Q8_0, Wp, x, N, K, y)
+
+
+def qgemv_q4_0_q8act(Wp, x, N: int, K: int, y=None):
+    """y[M][N] = Q4_0 weights times fp16 x quantized to 8-bit blocks inside the
+    launch (int8 dot products); 1 <= M <= 4."""
+    return _gemv("qgemv_q4_0_q8act", Q4_0, Wp, x, N, K, y)
 
 
 def _f32in(fn: str, Wp, x, N: int, K: int, y, rows: int):

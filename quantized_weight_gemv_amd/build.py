@@ -26,7 +26,8 @@ ARCH = "gfx950"
 # Packed-FP32 instruction generation is switched off: only fp16 packed math is
 # used on purpose, and fp32 code stays scalar.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
-          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-command-line-argument"]
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-fhip-fp32-correctly-rounded-divide-sqrt",
+          "-Wno-unused-command-line-argument"]
 
 
 def _hipcc() -> str:

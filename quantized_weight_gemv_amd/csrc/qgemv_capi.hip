@@ -87,12 +87,20 @@ bool choose_shape(int fmt, int M, int64_t N, int64_t K, int items, int cus, int 
     // With fp16 activations (half the bytes), on smaller tables and at one
     // token up to 8192 rows (4096 x 4096: 5.0 against 4.6 us with 16 lanes per
     // row) the register copy stays faster.
+    // 8-bit activations are quantized into LDS: always XL; two row sets per
+    // group for one token on tables of 8192 rows and more (rows of at most
+    // 256 blocks), one otherwise (launch sweeps on MI355X: 28672 x 4096
+    // 11.8 against 12.3 us; 2048 x 6144 at four tokens 6.6 against 7.2).
     bool xl = false;
-    const int xl_r = glu ? 2 : (M == 1 ? 1 : 2);
+    int xl_r = glu ? 2 : (M == 1 ? 1 : 2);
+    if (mode == kModeQ8Act)
+        xl_r = (M == 1 && N >= 8192 && (KB + 63) / 64 <= 4) ? 2 : 1;
     if (o_xl >= 0)
         xl = (o_xl == 1);
+    else if (mode == kModeQ8Act)
+        xl = true;
     else if (mode != kModeF16 && items == 1)
-        xl = (KB + 63) / 64 * xl_r <= 8 && gemv_xl_lds_bytes(static_cast<int>(K), M) <= 65536 &&
+        xl = (KB + 63) / 64 * xl_r <= 8 && gemv_xl_lds_bytes(static_cast<int>(K), M, mode) <= 65536 &&
              N / (glu ? 1 : xl_r) >= 4LL * cus && (M > 1 || glu || N > 8192);
     const bool xl_auto = xl && o_xl < 0;
     // Lanes per row: one token with rows of 65..128 blocks spreads a row over
@@ -183,7 +191,7 @@ bool choose_shape(int fmt, int M, int64_t N, int64_t K, int items, int cus, int 
         R = o_R;
     if (o_teams_per_wg)
         teams_per_wg = o_teams_per_wg;
-    if (xl && (ksplit > 1 || M > 4 || gemv_xl_lds_bytes(static_cast<int>(K), M) > 65536))
+    if (xl && (ksplit > 1 || M > 4 || gemv_xl_lds_bytes(static_cast<int>(K), M, mode) > 65536))
         return false;
     if (!gemv_fits(fmt, M, G, J, R, xl, mode))
         return false;
@@ -204,6 +212,8 @@ bool choose_shape(int fmt, int M, int64_t N, int64_t K, int items, int cus, int 
         per_cu = 64;
     if (xl_auto)
         per_cu = (M == 1 && !glu) || (glu && KB <= 64) ? 16 : 8;
+    if (xl_auto && mode == kModeQ8Act)
+        per_cu = (KB + 63) / 64 > 4 ? 8 : 16;   // 4096 x 14336: 8.6 against 9.2 us
     int64_t teams = std::max<int64_t>(1, static_cast<int64_t>(cus) * per_cu / std::max(1, items));
     // Several tokens, two blocks per lane, whole rows per wave: at least two
     // groups per team, so the prefetch of the next group overlaps the current
@@ -222,12 +232,13 @@ bool choose_shape(int fmt, int M, int64_t N, int64_t K, int items, int cus, int 
 qg_status run_gemv(int fmt, const void *Wp, const int32_t *idx, int64_t P, const uint16_t *x, float *y, int M,
                    int items, int64_t N, int64_t K, void *stream, int mode = kModeF16, const float *xf = nullptr)
 {
-    const void *xa = (mode == kModeF16) ? static_cast<const void *>(x) : static_cast<const void *>(xf);
+    const void *xa = (mode == kModeF16 || mode == kModeQ8Act) ? static_cast<const void *>(x)
+                                                               : static_cast<const void *>(xf);
     if (!Wp || !xa || !y)
         return QG_ERR_NULL;
     const int64_t nmax = (mode == kModeGlu) ? INT32_MAX / 2 : INT32_MAX;   // SwiGLU reads 2N rows
     // fp32 activations: up to 4 tokens (their raw words stay in registers
-    // until converted)
+    // until converted); 8-bit activations: up to 4 tokens (the LDS copy)
     const int mmax = (mode == kModeF16) ? 8 : 4;
     if (M < 1 || M > mmax || N < 1 || N > nmax || K < 32 || K % 32 != 0 || K > (1 << 20) || items < 1 ||
         items > 65535)
@@ -408,6 +419,11 @@ qg_status qgemv_q4_0_swiglu_f32in(const void *Wp, const float *x, float *y, int 
                                   void *stream)
 {
     return qg::run_gemv(qg::kQ4_0, Wp, nullptr, 1, nullptr, y, M, 1, N, K, stream, qg::kModeGlu, x);
+}
+
+qg_status qgemv_q4_0_q8act(const void *Wp, const uint16_t *x, float *y, int M, int64_t N, int64_t K, void *stream)
+{
+    return qg::run_gemv(qg::kQ4_0, Wp, nullptr, 1, x, y, M, 1, N, K, stream, qg::kModeQ8Act);
 }
 
 qg_status qmoe_gemv_q4_0(const void *pool, int64_t P, const int32_t *idx, const uint16_t *x, float *y, int E,

@@ -335,7 +335,7 @@ __device__ __forceinline__ float block_dot(const h2_t (&v0)[8], const h2_t (&v1)
 // one token's share in uint4).  With XL a block's activations are read once
 // per group and used by every row set before the next block's are read (read
 // per row set, the compiler keeps them all live across row sets instead).
-template <int FMT, int M, int J, int R, bool XL>
+template <int FMT, int M, int J, int R, bool XL, int MODE>
 __device__ __forceinline__ void compute_group(const Group<FMT, J, R> &g,
                                               const uint32_t (&X)[XL ? 1 : M][XL ? 1 : J][16],
                                               const uint4 *xs, uint32_t xstride, const uint32_t (&xoff)[J],
@@ -346,7 +346,54 @@ __device__ __forceinline__ void compute_group(const Group<FMT, J, R> &g,
 #pragma unroll
         for (int m = 0; m < M; ++m)
             acc[i][m] = 0.0f;
-    if constexpr (XL) {
+    if constexpr (MODE == kModeQ8Act) {
+        // 8-bit activations: per block and token 32 int8 codes (natural
+        // order) and the binary32 scale and the integer -8 * sum(codes).  The
+        // nibbles themselves are the int8 operands (0..15): the block sum
+        // starts from the offset term, so it ends at sum (q - 8) qx, exact.
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            uint32_t qw[M][8];
+            float dxm[M];
+            int bias[M];
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const uint4 *q = xs + m * xstride + xoff[j] * 3;
+                const uint4 a = q[0], b = q[1], c = q[2];
+                qw[m][0] = a.x;
+                qw[m][1] = a.y;
+                qw[m][2] = a.z;
+                qw[m][3] = a.w;
+                qw[m][4] = b.x;
+                qw[m][5] = b.y;
+                qw[m][6] = b.z;
+                qw[m][7] = b.w;
+                dxm[m] = __builtin_bit_cast(float, c.x);
+                bias[m] = (int)c.y;
+            }
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                const float d = (float)__builtin_bit_cast(_Float16, g.scale[i][j]);
+                const uint32_t w[4] = {g.code[i][j].c.x, g.code[i][j].c.y, g.code[i][j].c.z, g.code[i][j].c.w};
+                uint32_t lo[4], hi[4];   // word t: elements 4t..4t+3 / 16+4t..19+4t
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    lo[t] = w[t] & 0x0F0F0F0Fu;
+                    hi[t] = (w[t] >> 4) & 0x0F0F0F0Fu;
+                }
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    int sum = bias[m];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        sum = __builtin_amdgcn_sdot4((int)lo[t], (int)qw[m][t], sum, false);
+                        sum = __builtin_amdgcn_sdot4((int)hi[t], (int)qw[m][4 + t], sum, false);
+                    }
+                    acc[i][m] = __builtin_fmaf(d, dxm[m] * (float)sum, acc[i][m]);
+                }
+            }
+        }
+    } else if constexpr (XL) {
 #pragma unroll
         for (int j = 0; j < J; ++j) {
             uint32_t xw[M][16];
@@ -521,7 +568,8 @@ template <int FMT, int M, int G, int J, int R, bool XL, int MODE>
 __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
 {
     static_assert(!XL || M <= 4, "LDS-staged activations: up to 4 tokens");
-    static_assert(MODE == kModeF16 || FMT == kQ4_0, "fp32 activations: Q4_0");
+    static_assert(MODE == kModeF16 || FMT == kQ4_0, "fp32 and 8-bit activations: Q4_0");
+    static_assert(MODE != kModeQ8Act || XL, "8-bit activations are quantized into LDS");
     constexpr bool GLU = MODE == kModeGlu;
     static_assert(!GLU || R == 2, "SwiGLU: one gate and one up row set per group");
     constexpr int P = 64 / G;
@@ -594,8 +642,51 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
     // also cover these weights
     load_group<FMT, G, J, R, GLU>(ga, W, S, g * rows_per_group, rmax, KB, nblocks, coff, soff, p.N);
     __builtin_amdgcn_sched_barrier(0);
-    const uint32_t xstride = (uint32_t)(KB + 1) * 4u;
-    if constexpr (XL) {
+    const uint32_t xstride = (uint32_t)(KB + 1) * (MODE == kModeQ8Act ? 3u : 4u);
+    if constexpr (XL && MODE == kModeQ8Act) {
+        // the workgroup quantizes x once, token after token, to 8-bit blocks
+        // (each token followed by a zero block): amax = the block's largest
+        // |x|, dx = amax / 127 and inv = 127 / amax (binary32 divisions,
+        // correctly rounded), codes rint(x * inv) with ties to even; stored
+        // as 32 int8 codes, dx and -8 * sum(codes) [sm8x-bench, "our kernel":
+        // the activations quantized to 8-bit blocks once]
+        for (int i = threadIdx.x; i < M * (KB + 1); i += blockDim.x) {
+            const int m = i / (KB + 1);
+            const int b = i - m * (KB + 1);
+            uint32_t cw[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+            float dq = 0.0f;
+            int qsum = 0;
+            if (b < KB) {
+                uint4 r[4];
+                load_x_raw(x + (int64_t)m * p.K + (int64_t)b * 32, r);
+                const uint32_t hw[16] = {r[0].x, r[0].y, r[0].z, r[0].w, r[1].x, r[1].y, r[1].z, r[1].w,
+                                         r[2].x, r[2].y, r[2].z, r[2].w, r[3].x, r[3].y, r[3].z, r[3].w};
+                float v[32];
+                float amax = 0.0f;
+#pragma unroll
+                for (int k = 0; k < 32; ++k) {
+                    const uint16_t h = (uint16_t)(hw[k >> 1] >> (16 * (k & 1)));
+                    v[k] = (float)__builtin_bit_cast(_Float16, h);
+                    amax = fmaxf(amax, fabsf(v[k]));
+                }
+                float inv = 0.0f;
+                if (amax > 0.0f) {
+                    dq = amax / 127.0f;
+                    inv = 127.0f / amax;
+                }
+#pragma unroll
+                for (int k = 0; k < 32; ++k) {
+                    const int q = (int)__builtin_rintf(v[k] * inv);
+                    qsum += q;
+                    cw[k >> 2] |= ((uint32_t)q & 0xFFu) << (8 * (k & 3));
+                }
+            }
+            xs_dyn[i * 3 + 0] = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+            xs_dyn[i * 3 + 1] = make_uint4(cw[4], cw[5], cw[6], cw[7]);
+            xs_dyn[i * 3 + 2] = make_uint4(__builtin_bit_cast(uint32_t, dq), (uint32_t)(-8 * qsum), 0u, 0u);
+        }
+        __syncthreads();
+    } else if constexpr (XL) {
         // the workgroup stages x once, token after token, in pair order, each
         // token followed by a zero block (fp32 input: rounded here)
         for (int i = threadIdx.x; i < M * (KB + 1); i += blockDim.x) {
@@ -649,12 +740,12 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
         float acc[R][M];
         load_group<FMT, G, J, R, GLU>(gb, W, S, (g + teams_total) * rows_per_group, rmax, KB, nblocks, coff, soff, p.N);
         __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the compute
-        compute_group<FMT, M, J, R, XL>(ga, X, xs_dyn, xstride, xoff, magic, acc);
+        compute_group<FMT, M, J, R, XL, MODE>(ga, X, xs_dyn, xstride, xoff, magic, acc);
         finish<G, M, R, GLU>(acc, y, g * rows_per_group, rmax, p.N, lane, wave, team, kw, p.ksplit, red, buf);
         g += teams_total;
         load_group<FMT, G, J, R, GLU>(ga, W, S, (g + teams_total) * rows_per_group, rmax, KB, nblocks, coff, soff, p.N);
         __builtin_amdgcn_sched_barrier(0);
-        compute_group<FMT, M, J, R, XL>(gb, X, xs_dyn, xstride, xoff, magic, acc);
+        compute_group<FMT, M, J, R, XL, MODE>(gb, X, xs_dyn, xstride, xoff, magic, acc);
         finish<G, M, R, GLU>(acc, y, g * rows_per_group, rmax, p.N, lane, wave, team, kw, p.ksplit, red, buf);
         g += teams_total;
     }
@@ -662,14 +753,14 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
         float acc[R][M];
         load_group<FMT, G, J, R, GLU>(gb, W, S, (g + teams_total) * rows_per_group, rmax, KB, nblocks, coff, soff, p.N);
         __builtin_amdgcn_sched_barrier(0);
-        compute_group<FMT, M, J, R, XL>(ga, X, xs_dyn, xstride, xoff, magic, acc);
+        compute_group<FMT, M, J, R, XL, MODE>(ga, X, xs_dyn, xstride, xoff, magic, acc);
         finish<G, M, R, GLU>(acc, y, g * rows_per_group, rmax, p.N, lane, wave, team, kw, p.ksplit, red, buf);
         g += teams_total;
-        compute_group<FMT, M, J, R, XL>(gb, X, xs_dyn, xstride, xoff, magic, acc);
+        compute_group<FMT, M, J, R, XL, MODE>(gb, X, xs_dyn, xstride, xoff, magic, acc);
         finish<G, M, R, GLU>(acc, y, g * rows_per_group, rmax, p.N, lane, wave, team, kw, p.ksplit, red, buf);
     } else if (n - k == 1) {
         float acc[R][M];
-        compute_group<FMT, M, J, R, XL>(ga, X, xs_dyn, xstride, xoff, magic, acc);
+        compute_group<FMT, M, J, R, XL, MODE>(ga, X, xs_dyn, xstride, xoff, magic, acc);
         finish<G, M, R, GLU>(acc, y, g * rows_per_group, rmax, p.N, lane, wave, team, kw, p.ksplit, red, buf);
     }
 }
@@ -732,7 +823,10 @@ static hipError_t launch_g(int G, int J, int R, const GemvParams &p, dim3 grid, 
     return hipErrorInvalidValue;
 }
 
-size_t gemv_xl_lds_bytes(int K, int M) { return (size_t)M * (K / 32 + 1) * 64; }
+size_t gemv_xl_lds_bytes(int K, int M, int mode)
+{
+    return (size_t)M * (K / 32 + 1) * (mode == kModeQ8Act ? 48 : 64);
+}
 
 hipError_t launch_gemv(int fmt, int M, int G, int J, int R, bool xl, int mode, const GemvParams &p, dim3 grid,
                        dim3 block, hipStream_t stream)
@@ -745,7 +839,7 @@ hipError_t launch_gemv(int fmt, int M, int G, int J, int R, bool xl, int mode, c
     if (xl) {
         if (M > 4 || p.ksplit != 1)
             return hipErrorInvalidValue;
-        const size_t shmem = gemv_xl_lds_bytes(p.K, M);
+        const size_t shmem = gemv_xl_lds_bytes(p.K, M, mode);
 #define QG_CASE_XL(FMT, MODE)                                                                  \
     switch (M) {                                                                               \
     case 1: return launch_g<FMT, 1, true, MODE>(G, J, R, p, grid, block, shmem, stream);       \
@@ -755,6 +849,8 @@ hipError_t launch_gemv(int fmt, int M, int G, int J, int R, bool xl, int mode, c
     }
         if (mode == kModeF32) {
             QG_CASE_XL(kQ4_0, kModeF32)
+        } else if (mode == kModeQ8Act) {
+            QG_CASE_XL(kQ4_0, kModeQ8Act)
         } else if (mode == kModeGlu) {
             QG_CASE_XL(kQ4_0, kModeGlu)
         } else if (fmt == kQ4_0) {
@@ -776,7 +872,9 @@ hipError_t launch_gemv(int fmt, int M, int G, int J, int R, bool xl, int mode, c
     case 7: return launch_g<FMT, 7, false, MODE>(G, J, R, p, grid, block, 0, stream);         \
     case 8: return launch_g<FMT, 8, false, MODE>(G, J, R, p, grid, block, 0, stream);         \
     }
-    if (mode == kModeF32) {
+    if (mode == kModeQ8Act) {
+        return hipErrorInvalidValue;   // quantized into LDS: XL only
+    } else if (mode == kModeF32) {
         QG_CASE_M(kQ4_0, kModeF32)
     } else if (mode == kModeGlu) {
         QG_CASE_M(kQ4_0, kModeGlu)

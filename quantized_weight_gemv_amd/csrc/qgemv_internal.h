@@ -74,10 +74,12 @@ inline hipError_t launch_kernel(const void *fn, dim3 grid, dim3 block, size_t sh
 // activations rounded to binary16 as they are loaded (Q4_0); fp32
 // activations and a stacked gate + up table (2N rows) with the SwiGLU
 // epilogue y = silu(gate) * up (Q4_0, two row sets: a gate set and the up
-// set N rows further).
+// set N rows further); fp16 activations quantized to 8-bit blocks in LDS and
+// multiplied with int8 dot products (Q4_0, LDS staging only).
 constexpr int kModeF16 = 0;
 constexpr int kModeF32 = 1;
 constexpr int kModeGlu = 2;
+constexpr int kModeQ8Act = 3;
 
 // Which vector-ALU GEMV instantiations exist (G lanes per row, J blocks per
 // lane, R row sets per group, xl: activations in LDS).  Register estimate: R *
@@ -95,6 +97,8 @@ constexpr bool gemv_fits(int fmt, int M, int G, int J, int R, bool xl, int mode 
         return false;
     if (xl && (G != 64 || M > 4))
         return false;
+    if (mode == kModeQ8Act && (!xl || fmt != kQ4_0))
+        return false;
     if (R * J > (fmt == kQ4_0 ? 8 : 4) || J > (xl ? 8 : 7) || (!xl && J * M > 8))
         return false;
     // fp32 activations (mode != 0) hold 32 raw words per block until they
@@ -103,8 +107,10 @@ constexpr bool gemv_fits(int fmt, int M, int G, int J, int R, bool xl, int mode 
     return regs <= 256 && R * M * (64 / G) <= kMaxRM;
 }
 
-// LDS bytes of the XL activation copy of M tokens for rows of K weights.
-size_t gemv_xl_lds_bytes(int K, int M);
+// LDS bytes of the XL activation copy of M tokens for rows of K weights
+// (per block: 64 bytes of fp16 pairs, or 32 int8 codes and 16 bytes of scale
+// and offset with 8-bit activations).
+size_t gemv_xl_lds_bytes(int K, int M, int mode);
 
 
 hipError_t launch_gemv(int fmt, int M, int G, int J, int R, bool xl, int mode, const GemvParams &p, dim3 grid,
