@@ -25,6 +25,7 @@ import numpy as np
 
 Q4_0 = 0
 Q8_0 = 1
+Q2W = 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")

@@ -49,6 +49,16 @@
  *    "Results", the few-tokens bullet: gate and up stacked into one table,
  *    the activations converted once; the FFN fusion step of the CUDA-kernel
  *    diary: gate, up and SwiGLU in one kernel, the activations read once].
+ *  - Plain 2-bit block (q2w): 32 weights share one binary16 scale d and
+ *    carry codes c in -2..1, the weight is c * d; stored as u = c + 2 in two
+ *    bits, byte j of the block's 8 code bytes holding elements j, j + 8,
+ *    j + 16, j + 24 in bits 0-1, 2-3, 4-5, 6-7 (2.5 bits per weight)
+ *    [volta-kernel-bakeoff, "What's in the race": q2w, codes -2..1, one fp16
+ *    scale per 32].  The pages give no quantizer; the reading here: m = the
+ *    block's weight of largest magnitude (the first on ties), d =
+ *    fp16(fl32(m / -2)), so m lands exactly on code -2 and all four codes are
+ *    used, c = clamp(round(w / d), -2, 1) with w / d in fp64 against the
+ *    stored d and round half away from zero as for Q4_0; d = 0 gives c = 0.
  *  - 8-bit activations: each 32-block of a token's fp16 activations becomes
  *    int8 codes qx with one binary32 scale dx: amax = the block's largest
  *    |x|, dx = amax / 127 and inv = 127 / amax (binary32 divisions),
@@ -62,8 +72,9 @@
  *
  * Packed buffer layout (one N x K matrix, K % 32 == 0, blocks along K, block
  * index i = n * (K / 32) + b):
- *   codes  : at byte 0; 16 bytes per Q4_0 block / 32 per Q8_0 block, block i
- *            at byte 16 * i / 32 * i.  Q8_0 codes are two's complement int8.
+ *   codes  : at byte 0; 16 bytes per Q4_0 block / 32 per Q8_0 block / 8 per
+ *            q2w block, block i at byte 16 * i / 32 * i / 8 * i.  Q8_0 codes
+ *            are two's complement int8.
  *   scales : binary16 little-endian, scale i at byte S0 + 2 * i, where S0 is
  *            the code-region size rounded up to a multiple of 256.
  *   total  : (S0 + 2 * N * K / 32) rounded up to a multiple of 256.
@@ -75,6 +86,7 @@
 
 #define ORC_Q4_0 0
 #define ORC_Q8_0 1
+#define ORC_Q2W 2
 
 /* ---------------------------------------------------------------- binary16 */
 
@@ -135,11 +147,11 @@ uint16_t orc_float_to_half(float f) { return orc_double_to_half((double)f); }
 
 static size_t round256(size_t v) { return (v + 255u) & ~(size_t)255u; }
 
-static size_t code_bytes_per_block(int fmt) { return fmt == ORC_Q4_0 ? 16u : 32u; }
+static size_t code_bytes_per_block(int fmt) { return fmt == ORC_Q4_0 ? 16u : fmt == ORC_Q2W ? 8u : 32u; }
 
 size_t orc_packed_bytes(int fmt, int64_t N, int64_t K)
 {
-    if (N <= 0 || K <= 0 || K % 32 != 0 || (fmt != ORC_Q4_0 && fmt != ORC_Q8_0))
+    if (N <= 0 || K <= 0 || K % 32 != 0 || (fmt != ORC_Q4_0 && fmt != ORC_Q8_0 && fmt != ORC_Q2W))
         return 0;
     size_t nb = (size_t)N * (size_t)(K / 32);
     size_t s0 = round256(nb * code_bytes_per_block(fmt));
@@ -153,9 +165,18 @@ static size_t scale_offset(int fmt, int64_t N, int64_t K)
 }
 
 /* Signed weight multiplier of element k (0..31) of block i:
- * Q4_0 -> q - 8, Q8_0 -> q. */
+ * Q4_0 -> q - 8, Q8_0 -> q, q2w -> u - 2. */
 static int code_value(int fmt, const uint8_t *p, size_t i, int k)
 {
+    if (fmt == ORC_Q2W) {
+        const uint8_t *blk = p + 8u * i;
+#if defined(ORC_PLANT_Q2ORDER)
+        int u = (blk[k / 4] >> (2 * (k % 4))) & 3;
+#else
+        int u = (blk[k % 8] >> (2 * (k / 8))) & 3;
+#endif
+        return u - 2;
+    }
     if (fmt == ORC_Q4_0) {
         const uint8_t *blk = p + 16u * i;
 #if defined(ORC_PLANT_NIBBLE)
@@ -185,6 +206,37 @@ static double scale_value(int fmt, const uint8_t *p, int64_t N, int64_t K, size_
 
 /* ------------------------------------------------------------- quantizer */
 
+/* One q2w block (the reading in the header): codes into c[8], scale bits
+ * into *d16; sets *err to 4 for a non-finite weight or scale. */
+static void quantize_q2w_block(const float *blk, uint8_t *c, uint16_t *d16, int *err)
+{
+    float m = 0.0f;
+    for (int k = 0; k < 32; ++k) {
+        if (!isfinite(blk[k]))
+            *err = 4;
+        if (fabsf(blk[k]) > fabsf(m))
+            m = blk[k];
+    }
+    float d32 = m / -2.0f;   /* binary32 division */
+    *d16 = orc_float_to_half(d32);
+    if ((*d16 & 0x7c00u) == 0x7c00u)
+        *err = 4;
+    double d = orc_half_to_double(*d16);
+    int u[32];
+    for (int k = 0; k < 32; ++k) {
+        int v = 0;
+        if (d != 0.0 && isfinite(d)) {
+            double r = round((double)blk[k] / d);   /* half away from zero */
+            if (r > 1.0) r = 1.0;
+            if (r < -2.0) r = -2.0;
+            v = (int)r;
+        }
+        u[k] = v + 2;
+    }
+    for (int j = 0; j < 8; ++j)
+        c[j] = (uint8_t)(u[j] | (u[j + 8] << 2) | (u[j + 16] << 4) | (u[j + 24] << 6));
+}
+
 /* Returns 0 on success, 4 (range error) if a weight is non-finite or a scale
  * overflows binary16, 2 on a bad shape, 5 if `out_bytes` is too small. */
 int orc_quantize(int fmt, const float *w, int64_t N, int64_t K, uint8_t *out, size_t out_bytes)
@@ -203,6 +255,13 @@ int orc_quantize(int fmt, const float *w, int64_t N, int64_t K, uint8_t *out, si
         for (int64_t b = 0; b < KB; ++b) {
             const float *blk = w + n * K + b * 32;
             size_t i = (size_t)(n * KB + b);
+            if (fmt == ORC_Q2W) {
+                uint16_t d2;
+                quantize_q2w_block(blk, out + 8u * i, &d2, &err);
+                out[s0 + 2u * i] = (uint8_t)(d2 & 0xff);
+                out[s0 + 2u * i + 1] = (uint8_t)(d2 >> 8);
+                continue;
+            }
             float a = 0.0f;
             for (int k = 0; k < 32; ++k) {
                 if (!isfinite(blk[k]))

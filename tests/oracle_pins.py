@@ -41,7 +41,7 @@ import numpy as np
 import seeded_inputs as si
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
-Q4_0, Q8_0 = 0, 1
+Q4_0, Q8_0, Q2W = 0, 1, 2
 
 
 def load_golden(name: str) -> dict:
@@ -175,10 +175,13 @@ def pin_golden(orc) -> list:
 def _parse(fmt, p, N, K):
     """Codes (signed multipliers) and scales straight from the documented layout."""
     nb = N * K // 32
-    cb = 16 if fmt == Q4_0 else 32
+    cb = {Q4_0: 16, Q8_0: 32, Q2W: 8}[fmt]
     codes_raw = p[:nb * cb].reshape(nb, cb)
     if fmt == Q4_0:
         q = np.concatenate([codes_raw & 0x0F, codes_raw >> 4], axis=1).astype(np.int64) - 8
+    elif fmt == Q2W:
+        # element 8 r + j sits in bits 2r..2r+1 of byte j
+        q = np.concatenate([(codes_raw >> (2 * r)) & 3 for r in range(4)], axis=1).astype(np.int64) - 2
     else:
         q = codes_raw.view(np.int8).astype(np.int64)
     s0 = (nb * cb + 255) // 256 * 256
@@ -263,7 +266,7 @@ def pin_invariants(orc) -> list:
 # ------------------------------------------------------------- exact gemv
 def pin_exact_gemv(orc) -> list:
     fails = []
-    for fmt in (Q4_0, Q8_0):
+    for fmt in (Q4_0, Q8_0, Q2W):
         for (N, K, M) in ((1, 32, 1), (3, 64, 2), (5, 96, 3), (8, 128, 8)):
             w = si.weights(N, K, seed=3)
             x = si.activations(M, K, seed=3)
@@ -532,5 +535,81 @@ def pin_act8(orc) -> list:
     return fails
 
 
+def pin_q2w(orc) -> list:
+    """Plain 2-bit blocks: the hand-derived block, the scale rule, nearest
+    codes by brute force, invariants, and the GEMV against numpy's matmul."""
+    fails = []
+    g = load_golden("q2w_we6.txt")
+    w = _golden_weights(g)
+    p = orc.quantize(Q2W, w)
+    if p.size != orc.packed_bytes(Q2W, 1, 32) or p.size != 512:
+        fails.append(f"q2w: packed size {p.size} for one block, want 512 (8 code bytes and a scale, 256-aligned)")
+    want = bytes.fromhex("".join(g["code_bytes"].split()))
+    if bytes(p[:8]) != want:
+        fails.append(f"q2w WE6: code bytes {bytes(p[:8]).hex()} vs {want.hex()}")
+    sbits = int(p[256]) | (int(p[257]) << 8)
+    if sbits != int(g["scale_bits"], 16):
+        fails.append(f"q2w WE6: scale {sbits:#06x} vs {g['scale_bits']}")
+    q, scale = _parse(Q2W, p, 1, 32)
+    codes = np.array([int(c) for c in g["codes"].split()])
+    if not np.array_equal(q[0], codes):
+        fails.append(f"q2w WE6: parsed codes {q[0]} vs {codes}")
+    if not np.array_equal(orc.dequant(Q2W, p, 1, 32, "f64")[0], codes * scale[0]):
+        fails.append("q2w WE6: dequant is not code * scale")
+    y, _ = orc.gemv(Q2W, p, 1, 32, np.ones((1, 32), np.float16))
+    if y[0, 0] != float(g["y_ones"]):
+        fails.append(f"q2w WE6: y_ones {y[0, 0]!r} vs {g['y_ones']}")
+    for key in ("y_e3", "y_e8"):
+        x = np.zeros((1, 32), np.float16)
+        x[0, int(key[3:])] = 1.0
+        y, _ = orc.gemv(Q2W, p, 1, 32, x)
+        if y[0, 0] != float(g[key]):
+            fails.append(f"q2w WE6: {key} {y[0, 0]!r} vs {g[key]}")
+    # scale rule and nearest codes by brute force on many blocks, with ties,
+    # both signs of the extreme weight, zero and tiny blocks
+    N, K = 256, 256
+    w = si.weights(N, K, seed=17)
+    w[0, :32] = 0.0
+    w[1, :32] = np.float32(1e-9)
+    w[2, :32] = (np.arange(32) - 14).astype(np.float32) * np.float32(2.0 ** -6)
+    w[3, :32] = -w[2, :32]
+    w[4, 32:64] = np.float32(0.25) * ((np.arange(32) % 5) - 2).astype(np.float32)
+    p = orc.quantize(Q2W, w)
+    q, scale = _parse(Q2W, p, N, K)
+    blocks = w.reshape(-1, 32)
+    first = np.abs(blocks).argmax(axis=1)                 # numpy: the first maximum
+    m = blocks[np.arange(blocks.shape[0]), first]
+    d16 = (m / np.float32(-2.0)).astype(np.float16)
+    if not np.array_equal(scale, d16.astype(np.float64)):
+        fails.append(f"q2w: scales differ from fp16(m / -2) at {np.flatnonzero(scale != d16)[:5]}")
+    d = d16.astype(np.float64)
+    best = np.zeros(blocks.shape, np.int64)
+    bestd = np.full(blocks.shape, np.inf)
+    for c in (-2, -1, 0, 1):
+        dist = np.abs(blocks.astype(np.float64) - c * d[:, None])
+        better = (dist < bestd) | ((dist == bestd) & (abs(c) > np.abs(best)))
+        best = np.where(better, c, best)
+        bestd = np.where(better, dist, bestd)
+    best[d == 0.0] = 0
+    bad = np.flatnonzero((q != best).any(axis=1))
+    if bad.size:
+        fails.append(f"q2w: {bad.size} blocks with codes off the nearest grid point (first {bad[0]})")
+    normal = np.abs(d) >= 2.0 ** -14
+    if not (q[np.arange(q.shape[0]), first][normal] == -2).all():
+        fails.append("q2w: the largest-magnitude weight is not at code -2")
+    p2 = orc.quantize(Q2W, orc.dequant(Q2W, p, N, K, "f32"))
+    if not np.array_equal(p, p2):
+        fails.append("q2w: quantize(dequant(.)) is not the identity")
+    # the GEMV against numpy's fp64 matmul of the dequantized weights
+    x = si.activations(3, K, seed=17)
+    y, s_ = orc.gemv(Q2W, p, N, K, x)
+    W = (q * scale[:, None]).reshape(N, K)
+    yr = x.astype(np.float64) @ W.T
+    sr = np.abs(x.astype(np.float64)) @ np.abs(W).T
+    if not (np.abs(y - yr) <= 1e-12 * sr).all():
+        fails.append("q2w GEMV differs from the matmul of the parsed weights")
+    return fails
+
+
 ALL_PINS = [pin_codec, pin_golden, pin_nearest, pin_invariants, pin_exact_gemv, pin_special, pin_moe,
-            pin_prefill, pin_f32in, pin_silu, pin_swiglu, pin_act8]
+            pin_prefill, pin_f32in, pin_silu, pin_swiglu, pin_act8, pin_q2w]

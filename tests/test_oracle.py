@@ -30,6 +30,7 @@ PLANTS = {
     "glu": [pins.pin_swiglu],             # silu applied to the up half, not the gate
     "actround": [pins.pin_act8],          # activation codes rounded half away from zero
     "actscale": [pins.pin_act8],          # the next block's activation scale used
+    "q2order": [pins.pin_q2w],            # 2-bit codes read as four consecutive per byte
 }
 
 
