@@ -272,6 +272,27 @@ def suite(qg, torch, reps: int):
             pool_copies=copies)
         del buf
 
+    # plain 2-bit weights (q2w), beside Q4_0 on the same shapes
+    q2_cases = [(N, K, 1) for (N, K) in si.LLAMA3_8B_SHAPES] + \
+        [(N, K, M) for (N, K) in si.SMALL_BATCH_SHAPES for M in (1, 2, 4, 8)]
+    for (N, K, M) in q2_cases:
+        w = si.weights(N, K, seed=0)
+        buf, nb, copies = _copies(torch, qg.qquantize_q2w(w))
+        x = torch.from_numpy(si.activations(M, K, seed=0)).to("cuda")
+        y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        calls = [qg.PreparedGemv(qg.Q2W, buf[c * nb:(c + 1) * nb], x, y, N, K) for c in range(copies)]
+        med, mean = _time_calls(qg, torch, calls, reps)
+        del buf
+        buf4, nb4, copies4 = _copies(torch, qg.qquantize_q4_0(w))
+        del w
+        c4 = [qg.PreparedGemv(qg.Q4_0, buf4[c * nb4:(c + 1) * nb4], x, y, N, K) for c in range(copies4)]
+        med4, _ = _time_calls(qg, torch, c4, reps)
+        del buf4
+        b = N * K // 32 * 10 + 2 * M * K + 4 * M * N
+        rec(kind="q2w", fmt="q2w", N=N, K=K, M=M, us_median=round(med, 3), us_mean=round(mean, 3),
+            GBps=round(b / med / 1e3, 1), pct_of_8TBps=round(b / med / 1e3 / 80, 2), algorithmic_bytes=b,
+            q4_0_us_median=round(med4, 3), copies=copies)
+
     # activations quantized to 8-bit blocks inside the launch (int8 dot
     # products), beside the fp16-activation GEMV on the same weights
     q8_cases = [(N, K, 1) for (N, K) in si.LLAMA3_8B_SHAPES] + \

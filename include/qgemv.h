@@ -11,11 +11,16 @@
  *   Q8_0  int8 codes q (two's complement), weight = q * d
  *         [H100-KERNEL-5X-ROADMAP, Lever 1: int8 codes plus a per-block
  *          scale; the scale is binary16 here].
+ *   q2w   plain 2-bit codes c in -2..1 stored as u = c + 2, weight = c * d;
+ *         byte j of a block's 8 code bytes holds elements j, j + 8, j + 16,
+ *         j + 24 in bits 0-1, 2-3, 4-5, 6-7 (2.5 bits per weight)
+ *         [volta-kernel-bakeoff, "What's in the race": q2w, codes -2..1,
+ *          one fp16 scale per 32].
  *
  * Packed buffer of one N x K matrix (row-major weights, K % 32 == 0, blocks
  * along K, block index i = n * (K/32) + b):
- *   codes   at byte 0: 16 B (Q4_0) or 32 B (Q8_0) per block, block i at
- *           byte 16 i (32 i).
+ *   codes   at byte 0: 16 B (Q4_0), 32 B (Q8_0) or 8 B (q2w) per block,
+ *           block i at byte 16 i (32 i, 8 i).
  *   scales  binary16 little-endian, scale i at byte S0 + 2 i, where S0 is the
  *           code-region size rounded up to a multiple of 256.
  *   total   (S0 + 2 N K / 32) rounded up to a multiple of 256, so packed
@@ -35,12 +40,12 @@
  *     4 B (QG_ERR_ALIGN otherwise).
  *   - Outputs are fp32, accumulated in fp32 from exactly dequantized weights
  *     and fp16 activations (products are exact; only the sums round).  The
- *     vector-ALU GEMV forms each block sum from the biased codes (1024 + q
- *     as fp16) and subtracts the bias times the block's activation sum, so
- *     its fp32 rounding is relative to about 1152 * sum |x| per block, far
- *     inside the 1e-3 * sum |w x| tolerance; a one-hot activation still
- *     returns a weight column exactly.  A block with a non-finite scale makes
- *     its row non-finite (inf or NaN).
+ *     GEMV kernels multiply the exact integer multipliers (q - 8, q or c, as
+ *     fp16) and scale each block sum once, so the fp32 sums only ever hold
+ *     partial sums of the result's own terms: their rounding stays far
+ *     inside 1e-3 * sum |w x| for every finite input, and a one-hot
+ *     activation returns a weight column exactly.  A block with a non-finite
+ *     scale makes its row non-finite (inf or NaN).
  *   - The GEMV / MoE kernels use no atomics: for a fixed shape and launch
  *     their results are bitwise reproducible.  The prefill adds split-K
  *     partial tiles atomically (last-bit differences between runs).
@@ -76,6 +81,7 @@ const char *qg_status_str(qg_status s);
  * K % 32 != 0. */
 size_t qpacked_bytes_q4_0(int64_t N, int64_t K);
 size_t qpacked_bytes_q8_0(int64_t N, int64_t K);
+size_t qpacked_bytes_q2w(int64_t N, int64_t K);
 
 /* Quantize and pack fp32 weights w[N][K] (host memory) into `packed` (host
  * memory, at least qpacked_bytes_*(N, K) bytes; padding bytes are zeroed).
@@ -91,6 +97,14 @@ size_t qpacked_bytes_q8_0(int64_t N, int64_t K);
  *  H100-KERNEL-5X-ROADMAP, Lever 1, resident device weights] */
 qg_status qquantize_q4_0(const float *w, int64_t N, int64_t K, void *packed, size_t packed_bytes);
 qg_status qquantize_q8_0(const float *w, int64_t N, int64_t K, void *packed, size_t packed_bytes);
+
+/* The same for q2w: m = the block's weight of largest magnitude (the first
+ * on ties), d = fp16(fl32(m / -2)) (so m is exactly code -2),
+ * c = clamp(round(w / d), -2, 1) with w / d in binary64 against the stored d
+ * and round half away from zero; d = 0 stores c = 0.  The pages give the
+ * format, not a quantizer: this rule is the library's.  Returns
+ * QG_ERR_RANGE as above.  [volta-kernel-bakeoff, "What's in the race"] */
+qg_status qquantize_q2w(const float *w, int64_t N, int64_t K, void *packed, size_t packed_bytes);
 
 /* ----------------------------------------------------------- device side */
 
@@ -108,6 +122,14 @@ qg_status qgemv_q4_0(const void *Wp, const uint16_t *x, float *y, int M, int64_t
                      void *stream);
 qg_status qgemv_q8_0(const void *Wp, const uint16_t *x, float *y, int M, int64_t N, int64_t K,
                      void *stream);
+
+/* The same GEMV for plain 2-bit weights (q2w), 1 <= M <= 8:
+ *   y[m][n] = sum_k c[n][k] * d * x[m][k]
+ * with the conventions and limits of qgemv_q4_0 (K <= 16384 * min(floor(8 /
+ * M), 7)); vector-ALU kernel only.  [volta-kernel-bakeoff, "What's in the
+ * race" (q2w_alu: unpack in registers, fp32 sums) and "Results", the 2-bit
+ * bullets] */
+qg_status qgemv_q2w(const void *Wp, const uint16_t *x, float *y, int M, int64_t N, int64_t K, void *stream);
 
 /* Q4_0 GEMV on fp32 activations, 1 <= M <= 4 tokens: each activation is
  * rounded to binary16 inside the kernel (nearest, ties to even; a magnitude
@@ -188,6 +210,7 @@ qg_status qgemm_q4_0_prefill(const void *Wp, const uint16_t *X, float *Y, int64_
  *  fp16 before a dense multiply] */
 qg_status qdequant_q4_0(const void *Wp, int64_t N, int64_t K, int out_fp16, void *out, void *stream);
 qg_status qdequant_q8_0(const void *Wp, int64_t N, int64_t K, int out_fp16, void *out, void *stream);
+qg_status qdequant_q2w(const void *Wp, int64_t N, int64_t K, int out_fp16, void *out, void *stream);
 
 /* ------------------------------------------------------------ measurement */
 

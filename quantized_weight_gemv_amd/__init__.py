@@ -27,6 +27,7 @@ QG_STATUS = {0: "ok", 1: "null pointer", 2: "shape out of range", 3: "misaligned
 
 Q4_0 = 0
 Q8_0 = 1
+Q2W = 2
 
 
 class QGError(RuntimeError):
@@ -58,6 +59,10 @@ def lib() -> ctypes.CDLL:
         "qpacked_bytes_q8_0": (sz, [i64, i64]),
         "qquantize_q4_0": (c_int, [vp, i64, i64, vp, sz]),
         "qquantize_q8_0": (c_int, [vp, i64, i64, vp, sz]),
+        "qpacked_bytes_q2w": (sz, [i64, i64]),
+        "qquantize_q2w": (c_int, [vp, i64, i64, vp, sz]),
+        "qgemv_q2w": (c_int, [vp, vp, vp, c_int, i64, i64, vp]),
+        "qdequant_q2w": (c_int, [vp, i64, i64, c_int, vp, vp]),
         "qgemv_q4_0": (c_int, [vp, vp, vp, c_int, i64, i64, vp]),
         "qgemv_q8_0": (c_int, [vp, vp, vp, c_int, i64, i64, vp]),
         "qgemv_q4_0_f32in": (c_int, [vp, vp, vp, c_int, i64, i64, vp]),
@@ -86,7 +91,8 @@ def exported_symbols() -> list[str]:
             "qgemv_q4_0", "qgemv_q8_0", "qgemv_q4_0_f32in", "qgemv_q4_0_swiglu_f32in", "qgemv_q4_0_q8act",
             "qmoe_gemv_q4_0",
             "qgemm_q4_0_prefill", "qdequant_q4_0",
-            "qdequant_q8_0", "qg_time_next_launch", "qg_device_cus", "qg_set_gemv_shape", "qg_read_probe", "qg_set_prefill_shape"]
+            "qdequant_q8_0", "qpacked_bytes_q2w", "qquantize_q2w", "qgemv_q2w", "qdequant_q2w",
+            "qg_time_next_launch", "qg_device_cus", "qg_set_gemv_shape", "qg_read_probe", "qg_set_prefill_shape"]
 
 
 def _check(fn: str, st: int):
@@ -103,7 +109,13 @@ def qpacked_bytes_q8_0(N: int, K: int) -> int:
     return int(lib().qpacked_bytes_q8_0(N, K))
 
 
+def qpacked_bytes_q2w(N: int, K: int) -> int:
+    return int(lib().qpacked_bytes_q2w(N, K))
+
+
 def packed_bytes(fmt: int, N: int, K: int) -> int:
+    if fmt == Q2W:
+        return qpacked_bytes_q2w(N, K)
     return qpacked_bytes_q4_0(N, K) if fmt == Q4_0 else qpacked_bytes_q8_0(N, K)
 
 
@@ -131,6 +143,11 @@ def qquantize_q4_0(w: np.ndarray, out: np.ndarray | None = None) -> np.ndarray:
 def qquantize_q8_0(w: np.ndarray, out: np.ndarray | None = None) -> np.ndarray:
     """Quantize + pack fp32 [N][K] host weights into the Q8_0 layout (host bytes)."""
     return _quantize("qquantize_q8_0", Q8_0, w, out)
+
+
+def qquantize_q2w(w: np.ndarray, out: np.ndarray | None = None) -> np.ndarray:
+    """Quantize + pack fp32 [N][K] host weights into the plain 2-bit (q2w) layout."""
+    return _quantize("qquantize_q2w", Q2W, w, out)
 
 
 # ---------------------------------------------------------------- device side
@@ -188,8 +205,8 @@ class PreparedGemv:
         if x.dim() != 2 or x.shape[1] != K or y.shape != (x.shape[0], N):
             raise ValueError("x must be [M][K] and y [M][N]")
         self._keep = (Wp, x, y)
-        self._fn = lib().qgemv_q4_0 if fmt == Q4_0 else lib().qgemv_q8_0
-        self._name = "qgemv_q4_0" if fmt == Q4_0 else "qgemv_q8_0"
+        self._name = {Q4_0: "qgemv_q4_0", Q8_0: "qgemv_q8_0", Q2W: "qgemv_q2w"}[fmt]
+        self._fn = getattr(lib(), self._name)
         self._args = (_dev(Wp, torch.uint8, "Wp", packed_bytes(fmt, N, K)).value,
                       _dev(_x16(x), torch.int16, "x", x.shape[0] * K).value,
                       _dev(y, torch.float32, "y", x.shape[0] * N).value,
@@ -209,6 +226,11 @@ def qgemv_q4_0(Wp, x, N: int, K: int, y=None):
 def qgemv_q8_0(Wp, x, N: int, K: int, y=None):
     """y[M][N] (fp32) = dequant(Wp) @ x[M][K]^T; Wp uint8 packed Q8_0, x fp16, 1 <= M <= 8."""
     return _gemv("qgemv_q8_0", Q8_0, Wp, x, N, K, y)
+
+
+def qgemv_q2w(Wp, x, N: int, K: int, y=None):
+    """y[M][N] (fp32) = dequant(Wp) @ x[M][K]^T; Wp uint8 packed q2w, x fp16, 1 <= M <= 8."""
+    return _gemv("qgemv_q2w", Q2W, Wp, x, N, K, y)
 
 
 def qgemv_q4_0_q8act(Wp, x, N: int, K: int, y=None):
@@ -289,6 +311,10 @@ def qdequant_q4_0(Wp, N: int, K: int, fp16: bool = False, out=None):
 
 def qdequant_q8_0(Wp, N: int, K: int, fp16: bool = False, out=None):
     return _dequant("qdequant_q8_0", Q8_0, Wp, N, K, fp16, out)
+
+
+def qdequant_q2w(Wp, N: int, K: int, fp16: bool = False, out=None):
+    return _dequant("qdequant_q2w", Q2W, Wp, N, K, fp16, out)
 
 
 # --------------------------------------------------------------- measurement

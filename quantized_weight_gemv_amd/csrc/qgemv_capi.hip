@@ -59,7 +59,7 @@ inline size_t round256(size_t v) { return (v + 255) / 256 * 256; }
 inline int64_t scale_offset(int fmt, int64_t N, int64_t K)
 {
     return static_cast<int64_t>(round256(static_cast<size_t>(N) * static_cast<size_t>(K / 32) *
-                                         (fmt == kQ4_0 ? 16u : 32u)));
+                                         static_cast<size_t>(code_bytes_per_block(fmt))));
 }
 
 // Launch shape for one GEMV / MoE call.
@@ -106,7 +106,9 @@ bool choose_shape(int fmt, int M, int64_t N, int64_t K, int items, int cus, int 
     // Lanes per row: one token with rows of 65..128 blocks spreads a row over
     // 16 (up to 4096 rows) or 32 lanes (up to 64K rows; Q4_0 GEMV: up to 8192),
     // so a wave reduces several rows at once; shorter rows take one wave each.
-    const bool q4_one = fmt == kQ4_0 && M == 1 && items == 1 && !xl;
+    // (q2w follows the Q4_0 one-token rules: launch sweeps on MI355X,
+    // 14336 x 4096 7.2 against 8.1 us, 4096 x 14336 7.6 against 9.3)
+    const bool q4_one = (fmt == kQ4_0 || fmt == kQ2W) && M == 1 && items == 1 && !xl;
     int G = 64;
     if (M == 1 && !xl && KB > 64 && KB <= 128) {
         if (N <= 4096 && N >= 4)
@@ -142,7 +144,7 @@ bool choose_shape(int fmt, int M, int64_t N, int64_t K, int items, int cus, int 
     if (q4_one && o_G == 0 && G == 64 && ((KB > 64 && KB <= 128) || (KB > 256 && KB <= 448)))
         J = static_cast<int>((KB + 63) / 64);
     int ksplit = static_cast<int>((KB + static_cast<int64_t>(G) * J - 1) / (static_cast<int64_t>(G) * J));
-    const int rj = (fmt == kQ4_0) ? 8 : 4;   // R * J budget of the kernel table
+    const int rj = (fmt == kQ8_0) ? 4 : 8;   // R * J budget of the kernel table
     // Two row sets per group, four for full-wave rows beyond 64K rows, and
     // four for several tokens with K split over waves (launch sweeps on
     // MI355X, 256 CUs: Q4_0 2048 x 6144 at six tokens 7.9 against 8.5 us).
@@ -155,7 +157,7 @@ bool choose_shape(int fmt, int M, int64_t N, int64_t K, int items, int cus, int 
     if (glu)
         R = 2;   // SwiGLU: one gate and one up row set per group
     if (M >= 2 && J == 1 && ksplit > 1 && !glu &&
-        (fmt == kQ4_0 || N <= 4LL * cus * std::max(2, 8 / ksplit)))
+        (fmt != kQ8_0 || N <= 4LL * cus * std::max(2, 8 / ksplit)))
         R = 4;
     if (xl_auto)
         R = xl_r;   // one row set per group at one token, two at 2-4 tokens
@@ -209,7 +211,7 @@ bool choose_shape(int fmt, int M, int64_t N, int64_t K, int items, int cus, int 
     if (M == 1 && ksplit == 1 && J > 2)
         per_cu = 4;   // long whole rows per wave: 4096 x 14336 7.95 us at 4, 8.9 at 8
     if (N > 65536 && M == 1)
-        per_cu = 64;
+        per_cu = fmt == kQ2W ? 32 : 64;   // q2w 128256 x 4096: 39.6 against 42.4 us
     if (xl_auto)
         per_cu = (M == 1 && !glu) || (glu && KB <= 64) ? 16 : 8;
     if (xl_auto && mode == kModeQ8Act)
@@ -265,8 +267,8 @@ qg_status run_gemv(int fmt, const void *Wp, const int32_t *idx, int64_t P, const
                  (N >= 8LL * cus && fmt == kQ4_0 && M == 8 && KB <= 256));
     if (o_engine >= 0)
         mfma = (o_engine == 1);
-    if (mfma && mode != kModeF16)
-        return QG_ERR_SHAPE;   // the matrix-core kernel reads fp16 activations
+    if (mfma && (mode != kModeF16 || fmt == kQ2W))
+        return QG_ERR_SHAPE;   // the matrix-core kernel: Q4_0 / Q8_0, fp16 activations
     if (mfma) {
         if (idx != nullptr || KB > 256 || N > INT32_MAX)
             return QG_ERR_SHAPE;
@@ -291,7 +293,9 @@ qg_status run_gemv(int fmt, const void *Wp, const int32_t *idx, int64_t P, const
     p.x = x;
     p.xf = xf;
     p.y = y;
-    p.matrix_stride = static_cast<int64_t>(fmt == kQ4_0 ? qpacked_bytes_q4_0(rows, K) : qpacked_bytes_q8_0(rows, K));
+    p.matrix_stride = static_cast<int64_t>(fmt == kQ4_0   ? qpacked_bytes_q4_0(rows, K)
+                                           : fmt == kQ2W ? qpacked_bytes_q2w(rows, K)
+                                                         : qpacked_bytes_q8_0(rows, K));
     p.scale_offset = scale_offset(fmt, rows, K);
     p.N = static_cast<int>(N);
     p.K = static_cast<int>(K);
@@ -309,7 +313,7 @@ qg_status run_gemv(int fmt, const void *Wp, const int32_t *idx, int64_t P, const
 
 // ---------------------------------------------------------------- dequant
 
-// One thread per block of 32 weights: the exact (q - 8) * d (or q * d) in
+// One thread per block of 32 weights: the exact (q - 8) * d (q * d, c * d) in
 // fp32, or that value rounded to nearest-even binary16.
 template <int FMT, bool F16>
 __device__ __forceinline__ void dequant_kernel(const uint8_t *__restrict__ W, int64_t blocks,
@@ -328,6 +332,24 @@ __device__ __forceinline__ void dequant_kernel(const uint8_t *__restrict__ W, in
             const uint32_t byte = (w[j >> 2] >> (8 * (j & 3))) & 0xFFu;
             v[j] = (float)((int)(byte & 0xFu) - 8) * d;
             v[j + 16] = (float)((int)(byte >> 4) - 8) * d;
+        }
+    } else if constexpr (FMT == kQ2W) {
+        // c * d is exact in binary16 too; with fp16 output it is formed there
+        // (an fp32 product rounded to fp16 is fused by the compiler into
+        // fma(c, d, +0), which turns 0 * (negative d) into +0 instead of -0)
+        const uint2 c = reinterpret_cast<const uint2 *>(W)[b];
+        const _Float16 dh = __builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t *>(W + scale_off)[b]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t byte = ((j < 4 ? c.x : c.y) >> (8 * (j & 3))) & 0xFFu;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int cc = (int)((byte >> (2 * r)) & 3u) - 2;
+                if constexpr (F16)
+                    v[j + 8 * r] = (float)((_Float16)cc * dh);
+                else
+                    v[j + 8 * r] = (float)cc * d;
+            }
         }
     } else {
         const uint4 *c = reinterpret_cast<const uint4 *>(W + b * 32);
@@ -387,6 +409,9 @@ qg_status run_dequant(int fmt, const void *Wp, int64_t N, int64_t K, int out_fp1
     if (fmt == kQ4_0)
         fn = out_fp16 ? reinterpret_cast<const void *>(&dequant_entry<kQ4_0, true>)
                       : reinterpret_cast<const void *>(&dequant_entry<kQ4_0, false>);
+    else if (fmt == kQ2W)
+        fn = out_fp16 ? reinterpret_cast<const void *>(&dequant_entry<kQ2W, true>)
+                      : reinterpret_cast<const void *>(&dequant_entry<kQ2W, false>);
     else
         fn = out_fp16 ? reinterpret_cast<const void *>(&dequant_entry<kQ8_0, true>)
                       : reinterpret_cast<const void *>(&dequant_entry<kQ8_0, false>);
@@ -424,6 +449,16 @@ qg_status qgemv_q4_0_swiglu_f32in(const void *Wp, const float *x, float *y, int 
 qg_status qgemv_q4_0_q8act(const void *Wp, const uint16_t *x, float *y, int M, int64_t N, int64_t K, void *stream)
 {
     return qg::run_gemv(qg::kQ4_0, Wp, nullptr, 1, x, y, M, 1, N, K, stream, qg::kModeQ8Act);
+}
+
+qg_status qgemv_q2w(const void *Wp, const uint16_t *x, float *y, int M, int64_t N, int64_t K, void *stream)
+{
+    return qg::run_gemv(qg::kQ2W, Wp, nullptr, 1, x, y, M, 1, N, K, stream);
+}
+
+qg_status qdequant_q2w(const void *Wp, int64_t N, int64_t K, int out_fp16, void *out, void *stream)
+{
+    return qg::run_dequant(qg::kQ2W, Wp, N, K, out_fp16, out, stream);
 }
 
 qg_status qmoe_gemv_q4_0(const void *pool, int64_t P, const int32_t *idx, const uint16_t *x, float *y, int E,

@@ -1,6 +1,7 @@
-// Fused dequantize-and-multiply GEMV kernels (Q4_0, Q8_0, and the one-launch
-// MoE variant) for gfx950: the vector-ALU path (1..8 tokens; the library uses
-// it for 1..3 tokens and for rows too long for the matrix-core kernel).
+// Fused dequantize-and-multiply GEMV kernels (Q4_0, Q8_0, plain 2-bit q2w,
+// and the one-launch MoE variant) for gfx950: the vector-ALU path (1..8
+// tokens; the library uses it for 1..3 tokens and for rows too long for the
+// matrix-core kernel).
 //
 // The work is bound by streaming the packed weights from HBM once per call
 // [volta-kernel-bakeoff, "Why the V100 is interesting here";
@@ -128,6 +129,30 @@ __device__ __forceinline__ void unpack_q8(const uint4 c0, const uint4 c1, uint32
     }
 }
 
+// q2w: word h (bytes 4h..4h+3) holds in bit pair r of byte 4h+i element
+// 4h + i + 8r, stored as u = c + 2.  With a = word, b = word >> 8, the mask
+// 0x00030003 << 2r picks bytes 0 and 2 (or 1 and 3) at bit pair r; OR-ed into
+// 0x6400 that is 1024 + 4^r u exactly, and one v_pk_fma_f16 (x / 4^r - 1024 /
+// 4^r - 2, every step exact) leaves c in -2..1:
+//   v[2r]   = (c[4h + 8r],     c[4h + 8r + 2])   partner X[8h + 2r]
+//   v[2r+1] = (c[4h + 8r + 1], c[4h + 8r + 3])   partner X[8h + 2r + 1]
+// for word 0 into v0 and word 1 into v1.
+__device__ __forceinline__ void unpack_q2_word(uint32_t w, uint32_t kMagic, h2_t (&v)[8])
+{
+    const uint32_t a = w;
+    const uint32_t b = w >> 8;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t mask = 0x00030003u << (2 * r);
+        const _Float16 sc = (_Float16)(1.0f / (float)(1 << (2 * r)));
+        const _Float16 off = (_Float16)(-(1024.0f / (float)(1 << (2 * r))) - 2.0f);
+        const h2_t ksc = {sc, sc};
+        const h2_t koff = {off, off};
+        v[2 * r + 0] = as_h2((a & mask) | kMagic) * ksc + koff;
+        v[2 * r + 1] = as_h2((b & mask) | kMagic) * ksc + koff;
+    }
+}
+
 __device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
 __device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
 
@@ -139,7 +164,16 @@ __device__ __forceinline__ void pair_x_block(const uint4 (&r)[4], uint32_t (&X)[
     const uint32_t d[16] = {r[0].x, r[0].y, r[0].z, r[0].w, r[1].x, r[1].y, r[1].z, r[1].w,
                             r[2].x, r[2].y, r[2].z, r[2].w, r[3].x, r[3].y, r[3].z, r[3].w};
     // d[i] = (x[2i], x[2i+1])
-    if constexpr (FMT == kQ4_0) {
+    if constexpr (FMT == kQ2W) {
+        // X[8h + 2r + s]: elements (4h + 8r + s, 4h + 8r + s + 2)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                X[8 * h + 2 * r + 0] = pair_lo(d[2 * h + 4 * r], d[2 * h + 4 * r + 1]);
+                X[8 * h + 2 * r + 1] = pair_hi(d[2 * h + 4 * r], d[2 * h + 4 * r + 1]);
+            }
+    } else if constexpr (FMT == kQ4_0) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             X[4 * t + 0] = pair_lo(d[2 * t], d[2 * t + 1]);
@@ -241,6 +275,10 @@ template <>
 struct Codes<kQ8_0> {
     uint4 c0, c1;
 };
+template <>
+struct Codes<kQ2W> {
+    uint2 c;
+};
 
 template <int FMT, int J, int R>
 struct Group {
@@ -261,7 +299,7 @@ __device__ __forceinline__ void load_group(Group<FMT, J, R> &g, const uint8_t *_
                                            int64_t N)
 {
     constexpr int P = 64 / G;
-    constexpr int CB = (FMT == kQ4_0) ? 16 : 32;   // code bytes per block
+    constexpr int CB = code_bytes_per_block(FMT);
 #pragma unroll
     for (int i = 0; i < R; ++i) {
         // GLU: row set 0 holds gate rows, row set 1 the up rows N further
@@ -273,6 +311,8 @@ __device__ __forceinline__ void load_group(Group<FMT, J, R> &g, const uint8_t *_
         for (int j = 0; j < J; ++j) {
             if constexpr (FMT == kQ4_0) {
                 g.code[i][j].c = stream_load16(rc, coff[j]);
+            } else if constexpr (FMT == kQ2W) {
+                g.code[i][j].c = stream_load8(rc, coff[j]);
             } else {
                 g.code[i][j].c0 = stream_load16(rc, coff[j]);
                 g.code[i][j].c1 = stream_load16(rc, coff[j] + 16u);
@@ -288,6 +328,9 @@ __device__ __forceinline__ void unpack_block(const Codes<FMT> &c, uint32_t magic
 {
     if constexpr (FMT == kQ4_0) {
         unpack_q4(c.c, magic, v0, v1);
+    } else if constexpr (FMT == kQ2W) {
+        unpack_q2_word(c.c.x, magic, v0);
+        unpack_q2_word(c.c.y, magic, v1);
     } else {
         h2_t v[16];
         unpack_q8(c.c0, c.c1, magic, v);
@@ -299,8 +342,9 @@ __device__ __forceinline__ void unpack_block(const Codes<FMT> &c, uint32_t magic
     }
 }
 
-// sum (q - 8) x (Q4_0) or sum q x (Q8_0) of one block against one token's 16
-// activation pairs.
+// sum (q - 8) x (Q4_0), sum q x (Q8_0) or sum c x (q2w) of one block against
+// one token's 16 activation pairs (q2w and Q8_0 share the pair order: chain 0
+// takes pairs 0..7, chain 1 pairs 8..15).
 template <int FMT>
 __device__ __forceinline__ float block_dot(const h2_t (&v0)[8], const h2_t (&v1)[8], const uint32_t (&xw)[16])
 {
@@ -603,7 +647,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
         blk[j] = (uint32_t)(ok[j] ? b : bend - 1);
         xoff[j] = (uint32_t)(ok[j] ? b : KB);   // LDS block KB is all zeros
         const uint32_t e = (uint32_t)lr * (uint32_t)KB + blk[j];   // block offset from the row set
-        coff[j] = e * (FMT == kQ4_0 ? 16u : 32u);
+        coff[j] = e * (uint32_t)code_bytes_per_block(FMT);
         soff[j] = e * 2u;
     }
 
@@ -855,6 +899,8 @@ hipError_t launch_gemv(int fmt, int M, int G, int J, int R, bool xl, int mode, c
             QG_CASE_XL(kQ4_0, kModeGlu)
         } else if (fmt == kQ4_0) {
             QG_CASE_XL(kQ4_0, kModeF16)
+        } else if (fmt == kQ2W) {
+            QG_CASE_XL(kQ2W, kModeF16)
         } else {
             QG_CASE_XL(kQ8_0, kModeF16)
         }
@@ -880,6 +926,8 @@ hipError_t launch_gemv(int fmt, int M, int G, int J, int R, bool xl, int mode, c
         QG_CASE_M(kQ4_0, kModeGlu)
     } else if (fmt == kQ4_0) {
         QG_CASE_M(kQ4_0, kModeF16)
+    } else if (fmt == kQ2W) {
+        QG_CASE_M(kQ2W, kModeF16)
     } else {
         QG_CASE_M(kQ8_0, kModeF16)
     }

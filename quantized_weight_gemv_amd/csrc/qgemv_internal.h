@@ -9,6 +9,10 @@ namespace qg {
 
 constexpr int kQ4_0 = 0;
 constexpr int kQ8_0 = 1;
+constexpr int kQ2W = 2;   // plain 2-bit: codes -2..1, one fp16 scale per 32
+
+// Code bytes per 32-weight block of each packed format.
+constexpr int code_bytes_per_block(int fmt) { return fmt == kQ4_0 ? 16 : fmt == kQ2W ? 8 : 32; }
 
 constexpr int kMaxWavesPerWg = 8;   // 512 threads
 constexpr int kMaxRM = 32;          // rows per group (<= 4) x tokens (<= 8)
@@ -33,6 +37,12 @@ __device__ __forceinline__ uint4 stream_load16(__amdgpu_buffer_rsrc_t r, uint32_
 {
     const auto t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNtAux);
     return make_uint4(t[0], t[1], t[2], t[3]);
+}
+
+__device__ __forceinline__ uint2 stream_load8(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    const auto t = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kNtAux);
+    return make_uint2(t[0], t[1]);
 }
 
 __device__ __forceinline__ uint16_t stream_load2(__amdgpu_buffer_rsrc_t r, uint32_t off)
@@ -99,11 +109,12 @@ constexpr bool gemv_fits(int fmt, int M, int G, int J, int R, bool xl, int mode 
         return false;
     if (mode == kModeQ8Act && (!xl || fmt != kQ4_0))
         return false;
-    if (R * J > (fmt == kQ4_0 ? 8 : 4) || J > (xl ? 8 : 7) || (!xl && J * M > 8))
+    if (R * J > (fmt == kQ8_0 ? 4 : 8) || J > (xl ? 8 : 7) || (!xl && J * M > 8))
         return false;
     // fp32 activations (mode != 0) hold 32 raw words per block until they
     // are converted, 16 more than fp16 ones
-    const int regs = 2 * R * J * (fmt == kQ4_0 ? 5 : 9) + (xl ? 0 : J * M * (mode ? 34 : 18)) + R * M + 36;
+    const int regs = 2 * R * J * (fmt == kQ4_0 ? 5 : fmt == kQ2W ? 3 : 9) + (xl ? 0 : J * M * (mode ? 34 : 18)) +
+                     R * M + 36;
     return regs <= 256 && R * M * (64 / G) <= kMaxRM;
 }
 

@@ -1,4 +1,4 @@
-// Host quantizer / packer for the Q4_0 and Q8_0 packed layout of qgemv.h.
+// Host quantizer / packer for the Q4_0, Q8_0 and q2w packed layouts of qgemv.h.
 //
 // Runs on the host, once per weight matrix, off the timed path: weights are
 // quantized and uploaded once and stay resident on the device
@@ -98,12 +98,65 @@ qg_status quantize(const float *w, int64_t N, int64_t K, void *packed, size_t nb
     return st;
 }
 
+// Plain 2-bit (q2w): m = the block's weight of largest magnitude (the first
+// on ties), scale fp16(m / -2), multipliers round(w / d) clamped to -2..1
+// (half away from zero), stored as u = c + 2; byte j holds elements j, j + 8,
+// j + 16, j + 24 in bits 0-1, 2-3, 4-5, 6-7.
+qg_status quantize_q2w(const float *w, int64_t N, int64_t K, void *packed, size_t nbytes)
+{
+    if (!w || !packed)
+        return QG_ERR_NULL;
+    const size_t need = packed_bytes(N, K, 8);
+    if (need == 0)
+        return QG_ERR_SHAPE;
+    if (nbytes < need)
+        return QG_ERR_SIZE;
+    auto *out = static_cast<uint8_t *>(packed);
+    std::memset(out, 0, need);
+    const size_t blocks = static_cast<size_t>(N) * static_cast<size_t>(K / 32);
+    uint8_t *scales = out + round_up(blocks * 8);
+    qg_status st = QG_OK;
+    for (size_t blk = 0; blk < blocks; ++blk) {
+        const float *v = w + blk * 32;
+        float m = 0.0f;
+        for (int k = 0; k < 32; ++k) {
+            if (!std::isfinite(v[k]))
+                st = QG_ERR_RANGE;
+            if (std::fabs(v[k]) > std::fabs(m))
+                m = v[k];
+        }
+        const uint16_t dbits = f32_to_f16_bits(m / -2.0f);   // binary32 division
+        if ((dbits & 0x7c00u) == 0x7c00u)
+            st = QG_ERR_RANGE;
+        const double d = f16_bits_to_f64(dbits);
+        uint8_t u[32];
+        for (int k = 0; k < 32; ++k) {
+            int c = 0;
+            if (d != 0.0 && std::isfinite(d))
+                c = static_cast<int>(std::fmin(std::fmax(std::round(static_cast<double>(v[k]) / d), -2.0), 1.0));
+            u[k] = static_cast<uint8_t>(c + 2);
+        }
+        uint8_t *c = out + blk * 8;
+        for (int j = 0; j < 8; ++j)
+            c[j] = static_cast<uint8_t>(u[j] | (u[j + 8] << 2) | (u[j + 16] << 4) | (u[j + 24] << 6));
+        scales[2 * blk] = static_cast<uint8_t>(dbits & 0xffu);
+        scales[2 * blk + 1] = static_cast<uint8_t>(dbits >> 8);
+    }
+    return st;
+}
+
 }  // namespace
 
 extern "C" {
 
 size_t qpacked_bytes_q4_0(int64_t N, int64_t K) { return packed_bytes(N, K, 16); }
 size_t qpacked_bytes_q8_0(int64_t N, int64_t K) { return packed_bytes(N, K, 32); }
+size_t qpacked_bytes_q2w(int64_t N, int64_t K) { return packed_bytes(N, K, 8); }
+
+qg_status qquantize_q2w(const float *w, int64_t N, int64_t K, void *packed, size_t packed_bytes)
+{
+    return quantize_q2w(w, N, K, packed, packed_bytes);
+}
 
 qg_status qquantize_q4_0(const float *w, int64_t N, int64_t K, void *packed, size_t packed_bytes)
 {

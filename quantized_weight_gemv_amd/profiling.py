@@ -132,7 +132,8 @@ def suite(stats_csv, suite_jsonl, out_md, cmd):
              "8192x2048;", "one-launch MoE (10 of 128 experts 640x2560, 8 of 256 experts 512x2048); Q4_0 prefill "
              "at 64 and 512 tokens", "on 12288x2560, 2560x6144, 6144x2048 with the dense fp16 GEMM on "
              "pre-dequantized weights beside it; fp32-activation GEMV and stacked gate+up+SwiGLU with",
-             "their unfused steps beside them; the GEMV on 8-bit activations beside the fp16-activation one.", "", "Command:", "", "```", cmd, "```", "",
+             "their unfused steps beside them; the GEMV on 8-bit activations beside the fp16-activation one;",
+             "plain 2-bit weights (q2w) beside Q4_0.", "", "Command:", "", "```", cmd, "```", "",
              "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
     for r in rows:
         lines.append(f"| `{r['Name'][:80]}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | "
@@ -143,6 +144,9 @@ def suite(stats_csv, suite_jsonl, out_md, cmd):
     for r in recs:
         if r["kind"] == "gemv":
             lines.append(f"| GEMV {r['fmt']} {r['N']}x{r['K']} M={r['M']} | {r['us_median']} | {r['GBps']} GB/s |")
+        elif r["kind"] == "q2w":
+            lines.append(f"| GEMV q2w (2-bit) {r['N']}x{r['K']} M={r['M']} | {r['us_median']} "
+                         f"(Q4_0 {r['q4_0_us_median']}) | {r['GBps']} GB/s |")
         elif r["kind"] == "q8act":
             lines.append(f"| GEMV {r['fmt']} 8-bit activations {r['N']}x{r['K']} M={r['M']} | {r['us_median']} "
                          f"(fp16 activations {r['fp16_activations_us_median']}) | {r['GBps']} GB/s |")

@@ -13,7 +13,7 @@ import pytest
 import oracle
 import seeded_inputs as si
 
-Q4_0, Q8_0 = 0, 1
+Q4_0, Q8_0, Q2W = 0, 1, 2
 REL, ABS = 1e-3, 1e-6
 
 
@@ -33,7 +33,7 @@ def qg():
 def pack_both(fmt: int, w: np.ndarray):
     """(library bytes, oracle bytes) for the same weights; asserts equality."""
     q = qg()
-    pb = q.qquantize_q4_0(w) if fmt == Q4_0 else q.qquantize_q8_0(w)
+    pb = {Q4_0: q.qquantize_q4_0, Q8_0: q.qquantize_q8_0, Q2W: q.qquantize_q2w}[fmt](w)
     po = oracle.get().quantize(fmt, w)
     assert pb.size == po.size and np.array_equal(pb, po), "library packer differs from the oracle packer"
     return pb, po

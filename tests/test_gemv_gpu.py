@@ -9,17 +9,28 @@ import pytest
 
 import oracle
 import seeded_inputs as si
-from gpu_util import Q4_0, Q8_0, acts, assert_within, pack_both, qg, sample_rows, to_dev, torch_cuda, weights
+from gpu_util import Q2W, Q4_0, Q8_0, acts, assert_within, pack_both, qg, sample_rows, to_dev, torch_cuda, weights
 
 pytestmark = pytest.mark.gpu
 
-FMTS = [Q4_0, Q8_0]
-FNAME = {Q4_0: "q4_0", Q8_0: "q8_0"}
+FMTS = [Q4_0, Q8_0, Q2W]
+FNAME = {Q4_0: "q4_0", Q8_0: "q8_0", Q2W: "q2w"}
+CODE_BYTES = {Q4_0: 16, Q8_0: 32, Q2W: 8}
+
+
+def _gemv_fn(fmt):
+    q = qg()
+    return {Q4_0: q.qgemv_q4_0, Q8_0: q.qgemv_q8_0, Q2W: q.qgemv_q2w}[fmt]
+
+
+def _dequant_fn(fmt):
+    q = qg()
+    return {Q4_0: q.qdequant_q4_0, Q8_0: q.qdequant_q8_0, Q2W: q.qdequant_q2w}[fmt]
 
 
 def _gemv(fmt, Wd, xd, N, K):
     q = qg()
-    y = (q.qgemv_q4_0 if fmt == Q4_0 else q.qgemv_q8_0)(Wd, xd, N, K)
+    y = _gemv_fn(fmt)(Wd, xd, N, K)
     torch_cuda().cuda.synchronize()
     return y.cpu().numpy()
 
@@ -38,7 +49,7 @@ def test_dequant_bit_exact(fmt, N, K):
     w = weights(N, K, seed=N + K)
     pb, po = pack_both(fmt, w)
     Wd = to_dev(pb)
-    deq = q.qdequant_q4_0 if fmt == Q4_0 else q.qdequant_q8_0
+    deq = _dequant_fn(fmt)
     f32 = deq(Wd, N, K, fp16=False)
     f16 = deq(Wd, N, K, fp16=True)
     torch.cuda.synchronize()
@@ -52,7 +63,7 @@ def test_dequant_bit_exact(fmt, N, K):
 @pytest.mark.parametrize("N,K", SMALL_SHAPES)
 def test_gemv_small_parity(fmt, M, N, K):
     q = qg()
-    limit = 16384 * min(8 // M, 7 if fmt == Q4_0 else 4)
+    limit = 16384 * min(8 // M, 4 if fmt == Q8_0 else 7)
     w = weights(N, K, seed=3 * N + K)
     x = acts(M, K, seed=M + K)
     pb, po = pack_both(fmt, w)
@@ -88,6 +99,21 @@ def test_gemv_q4_0_llama3_8b_full_size(N, K):
     rows = sample_rows(N)
     y_ref, s = oracle.get().gemv_rows(Q4_0, po, N, K, x, rows)
     assert_within(y[:, rows], y_ref, s, f"{N}x{K}")
+    assert np.isfinite(y).all()
+
+
+@pytest.mark.parametrize("N,K", si.LLAMA3_8B_SHAPES)
+def test_gemv_q2w_llama3_8b_full_size(N, K):
+    """Plain 2-bit weights on the full-size Llama-3-8B shapes at one token,
+    checked on sampled rows."""
+    w = si.weights(N, K, seed=0)
+    x = si.activations(1, K, seed=0)
+    pb, po = pack_both(Q2W, w)
+    del w
+    y = _gemv(Q2W, to_dev(pb), to_dev(x), N, K)
+    rows = sample_rows(N)
+    y_ref, s = oracle.get().gemv_rows(Q2W, po, N, K, x, rows)
+    assert_within(y[:, rows], y_ref, s, f"q2w {N}x{K}")
     assert np.isfinite(y).all()
 
 
@@ -159,7 +185,7 @@ def test_outliers_on_zero_weights(fmt, K):
     Wd, xd = to_dev(pb), to_dev(x)
     y_ref, s = oracle.get().gemv(fmt, po, N, K, x)
     try:
-        for engine in (-1, 0, 1):
+        for engine in ((-1, 0) if fmt == Q2W else (-1, 0, 1)):
             q.qg_set_gemv_shape(0, 0, 0, 0, 0, -1, engine, 0)
             for m in (1, 2, M):
                 if engine == 1 and m < 2:
@@ -201,7 +227,7 @@ def test_deterministic_and_copy_invariant(fmt):
     A, B = to_dev(pb), to_dev(pb)
     xd = to_dev(x)
     q = qg()
-    f = q.qgemv_q4_0 if fmt == Q4_0 else q.qgemv_q8_0
+    f = _gemv_fn(fmt)
     ys = [f(A, xd, N, K), f(B, xd, N, K), f(A, xd, N, K)]
     torch.cuda.synchronize()
     assert torch.equal(ys[0], ys[1]) and torch.equal(ys[0], ys[2])
@@ -221,7 +247,7 @@ def test_sabotaged_weights_fail_every_check(fmt):
         pb, po = pack_both(fmt, w)
         bad = pb.copy()
         nb = N * K // 32
-        cb = 16 if fmt == Q4_0 else 32
+        cb = CODE_BYTES[fmt]
         bad[:nb * cb] ^= 0x11
         s0 = (nb * cb + 255) // 256 * 256
         bad[s0 + 1:s0 + 2 * nb:2] ^= 0x80
@@ -229,7 +255,7 @@ def test_sabotaged_weights_fail_every_check(fmt):
         y_ref, s = o.gemv(fmt, po, N, K, x)
         checks += 1
         failed += int(not oracle.within_bound(y, y_ref, s).all())
-        deq = (qg().qdequant_q4_0 if fmt == Q4_0 else qg().qdequant_q8_0)(to_dev(bad), N, K)
+        deq = _dequant_fn(fmt)(to_dev(bad), N, K)
         torch.cuda.synchronize()
         checks += 1
         failed += int(not np.array_equal(deq.cpu().numpy(), o.dequant(fmt, po, N, K, "f32")))
@@ -268,7 +294,7 @@ def test_outputs_stay_in_bounds():
             x = to_dev(acts(M, K, seed=1))
             buf = torch.full((M * N + 128,), 7.0, dtype=torch.float32, device="cuda")
             y = buf[64:64 + M * N].view(M, N)
-            (q.qgemv_q4_0 if fmt == Q4_0 else q.qgemv_q8_0)(to_dev(pb), x, N, K, y)
+            _gemv_fn(fmt)(to_dev(pb), x, N, K, y)
             torch.cuda.synchronize()
             assert (buf[:64] == 7.0).all() and (buf[64 + M * N:] == 7.0).all()
 
@@ -319,6 +345,14 @@ def test_gemv_matrix_core_engine(fmt, N, K, M):
     x = acts(M, K, seed=K + 1)
     pb, po = pack_both(fmt, w)
     Wd, xd = to_dev(pb), to_dev(x)
+    if fmt == Q2W:   # the matrix-core kernel takes Q4_0 and Q8_0 only
+        try:
+            q.qg_set_gemv_shape(0, 0, 0, 0, 0, -1, 1, 0)
+            with pytest.raises(q.QGError):
+                _gemv(fmt, Wd, xd, N, K)
+        finally:
+            q.qg_set_gemv_shape(0, 0, 0, 0, 0, -1, -1, 0)
+        return
     y_ref, s = oracle.get().gemv(fmt, po, N, K, x)
     tried = 0
     try:
@@ -343,3 +377,20 @@ def test_gemv_matrix_core_engine(fmt, N, K, M):
     finally:
         q.qg_set_gemv_shape(0, 0, 0, 0, 0, -1, -1, 0)
     assert tried >= 2   # long rows admit only the larger wave counts (<= 32 blocks per wave)
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FNAME[f])
+def test_prepared_call_matches_direct_call(fmt):
+    """The pre-validated launch object calls the entry point of its format."""
+    q = qg()
+    torch = torch_cuda()
+    N, K, M = 300, 2560, 2
+    pb, po = pack_both(fmt, weights(N, K, seed=8))
+    Wd, xd = to_dev(pb), to_dev(acts(M, K, seed=8))
+    y1 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    q.PreparedGemv(fmt, Wd, xd, y1, N, K)()
+    y2 = _gemv_fn(fmt)(Wd, xd, N, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(y1.cpu().numpy().view(np.uint32), y2.cpu().numpy().view(np.uint32))
+    y_ref, s = oracle.get().gemv(fmt, po, N, K, acts(M, K, seed=8))
+    assert_within(y1.cpu().numpy(), y_ref, s, f"prepared {FNAME[fmt]}")

@@ -48,7 +48,11 @@ def test_status_strings():
         assert L.qg_status_str(st)
 
 
-@pytest.mark.parametrize("fmt", [0, 1])
+def _quantize_fn(q, fmt):
+    return {0: q.qquantize_q4_0, 1: q.qquantize_q8_0, 2: q.qquantize_q2w}[fmt]
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
 @pytest.mark.parametrize("N,K", [(1, 32), (3, 96), (17, 640), (64, 2560), (33, 4096), (8, 14336)])
 def test_host_packer_matches_oracle(fmt, N, K):
     q = _qg()
@@ -57,7 +61,8 @@ def test_host_packer_matches_oracle(fmt, N, K):
         w[1, :32] = 0.0                                   # zero block
         w[2, :] *= np.float32(1e-5)                       # subnormal scales
         w[0, :32] = (np.arange(32) - 14).astype(np.float32) * np.float32(2.0 ** -8)   # exact ties
-    pb = (q.qquantize_q4_0 if fmt == 0 else q.qquantize_q8_0)(w)
+        w[2, 32:64] = -w[0, :32]                          # the extreme weight of either sign
+    pb = _quantize_fn(q, fmt)(w)
     po = oracle.get().quantize(fmt, w)
     assert q.packed_bytes(fmt, N, K) == oracle.get().packed_bytes(fmt, N, K) == pb.size
     assert np.array_equal(pb, po)
@@ -67,12 +72,12 @@ def test_host_packer_golden_blocks():
     """The library packer reproduces the hand-derived worked blocks."""
     import oracle_pins as pins
     q = _qg()
-    for name in ("q4_0_we1.txt", "q8_0_we2.txt", "q4_0_we3_subnormal.txt"):
+    for name in ("q4_0_we1.txt", "q8_0_we2.txt", "q4_0_we3_subnormal.txt", "q2w_we6.txt"):
         g = pins.load_golden(name)
         w = pins._golden_weights(g)
-        fmt = 0 if g["format"] == "q4_0" else 1
-        p = (q.qquantize_q4_0 if fmt == 0 else q.qquantize_q8_0)(w)
-        nb = 16 if fmt == 0 else 32
+        fmt = {"q4_0": 0, "q8_0": 1, "q2w": 2}[g["format"]]
+        p = _quantize_fn(q, fmt)(w)
+        nb = {0: 16, 1: 32, 2: 8}[fmt]
         assert bytes(p[:nb]) == bytes.fromhex("".join(g["code_bytes"].split())), name
         assert int(p[256]) | (int(p[257]) << 8) == int(g["scale_bits"], 16), name
 
@@ -88,7 +93,10 @@ def test_host_packer_errors():
         q.qquantize_q8_0(np.full((1, 32), 1e9, np.float32))
     with pytest.raises(q.QGError):
         q.qquantize_q4_0(np.zeros((2, 40), np.float32))
-    assert q.qpacked_bytes_q4_0(4, 48) == 0 and q.qpacked_bytes_q8_0(0, 64) == 0
+    assert q.qpacked_bytes_q4_0(4, 48) == 0 and q.qpacked_bytes_q8_0(0, 64) == 0 and q.qpacked_bytes_q2w(4, 48) == 0
+    with pytest.raises(q.QGError) as e:
+        q.qquantize_q2w(np.full((1, 32), np.inf, np.float32))
+    assert e.value.status == 4
     small = np.empty(10, np.uint8)
     with pytest.raises(ValueError):
         q.qquantize_q4_0(np.zeros((1, 32), np.float32), out=small)
