@@ -57,6 +57,8 @@ class Oracle:
             if path != _LIB:
                 raise FileNotFoundError(path)
             build()
+        elif path == _LIB and os.path.getmtime(_SRC) > os.path.getmtime(_LIB):
+            build()   # the source changed since the library was built
         L = ctypes.CDLL(path)
         self._L = L
         u8p, u16p, f32p, f64p = (ctypes.POINTER(t) for t in
@@ -94,7 +96,7 @@ class Oracle:
         L.orc_quantize_act8.restype = None
         L.orc_quantize_act8.argtypes = [u16p, i64, i64, i8p, f32p]
         L.orc_gemv_q8act.restype = None
-        L.orc_gemv_q8act.argtypes = [u8p, i64, i64, i8p, f32p, i64, f64p, f64p]
+        L.orc_gemv_q8act.argtypes = [ctypes.c_int, u8p, i64, i64, i8p, f32p, i64, f64p, f64p]
 
     # -- helpers ---------------------------------------------------------
     @staticmethod
@@ -243,8 +245,9 @@ class Oracle:
                                   self._p(dx, ctypes.c_float))
         return qx, dx
 
-    def gemv_q8act_codes(self, packed: np.ndarray, N: int, K: int, qx: np.ndarray, dx: np.ndarray):
-        """(y, s) of Q4_0 weights against given 8-bit activations (qx, dx)."""
+    def gemv_q8act_codes(self, packed: np.ndarray, N: int, K: int, qx: np.ndarray, dx: np.ndarray,
+                         fmt: int = Q4_0):
+        """(y, s) of Q4_0 (or q2w) weights against given 8-bit activations (qx, dx)."""
         packed = np.ascontiguousarray(packed, dtype=np.uint8)
         qx = np.ascontiguousarray(qx, dtype=np.int8)
         dx = np.ascontiguousarray(dx, dtype=np.float32)
@@ -252,15 +255,16 @@ class Oracle:
         assert qx.shape == (M, K) and dx.shape == (M, K // 32)
         y = np.empty((M, N), np.float64)
         s = np.empty((M, N), np.float64)
-        self._L.orc_gemv_q8act(self._p(packed, ctypes.c_uint8), N, K, self._p(qx, ctypes.c_int8),
+        assert fmt in (Q4_0, Q2W)
+        self._L.orc_gemv_q8act(fmt, self._p(packed, ctypes.c_uint8), N, K, self._p(qx, ctypes.c_int8),
                                self._p(dx, ctypes.c_float), M, self._p(y, ctypes.c_double),
                                self._p(s, ctypes.c_double))
         return y, s
 
-    def gemv_q8act(self, packed: np.ndarray, N: int, K: int, x: np.ndarray):
+    def gemv_q8act(self, packed: np.ndarray, N: int, K: int, x: np.ndarray, fmt: int = Q4_0):
         """(y, s): the activations quantized to 8-bit blocks, then the GEMV."""
         qx, dx = self.quantize_act8(x)
-        return self.gemv_q8act_codes(packed, N, K, qx, dx)
+        return self.gemv_q8act_codes(packed, N, K, qx, dx, fmt)
 
 
 def within_bound(y, y_ref, s, rel: float = 1e-3, abs_: float = 1e-6):

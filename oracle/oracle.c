@@ -496,14 +496,16 @@ void orc_quantize_act8(const uint16_t *x, int64_t M, int64_t K, int8_t *qx, floa
         }
 }
 
-/* Q4_0 weights against 8-bit activations (qx, dx from orc_quantize_act8):
- *   y[m][n] = sum_b dw[n][b] * dx[m][b] * sum_k (q - 8) * qx   (fp64)
- *   s[m][n] = sum_b |dw dx| * sum_k |(q - 8) qx|
+/* Q4_0 (or q2w) weights against 8-bit activations (qx, dx from
+ * orc_quantize_act8):
+ *   y[m][n] = sum_b dw[n][b] * dx[m][b] * sum_k c_k * qx_k   (fp64)
+ *   s[m][n] = sum_b |dw dx| * sum_k |c_k qx_k|
+ * with c the signed multiplier of the weight format (q - 8, or u - 2).
  * The integer sums are exact; the products of the three factors are exact
  * in fp64 (11 + 24 + 16 significant bits), so y is the exact value up to
  * the fp64 rounding of the sum over blocks. */
-void orc_gemv_q8act(const uint8_t *p, int64_t N, int64_t K, const int8_t *qx, const float *dx, int64_t M,
-                    double *y, double *s)
+void orc_gemv_q8act(int fmt, const uint8_t *p, int64_t N, int64_t K, const int8_t *qx, const float *dx,
+                    int64_t M, double *y, double *s)
 {
     const int64_t KB = K / 32;
     for (int64_t m = 0; m < M; ++m) {
@@ -512,7 +514,7 @@ void orc_gemv_q8act(const uint8_t *p, int64_t N, int64_t K, const int8_t *qx, co
             double acc = 0.0, sabs = 0.0;
             for (int64_t b = 0; b < KB; ++b) {
                 size_t i = (size_t)(n * KB + b);
-                double dw = scale_value(ORC_Q4_0, p, N, K, i);
+                double dw = scale_value(fmt, p, N, K, i);
 #if defined(ORC_PLANT_ACTSCALE)
                 double d = (double)dx[m * KB + (b + 1) % KB];
 #else
@@ -520,7 +522,7 @@ void orc_gemv_q8act(const uint8_t *p, int64_t N, int64_t K, const int8_t *qx, co
 #endif
                 int64_t isum = 0, iabs = 0;
                 for (int k = 0; k < 32; ++k) {
-                    int64_t t = (int64_t)code_value(ORC_Q4_0, p, i, k) * (int64_t)qx[m * K + b * 32 + k];
+                    int64_t t = (int64_t)code_value(fmt, p, i, k) * (int64_t)qx[m * K + b * 32 + k];
                     isum += t;
                     iabs += t < 0 ? -t : t;
                 }

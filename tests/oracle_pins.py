@@ -510,23 +510,27 @@ def pin_act8(orc) -> list:
     if (err > 0.5 * d.astype(np.float64)[..., None] * (1 + 1e-5)).any():
         fails.append("act8: reconstruction error above half a step")
     # the GEMV on the codes equals numpy's fp64 matmul of the exactly
-    # dequantized weights with the dequantized activations qx * dx
+    # dequantized weights (Q4_0 and q2w) with the dequantized activations
     N, K, M = 9, 160, 3
-    p = orc.quantize(Q4_0, si.weights(N, K, seed=41))
     xa = (rng.standard_normal((M, K)) * 2).astype(np.float16)
     q, d = orc.quantize_act8(xa)
-    y, s_ = orc.gemv_q8act_codes(p, N, K, q, d)
-    W = orc.dequant(Q4_0, p, N, K, "f64")
     A = q.astype(np.float64) * np.repeat(d.astype(np.float64), 32, axis=1)
-    yr = A @ W.T
-    sr = np.abs(A) @ np.abs(W).T
-    if not (np.abs(y - yr) <= 1e-12 * sr).all():
-        fails.append("act8 GEMV differs from the matmul of dequantized weights and activations")
-    if not (np.abs(s_ - sr) <= 1e-12 * sr).all():
-        fails.append("act8 GEMV: sum |w x| differs from the matmul of the absolute values")
-    y2, _ = orc.gemv_q8act(p, N, K, xa)
-    if not np.array_equal(y, y2):
-        fails.append("act8: gemv_q8act is not quantize_act8 then the GEMV on the codes")
+    for fmt in (Q4_0, Q2W):
+        p = orc.quantize(fmt, si.weights(N, K, seed=41))
+        y, s_ = orc.gemv_q8act_codes(p, N, K, q, d, fmt)
+        W = orc.dequant(fmt, p, N, K, "f64")
+        yr = A @ W.T
+        sr = np.abs(A) @ np.abs(W).T
+        if not (np.abs(y - yr) <= 1e-12 * sr).all():
+            fails.append(f"act8 GEMV (fmt {fmt}) differs from the matmul of dequantized weights and activations")
+        if not (np.abs(s_ - sr) <= 1e-12 * sr).all():
+            fails.append(f"act8 GEMV (fmt {fmt}): sum |w x| differs from the matmul of the absolute values")
+        y2, _ = orc.gemv_q8act(p, N, K, xa, fmt)
+        if not np.array_equal(y, y2):
+            fails.append("act8: gemv_q8act is not quantize_act8 then the GEMV on the codes")
+    p = orc.quantize(Q4_0, si.weights(N, K, seed=41))
+    y, _ = orc.gemv_q8act(p, N, K, xa)
+    W = orc.dequant(Q4_0, p, N, K, "f64")
     # within the activation rounding of the exact fp16 GEMV
     ye, _ = orc.gemv(Q4_0, p, N, K, xa)
     bound = np.abs(W) @ (0.5 * np.repeat(d.astype(np.float64), 32, axis=1) * (1 + 1e-5)).T
