@@ -282,6 +282,10 @@ def suite(qg, torch, reps: int):
         y = torch.empty((M, N), dtype=torch.float32, device="cuda")
         calls = [qg.PreparedGemv(qg.Q2W, buf[c * nb:(c + 1) * nb], x, y, N, K) for c in range(copies)]
         med, mean = _time_calls(qg, torch, calls, reps)
+        i8med = None
+        if M <= 4:   # the same weights against activations quantized to 8-bit blocks
+            c8 = [lambda c=c: qg.qgemv_q2w_q8act(buf[c * nb:(c + 1) * nb], x, N, K, y) for c in range(copies)]
+            i8med, _ = _time_calls(qg, torch, c8, reps)
         del buf
         buf4, nb4, copies4 = _copies(torch, qg.qquantize_q4_0(w))
         del w
@@ -291,7 +295,8 @@ def suite(qg, torch, reps: int):
         b = N * K // 32 * 10 + 2 * M * K + 4 * M * N
         rec(kind="q2w", fmt="q2w", N=N, K=K, M=M, us_median=round(med, 3), us_mean=round(mean, 3),
             GBps=round(b / med / 1e3, 1), pct_of_8TBps=round(b / med / 1e3 / 80, 2), algorithmic_bytes=b,
-            q4_0_us_median=round(med4, 3), copies=copies)
+            q4_0_us_median=round(med4, 3),
+            int8_activations_us_median=None if i8med is None else round(i8med, 3), copies=copies)
 
     # activations quantized to 8-bit blocks inside the launch (int8 dot
     # products), beside the fp16-activation GEMV on the same weights

@@ -181,6 +181,15 @@ qg_status qgemv_q4_0_swiglu_f32in(const void *Wp, const float *x, float *y, int 
 qg_status qgemv_q4_0_q8act(const void *Wp, const uint16_t *x, float *y, int M, int64_t N, int64_t K,
                            void *stream);
 
+/* The same on plain 2-bit weights (q2w): y[m][n] = sum_b d dx sum c * qx,
+ * the 2-bit codes used directly as int8 operands (mask 0x03030303 per bit
+ * pair, four weights per dot instruction) with the -2 * sum(qx) offset; the
+ * same limits and accuracy statement.  [volta-kernel-bakeoff, "Results",
+ * the 2-bit bullet: a plain 2-bit format multiplied against activations
+ * converted to 8-bit integers once, four weights per instruction] */
+qg_status qgemv_q2w_q8act(const void *Wp, const uint16_t *x, float *y, int M, int64_t N, int64_t K,
+                          void *stream);
+
 /* Mixture-of-experts GEMV in one launch, Q4_0: expert slot e (0 <= e < E)
  * multiplies pool matrix idx[e] by its own token x[e]:
  *   y[e][n] = sum_k w_{idx[e]}[n][k] * x[e][k]

@@ -62,6 +62,7 @@ def lib() -> ctypes.CDLL:
         "qpacked_bytes_q2w": (sz, [i64, i64]),
         "qquantize_q2w": (c_int, [vp, i64, i64, vp, sz]),
         "qgemv_q2w": (c_int, [vp, vp, vp, c_int, i64, i64, vp]),
+        "qgemv_q2w_q8act": (c_int, [vp, vp, vp, c_int, i64, i64, vp]),
         "qdequant_q2w": (c_int, [vp, i64, i64, c_int, vp, vp]),
         "qgemv_q4_0": (c_int, [vp, vp, vp, c_int, i64, i64, vp]),
         "qgemv_q8_0": (c_int, [vp, vp, vp, c_int, i64, i64, vp]),
@@ -91,7 +92,7 @@ def exported_symbols() -> list[str]:
             "qgemv_q4_0", "qgemv_q8_0", "qgemv_q4_0_f32in", "qgemv_q4_0_swiglu_f32in", "qgemv_q4_0_q8act",
             "qmoe_gemv_q4_0",
             "qgemm_q4_0_prefill", "qdequant_q4_0",
-            "qdequant_q8_0", "qpacked_bytes_q2w", "qquantize_q2w", "qgemv_q2w", "qdequant_q2w",
+            "qdequant_q8_0", "qpacked_bytes_q2w", "qquantize_q2w", "qgemv_q2w", "qgemv_q2w_q8act", "qdequant_q2w",
             "qg_time_next_launch", "qg_device_cus", "qg_set_gemv_shape", "qg_read_probe", "qg_set_prefill_shape"]
 
 
@@ -231,6 +232,12 @@ def qgemv_q8_0(Wp, x, N: int, K: int, y=None):
 def qgemv_q2w(Wp, x, N: int, K: int, y=None):
     """y[M][N] (fp32) = dequant(Wp) @ x[M][K]^T; Wp uint8 packed q2w, x fp16, 1 <= M <= 8."""
     return _gemv("qgemv_q2w", Q2W, Wp, x, N, K, y)
+
+
+def qgemv_q2w_q8act(Wp, x, N: int, K: int, y=None):
+    """y[M][N] = q2w weights times fp16 x quantized to 8-bit blocks inside the
+    launch (int8 dot products); 1 <= M <= 4."""
+    return _gemv("qgemv_q2w_q8act", Q2W, Wp, x, N, K, y)
 
 
 def qgemv_q4_0_q8act(Wp, x, N: int, K: int, y=None):

@@ -456,6 +456,11 @@ qg_status qgemv_q2w(const void *Wp, const uint16_t *x, float *y, int M, int64_t 
     return qg::run_gemv(qg::kQ2W, Wp, nullptr, 1, x, y, M, 1, N, K, stream);
 }
 
+qg_status qgemv_q2w_q8act(const void *Wp, const uint16_t *x, float *y, int M, int64_t N, int64_t K, void *stream)
+{
+    return qg::run_gemv(qg::kQ2W, Wp, nullptr, 1, x, y, M, 1, N, K, stream, qg::kModeQ8Act);
+}
+
 qg_status qdequant_q2w(const void *Wp, int64_t N, int64_t K, int out_fp16, void *out, void *stream)
 {
     return qg::run_dequant(qg::kQ2W, Wp, N, K, out_fp16, out, stream);

@@ -418,21 +418,38 @@ __device__ __forceinline__ void compute_group(const Group<FMT, J, R> &g,
 #pragma unroll
             for (int i = 0; i < R; ++i) {
                 const float d = (float)__builtin_bit_cast(_Float16, g.scale[i][j]);
-                const uint32_t w[4] = {g.code[i][j].c.x, g.code[i][j].c.y, g.code[i][j].c.z, g.code[i][j].c.w};
-                uint32_t lo[4], hi[4];   // word t: elements 4t..4t+3 / 16+4t..19+4t
+                // the unsigned codes as int8 operands, each word paired with
+                // the activation word of the same four elements
+                uint32_t ops[8];
+                int qi[8];
+                if constexpr (FMT == kQ2W) {
+                    // word h, bit pair r: elements 4h + 8r .. 4h + 8r + 3
+                    const uint32_t w[2] = {g.code[i][j].c.x, g.code[i][j].c.y};
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    lo[t] = w[t] & 0x0F0F0F0Fu;
-                    hi[t] = (w[t] >> 4) & 0x0F0F0F0Fu;
+                    for (int h = 0; h < 2; ++h)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            ops[4 * h + r] = (w[h] >> (2 * r)) & 0x03030303u;
+                            qi[4 * h + r] = 2 * r + h;
+                        }
+                } else {
+                    // word t: elements 4t..4t+3 (low nibbles), 16+4t..19+4t (high)
+                    const uint32_t w[4] = {g.code[i][j].c.x, g.code[i][j].c.y, g.code[i][j].c.z,
+                                           g.code[i][j].c.w};
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        ops[2 * t] = w[t] & 0x0F0F0F0Fu;
+                        qi[2 * t] = t;
+                        ops[2 * t + 1] = (w[t] >> 4) & 0x0F0F0F0Fu;
+                        qi[2 * t + 1] = 4 + t;
+                    }
                 }
 #pragma unroll
                 for (int m = 0; m < M; ++m) {
                     int sum = bias[m];
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        sum = __builtin_amdgcn_sdot4((int)lo[t], (int)qw[m][t], sum, false);
-                        sum = __builtin_amdgcn_sdot4((int)hi[t], (int)qw[m][4 + t], sum, false);
-                    }
+                    for (int t = 0; t < 8; ++t)
+                        sum = __builtin_amdgcn_sdot4((int)ops[t], (int)qw[m][qi[t]], sum, false);
                     acc[i][m] = __builtin_fmaf(d, dxm[m] * (float)sum, acc[i][m]);
                 }
             }
@@ -612,7 +629,8 @@ template <int FMT, int M, int G, int J, int R, bool XL, int MODE>
 __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
 {
     static_assert(!XL || M <= 4, "LDS-staged activations: up to 4 tokens");
-    static_assert(MODE == kModeF16 || FMT == kQ4_0, "fp32 and 8-bit activations: Q4_0");
+    static_assert(MODE == kModeF16 || FMT == kQ4_0 || (MODE == kModeQ8Act && FMT == kQ2W),
+                  "fp32 activations: Q4_0; 8-bit activations: Q4_0 or q2w");
     static_assert(MODE != kModeQ8Act || XL, "8-bit activations are quantized into LDS");
     constexpr bool GLU = MODE == kModeGlu;
     static_assert(!GLU || R == 2, "SwiGLU: one gate and one up row set per group");
@@ -727,7 +745,9 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
             }
             xs_dyn[i * 3 + 0] = make_uint4(cw[0], cw[1], cw[2], cw[3]);
             xs_dyn[i * 3 + 1] = make_uint4(cw[4], cw[5], cw[6], cw[7]);
-            xs_dyn[i * 3 + 2] = make_uint4(__builtin_bit_cast(uint32_t, dq), (uint32_t)(-8 * qsum), 0u, 0u);
+            // the codes' offset times the activation sum: 8 (Q4_0) or 2 (q2w)
+            xs_dyn[i * 3 + 2] = make_uint4(__builtin_bit_cast(uint32_t, dq),
+                                           (uint32_t)(-(FMT == kQ2W ? 2 : 8) * qsum), 0u, 0u);
         }
         __syncthreads();
     } else if constexpr (XL) {
@@ -875,8 +895,8 @@ size_t gemv_xl_lds_bytes(int K, int M, int mode)
 hipError_t launch_gemv(int fmt, int M, int G, int J, int R, bool xl, int mode, const GemvParams &p, dim3 grid,
                        dim3 block, hipStream_t stream)
 {
-    // fp32 activations (and SwiGLU): Q4_0 only
-    if (mode != kModeF16 && fmt != kQ4_0)
+    // fp32 activations (and SwiGLU): Q4_0 only; 8-bit activations: Q4_0, q2w
+    if (mode != kModeF16 && fmt != kQ4_0 && !(mode == kModeQ8Act && fmt == kQ2W))
         return hipErrorInvalidValue;
     // XL: up to 4 tokens with whole rows per wave, activations staged in LDS
     // (per token K/32 blocks of 64 bytes plus a zero block)
@@ -893,6 +913,8 @@ hipError_t launch_gemv(int fmt, int M, int G, int J, int R, bool xl, int mode, c
     }
         if (mode == kModeF32) {
             QG_CASE_XL(kQ4_0, kModeF32)
+        } else if (mode == kModeQ8Act && fmt == kQ2W) {
+            QG_CASE_XL(kQ2W, kModeQ8Act)
         } else if (mode == kModeQ8Act) {
             QG_CASE_XL(kQ4_0, kModeQ8Act)
         } else if (mode == kModeGlu) {

@@ -107,7 +107,7 @@ constexpr bool gemv_fits(int fmt, int M, int G, int J, int R, bool xl, int mode 
         return false;
     if (xl && (G != 64 || M > 4))
         return false;
-    if (mode == kModeQ8Act && (!xl || fmt != kQ4_0))
+    if (mode == kModeQ8Act && (!xl || fmt == kQ8_0))
         return false;
     if (R * J > (fmt == kQ8_0 ? 4 : 8) || J > (xl ? 8 : 7) || (!xl && J * M > 8))
         return false;

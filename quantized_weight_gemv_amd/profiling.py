@@ -145,8 +145,10 @@ def suite(stats_csv, suite_jsonl, out_md, cmd):
         if r["kind"] == "gemv":
             lines.append(f"| GEMV {r['fmt']} {r['N']}x{r['K']} M={r['M']} | {r['us_median']} | {r['GBps']} GB/s |")
         elif r["kind"] == "q2w":
+            i8 = r.get("int8_activations_us_median")
+            i8s = f"; 8-bit activations {i8}" if i8 is not None else ""
             lines.append(f"| GEMV q2w (2-bit) {r['N']}x{r['K']} M={r['M']} | {r['us_median']} "
-                         f"(Q4_0 {r['q4_0_us_median']}) | {r['GBps']} GB/s |")
+                         f"(Q4_0 {r['q4_0_us_median']}{i8s}) | {r['GBps']} GB/s |")
         elif r["kind"] == "q8act":
             lines.append(f"| GEMV {r['fmt']} 8-bit activations {r['N']}x{r['K']} M={r['M']} | {r['us_median']} "
                          f"(fp16 activations {r['fp16_activations_us_median']}) | {r['GBps']} GB/s |")

@@ -6,14 +6,15 @@ import pytest
 
 import oracle
 import seeded_inputs as si
-from gpu_util import Q4_0, assert_within, pack_both, qg, to_dev, torch_cuda
+from gpu_util import Q2W, Q4_0, assert_within, pack_both, qg, to_dev, torch_cuda
 
 pytestmark = pytest.mark.gpu
 
 
-def _q8act(Wd, x16, N, K, y=None):
+def _q8act(Wd, x16, N, K, y=None, fmt=Q4_0):
     q = qg()
-    out = q.qgemv_q4_0_q8act(Wd, to_dev(x16) if isinstance(x16, np.ndarray) else x16, N, K, y)
+    f = q.qgemv_q4_0_q8act if fmt == Q4_0 else q.qgemv_q2w_q8act
+    out = f(Wd, to_dev(x16) if isinstance(x16, np.ndarray) else x16, N, K, y)
     torch_cuda().cuda.synchronize()
     return out.cpu().numpy()
 
@@ -33,16 +34,28 @@ def _acts(M, K, seed, planted=True):
     return x.astype(np.float16)
 
 
+@pytest.mark.parametrize("fmt", [Q4_0, Q2W], ids=["q4_0", "q2w"])
 @pytest.mark.parametrize("M,N,K", [(1, 17, 32), (1, 4096, 4096), (2, 130, 2048), (3, 4099, 640), (4, 1000, 4096),
                                    (1, 5, 14336), (2, 257, 16384), (4, 64, 8192), (1, 3, 16384)])
-def test_q8act_parity(M, N, K):
+def test_q8act_parity(fmt, M, N, K):
     w = si.weights(N, K, seed=M + N + 3)
     x = _acts(M, K, seed=K)
-    pb, po = pack_both(Q4_0, w)
-    y = _q8act(to_dev(pb), x, N, K)
-    y_ref, s = oracle.get().gemv_q8act(po, N, K, x)
-    assert_within(y, y_ref, s, f"q8act M={M} {N}x{K}")
+    pb, po = pack_both(fmt, w)
+    y = _q8act(to_dev(pb), x, N, K, fmt=fmt)
+    y_ref, s = oracle.get().gemv_q8act(po, N, K, x, fmt)
+    assert_within(y, y_ref, s, f"q8act fmt={fmt} M={M} {N}x{K}")
     # fp32 sums of exact block integers: far tighter than the bound
+    assert (np.abs(y - y_ref) <= 2e-5 * s + 1e-6).all()
+
+
+@pytest.mark.parametrize("N,K", si.LLAMA3_8B_SHAPES)
+def test_q2w_q8act_llama3_8b_full_size(N, K):
+    w = si.weights(N, K, seed=0)
+    x = si.activations(1, K, seed=0)
+    pb, po = pack_both(Q2W, w)
+    y = _q8act(to_dev(pb), x, N, K, fmt=Q2W)
+    y_ref, s = oracle.get().gemv_q8act(po, N, K, x, Q2W)
+    assert_within(y, y_ref, s, f"q2w q8act {N}x{K}")
     assert (np.abs(y - y_ref) <= 2e-5 * s + 1e-6).all()
 
 
@@ -99,15 +112,17 @@ def test_q8act_codes_bit_exact():
     assert (y[~nz] == 0).all() and (qx[~nz] == 0).all()
 
 
-def test_q8act_every_launch_shape():
+@pytest.mark.parametrize("fmt", [Q4_0, Q2W], ids=["q4_0", "q2w"])
+def test_q8act_every_launch_shape(fmt):
     q = qg()
     torch = torch_cuda()
+    f = q.qgemv_q4_0_q8act if fmt == Q4_0 else q.qgemv_q2w_q8act
     for (M, N, K) in [(1, 257, 4096), (2, 70, 6144), (3, 33, 2560), (4, 130, 2048)]:
         w = si.weights(N, K, seed=N)
         x = _acts(M, K, seed=K + 1)
-        pb, po = pack_both(Q4_0, w)
+        pb, po = pack_both(fmt, w)
         Wd, xd = to_dev(pb), to_dev(x)
-        y_ref, s = oracle.get().gemv_q8act(po, N, K, x)
+        y_ref, s = oracle.get().gemv_q8act(po, N, K, x, fmt)
         buf = torch.full((M * N + 128,), 7.0, dtype=torch.float32, device="cuda")
         yv = buf[64:64 + M * N].view(M, N)
         tried = set()
@@ -118,7 +133,7 @@ def test_q8act_every_launch_shape():
                         for xl in (-1, 0, 1):
                             q.qg_set_gemv_shape(J, R, 0, tpw, teams, xl, 0, 0)
                             try:
-                                q.qgemv_q4_0_q8act(Wd, xd, N, K, yv)
+                                f(Wd, xd, N, K, yv)
                             except q.QGError:
                                 assert xl != -1 or J or R, "the built-in choice must launch"
                                 continue
