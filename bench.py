@@ -286,6 +286,10 @@ def suite(qg, torch, reps: int):
         if M <= 4:   # the same weights against activations quantized to 8-bit blocks
             c8 = [lambda c=c: qg.qgemv_q2w_q8act(buf[c * nb:(c + 1) * nb], x, N, K, y) for c in range(copies)]
             i8med, _ = _time_calls(qg, torch, c8, reps)
+        lutmed = None
+        if M == 1 and K <= 4096:   # the same weights through per-pair lookup tables
+            cl = [lambda c=c: qg.qgemv_q2w_lut(buf[c * nb:(c + 1) * nb], x, N, K, y) for c in range(copies)]
+            lutmed, _ = _time_calls(qg, torch, cl, reps)
         del buf
         buf4, nb4, copies4 = _copies(torch, qg.qquantize_q4_0(w))
         del w
@@ -296,7 +300,8 @@ def suite(qg, torch, reps: int):
         rec(kind="q2w", fmt="q2w", N=N, K=K, M=M, us_median=round(med, 3), us_mean=round(mean, 3),
             GBps=round(b / med / 1e3, 1), pct_of_8TBps=round(b / med / 1e3 / 80, 2), algorithmic_bytes=b,
             q4_0_us_median=round(med4, 3),
-            int8_activations_us_median=None if i8med is None else round(i8med, 3), copies=copies)
+            int8_activations_us_median=None if i8med is None else round(i8med, 3),
+            lookup_table_us_median=None if lutmed is None else round(lutmed, 3), copies=copies)
 
     # activations quantized to 8-bit blocks inside the launch (int8 dot
     # products), beside the fp16-activation GEMV on the same weights

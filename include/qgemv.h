@@ -190,6 +190,21 @@ qg_status qgemv_q4_0_q8act(const void *Wp, const uint16_t *x, float *y, int M, i
 qg_status qgemv_q2w_q8act(const void *Wp, const uint16_t *x, float *y, int M, int64_t N, int64_t K,
                           void *stream);
 
+/* Times-table GEMV on q2w weights, one token: every pair of activations
+ * (x_a, x_b) gets the 16 sums c_a x_a + c_b x_b (c in -2..1) as fp16 in LDS,
+ * and the nibble holding a weight pair's two codes looks its sum up instead
+ * of multiplying.  y[n] = sum_b d * sum of the block's 16 looked-up pair sums.
+ * The fp16 entries round each pair sum, so y is within 2^-11 sum |w x| plus
+ * fp32 accumulation of the exact GEMV (inside 1e-3 sum |w x|).  x: fp16 bits
+ * [K] (16-byte aligned), |x| < 16384 (an entry reaches 2 |x_a| + 2 |x_b|;
+ * beyond binary16's range it becomes infinity); y: fp32 [N];
+ * 1 <= N <= 2^31 - 1, K % 32 == 0, K <= 4096 (the tables fill 64 KB of
+ * LDS).  Built to measure the design on gfx950, not as the fast path
+ * (qgemv_q2w and qgemv_q2w_q8act are faster).
+ * [volta-kernel-bakeoff, "What's in the race": q2_lut / q2w_lut, the "times
+ *  table"; "Results": it lost to unpacking on V100] */
+qg_status qgemv_q2w_lut(const void *Wp, const uint16_t *x, float *y, int64_t N, int64_t K, void *stream);
+
 /* Mixture-of-experts GEMV in one launch, Q4_0: expert slot e (0 <= e < E)
  * multiplies pool matrix idx[e] by its own token x[e]:
  *   y[e][n] = sum_k w_{idx[e]}[n][k] * x[e][k]

@@ -63,6 +63,7 @@ def lib() -> ctypes.CDLL:
         "qquantize_q2w": (c_int, [vp, i64, i64, vp, sz]),
         "qgemv_q2w": (c_int, [vp, vp, vp, c_int, i64, i64, vp]),
         "qgemv_q2w_q8act": (c_int, [vp, vp, vp, c_int, i64, i64, vp]),
+        "qgemv_q2w_lut": (c_int, [vp, vp, vp, i64, i64, vp]),
         "qdequant_q2w": (c_int, [vp, i64, i64, c_int, vp, vp]),
         "qgemv_q4_0": (c_int, [vp, vp, vp, c_int, i64, i64, vp]),
         "qgemv_q8_0": (c_int, [vp, vp, vp, c_int, i64, i64, vp]),
@@ -92,7 +93,7 @@ def exported_symbols() -> list[str]:
             "qgemv_q4_0", "qgemv_q8_0", "qgemv_q4_0_f32in", "qgemv_q4_0_swiglu_f32in", "qgemv_q4_0_q8act",
             "qmoe_gemv_q4_0",
             "qgemm_q4_0_prefill", "qdequant_q4_0",
-            "qdequant_q8_0", "qpacked_bytes_q2w", "qquantize_q2w", "qgemv_q2w", "qgemv_q2w_q8act", "qdequant_q2w",
+            "qdequant_q8_0", "qpacked_bytes_q2w", "qquantize_q2w", "qgemv_q2w", "qgemv_q2w_q8act", "qgemv_q2w_lut", "qdequant_q2w",
             "qg_time_next_launch", "qg_device_cus", "qg_set_gemv_shape", "qg_read_probe", "qg_set_prefill_shape"]
 
 
@@ -238,6 +239,21 @@ def qgemv_q2w_q8act(Wp, x, N: int, K: int, y=None):
     """y[M][N] = q2w weights times fp16 x quantized to 8-bit blocks inside the
     launch (int8 dot products); 1 <= M <= 4."""
     return _gemv("qgemv_q2w_q8act", Q2W, Wp, x, N, K, y)
+
+
+def qgemv_q2w_lut(Wp, x, N: int, K: int, y=None):
+    """y[1][N] = q2w weights times one fp16 token through per-pair lookup
+    tables in LDS (the times-table design); K <= 4096."""
+    torch = _torch()
+    if x.dim() != 2 or x.shape != (1, K):
+        raise ValueError(f"x must be [1][{K}]")
+    if y is None:
+        y = torch.empty((1, N), dtype=torch.float32, device=x.device)
+    wp = _dev(Wp, torch.uint8, "Wp", packed_bytes(Q2W, N, K))
+    xp = _dev(_x16(x), torch.int16, "x", K)
+    yp = _dev(y, torch.float32, "y", N)
+    _check("qgemv_q2w_lut", lib().qgemv_q2w_lut(wp, xp, yp, N, K, _stream()))
+    return y
 
 
 def qgemv_q4_0_q8act(Wp, x, N: int, K: int, y=None):

@@ -461,6 +461,25 @@ qg_status qgemv_q2w_q8act(const void *Wp, const uint16_t *x, float *y, int M, in
     return qg::run_gemv(qg::kQ2W, Wp, nullptr, 1, x, y, M, 1, N, K, stream, qg::kModeQ8Act);
 }
 
+qg_status qgemv_q2w_lut(const void *Wp, const uint16_t *x, float *y, int64_t N, int64_t K, void *stream)
+{
+    if (!Wp || !x || !y)
+        return QG_ERR_NULL;
+    if (N < 1 || N > INT32_MAX || K < 32 || K % 32 != 0 || qg::gemv_lut_lds_bytes(static_cast<int>(std::min<int64_t>(K, 1 << 20))) > 65536)
+        return QG_ERR_SHAPE;
+    if (!qg::aligned(Wp, 256) || !qg::aligned(x, 16) || !qg::aligned(y, 4))
+        return QG_ERR_ALIGN;
+    const int cus = qg::device_cus();
+    if (cus <= 0)
+        return QG_ERR_DEVICE;
+    hipError_t e = qg::launch_gemv_q2w_lut(static_cast<const uint8_t *>(Wp), qg::scale_offset(qg::kQ2W, N, K), x, y,
+                                           static_cast<int>(N), static_cast<int>(K), cus,
+                                           static_cast<hipStream_t>(stream));
+    if (e == hipErrorInvalidValue)
+        return QG_ERR_SHAPE;
+    return e == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
+}
+
 qg_status qdequant_q2w(const void *Wp, int64_t N, int64_t K, int out_fp16, void *out, void *stream)
 {
     return qg::run_dequant(qg::kQ2W, Wp, N, K, out_fp16, out, stream);

@@ -132,4 +132,11 @@ hipError_t launch_gemv(int fmt, int M, int G, int J, int R, bool xl, int mode, c
 hipError_t launch_gemv_mfma(int fmt, const uint8_t *W, int64_t scale_offset, const uint16_t *x, float *y, int M,
                             int N, int K, int waves, int64_t wgs, int cus, hipStream_t stream);
 
+// Times-table GEMV for q2w at one token (qgemv_lut.hip): LDS bytes of the
+// tables for rows of K weights (64 KB for 32 <= K <= 4096, else SIZE_MAX),
+// and the launcher (up to two workgroups per CU of `cus`).
+size_t gemv_lut_lds_bytes(int K);
+hipError_t launch_gemv_q2w_lut(const uint8_t *W, int64_t scale_offset, const uint16_t *x, float *y, int N, int K,
+                               int cus, hipStream_t stream);
+
 }  // namespace qg

@@ -133,7 +133,7 @@ def suite(stats_csv, suite_jsonl, out_md, cmd):
              "at 64 and 512 tokens", "on 12288x2560, 2560x6144, 6144x2048 with the dense fp16 GEMM on "
              "pre-dequantized weights beside it; fp32-activation GEMV and stacked gate+up+SwiGLU with",
              "their unfused steps beside them; the GEMV on 8-bit activations beside the fp16-activation one;",
-             "plain 2-bit weights (q2w) beside Q4_0.", "", "Command:", "", "```", cmd, "```", "",
+             "plain 2-bit weights (q2w) beside Q4_0, with 8-bit activations and through lookup tables.", "", "Command:", "", "```", cmd, "```", "",
              "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
     for r in rows:
         lines.append(f"| `{r['Name'][:80]}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | "
@@ -147,8 +147,10 @@ def suite(stats_csv, suite_jsonl, out_md, cmd):
         elif r["kind"] == "q2w":
             i8 = r.get("int8_activations_us_median")
             i8s = f"; 8-bit activations {i8}" if i8 is not None else ""
+            lt = r.get("lookup_table_us_median")
+            lts = f"; lookup tables {lt}" if lt is not None else ""
             lines.append(f"| GEMV q2w (2-bit) {r['N']}x{r['K']} M={r['M']} | {r['us_median']} "
-                         f"(Q4_0 {r['q4_0_us_median']}{i8s}) | {r['GBps']} GB/s |")
+                         f"(Q4_0 {r['q4_0_us_median']}{i8s}{lts}) | {r['GBps']} GB/s |")
         elif r["kind"] == "q8act":
             lines.append(f"| GEMV {r['fmt']} 8-bit activations {r['N']}x{r['K']} M={r['M']} | {r['us_median']} "
                          f"(fp16 activations {r['fp16_activations_us_median']}) | {r['GBps']} GB/s |")
