@@ -406,6 +406,9 @@ def main() -> int:
                     help="instead of the headline step, time every workload (GEMV both formats and M = 1..8, "
                          "MoE, prefill with its dense fp16 comparator) and write one JSON record per line to FILE")
     ap.add_argument("--reps", type=int, default=100)
+    ap.add_argument("--q2w-calls", type=int, nargs=3, default=None, metavar=("N", "K", "CALLS"),
+                    help="for counter passes: CALLS calls of the times-table kernel, then CALLS of the unpacking "
+                         "q2w kernel, on one seeded N x K q2w table at one token; prints nothing else")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the GEMV path runs on a single MI355X (no collectives); "
@@ -418,6 +421,17 @@ def main() -> int:
         return 2
     import quantized_weight_gemv_amd as qg
     qg.lib()
+
+    if args.q2w_calls:
+        N, K, calls = args.q2w_calls
+        W = torch.from_numpy(qg.qquantize_q2w(si.weights(N, K, seed=0))).to("cuda")
+        x = torch.from_numpy(si.activations(1, K, seed=0)).to("cuda")
+        y = torch.empty((1, N), dtype=torch.float32, device="cuda")
+        for fn in (qg.qgemv_q2w_lut, qg.qgemv_q2w):
+            for _ in range(calls):
+                fn(W, x, N, K, y)
+        torch.cuda.synchronize()
+        return 0
 
     if args.suite:
         recs = suite(qg, torch, args.reps)

@@ -172,6 +172,37 @@ def suite(stats_csv, suite_jsonl, out_md, cmd):
     print("\n".join(lines))
 
 
+def counters(title, out_md, stats_csv, stats_cmd, *pairs):
+    """Median of each rocprofv3 --pmc counter per kernel (per dispatch), next
+    to the kernel-trace statistics of the same program.  `pairs`: counter
+    CSV, command, counter CSV, command, ..."""
+    per = {}
+    cmds = [stats_cmd]
+    for csv_path, cmd in zip(pairs[0::2], pairs[1::2]):
+        cmds.append(cmd)
+        for r in csv.DictReader(open(csv_path)):
+            if "copyBuffer" in r["Kernel_Name"]:
+                continue
+            per.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    lines = [f"# rocprofv3 counters: {title}", "", "Commands (counter passes each in a run of their own):", "", "```"]
+    lines += cmds + ["```", "", "| kernel | calls | average ns |", "|---|---|---|"]
+    for r in csv.DictReader(open(stats_csv)):
+        if "copyBuffer" not in r["Name"]:
+            lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']):.0f} |")
+    names = sorted({c for d in per.values() for c in d})
+    lines += ["", "Median per dispatch:", "", "| counter | " + " | ".join(f"`{k[:60]}`" for k in per) + " |",
+              "|---|" + "---|" * len(per)]
+    for c in names:
+        vals = []
+        for d in per.values():
+            v = sorted(d.get(c, []))
+            vals.append(f"{v[len(v) // 2]:.4g}" if v else "")
+        lines.append(f"| {c} | " + " | ".join(vals) + " |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         stats(*sys.argv[2:6])
@@ -179,5 +210,7 @@ if __name__ == "__main__":
         traffic(*sys.argv[2:7])
     elif sys.argv[1] == "suite":
         suite(*sys.argv[2:6])
+    elif sys.argv[1] == "counters":
+        counters(*sys.argv[2:])
     else:
         raise SystemExit(__doc__)

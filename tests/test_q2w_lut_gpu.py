@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 import seeded_inputs as si
-from gpu_util import Q2W, assert_within, pack_both, qg, to_dev, torch_cuda
+from gpu_util import Q2W, assert_within, pack_both, qg, sample_rows, to_dev, torch_cuda
 
 pytestmark = pytest.mark.gpu
 
@@ -73,3 +73,34 @@ def test_q2w_lut_abi_errors():
     assert f(Wd.data_ptr(), None, y.data_ptr(), N, 256, s) == 1                 # NULL activations
     assert f(Wd.data_ptr(), x.data_ptr() + 2, y.data_ptr(), N, 256, s) == 3     # misaligned
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("N,K", [(N, K) for (N, K) in si.LLAMA3_8B_SHAPES if K <= 4096])
+def test_q2w_lut_llama3_8b_full_size(N, K):
+    """The Llama-3-8B shapes the tables fit (K <= 4096) at full size, in the
+    launch the suite times, checked on sampled rows; every output finite."""
+    w = si.weights(N, K, seed=0)
+    x = si.activations(1, K, seed=0)
+    pb, po = pack_both(Q2W, w)
+    del w
+    y = _lut(to_dev(pb), x, N, K)
+    rows = sample_rows(N)
+    y_ref, s = oracle.get().gemv_rows(Q2W, po, N, K, x, rows)
+    assert_within(y[:, rows], y_ref, s, f"q2w lut {N}x{K}")
+    assert np.isfinite(y).all()
+
+
+def test_q2w_lut_matches_unpacking_kernel_within_bound():
+    """Both 2-bit kernels on the same weights agree to the sum of their
+    bounds on every output of a 28672 x 4096 table (two passes, 512
+    workgroups), against the oracle's s."""
+    N, K = 28672, 4096
+    w = si.weights(N, K, seed=3)
+    x = si.activations(1, K, seed=3)
+    pb, po = pack_both(Q2W, w)
+    del w
+    Wd = to_dev(pb)
+    y_lut = _lut(Wd, x, N, K)
+    y_unp = qg().qgemv_q2w(Wd, to_dev(x), N, K).cpu().numpy()
+    _, s = oracle.get().gemv_rows(Q2W, po, N, K, x, np.arange(N))
+    assert (np.abs(y_lut.astype(np.float64) - y_unp) <= 2e-3 * s + 2e-6).all()
