@@ -45,7 +45,10 @@
  *     partial sums of the result's own terms: their rounding stays far
  *     inside 1e-3 * sum |w x| for every finite input, and a one-hot
  *     activation returns a weight column exactly.  A block with a non-finite
- *     scale makes its row non-finite (inf or NaN).
+ *     scale makes its row non-finite (inf or NaN).  Exceptions, each stated
+ *     at its entry point: the fp32-input variants round x to binary16 first,
+ *     the 8-bit-activation variants quantize x to 8-bit blocks first, and
+ *     the times-table GEMV rounds its pair sums to binary16.
  *   - The GEMV / MoE kernels use no atomics: for a fixed shape and launch
  *     their results are bitwise reproducible.  The prefill adds split-K
  *     partial tiles atomically (last-bit differences between runs).
@@ -256,12 +259,13 @@ qg_status qg_device_cus(int device, int *cus);
  * number of teams, xl (activations of 1-4 tokens staged once per workgroup
  * in LDS, whole rows per wave: 1; kept in each lane's registers: 0), engine
  * (vector-ALU kernel: 0; matrix-core kernel for 2..8 tokens and rows of at
- * most 256 blocks: 1, where ksplit is its number of waves along K and teams
- * its number of persistent workgroups) and lanes_per_row (lanes of a wave
- * that share one row in the vector-ALU kernel: 16, 32 or 64; below 64 one
- * token only) for later calls from the calling thread.  A zero (-1 for xl and engine) keeps
- * the built-in per-shape choice for that field.  An impossible combination
- * makes the later calls return QG_ERR_SHAPE. */
+ * most 256 blocks, for q2w an even number: 1, where ksplit is its number of
+ * waves along K and teams its number of persistent workgroups) and
+ * lanes_per_row (lanes of a wave that share one row in the vector-ALU
+ * kernel: 16, 32 or 64; below 64 one token only) for later calls from the
+ * calling thread.  A zero (-1 for xl and engine) keeps the built-in
+ * per-shape choice for that field.  An impossible combination makes the
+ * later calls return QG_ERR_SHAPE. */
 void qg_set_gemv_shape(int J, int R, int ksplit, int teams_per_wg, int64_t teams, int xl, int engine,
                        int lanes_per_row);
 

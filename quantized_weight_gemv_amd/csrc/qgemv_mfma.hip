@@ -1,4 +1,5 @@
-// Few-token GEMV (2..8 tokens) on the gfx950 matrix cores, Q4_0 and Q8_0.
+// Few-token GEMV (2..8 tokens) on the gfx950 matrix cores, Q4_0, Q8_0 and
+// plain 2-bit (q2w).
 //
 // With several tokens the vector-ALU kernel spends M dot products per
 // unpacked weight pair and every wave re-reads all M activation rows; here one
@@ -21,7 +22,9 @@
 // across the four 16-lane groups with v_permlane32_swap and v_permlane16_swap
 // (Q8_0 blocks are 32 bytes: two blocks per load, one swap stage, and the k
 // order inside a block is permuted the same way in the activations, which
-// leaves the contraction unchanged).  Each wave issues all of a tile's code
+// leaves the contraction unchanged; q2w blocks are 8 bytes: eight blocks per
+// load, and ten swaps give every lane group the word of each block that holds
+// its eight elements).  Each wave issues all of a tile's code
 // and scale loads (one scale per lane per step, broadcast to the row's lane
 // groups with the same swaps) before that tile's first MFMA, and the next
 // tile's while it multiplies the current one.  It stages its activation slice
@@ -80,6 +83,12 @@ __device__ __forceinline__ void swap16(uint32_t &a, uint32_t &b)
 
 constexpr size_t kMaxLds = 131072;   // dynamic LDS cap of the staged activations
 
+// Blocks of 16 rows per 16-byte load step, and code bytes per block.
+template <int FMT>
+constexpr int blocks_per_load() { return FMT == kQ4_0 ? 4 : (FMT == kQ8_0 ? 2 : 8); }
+template <int FMT>
+constexpr int mfma_code_bytes() { return FMT == kQ4_0 ? 16 : (FMT == kQ8_0 ? 32 : 8); }
+
 struct MfmaParams {
     const uint8_t *W;
     const uint16_t *x;     // fp16 [M][K]
@@ -117,12 +126,34 @@ __device__ __forceinline__ half8_t q8_operand(uint32_t w0, uint32_t w1, uint32_t
     return pack8(as_u32(p0), as_u32(p1), as_u32(p2), as_u32(p3));
 }
 
+// q2w B operand of one block from the code word holding lane group g's
+// elements, already shifted right by 4 (g & 1) so that its bit pairs 0 and 1
+// are the block's bit pairs r0 = 2 (g & 1) and r0 + 1.  Byte t' of word
+// t = g >> 1 is byte 4t + t' of the block, whose bit pair r is element
+// 4t + t' + 8r; halves (for r = r0, then r0 + 1)
+//   (e[4t + 8r], e[4t + 2 + 8r], e[4t + 1 + 8r], e[4t + 3 + 8r]) as c = u - 2:
+// (u | 0x6400) - 1026 and ((4u) | 0x6400) / 4 - 258, every step exact.
+__device__ __forceinline__ half8_t q2_operand(uint32_t w, uint32_t magic)
+{
+    const h2_t kOff0 = {(_Float16)-1026.0f, (_Float16)-1026.0f};
+    const h2_t kScale1 = {(_Float16)0.25f, (_Float16)0.25f};
+    const h2_t kOff1 = {(_Float16)-258.0f, (_Float16)-258.0f};
+    const uint32_t b = w >> 8;
+    const h2_t p0 = as_h2((w & 0x00030003u) | magic) + kOff0;
+    const h2_t p1 = as_h2((b & 0x00030003u) | magic) + kOff0;
+    const h2_t p2 = as_h2((w & 0x000C000Cu) | magic) * kScale1 + kOff1;
+    const h2_t p3 = as_h2((b & 0x000C000Cu) | magic) * kScale1 + kOff1;
+    return pack8(as_u32(p0), as_u32(p1), as_u32(p2), as_u32(p3));
+}
+
 // Activations of one (token, block): 32 fp16 as 16 words in the pair order
 //   word 4t+0 = (x[4t], x[4t+2])      word 4t+2 = (x[4t+1], x[4t+3])
 //   word 4t+1 = (x[16+4t], x[18+4t])  word 4t+3 = (x[17+4t], x[19+4t])   (Q4_0)
 //   word 2t   = (x[4t], x[4t+2])      word 2t+1 = (x[4t+1], x[4t+3])     (Q8_0)
+//   words 4g..4g+3 = the pairs (x[e], x[e+2]), (x[e+1], x[e+3]) for
+//   e = 4(g >> 1) + 8 r, r = 2 (g & 1), then r + 1                     (q2w)
 // so that the 8 halves lane group g feeds to the MFMA are the 16 bytes at
-// word 4g (Q4_0) or 4p, p = {0,2,1,3}[g] (Q8_0: the swap pattern below).
+// word 4g (Q4_0, q2w) or 4p, p = {0,2,1,3}[g] (Q8_0: the swap pattern below).
 template <int FMT>
 __device__ __forceinline__ void permute_x(const uint4 (&r)[4], uint4 (&o)[4])
 {
@@ -137,11 +168,21 @@ __device__ __forceinline__ void permute_x(const uint4 (&r)[4], uint4 (&o)[4])
             w[4 * t + 2] = pair_hi(d[2 * t], d[2 * t + 1]);
             w[4 * t + 3] = pair_hi(d[8 + 2 * t], d[9 + 2 * t]);
         }
-    } else {
+    } else if constexpr (FMT == kQ8_0) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             w[2 * t + 0] = pair_lo(d[2 * t], d[2 * t + 1]);
             w[2 * t + 1] = pair_hi(d[2 * t], d[2 * t + 1]);
+        }
+    } else {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int e0 = 2 * (g >> 1) + 8 * (g & 1);   // word of x[4(g >> 1) + 8 r0]
+            const int e1 = e0 + 4;                       // r0 + 1
+            w[4 * g + 0] = pair_lo(d[e0], d[e0 + 1]);
+            w[4 * g + 1] = pair_hi(d[e0], d[e0 + 1]);
+            w[4 * g + 2] = pair_lo(d[e1], d[e1 + 1]);
+            w[4 * g + 3] = pair_hi(d[e1], d[e1 + 1]);
         }
     }
 #pragma unroll
@@ -151,7 +192,7 @@ __device__ __forceinline__ void permute_x(const uint4 (&r)[4], uint4 (&o)[4])
 
 // One 16-row tile's codes and scales for a wave's K slice (KW blocks per
 // wave at most).  Codes: per step one 16-byte load per lane (lane group g:
-// block b0 + g, Q4_0; block b0 + g/2, Q8_0).  Scales, WS (rows of an even
+// block b0 + g, Q4_0; block b0 + g/2, Q8_0; blocks b0 + 2g, b0 + 2g + 1, q2w).  Scales, WS (rows of an even
 // number of blocks, so every row's scales are 4-byte aligned): one load per
 // lane per tile of the KW/4 scales of row c starting at block kbeg + g*KW/4
 // (16 rows x KW*2 bytes per instruction rather than one instruction per step,
@@ -159,7 +200,8 @@ __device__ __forceinline__ void permute_x(const uint4 (&r)[4], uint4 (&o)[4])
 // step (lane group g: the block its code load covers).
 template <int FMT, int KW, bool WS>
 struct TileRegs {
-    static constexpr int kSteps = KW / ((FMT == kQ4_0) ? 4 : 2);
+    static_assert(FMT != kQ2W || WS, "q2w tiles take their scales per lane group");
+    static constexpr int kSteps = KW / blocks_per_load<FMT>();
     static constexpr int kScaleRegs = WS ? KW / 8 : kSteps;
     uint4 code[kSteps];
     uint32_t scl[kScaleRegs];
@@ -177,8 +219,8 @@ template <int FMT, int KW, bool WS>
 __device__ __forceinline__ void load_tile(const MfmaParams &p, int tile, int ntiles, int KB, uint32_t coff,
                                           uint32_t soff, TileRegs<FMT, KW, WS> &t)
 {
-    constexpr int kBlocksPerLoad = (FMT == kQ4_0) ? 4 : 2;
-    constexpr int CB = (FMT == kQ4_0) ? 16 : 32;   // code bytes per block
+    constexpr int kBlocksPerLoad = blocks_per_load<FMT>();
+    constexpr int CB = mfma_code_bytes<FMT>();
     const int64_t nblocks = (int64_t)p.N * KB;
     const bool real = tile < ntiles;
     const int64_t base = (int64_t)(real ? tile : 0) * 16 * KB;
@@ -226,8 +268,9 @@ template <int FMT, int KW, bool WS>
 __device__ __forceinline__ f4_t compute_tile(TileRegs<FMT, KW, WS> &t, const uint4 *xs, int M, int cm, int xq,
                                              int kbeg, int kend, int nsteps, uint32_t magic)
 {
-    constexpr int kBlocksPerLoad = (FMT == kQ4_0) ? 4 : 2;
+    constexpr int kBlocksPerLoad = blocks_per_load<FMT>();
     constexpr int kSteps = TileRegs<FMT, KW, WS>::kSteps;
+    const uint32_t q2_shift = ((threadIdx.x >> 4) & 1u) * 4u;   // q2w: 4 (g & 1)
     // WS: every lane group's scale words to all four groups: bc[d][src] is
     // word d of lane group src (scales of blocks kbeg + src*KW/4 + 2d, +1)
     uint32_t bc[WS ? KW / 8 : 1][4];
@@ -265,6 +308,7 @@ __device__ __forceinline__ f4_t compute_tile(TileRegs<FMT, KW, WS> &t, const uin
                     sc[0] = sa; sc[1] = sb;          // Q8_0: [s0 s0 s0 s0], [s1 s1 s1 s1]
                 }
             }
+            uint32_t q2[FMT == kQ2W ? 8 : 1];
             if constexpr (FMT == kQ4_0) {
                 // 4 x 4 transpose across lane groups: afterwards register j
                 // of lane group g holds word g of block b0 + j
@@ -272,6 +316,22 @@ __device__ __forceinline__ f4_t compute_tile(TileRegs<FMT, KW, WS> &t, const uin
                 swap32(w1, w3);
                 swap16(w0, w1);
                 swap16(w2, w3);
+            } else if constexpr (FMT == kQ2W) {
+                // lane group h holds (w0, w1) of block b0 + 2h and (w2, w3) of
+                // b0 + 2h + 1; afterwards q2[j] of lane group g is word g >> 1
+                // of block b0 + j (each word reaches two lane groups)
+                swap16(w0, w1);   // w0 = words (0, 1) of blocks 0, 4; w1: blocks 2, 6
+                swap16(w2, w3);   // w2: blocks 1, 5; w3: blocks 3, 7
+                const uint32_t src[4] = {w0, w1, w2, w3};
+                const int first[4] = {0, 2, 1, 3};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    uint32_t a = src[k], b = src[k];
+                    swap16(a, b);   // a = [x.r0 x.r0 x.r2 x.r2], b = [x.r1 x.r1 x.r3 x.r3]
+                    swap32(a, b);   // a = [x.r0 x.r0 x.r1 x.r1], b = [x.r2 x.r2 x.r3 x.r3]
+                    q2[first[k]] = a;
+                    q2[first[k] + 4] = b;
+                }
             } else {
                 // afterwards (w0, w1) hold block b0 and (w2, w3) block b0 + 1:
                 // lane group g has code words 2p, 2p + 1, p = {0, 2, 1, 3}[g]
@@ -285,8 +345,10 @@ __device__ __forceinline__ f4_t compute_tile(TileRegs<FMT, KW, WS> &t, const uin
                     half8_t bop;
                     if constexpr (FMT == kQ4_0)
                         bop = q4_operand(j == 0 ? w0 : j == 1 ? w1 : j == 2 ? w2 : w3, magic);
-                    else
+                    else if constexpr (FMT == kQ8_0)
                         bop = (j == 0) ? q8_operand(w0, w1, magic) : q8_operand(w2, w3, magic);
+                    else
+                        bop = q2_operand(q2[j] >> q2_shift, magic);
                     const uint4 v = xs[((b - kbeg) * M + cm) * 4 + (xq ^ ((b - kbeg) & 3))];
                     const half8_t aop = pack8(v.x, v.y, v.z, v.w);
                     const f4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -347,7 +409,7 @@ __device__ __forceinline__ void reduce_store(const MfmaParams &p, f4_t acc, f4_t
 template <int FMT, int KWMAX, bool WS>
 __global__ __launch_bounds__(512) void gemv_mfma_kernel(MfmaParams p)
 {
-    constexpr int kBlocksPerLoad = (FMT == kQ4_0) ? 4 : 2;   // blocks of 16 rows per 16-byte load step
+    constexpr int kBlocksPerLoad = blocks_per_load<FMT>();   // blocks of 16 rows per 16-byte load step
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nwaves = blockDim.x >> 6;
@@ -380,9 +442,9 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(MfmaParams p)
 
     // 2. the first tile's codes and scales; lane offsets from a tile's first
     //    block (row c of the tile, this wave's first block, lane group g)
-    const int gb = (FMT == kQ4_0) ? g : (g >> 1);
-    const uint32_t coff = (uint32_t)(c * KB + kbeg + gb) * (FMT == kQ4_0 ? 16u : 32u) +
-                          ((FMT == kQ4_0) ? 0u : (uint32_t)(g & 1) * 16u);
+    const int gb = (FMT == kQ4_0) ? g : (FMT == kQ8_0 ? (g >> 1) : 2 * g);
+    const uint32_t coff = (uint32_t)(c * KB + kbeg + gb) * (uint32_t)mfma_code_bytes<FMT>() +
+                          ((FMT == kQ8_0) ? (uint32_t)(g & 1) * 16u : 0u);
     const uint32_t soff = WS ? (uint32_t)(c * KB + kbeg + g * (KWMAX / 4)) * 2u : (uint32_t)(c * KB + kbeg + gb) * 2u;
     int tile = blockIdx.x;
     TileRegs<FMT, KWMAX, WS> ta, tb;
@@ -414,7 +476,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(MfmaParams p)
     __shared__ f4_t red[2][kMaxWavesPerWg][64];
     const uint32_t magic = magic_reg();
     const int cm = min(c, p.M - 1);
-    const int xq = (FMT == kQ4_0) ? g : (((g & 1) << 1) | (g >> 1));
+    const int xq = (FMT == kQ8_0) ? (((g & 1) << 1) | (g >> 1)) : g;
     const int step = gridDim.x;
     const int last = ntiles - 1;
     for (int it = 0;; it += 2) {
@@ -469,15 +531,26 @@ template <int FMT>
 hipError_t launch_fmt(const MfmaParams &p, int kwmax, int waves, int64_t wgs, int cus, hipStream_t stream)
 {
     const bool ws = (p.K / 32) % 2 == 0;   // every row's scales 4-byte aligned
-    switch (kwmax) {
-    case 8: return ws ? launch_kw<FMT, 8, true>(p, waves, wgs, cus, stream)
-                      : launch_kw<FMT, 8, false>(p, waves, wgs, cus, stream);
-    case 16: return ws ? launch_kw<FMT, 16, true>(p, waves, wgs, cus, stream)
-                       : launch_kw<FMT, 16, false>(p, waves, wgs, cus, stream);
-    case 32: return ws ? launch_kw<FMT, 32, true>(p, waves, wgs, cus, stream)
-                       : launch_kw<FMT, 32, false>(p, waves, wgs, cus, stream);
+    if constexpr (FMT == kQ2W) {
+        if (!ws)
+            return hipErrorInvalidValue;   // q2w: an even number of blocks per row
+        switch (kwmax) {
+        case 8: return launch_kw<FMT, 8, true>(p, waves, wgs, cus, stream);
+        case 16: return launch_kw<FMT, 16, true>(p, waves, wgs, cus, stream);
+        case 32: return launch_kw<FMT, 32, true>(p, waves, wgs, cus, stream);
+        }
+        return hipErrorInvalidValue;
+    } else {
+        switch (kwmax) {
+        case 8: return ws ? launch_kw<FMT, 8, true>(p, waves, wgs, cus, stream)
+                          : launch_kw<FMT, 8, false>(p, waves, wgs, cus, stream);
+        case 16: return ws ? launch_kw<FMT, 16, true>(p, waves, wgs, cus, stream)
+                           : launch_kw<FMT, 16, false>(p, waves, wgs, cus, stream);
+        case 32: return ws ? launch_kw<FMT, 32, true>(p, waves, wgs, cus, stream)
+                           : launch_kw<FMT, 32, false>(p, waves, wgs, cus, stream);
+        }
+        return hipErrorInvalidValue;
     }
-    return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -497,8 +570,12 @@ hipError_t launch_gemv_mfma(int fmt, const uint8_t *W, int64_t scale_offset, con
         return hipErrorInvalidValue;
     const int kwmax = kw <= 8 ? 8 : (kw <= 16 ? 16 : 32);
     MfmaParams p{W, x, y, scale_offset, M, N, K, kw};
-    return fmt == kQ4_0 ? launch_fmt<kQ4_0>(p, kwmax, waves, wgs, cus, stream)
-                        : launch_fmt<kQ8_0>(p, kwmax, waves, wgs, cus, stream);
+    switch (fmt) {
+    case kQ4_0: return launch_fmt<kQ4_0>(p, kwmax, waves, wgs, cus, stream);
+    case kQ8_0: return launch_fmt<kQ8_0>(p, kwmax, waves, wgs, cus, stream);
+    case kQ2W: return launch_fmt<kQ2W>(p, kwmax, waves, wgs, cus, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace qg

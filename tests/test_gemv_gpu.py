@@ -185,7 +185,7 @@ def test_outliers_on_zero_weights(fmt, K):
     Wd, xd = to_dev(pb), to_dev(x)
     y_ref, s = oracle.get().gemv(fmt, po, N, K, x)
     try:
-        for engine in ((-1, 0) if fmt == Q2W else (-1, 0, 1)):
+        for engine in ((-1, 0) if fmt == Q2W and (K // 32) % 2 else (-1, 0, 1)):
             q.qg_set_gemv_shape(0, 0, 0, 0, 0, -1, engine, 0)
             for m in (1, 2, M):
                 if engine == 1 and m < 2:
@@ -345,7 +345,7 @@ def test_gemv_matrix_core_engine(fmt, N, K, M):
     x = acts(M, K, seed=K + 1)
     pb, po = pack_both(fmt, w)
     Wd, xd = to_dev(pb), to_dev(x)
-    if fmt == Q2W:   # the matrix-core kernel takes Q4_0 and Q8_0 only
+    if fmt == Q2W and (K // 32) % 2:   # q2w on the matrix cores: an even number of blocks per row
         try:
             q.qg_set_gemv_shape(0, 0, 0, 0, 0, -1, 1, 0)
             with pytest.raises(q.QGError):
