@@ -409,6 +409,9 @@ def main() -> int:
     ap.add_argument("--q2w-calls", type=int, nargs=3, default=None, metavar=("N", "K", "CALLS"),
                     help="for counter passes: CALLS calls of the times-table kernel, then CALLS of the unpacking "
                          "q2w kernel, on one seeded N x K q2w table at one token; prints nothing else")
+    ap.add_argument("--prefill-calls", type=int, nargs=4, default=None, metavar=("N", "K", "M", "CALLS"),
+                    help="for counter passes: CALLS calls of the Q4_0 prefill on one seeded N x K table and M "
+                         "tokens, then CALLS of the dense fp16 GEMM on its dequantized weights; prints nothing else")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the GEMV path runs on a single MI355X (no collectives); "
@@ -430,6 +433,19 @@ def main() -> int:
         for fn in (qg.qgemv_q2w_lut, qg.qgemv_q2w):
             for _ in range(calls):
                 fn(W, x, N, K, y)
+        torch.cuda.synchronize()
+        return 0
+
+    if args.prefill_calls:
+        N, K, M, calls = args.prefill_calls
+        W = torch.from_numpy(qg.qquantize_q4_0(si.weights(N, K, seed=0))).to("cuda")
+        w16 = qg.qdequant_q4_0(W, N, K, fp16=True).t().contiguous()
+        X = torch.from_numpy(si.activations(M, K, seed=0)).to("cuda")
+        Y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        for _ in range(calls):
+            qg.qgemm_q4_0_prefill(W, X, N, K, Y)
+        for _ in range(calls):
+            torch.matmul(X, w16)
         torch.cuda.synchronize()
         return 0
 
