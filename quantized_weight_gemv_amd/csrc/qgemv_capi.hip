@@ -254,10 +254,11 @@ qg_status run_gemv(int fmt, const void *Wp, const int32_t *idx, int64_t P, const
     // whose unpack cost per block does not grow with M.  It wants at least
     // one 16-row tile per CU; the vector kernel stays faster below four
     // tokens, and for Q8_0 (whose vector unpack is cheaper) below six on rows
-    // of 128 blocks.  Measured on MI355X: Q4_0 8192 x 2048 at 4 tokens 5.5
+    // of 128-256 blocks.  Measured on MI355X: Q4_0 8192 x 2048 at 4 tokens 5.5
     // against 6.3 us, at 8 tokens 5.9 against 9.6; 4096 x 8192 at 6 tokens
     // 10.5 against 12.9; Q8_0 14336 x 4096 at 4 tokens 19.0 against 16.3, at
-    // 8 tokens 19.9 against 25.0; q2w 14336 x 4096 at 4 tokens 10.6 against
+    // 8 tokens 19.9 against 25.0; Q8_0 4096 x 8192 at 6 / 8 tokens 12.6 / 13.1
+    // against 14.8 / 17.5; q2w 14336 x 4096 at 4 tokens 10.6 against
     // 13.2, at 8 tokens 11.3 against 23.6, at 2 tokens 10.5 against 9.2.
     // With 2048 rows half the chip idles and only Q4_0 at 8 tokens and q2w
     // from 6 tokens gain (2048 x 6144: Q4_0 9.0 against 9.6 us; q2w 7.8
@@ -268,7 +269,7 @@ qg_status run_gemv(int fmt, const void *Wp, const int32_t *idx, int64_t P, const
     const bool tiles_fill = N >= 16LL * cus;
     bool mfma = idx == nullptr && mode == kModeF16 &&
                 ((tiles_fill && fmt == kQ4_0 && M >= 4 && KB <= 256) ||
-                 (tiles_fill && fmt == kQ8_0 && ((M >= 4 && KB <= 64) || (M >= 6 && KB <= 128))) ||
+                 (tiles_fill && fmt == kQ8_0 && ((M >= 4 && KB <= 64) || (M >= 6 && KB <= 256))) ||
                  (N >= 8LL * cus && fmt == kQ4_0 && M == 8 && KB <= 256) ||
                  (fmt == kQ2W && KB % 2 == 0 && KB <= 256 &&
                   ((tiles_fill && M >= 4) || (N >= 8LL * cus && M >= 6))));
