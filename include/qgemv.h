@@ -134,15 +134,17 @@ qg_status qgemv_q8_0(const void *Wp, const uint16_t *x, float *y, int M, int64_t
  * bullets] */
 qg_status qgemv_q2w(const void *Wp, const uint16_t *x, float *y, int M, int64_t N, int64_t K, void *stream);
 
-/* Q4_0 GEMV on fp32 activations, 1 <= M <= 4 tokens: each activation is
+/* Q4_0 GEMV on fp32 activations, 1 <= M <= 8 tokens: each activation is
  * rounded to binary16 inside the kernel (nearest, ties to even; a magnitude
  * above 65504 becomes infinity, and so does its outputs' sum), then
  *   y[m][n] = sum_k w[n][k] * fp16(x[m][k])
  * with the conventions of qgemv_q4_0.  x: fp32 [M][K] row-major (device,
  * 16-byte aligned); Wp, y and the other limits as for qgemv_q4_0, with
- * K <= 16384 * min(floor(4 / M), 4).  The conversion is done inside the
- * GEMV launch, not in a separate pass: once per workgroup into LDS on large
- * tables, by each team for the blocks it reads otherwise.
+ * K <= 16384 * min(floor(4 / M), 4) for M <= 4 and K <= 8192 for M = 5..8.
+ * The conversion is done inside the GEMV launch, not in a separate pass:
+ * once per workgroup into LDS on large tables, by each team for the blocks
+ * it reads otherwise, and at 5-8 tokens (or 4 on large tables) by the
+ * matrix-core kernel as it stages each wave's activation slice.
  * [volta-kernel-bakeoff, "Results", the like-for-like bullets: fp32
  *  activations in, the conversion counted, inside the kernel at 1 token and
  *  at up to 4 tokens on expert-sized tables] */
@@ -154,7 +156,7 @@ qg_status qgemv_q4_0_f32in(const void *Wp, const float *x, float *y, int M, int6
  * GEMVs on fp16(x) (as qgemv_q4_0_f32in),
  *   y[m][n] = silu(g[m][n]) * u[m][n],   silu(v) = v / (1 + e^-v),
  * evaluated in fp32 on the fp32 sums; only y is written.  y: fp32 [M][N].
- * 1 <= N <= 2^30 - 1; K as for qgemv_q4_0_f32in.  Accuracy: g and u meet
+ * 1 <= N <= 2^30 - 1; K as for qgemv_q4_0_f32in at M tokens.  Accuracy: g and u meet
  * the GEMV bound, and y is within 1.1 eg (|u| + eu) + |g| eu + 1e-5 |y| of
  * the exact silu(g) u (eg, eu: the GEMV bounds of g and u).
  * [volta-kernel-bakeoff, "Results", the few-tokens bullet: gate and up

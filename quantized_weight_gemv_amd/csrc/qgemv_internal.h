@@ -127,10 +127,11 @@ size_t gemv_xl_lds_bytes(int K, int M, int mode);
 hipError_t launch_gemv(int fmt, int M, int G, int J, int R, bool xl, int mode, const GemvParams &p, dim3 grid,
                        dim3 block, hipStream_t stream);
 
-// Few-token GEMV on the matrix cores (qgemv_mfma.hip): `waves` waves split K;
-// `wgs` persistent workgroups (0: as many as fit, at most 2 per CU of `cus`).
-hipError_t launch_gemv_mfma(int fmt, const uint8_t *W, int64_t scale_offset, const uint16_t *x, float *y, int M,
-                            int N, int K, int waves, int64_t wgs, int cus, hipStream_t stream);
+// Few-token GEMV on the matrix cores (qgemv_mfma.hip), fp16 activations x or
+// fp32 activations xf (Q4_0, non-null xf): `waves` waves split K; `wgs`
+// persistent workgroups (0: as many as fit, at most 2 per CU of `cus`).
+hipError_t launch_gemv_mfma(int fmt, const uint8_t *W, int64_t scale_offset, const uint16_t *x, const float *xf,
+                            float *y, int M, int N, int K, int waves, int64_t wgs, int cus, hipStream_t stream);
 
 // Times-table GEMV for q2w at one token (qgemv_lut.hip): LDS bytes of the
 // tables for rows of K weights (64 KB for 32 <= K <= 4096, else SIZE_MAX),

@@ -91,7 +91,8 @@ constexpr int mfma_code_bytes() { return FMT == kQ4_0 ? 16 : (FMT == kQ8_0 ? 32 
 
 struct MfmaParams {
     const uint8_t *W;
-    const uint16_t *x;     // fp16 [M][K]
+    const uint16_t *x;     // fp16 [M][K] (fp16 input)
+    const float *xf;       // fp32 [M][K] (fp32 input, rounded to binary16 at staging)
     float *y;              // fp32 [M][N]
     int64_t scale_offset;
     int M, N, K;
@@ -406,7 +407,17 @@ __device__ __forceinline__ void reduce_store(const MfmaParams &p, f4_t acc, f4_t
 // Persistent over 16-row tiles: workgroup w takes tiles w, w + grid, ...;
 // its waves split K, stage their activation slices in LDS once, and prefetch
 // the next tile's codes and scales while the current tile is multiplied.
-template <int FMT, int KWMAX, bool WS>
+// fp32 activations rounded to binary16 (nearest, ties to even: the
+// conversion's default mode; beyond binary16's range: infinity), two per
+// word in natural order [volta-kernel-bakeoff, "Results": fp32 activations
+// in, the conversion inside the kernel].
+__device__ __forceinline__ uint32_t half2_bits(float a, float b)
+{
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+}
+
+template <int FMT, int KWMAX, bool WS, bool F32>
 __global__ __launch_bounds__(512) void gemv_mfma_kernel(MfmaParams p)
 {
     constexpr int kBlocksPerLoad = blocks_per_load<FMT>();   // blocks of 16 rows per 16-byte load step
@@ -426,18 +437,27 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(MfmaParams p)
     //    coalesced 16-byte loads, issued first (they come from cache; loads
     //    retire in order).  Pair i is (token i / nblk, block i % nblk); pairs
     //    past the slice re-read a valid block.
+    //    fp32 input: the raw words stay in registers until the staging
+    //    below rounds them (their loads overlap the first tile's).
     constexpr int kXPer = 8 * KWMAX / 64;    // (token, block) pairs per lane, M <= 8
     const int npairs = p.M * nblk;
-    uint4 xr[kXPer][4];
+    uint4 xr[kXPer][F32 ? 8 : 4];
 #pragma unroll
     for (int t = 0; t < kXPer; ++t) {
         const int i = min(lane + 64 * t, max(npairs, 1) - 1);
         const int m = i / max(nblk, 1), b = i - m * max(nblk, 1);
         const int blk = min(kbeg + b, KB - 1);
-        const uint4 *src = reinterpret_cast<const uint4 *>(p.x + (int64_t)m * p.K + (int64_t)blk * 32);
+        if constexpr (F32) {
+            const uint4 *src = reinterpret_cast<const uint4 *>(p.xf + (int64_t)m * p.K + (int64_t)blk * 32);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            xr[t][q] = src[q];
+            for (int q = 0; q < 8; ++q)
+                xr[t][q] = src[q];
+        } else {
+            const uint4 *src = reinterpret_cast<const uint4 *>(p.x + (int64_t)m * p.K + (int64_t)blk * 32);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                xr[t][q] = src[q];
+        }
     }
 
     // 2. the first tile's codes and scales; lane offsets from a tile's first
@@ -466,7 +486,20 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(MfmaParams p)
         if (i < npairs) {
             const int m = i / max(nblk, 1), b = i - m * max(nblk, 1);
             uint4 o[4];
-            permute_x<FMT>(xr[t], o);
+            if constexpr (F32) {
+                uint4 h[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const uint4 a = xr[t][2 * u], b = xr[t][2 * u + 1];
+                    h[u] = make_uint4(half2_bits(__builtin_bit_cast(float, a.x), __builtin_bit_cast(float, a.y)),
+                                      half2_bits(__builtin_bit_cast(float, a.z), __builtin_bit_cast(float, a.w)),
+                                      half2_bits(__builtin_bit_cast(float, b.x), __builtin_bit_cast(float, b.y)),
+                                      half2_bits(__builtin_bit_cast(float, b.z), __builtin_bit_cast(float, b.w)));
+                }
+                permute_x<FMT>(h, o);
+            } else {
+                permute_x<FMT>(xr[t], o);
+            }
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 xs[(b * p.M + m) * 4 + (q ^ (b & 3))] = o[q];
@@ -503,16 +536,24 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(MfmaParams p)
 template <int FMT, int KWMAX, bool WS>
 hipError_t launch_kw(const MfmaParams &p, int waves, int64_t wgs, int cus, hipStream_t stream)
 {
-    const void *fn = reinterpret_cast<const void *>(&gemv_mfma_kernel<FMT, KWMAX, WS>);
+    // fp32 activations: Q4_0 only (the fp32-input entry point's format)
+    const void *fn;
+    if constexpr (FMT == kQ4_0)
+        fn = p.xf ? reinterpret_cast<const void *>(&gemv_mfma_kernel<FMT, KWMAX, WS, true>)
+                  : reinterpret_cast<const void *>(&gemv_mfma_kernel<FMT, KWMAX, WS, false>);
+    else if (p.xf)
+        return hipErrorInvalidValue;
+    else
+        fn = reinterpret_cast<const void *>(&gemv_mfma_kernel<FMT, KWMAX, WS, false>);
     // every wave stages M x kw blocks of activations (64 bytes each)
     const size_t shmem = (size_t)waves * p.kw * p.M * 64;
     if (shmem > kMaxLds)
         return hipErrorInvalidValue;
-    static bool raised = false;   // allow more than the default dynamic LDS once per kernel
-    if (!raised) {
+    static bool raised[2] = {false, false};   // allow more than the default dynamic LDS once per kernel
+    if (!raised[p.xf ? 1 : 0]) {
         if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds) != hipSuccess)
             return hipErrorInvalidValue;
-        raised = true;
+        raised[p.xf ? 1 : 0] = true;
     }
     const int64_t ntiles = (p.N + 15) / 16;
     if (wgs <= 0) {
@@ -555,11 +596,12 @@ hipError_t launch_fmt(const MfmaParams &p, int kwmax, int waves, int64_t wgs, in
 
 }  // namespace
 
-// Launch the matrix-core GEMV: `waves` (1..8) split K; each wave takes
+// Launch the matrix-core GEMV on fp16 activations x, or on fp32 activations
+// xf (Q4_0; x then unused): `waves` (1..8) split K; each wave takes
 // kw = ceil(K/32 / waves) blocks rounded up to 4, at most 32; `wgs`
 // persistent workgroups walk the 16-row tiles (0: the built-in count).
-hipError_t launch_gemv_mfma(int fmt, const uint8_t *W, int64_t scale_offset, const uint16_t *x, float *y, int M,
-                            int N, int K, int waves, int64_t wgs, int cus, hipStream_t stream)
+hipError_t launch_gemv_mfma(int fmt, const uint8_t *W, int64_t scale_offset, const uint16_t *x, const float *xf,
+                            float *y, int M, int N, int K, int waves, int64_t wgs, int cus, hipStream_t stream)
 {
     const int KB = K / 32;
     if (M < 1 || M > 8 || waves < 1 || waves > kMaxWavesPerWg)
@@ -569,7 +611,7 @@ hipError_t launch_gemv_mfma(int fmt, const uint8_t *W, int64_t scale_offset, con
     if (kw > 32)
         return hipErrorInvalidValue;
     const int kwmax = kw <= 8 ? 8 : (kw <= 16 ? 16 : 32);
-    MfmaParams p{W, x, y, scale_offset, M, N, K, kw};
+    MfmaParams p{W, x, xf, y, scale_offset, M, N, K, kw};
     switch (fmt) {
     case kQ4_0: return launch_fmt<kQ4_0>(p, kwmax, waves, wgs, cus, stream);
     case kQ8_0: return launch_fmt<kQ8_0>(p, kwmax, waves, wgs, cus, stream);

@@ -51,6 +51,51 @@ def test_f32in_parity(M, N, K):
     assert_within(y, y_ref, s, f"f32in M={M} {N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(5, 17, 64), (8, 640, 2560), (6, 6144, 2048), (8, 4096, 4096), (7, 257, 8192),
+                                   (5, 33, 96), (8, 4099, 1024)])
+def test_f32in_five_to_eight_tokens(M, N, K):
+    """5-8 tokens of fp32 activations: the matrix-core kernel rounds them to
+    binary16 as it stages them; planted large, tiny and tie values."""
+    w = si.weights(N, K, seed=M + N + 1)
+    x = _x32(M, K, seed=K + M)
+    pb, po = pack_both(Q4_0, w)
+    y = _f32in(to_dev(pb), x, N, K)
+    y_ref, s = oracle.get().gemv_f32in(Q4_0, po, N, K, x)
+    assert_within(y, y_ref, s, f"f32in M={M} {N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(2, 130, 2048), (4, 1000, 4096), (8, 257, 8192), (3, 64, 96)])
+def test_f32in_matrix_core_engine_matches_fp16_call(M, N, K):
+    """The matrix-core kernel on fp32 activations, every wave count and three
+    grid sizes: bitwise equal to the same kernel on the fp16 rounding of x
+    (numpy's cast) in the same launch, and within the bound of the oracle."""
+    q = qg()
+    torch = torch_cuda()
+    w = si.weights(N, K, seed=N + 5)
+    x = _x32(M, K, seed=K + 5)
+    pb, po = pack_both(Q4_0, w)
+    Wd = to_dev(pb)
+    x16 = to_dev(x.astype(np.float16))
+    y_ref, s = oracle.get().gemv_f32in(Q4_0, po, N, K, x)
+    tried = 0
+    try:
+        for ks in (0, 1, 2, 4, 8):
+            for wgs in (0, 1, 3):
+                q.qg_set_gemv_shape(0, 0, ks, 0, wgs, -1, 1, 0)
+                try:
+                    y = _f32in(Wd, x, N, K)
+                except q.QGError:
+                    continue
+                y16 = q.qgemv_q4_0(Wd, x16, N, K)
+                torch.cuda.synchronize()
+                tried += 1
+                assert np.array_equal(y, y16.cpu().numpy()), f"waves={ks} workgroups={wgs}"
+                assert_within(y, y_ref, s, f"f32in mfma M={M} waves={ks} workgroups={wgs}")
+    finally:
+        q.qg_set_gemv_shape(0, 0, 0, 0, 0, -1, -1, 0)
+    assert tried >= 2
+
+
 def test_f32in_matches_fp16_path_bitwise():
     """Same launch shape as the fp16 kernel (one token, 28672 x 4096): the
     in-kernel conversion gives the fp16 call's bits exactly."""
@@ -228,14 +273,21 @@ def test_f32in_and_swiglu_abi_errors():
     x = torch.zeros((8, K), dtype=torch.float32, device="cuda")
     y = torch.zeros((8, N), dtype=torch.float32, device="cuda")
     s = torch.cuda.current_stream().cuda_stream
+    assert L.qgemv_q4_0_swiglu_f32in(Wd.data_ptr(), x.data_ptr(), y.data_ptr(), 5, N, K, s) == 2   # > 4 tokens
+    assert L.qgemv_q4_0_f32in(Wd.data_ptr(), x.data_ptr(), y.data_ptr(), 9, N, K, s) == 2          # > 8 tokens
+    xl = torch.zeros((5, 8224), dtype=torch.float32, device="cuda")
+    Wl = to_dev(q.qquantize_q4_0(si.weights(N, 8224, seed=1)))
+    assert L.qgemv_q4_0_f32in(Wl.data_ptr(), xl.data_ptr(), y.data_ptr(), 5, N, 8224, s) == 2      # 5+ tokens, K > 8192
     for fn in (L.qgemv_q4_0_f32in, L.qgemv_q4_0_swiglu_f32in):
-        assert fn(Wd.data_ptr(), x.data_ptr(), y.data_ptr(), 5, N, K, s) == 2       # more than 4 tokens
         assert fn(Wd.data_ptr(), None, y.data_ptr(), 1, N, K, s) == 1              # NULL activations
         assert fn(Wd.data_ptr(), x.data_ptr() + 4, y.data_ptr(), 1, N, K, s) == 3  # misaligned
         assert fn(Wd.data_ptr(), x.data_ptr(), y.data_ptr(), 1, N, 48, s) == 2     # K % 32 != 0
     try:
-        q.qg_set_gemv_shape(0, 0, 0, 0, 0, -1, 1, 0)   # matrix-core engine: fp16 activations only
-        assert L.qgemv_q4_0_f32in(Wd.data_ptr(), x.data_ptr(), y.data_ptr(), 4, N, K, s) == 2
+        q.qg_set_gemv_shape(0, 0, 0, 0, 0, -1, 1, 0)   # matrix-core engine: fp32 GEMV yes, SwiGLU no
+        assert L.qgemv_q4_0_f32in(Wd.data_ptr(), x.data_ptr(), y.data_ptr(), 4, N, K, s) == 0
+        assert L.qgemv_q4_0_swiglu_f32in(Wd.data_ptr(), x.data_ptr(), y.data_ptr(), 4, N, K, s) == 2
+        q.qg_set_gemv_shape(0, 0, 0, 0, 0, -1, 0, 0)   # vector engine: at most 4 fp32 tokens
+        assert L.qgemv_q4_0_f32in(Wd.data_ptr(), x.data_ptr(), y.data_ptr(), 5, N, K, s) == 2
     finally:
         q.qg_set_gemv_shape(0, 0, 0, 0, 0, -1, -1, 0)
     torch.cuda.synchronize()
