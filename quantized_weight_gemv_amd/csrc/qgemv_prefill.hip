@@ -328,11 +328,14 @@ hipError_t launch_prefill(PrefillParams p, int cus, hipStream_t stream)
     const int64_t tiles = tiles_n * tiles_m;
     if (tiles < (int64_t)cus * 5 / 8) {
         // Too few output tiles to occupy the chip: split K, about one
-        // workgroup per CU in total.  Each extra split adds an fp32 atomic per
-        // output element and needs a zero-filled Y, so splits stay few
-        // (sweeps on MI355X: 6144 x 2048 at 512 tokens 38.6 us unsplit
-        // against 47.0 us with 2 splits; 2560 x 6144 at 512 tokens best at 3).
-        splits = (int)std::min<int64_t>((cus + tiles / 2) / tiles, std::max(1, nsteps / 4));
+        // workgroup per CU in total (three per four CUs with 64-token tiles).
+        // Each extra split adds an fp32 atomic per output element and needs a
+        // zero-filled Y, so splits stay few (sweeps on MI355X: 6144 x 2048 at
+        // 512 tokens 38.6 us unsplit against 47.0 us with 2 splits; 2560 x
+        // 6144 at 512 tokens best at 3; 12288 x 2560 at 64 tokens 28.7 us with
+        // 2 splits against 31.8 with 4 and more with 3, cycled copies).
+        const int64_t target = BM == 64 ? (int64_t)cus * 3 / 4 : (int64_t)cus;
+        splits = (int)std::min<int64_t>((target + tiles / 2) / tiles, std::max(1, nsteps / 4));
         splits = std::max(1, std::min(splits, 16));
     }
     if (o_splits > 0)
