@@ -558,10 +558,13 @@ hipError_t launch_kw(const MfmaParams &p, int waves, int64_t wgs, int cus, hipSt
     const int64_t ntiles = (p.N + 15) / 16;
     if (wgs <= 0) {
         // workgroups per CU that fit in LDS (160 KB, 16 KB of it for the
-        // partial tiles) and in the wave slots (32 per CU), at most 2
+        // partial tiles) and in the wave slots (32 per CU), at most 2; one
+        // for fp32 activations, which every workgroup reads and rounds again
+        // (MI355X, 8 tokens: 6144 x 2048 7.2 against 8.1 us, 14336 x 4096
+        // 16.2 against 17.6; equal on the other shapes)
         const size_t per_wg = shmem + 2 * kMaxWavesPerWg * 64 * 16;
         const int64_t fit = std::max<int64_t>(1, std::min<int64_t>((160 * 1024) / per_wg, 32 / waves));
-        wgs = (int64_t)cus * std::min<int64_t>(2, fit);
+        wgs = (int64_t)cus * std::min<int64_t>(p.xf ? 1 : 2, fit);
     }
     wgs = std::min(wgs, ntiles);
     const dim3 grid((unsigned)wgs), block(64 * waves);
