@@ -1,5 +1,5 @@
 """Python binding of libqgemv.so (gfx950): fused dequantize-and-multiply of
-block-quantized weights (Q4_0 / Q8_0).
+block-quantized weights (Q4_0, Q8_0 and plain 2-bit q2w).
 
 This module only marshals arguments: it checks tensor devices, dtypes, shapes
 and sizes (the C ABI cannot see buffer sizes), passes raw pointers and the
@@ -277,7 +277,7 @@ def _f32in(fn: str, Wp, x, N: int, K: int, y, rows: int):
 
 
 def qgemv_q4_0_f32in(Wp, x, N: int, K: int, y=None):
-    """y[M][N] = dequant(Wp) @ fp16(x)^T with fp32 x rounded inside the kernel."""
+    """y[M][N] = dequant(Wp) @ fp16(x)^T with fp32 x rounded inside the kernel; 1 <= M <= 8."""
     return _f32in("qgemv_q4_0_f32in", Wp, x, N, K, y, N)
 
 
