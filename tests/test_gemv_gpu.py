@@ -334,7 +334,7 @@ def test_gemv_every_launch_shape(fmt, N, K, M):
 
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FNAME[f])
 @pytest.mark.parametrize("N,K,M", [(17, 32, 2), (257, 4096, 8), (100, 2560, 3), (33, 6144, 5), (130, 8192, 1),
-                                   (64, 96, 8), (4099, 2048, 2)])
+                                   (64, 96, 8), (4099, 2048, 2), (100, 192, 4), (50, 320, 8), (31, 1472, 6)])
 def test_gemv_matrix_core_engine(fmt, N, K, M):
     """The matrix-core few-token kernel, every wave count along K and a
     persistent grid of the built-in size, one workgroup (it walks every tile)
