@@ -150,15 +150,17 @@ qg_status qgemv_q2w(const void *Wp, const uint16_t *x, float *y, int M, int64_t 
  *  at up to 4 tokens on expert-sized tables] */
 qg_status qgemv_q4_0_f32in(const void *Wp, const float *x, float *y, int M, int64_t N, int64_t K, void *stream);
 
-/* Gate, up and SwiGLU in one launch, Q4_0, fp32 activations, 1 <= M <= 4:
+/* Gate, up and SwiGLU in one launch, Q4_0, fp32 activations, 1 <= M <= 8:
  * Wp is ONE packed table of 2N rows (the layout above for 2N x K): rows
  * 0..N-1 are the gate rows, rows N..2N-1 the up rows.  With g and u the two
  * GEMVs on fp16(x) (as qgemv_q4_0_f32in),
  *   y[m][n] = silu(g[m][n]) * u[m][n],   silu(v) = v / (1 + e^-v),
  * evaluated in fp32 on the fp32 sums; only y is written.  y: fp32 [M][N].
- * 1 <= N <= 2^30 - 1; K as for qgemv_q4_0_f32in at M tokens.  Accuracy: g and u meet
- * the GEMV bound, and y is within 1.1 eg (|u| + eu) + |g| eu + 1e-5 |y| of
- * the exact silu(g) u (eg, eu: the GEMV bounds of g and u).
+ * 1 <= N <= 2^30 - 1; K as for qgemv_q4_0_f32in at M tokens, and at 8
+ * tokens K <= 7168 (5-8 tokens run the matrix-core kernel, each workgroup
+ * pairing a gate tile with its up tile).  Accuracy: g and u meet the GEMV
+ * bound, and y is within 1.1 eg (|u| + eu) + |g| eu + 1e-5 |y| of the exact
+ * silu(g) u (eg, eu: the GEMV bounds of g and u).
  * [volta-kernel-bakeoff, "Results", the few-tokens bullet: gate and up
  *  stacked into one table, the activations converted once; the FFN fusion
  *  step of the CUDA-kernel diary: gate, up and SwiGLU in one kernel] */

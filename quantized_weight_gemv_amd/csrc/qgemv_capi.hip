@@ -239,10 +239,10 @@ qg_status run_gemv(int fmt, const void *Wp, const int32_t *idx, int64_t P, const
     if (!Wp || !xa || !y)
         return QG_ERR_NULL;
     const int64_t nmax = (mode == kModeGlu) ? INT32_MAX / 2 : INT32_MAX;   // SwiGLU reads 2N rows
-    // fp32 activations: up to 4 tokens on the vector kernel (their raw words
-    // stay in registers until converted), 5-8 on the matrix-core kernel;
-    // SwiGLU and 8-bit activations: up to 4 tokens (the LDS copy)
-    const int mmax = (mode == kModeF16 || mode == kModeF32) ? 8 : 4;
+    // fp32 activations and SwiGLU: up to 4 tokens on the vector kernel (their
+    // raw words stay in registers until converted), 5-8 on the matrix-core
+    // kernel; 8-bit activations: up to 4 tokens (the LDS copy)
+    const int mmax = (mode == kModeQ8Act) ? 4 : 8;
     if (M < 1 || M > mmax || N < 1 || N > nmax || K < 32 || K % 32 != 0 || K > (1 << 20) || items < 1 ||
         items > 65535)
         return QG_ERR_SHAPE;
@@ -271,9 +271,9 @@ qg_status run_gemv(int fmt, const void *Wp, const int32_t *idx, int64_t P, const
     // at most 4 tokens of raw fp32 words).
     const int64_t KB = K / 32;
     const bool tiles_fill = N >= 16LL * cus;
-    const bool f32_many = mode == kModeF32 && M > 4;
-    bool mfma = idx == nullptr && (mode == kModeF16 || mode == kModeF32) &&
-                (f32_many || (tiles_fill && fmt == kQ4_0 && M >= 4 && KB <= 256) ||
+    const bool f32_many = (mode == kModeF32 || mode == kModeGlu) && M > 4;
+    bool mfma = idx == nullptr && (mode == kModeF16 || mode == kModeF32 || mode == kModeGlu) &&
+                (f32_many || (mode != kModeGlu && tiles_fill && fmt == kQ4_0 && M >= 4 && KB <= 256) ||
                  (tiles_fill && fmt == kQ8_0 && ((M >= 4 && KB <= 64) || (M >= 6 && KB <= 256))) ||
                  (N >= 8LL * cus && fmt == kQ4_0 && M == 8 && KB <= 256) ||
                  (fmt == kQ2W && KB % 2 == 0 && KB <= 256 &&
@@ -282,9 +282,10 @@ qg_status run_gemv(int fmt, const void *Wp, const int32_t *idx, int64_t P, const
         mfma = (o_engine == 1);
     if (f32_many && !mfma)
         return QG_ERR_SHAPE;   // fp32 activations beyond 4 tokens: the matrix-core kernel only
-    if (mfma && (!(mode == kModeF16 || (mode == kModeF32 && fmt == kQ4_0)) || (fmt == kQ2W && KB % 2 != 0)))
-        return QG_ERR_SHAPE;   // the matrix-core kernel: fp16 activations, or fp32 with Q4_0; q2w rows of an
-                               // even block count
+    if (mfma && (!(mode == kModeF16 || ((mode == kModeF32 || mode == kModeGlu) && fmt == kQ4_0)) ||
+                 (fmt == kQ2W && KB % 2 != 0)))
+        return QG_ERR_SHAPE;   // the matrix-core kernel: fp16 activations, or fp32 (and SwiGLU) with Q4_0;
+                               // q2w rows of an even block count
     if (mfma) {
         if (idx != nullptr || KB > 256 || N > INT32_MAX)
             return QG_ERR_SHAPE;
@@ -292,10 +293,12 @@ qg_status run_gemv(int fmt, const void *Wp, const int32_t *idx, int64_t P, const
         int waves = static_cast<int>(std::min<int64_t>(8, std::max<int64_t>(1, (KB + 15) / 16)));
         if (o_ksplit)
             waves = o_ksplit;
-        const bool f32 = mode == kModeF32;
-        hipError_t e = launch_gemv_mfma(fmt, static_cast<const uint8_t *>(Wp), scale_offset(fmt, N, K),
+        const bool f32 = mode == kModeF32 || mode == kModeGlu;
+        const bool glu = mode == kModeGlu;   // the packed table holds 2N rows (gate, then up)
+        hipError_t e = launch_gemv_mfma(fmt, static_cast<const uint8_t *>(Wp), scale_offset(fmt, glu ? 2 * N : N, K),
                                         f32 ? nullptr : x, f32 ? xf : nullptr, y, M, static_cast<int>(N),
-                                        static_cast<int>(K), waves, o_teams, cus, static_cast<hipStream_t>(stream));
+                                        static_cast<int>(K), waves, o_teams, cus, static_cast<hipStream_t>(stream),
+                                        glu);
         if (e == hipErrorInvalidValue)
             return QG_ERR_SHAPE;
         return e == hipSuccess ? QG_OK : QG_ERR_LAUNCH;

@@ -128,10 +128,12 @@ hipError_t launch_gemv(int fmt, int M, int G, int J, int R, bool xl, int mode, c
                        dim3 block, hipStream_t stream);
 
 // Few-token GEMV on the matrix cores (qgemv_mfma.hip), fp16 activations x or
-// fp32 activations xf (Q4_0, non-null xf): `waves` waves split K; `wgs`
+// fp32 activations xf (Q4_0, non-null xf), with glu the SwiGLU of a stacked
+// gate + up table (Q4_0, fp32): `waves` waves split K; `wgs`
 // persistent workgroups (0: as many as fit, at most 2 per CU of `cus`).
 hipError_t launch_gemv_mfma(int fmt, const uint8_t *W, int64_t scale_offset, const uint16_t *x, const float *xf,
-                            float *y, int M, int N, int K, int waves, int64_t wgs, int cus, hipStream_t stream);
+                            float *y, int M, int N, int K, int waves, int64_t wgs, int cus, hipStream_t stream,
+                            bool glu = false);
 
 // Times-table GEMV for q2w at one token (qgemv_lut.hip): LDS bytes of the
 // tables for rows of K weights (64 KB for 32 <= K <= 4096, else SIZE_MAX),

@@ -97,6 +97,7 @@ struct MfmaParams {
     int64_t scale_offset;
     int M, N, K;
     int kw;                // blocks per wave (multiple of 4)
+    int glu;               // 1: stacked gate + up table of 2N rows, y = silu(gate) * up
 };
 
 // Q4_0 B operand of one block from word g (= lane group) of its codes:
@@ -216,15 +217,17 @@ struct TileRegs {
 // both.  A tile past the last one (the prefetch after a workgroup's final
 // tile) gets empty descriptors: its loads return zeros without touching
 // memory.
+// `row_shift` moves the tile down the table (SwiGLU: the up rows, N below
+// the gate rows) and `rows` is the table's row count (N, or 2N for SwiGLU).
 template <int FMT, int KW, bool WS>
 __device__ __forceinline__ void load_tile(const MfmaParams &p, int tile, int ntiles, int KB, uint32_t coff,
-                                          uint32_t soff, TileRegs<FMT, KW, WS> &t)
+                                          uint32_t soff, TileRegs<FMT, KW, WS> &t, int64_t row_shift, int64_t rows)
 {
     constexpr int kBlocksPerLoad = blocks_per_load<FMT>();
     constexpr int CB = mfma_code_bytes<FMT>();
-    const int64_t nblocks = (int64_t)p.N * KB;
+    const int64_t nblocks = rows * KB;
     const bool real = tile < ntiles;
-    const int64_t base = (int64_t)(real ? tile : 0) * 16 * KB;
+    const int64_t base = real ? ((int64_t)tile * 16 + row_shift) * KB : 0;
     const int64_t left = real ? nblocks - base : 0;
     const auto rc = make_rsrc(p.W + base * CB, left * CB);
     const auto rs = make_rsrc(p.W + p.scale_offset + base * 2, left * 2);
@@ -401,12 +404,39 @@ __device__ __forceinline__ void reduce_store(const MfmaParams &p, f4_t acc, f4_t
     }
 }
 
-// Persistent over 16-row tiles: workgroup w takes tiles w, w + grid, ...;
-// its waves split K, stage their activation slices in LDS once, and prefetch
-// the next tile's codes and scales while the current tile is multiplied.
-// Persistent over 16-row tiles: workgroup w takes tiles w, w + grid, ...;
-// its waves split K, stage their activation slices in LDS once, and prefetch
-// the next tile's codes and scales while the current tile is multiplied.
+// SwiGLU: the gate and up tiles' partial products, summed like
+// reduce_store (gate in red[par], up in red[2 + par]); the storing wave
+// writes silu(g) * u, evaluated in fp32 as the vector kernel's epilogue
+// does [the CUDA-kernel diary's FFN fusion step: gate, up and SwiGLU in one
+// kernel, only the final product written].
+__device__ __forceinline__ void reduce_store_glu(const MfmaParams &p, f4_t accg, f4_t accu,
+                                                 f4_t (*red)[kMaxWavesPerWg][64], int it, int tile, int wave,
+                                                 int nwaves, int lane, int g, int c)
+{
+    const int par = it & 1;
+    red[par][wave][lane] = accg;
+    red[2 + par][wave][lane] = accu;
+    __syncthreads();
+    if (wave == it % nwaves) {
+        f4_t sg = red[par][0][lane], su = red[2 + par][0][lane];
+        for (int w = 1; w < nwaves; ++w) {
+            const f4_t tg = red[par][w][lane], tu = red[2 + par][w][lane];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                sg[r] += tg[r];
+                su[r] += tu[r];
+            }
+        }
+        const int n = tile * 16 + c;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = 4 * g + r;
+            if (m < p.M && n < p.N)
+                p.y[(int64_t)m * p.N + n] = sg[r] / (1.0f + expf(-sg[r])) * su[r];
+        }
+    }
+}
+
 // fp32 activations rounded to binary16 (nearest, ties to even: the
 // conversion's default mode; beyond binary16's range: infinity), two per
 // word in natural order [volta-kernel-bakeoff, "Results": fp32 activations
@@ -417,9 +447,15 @@ __device__ __forceinline__ uint32_t half2_bits(float a, float b)
            ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
 }
 
-template <int FMT, int KWMAX, bool WS, bool F32>
+// Persistent over 16-row tiles: workgroup w takes tiles w, w + grid, ...;
+// its waves split K, stage their activation slices in LDS once, and prefetch
+// the next tile's codes and scales while the current tile is multiplied.
+// GLU: each tile is a gate tile and the up tile N rows below it (fp32 input).
+
+template <int FMT, int KWMAX, bool WS, bool F32, bool GLU>
 __global__ __launch_bounds__(512) void gemv_mfma_kernel(MfmaParams p)
 {
+    static_assert(!GLU || (F32 && FMT == kQ4_0), "SwiGLU: Q4_0 with fp32 activations");
     constexpr int kBlocksPerLoad = blocks_per_load<FMT>();   // blocks of 16 rows per 16-byte load step
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -467,8 +503,11 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(MfmaParams p)
                           ((FMT == kQ8_0) ? (uint32_t)(g & 1) * 16u : 0u);
     const uint32_t soff = WS ? (uint32_t)(c * KB + kbeg + g * (KWMAX / 4)) * 2u : (uint32_t)(c * KB + kbeg + gb) * 2u;
     int tile = blockIdx.x;
-    TileRegs<FMT, KWMAX, WS> ta, tb;
-    load_tile<FMT, KWMAX, WS>(p, tile, ntiles, KB, coff, soff, ta);
+    const int64_t rows = GLU ? 2 * (int64_t)p.N : (int64_t)p.N;   // rows of the packed table
+    TileRegs<FMT, KWMAX, WS> ta, tb, ua, ub;   // ua, ub: the up tiles (GLU)
+    load_tile<FMT, KWMAX, WS>(p, tile, ntiles, KB, coff, soff, ta, 0, rows);
+    if constexpr (GLU)
+        load_tile<FMT, KWMAX, WS>(p, tile, ntiles, KB, coff, soff, ua, p.N, rows);
     __builtin_amdgcn_sched_barrier(0);
 
     // 3. the activations into this wave's own LDS area, in MFMA operand
@@ -506,7 +545,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(MfmaParams p)
         }
     }
 
-    __shared__ f4_t red[2][kMaxWavesPerWg][64];
+    __shared__ f4_t red[GLU ? 4 : 2][kMaxWavesPerWg][64];
     const uint32_t magic = magic_reg();
     const int cm = min(c, p.M - 1);
     const int xq = (FMT == kQ8_0) ? (((g & 1) << 1) | (g >> 1)) : g;
@@ -516,17 +555,31 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(MfmaParams p)
         // tile in `ta`; prefetch the next into `tb` (past the end: empty
         // loads, never used)
         const int t1 = tile + step;
-        load_tile<FMT, KWMAX, WS>(p, t1, ntiles, KB, coff, soff, tb);
+        load_tile<FMT, KWMAX, WS>(p, t1, ntiles, KB, coff, soff, tb, 0, rows);
+        if constexpr (GLU)
+            load_tile<FMT, KWMAX, WS>(p, t1, ntiles, KB, coff, soff, ub, p.N, rows);
         __builtin_amdgcn_sched_barrier(0);
         f4_t acc = compute_tile<FMT, KWMAX, WS>(ta, xs, p.M, cm, xq, kbeg, kend, nsteps, magic);
-        reduce_store(p, acc, red, it, tile, wave, nwaves, lane, g, c);
+        if constexpr (GLU) {
+            const f4_t accu = compute_tile<FMT, KWMAX, WS>(ua, xs, p.M, cm, xq, kbeg, kend, nsteps, magic);
+            reduce_store_glu(p, acc, accu, red, it, tile, wave, nwaves, lane, g, c);
+        } else {
+            reduce_store(p, acc, red, it, tile, wave, nwaves, lane, g, c);
+        }
         if (t1 > last)
             break;
         const int t2 = t1 + step;
-        load_tile<FMT, KWMAX, WS>(p, t2, ntiles, KB, coff, soff, ta);
+        load_tile<FMT, KWMAX, WS>(p, t2, ntiles, KB, coff, soff, ta, 0, rows);
+        if constexpr (GLU)
+            load_tile<FMT, KWMAX, WS>(p, t2, ntiles, KB, coff, soff, ua, p.N, rows);
         __builtin_amdgcn_sched_barrier(0);
         acc = compute_tile<FMT, KWMAX, WS>(tb, xs, p.M, cm, xq, kbeg, kend, nsteps, magic);
-        reduce_store(p, acc, red, it + 1, t1, wave, nwaves, lane, g, c);
+        if constexpr (GLU) {
+            const f4_t accu = compute_tile<FMT, KWMAX, WS>(ub, xs, p.M, cm, xq, kbeg, kend, nsteps, magic);
+            reduce_store_glu(p, acc, accu, red, it + 1, t1, wave, nwaves, lane, g, c);
+        } else {
+            reduce_store(p, acc, red, it + 1, t1, wave, nwaves, lane, g, c);
+        }
         if (t2 > last)
             break;
         tile = t2;
@@ -537,23 +590,32 @@ template <int FMT, int KWMAX, bool WS>
 hipError_t launch_kw(const MfmaParams &p, int waves, int64_t wgs, int cus, hipStream_t stream)
 {
     // fp32 activations: Q4_0 only (the fp32-input entry point's format)
+    // fp32 activations and SwiGLU: Q4_0 only (their entry points' format)
     const void *fn;
-    if constexpr (FMT == kQ4_0)
-        fn = p.xf ? reinterpret_cast<const void *>(&gemv_mfma_kernel<FMT, KWMAX, WS, true>)
-                  : reinterpret_cast<const void *>(&gemv_mfma_kernel<FMT, KWMAX, WS, false>);
-    else if (p.xf)
-        return hipErrorInvalidValue;
-    else
-        fn = reinterpret_cast<const void *>(&gemv_mfma_kernel<FMT, KWMAX, WS, false>);
-    // every wave stages M x kw blocks of activations (64 bytes each)
+    int variant = 0;
+    if constexpr (FMT == kQ4_0) {
+        variant = p.glu ? 2 : (p.xf ? 1 : 0);
+        if (p.glu && !p.xf)
+            return hipErrorInvalidValue;
+        fn = variant == 2   ? reinterpret_cast<const void *>(&gemv_mfma_kernel<FMT, KWMAX, WS, true, true>)
+             : variant == 1 ? reinterpret_cast<const void *>(&gemv_mfma_kernel<FMT, KWMAX, WS, true, false>)
+                            : reinterpret_cast<const void *>(&gemv_mfma_kernel<FMT, KWMAX, WS, false, false>);
+    } else {
+        if (p.xf || p.glu)
+            return hipErrorInvalidValue;
+        fn = reinterpret_cast<const void *>(&gemv_mfma_kernel<FMT, KWMAX, WS, false, false>);
+    }
+    // every wave stages M x kw blocks of activations (64 bytes each); SwiGLU
+    // keeps 16 KB more of partial tiles in static LDS
+    const size_t red_bytes = (size_t)(p.glu ? 4 : 2) * kMaxWavesPerWg * 64 * 16;
     const size_t shmem = (size_t)waves * p.kw * p.M * 64;
-    if (shmem > kMaxLds)
+    if (shmem > kMaxLds - (p.glu ? 16384 : 0))
         return hipErrorInvalidValue;
-    static bool raised[2] = {false, false};   // allow more than the default dynamic LDS once per kernel
-    if (!raised[p.xf ? 1 : 0]) {
+    static bool raised[3] = {false, false, false};   // allow more than the default dynamic LDS once per kernel
+    if (!raised[variant]) {
         if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds) != hipSuccess)
             return hipErrorInvalidValue;
-        raised[p.xf ? 1 : 0] = true;
+        raised[variant] = true;
     }
     const int64_t ntiles = (p.N + 15) / 16;
     if (wgs <= 0) {
@@ -562,7 +624,7 @@ hipError_t launch_kw(const MfmaParams &p, int waves, int64_t wgs, int cus, hipSt
         // for fp32 activations, which every workgroup reads and rounds again
         // (MI355X, 8 tokens: 6144 x 2048 7.2 against 8.1 us, 14336 x 4096
         // 16.2 against 17.6; equal on the other shapes)
-        const size_t per_wg = shmem + 2 * kMaxWavesPerWg * 64 * 16;
+        const size_t per_wg = shmem + red_bytes;
         const int64_t fit = std::max<int64_t>(1, std::min<int64_t>((160 * 1024) / per_wg, 32 / waves));
         wgs = (int64_t)cus * std::min<int64_t>(p.xf ? 1 : 2, fit);
     }
@@ -600,11 +662,14 @@ hipError_t launch_fmt(const MfmaParams &p, int kwmax, int waves, int64_t wgs, in
 }  // namespace
 
 // Launch the matrix-core GEMV on fp16 activations x, or on fp32 activations
-// xf (Q4_0; x then unused): `waves` (1..8) split K; each wave takes
+// xf (Q4_0; x then unused), or with glu the SwiGLU of a stacked 2N-row
+// table (Q4_0, fp32 xf; scale_offset is the 2N-row table's, y is [M][N]):
+// `waves` (1..8) split K; each wave takes
 // kw = ceil(K/32 / waves) blocks rounded up to 4, at most 32; `wgs`
 // persistent workgroups walk the 16-row tiles (0: the built-in count).
 hipError_t launch_gemv_mfma(int fmt, const uint8_t *W, int64_t scale_offset, const uint16_t *x, const float *xf,
-                            float *y, int M, int N, int K, int waves, int64_t wgs, int cus, hipStream_t stream)
+                            float *y, int M, int N, int K, int waves, int64_t wgs, int cus, hipStream_t stream,
+                            bool glu)
 {
     const int KB = K / 32;
     if (M < 1 || M > 8 || waves < 1 || waves > kMaxWavesPerWg)
@@ -614,7 +679,7 @@ hipError_t launch_gemv_mfma(int fmt, const uint8_t *W, int64_t scale_offset, con
     if (kw > 32)
         return hipErrorInvalidValue;
     const int kwmax = kw <= 8 ? 8 : (kw <= 16 ? 16 : 32);
-    MfmaParams p{W, x, xf, y, scale_offset, M, N, K, kw};
+    MfmaParams p{W, x, xf, y, scale_offset, M, N, K, kw, glu ? 1 : 0};
     switch (fmt) {
     case kQ4_0: return launch_fmt<kQ4_0>(p, kwmax, waves, wgs, cus, stream);
     case kQ8_0: return launch_fmt<kQ8_0>(p, kwmax, waves, wgs, cus, stream);

@@ -246,6 +246,54 @@ def test_swiglu_saturation_and_every_launch_shape(M):
     assert any(t[3] == 1 for t in tried)
 
 
+@pytest.mark.parametrize("M,N,K", [(5, 17, 64), (8, 640, 2560), (6, 6144, 2048), (8, 1000, 4096), (7, 33, 8192),
+                                   (5, 4099, 96)])
+def test_swiglu_five_to_eight_tokens(M, N, K):
+    """5-8 tokens: the matrix-core kernel pairs each gate tile with its up
+    tile N rows below, rounds the fp32 activations as it stages them and
+    writes silu(g) * u; row counts that are not multiples of 16 leave gate
+    tiles reaching into the up rows, which must not be stored."""
+    w = np.concatenate([si.weights(N, K, seed=N + 11), si.weights(N, K, seed=N + 12)])
+    x = _x32(M, K, seed=K + 15)
+    pb, po = pack_both(Q4_0, w)
+    y = _swiglu(to_dev(pb), x, N, K)
+    _check_swiglu(y, oracle.get().swiglu(po, N, K, x), f"swiglu M={M} N={N} K={K}")
+
+
+def test_swiglu_matrix_core_every_wave_count_and_grid():
+    """The SwiGLU matrix-core kernel forced at 2-8 tokens, every wave count
+    along K and three grid sizes, large positive and negative gates, output
+    guarded on both sides."""
+    q = qg()
+    torch = torch_cuda()
+    N, K = 98, 1024
+    w = np.concatenate([si.weights(N, K, seed=51) * 40.0, si.weights(N, K, seed=52)])
+    pb, po = pack_both(Q4_0, w)
+    Wd = to_dev(pb)
+    tried = 0
+    try:
+        for M in (2, 4, 8):
+            x = _x32(M, K, seed=53 + M, scale=3.0, planted=False)
+            ref = oracle.get().swiglu(po, N, K, x)
+            buf = torch.full((M * N + 128,), 7.0, dtype=torch.float32, device="cuda")
+            yv = buf[64:64 + M * N].view(M, N)
+            for ks in (0, 1, 2, 4, 8):
+                for wgs in (0, 1, 3):
+                    q.qg_set_gemv_shape(0, 0, ks, 0, wgs, -1, 1, 0)
+                    try:
+                        q.qgemv_q4_0_swiglu_f32in(Wd, to_dev(x), N, K, yv)
+                    except q.QGError:
+                        continue
+                    torch.cuda.synchronize()
+                    tried += 1
+                    _check_swiglu(yv.cpu().numpy(), ref, f"swiglu mfma M={M} waves={ks} workgroups={wgs}")
+                    h = buf.cpu().numpy()
+                    assert (h[:64] == 7.0).all() and (h[64 + M * N:] == 7.0).all(), "wrote outside y"
+    finally:
+        q.qg_set_gemv_shape(0, 0, 0, 0, 0, -1, -1, 0)
+    assert tried >= 6
+
+
 def test_swiglu_one_token_narrow_rows():
     """One token, 16 and 32 lanes per row (the built-in choice below 8192
     rows of 65..128 blocks)."""
@@ -273,21 +321,26 @@ def test_f32in_and_swiglu_abi_errors():
     x = torch.zeros((8, K), dtype=torch.float32, device="cuda")
     y = torch.zeros((8, N), dtype=torch.float32, device="cuda")
     s = torch.cuda.current_stream().cuda_stream
-    assert L.qgemv_q4_0_swiglu_f32in(Wd.data_ptr(), x.data_ptr(), y.data_ptr(), 5, N, K, s) == 2   # > 4 tokens
-    assert L.qgemv_q4_0_f32in(Wd.data_ptr(), x.data_ptr(), y.data_ptr(), 9, N, K, s) == 2          # > 8 tokens
+    for fn in (L.qgemv_q4_0_f32in, L.qgemv_q4_0_swiglu_f32in):
+        assert fn(Wd.data_ptr(), x.data_ptr(), y.data_ptr(), 9, N, K, s) == 2      # > 8 tokens
     xl = torch.zeros((5, 8224), dtype=torch.float32, device="cuda")
     Wl = to_dev(q.qquantize_q4_0(si.weights(N, 8224, seed=1)))
     assert L.qgemv_q4_0_f32in(Wl.data_ptr(), xl.data_ptr(), y.data_ptr(), 5, N, 8224, s) == 2      # 5+ tokens, K > 8192
+    x8 = torch.zeros((8, 8192), dtype=torch.float32, device="cuda")
+    W8 = to_dev(q.qquantize_q4_0(si.weights(2 * N, 8192, seed=1)))
+    assert L.qgemv_q4_0_swiglu_f32in(W8.data_ptr(), x8.data_ptr(), y.data_ptr(), 8, N, 8192, s) == 2  # LDS: K <= 7168
+    assert L.qgemv_q4_0_swiglu_f32in(W8.data_ptr(), x8.data_ptr(), y.data_ptr(), 7, N, 8192, s) == 0
     for fn in (L.qgemv_q4_0_f32in, L.qgemv_q4_0_swiglu_f32in):
         assert fn(Wd.data_ptr(), None, y.data_ptr(), 1, N, K, s) == 1              # NULL activations
         assert fn(Wd.data_ptr(), x.data_ptr() + 4, y.data_ptr(), 1, N, K, s) == 3  # misaligned
         assert fn(Wd.data_ptr(), x.data_ptr(), y.data_ptr(), 1, N, 48, s) == 2     # K % 32 != 0
     try:
-        q.qg_set_gemv_shape(0, 0, 0, 0, 0, -1, 1, 0)   # matrix-core engine: fp32 GEMV yes, SwiGLU no
+        q.qg_set_gemv_shape(0, 0, 0, 0, 0, -1, 1, 0)   # matrix-core engine: fp32 GEMV and SwiGLU
         assert L.qgemv_q4_0_f32in(Wd.data_ptr(), x.data_ptr(), y.data_ptr(), 4, N, K, s) == 0
-        assert L.qgemv_q4_0_swiglu_f32in(Wd.data_ptr(), x.data_ptr(), y.data_ptr(), 4, N, K, s) == 2
+        assert L.qgemv_q4_0_swiglu_f32in(Wd.data_ptr(), x.data_ptr(), y.data_ptr(), 4, N, K, s) == 0
         q.qg_set_gemv_shape(0, 0, 0, 0, 0, -1, 0, 0)   # vector engine: at most 4 fp32 tokens
-        assert L.qgemv_q4_0_f32in(Wd.data_ptr(), x.data_ptr(), y.data_ptr(), 5, N, K, s) == 2
+        for fn in (L.qgemv_q4_0_f32in, L.qgemv_q4_0_swiglu_f32in):
+            assert fn(Wd.data_ptr(), x.data_ptr(), y.data_ptr(), 5, N, K, s) == 2
     finally:
         q.qg_set_gemv_shape(0, 0, 0, 0, 0, -1, -1, 0)
     torch.cuda.synchronize()
