@@ -106,4 +106,4 @@ F32IN_CASES = [(4096, 4096, 1), (14336, 4096, 1), (640, 2560, 1), (640, 2560, 4)
 # [volta-kernel-bakeoff, "Results"], Llama-3-8B's (14336 x 4096) and an
 # expert's gate / up (640 x 2560)
 SWIGLU_SHAPES = [(6144, 2048), (14336, 4096), (640, 2560)]
-SWIGLU_TOKENS = [1, 2, 4]
+SWIGLU_TOKENS = [1, 2, 4, 8]
