@@ -56,7 +56,7 @@ def measured_traffic():
     try:
         with open(path) as f:
             d = json.load(f)
-        from quantized_weight_gemv_amd.profiling import gemv_source_hash
+        from rocprof_summary import gemv_source_hash
         if d.get("gemv_source_sha256") != gemv_source_hash():
             return None
         return int(d["traffic_bytes_per_step"])

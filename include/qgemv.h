@@ -29,9 +29,12 @@
  *
  * Conventions for every entry point:
  *   - Device pointers are caller-owned device memory; the library allocates
- *     no device memory and keeps no per-call state.  Work is enqueued on
- *     `stream` (a hipStream_t; NULL = the null stream) and never
- *     synchronized: results are ready when the caller's stream reaches them.
+ *     no device memory and keeps no state between calls (the launch-shape
+ *     overrides and the timing hook of qgemv_tuning.h are the only state:
+ *     per calling thread, and only set by a caller that uses that header).
+ *     Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and never synchronized: results are ready when the caller's stream
+ *     reaches them.
  *   - Arguments are validated on the host before anything is enqueued; a
  *     non-zero status means nothing was launched.  QG_ERR_LAUNCH reports a
  *     launch the HIP runtime refused.  Faults inside a kernel surface at the
@@ -217,9 +220,10 @@ qg_status qgemv_q2w_lut(const void *Wp, const uint16_t *x, float *y, int64_t N, 
  *   y[e][n] = sum_k w_{idx[e]}[n][k] * x[e][k]
  * pool: P packed N x K matrices end to end, stride qpacked_bytes_q4_0(N, K)
  * (device); idx: int32 [E] (device); x: fp16 bits [E][K]; y: fp32 [E][N].
- * 1 <= E <= 65535.  Precondition (not checked on the device, since that
- * would need a synchronization): 0 <= idx[e] < P.  Repeated indices are
- * allowed.  [volta-kernel-bakeoff, "What's in the race" (moe_*: 8-10
+ * 1 <= E <= 65535, 1 <= P.  Repeated indices are allowed.  An index
+ * outside 0 <= idx[e] < P is never followed: no weight of that slot is read
+ * and every output of the slot, y[e][0..N-1], is NaN (the indices live in
+ * device memory, so the check happens on the device, not as a status).  [volta-kernel-bakeoff, "What's in the race" (moe_*: 8-10
  *  experts, one token each, one launch) and "Results"] */
 qg_status qmoe_gemv_q4_0(const void *pool, int64_t P, const int32_t *idx, const uint16_t *x, float *y,
                          int E, int64_t N, int64_t K, void *stream);
@@ -242,49 +246,6 @@ qg_status qgemm_q4_0_prefill(const void *Wp, const uint16_t *X, float *Y, int64_
 qg_status qdequant_q4_0(const void *Wp, int64_t N, int64_t K, int out_fp16, void *out, void *stream);
 qg_status qdequant_q8_0(const void *Wp, int64_t N, int64_t K, int out_fp16, void *out, void *stream);
 qg_status qdequant_q2w(const void *Wp, int64_t N, int64_t K, int out_fp16, void *out, void *stream);
-
-/* ------------------------------------------------------------ measurement */
-
-/* Arm kernel timing for the next launch this library makes from the calling
- * thread: that kernel records its own start and end into `start` and `stop`
- * (hipEvent_t, created by the caller) through hipExtLaunchKernel, so
- * hipEventElapsedTime(start, stop) is the kernel's execution time without
- * queueing gaps.  One-shot: the next launch consumes it.  Pass NULLs to
- * disarm.  Entry points that launch more than one kernel time the first. */
-void qg_time_next_launch(void *start, void *stop);
-
-/* Number of compute units the launch heuristics assume on `device`
- * (QG_ERR_DEVICE if the query fails). */
-qg_status qg_device_cus(int device, int *cus);
-
-/* Tuning knob for launch-shape sweeps of qgemv_* / qmoe_gemv_q4_0: fixes J
- * (blocks per lane per row, J * M <= 8), R (row sets per group: 1, 2 or 4),
- * ksplit (waves sharing a row along K), teams per workgroup, the total
- * number of teams, xl (activations of 1-4 tokens staged once per workgroup
- * in LDS, whole rows per wave: 1; kept in each lane's registers: 0), engine
- * (vector-ALU kernel: 0; matrix-core kernel for 2..8 tokens and rows of at
- * most 256 blocks, for q2w an even number: 1, where ksplit is its number of
- * waves along K and teams its number of persistent workgroups) and
- * lanes_per_row (lanes of a wave that share one row in the vector-ALU
- * kernel: 16, 32 or 64; below 64 one token only) for later calls from the
- * calling thread.  A zero (-1 for xl and engine) keeps the built-in
- * per-shape choice for that field.  An impossible combination makes the
- * later calls return QG_ERR_SHAPE. */
-void qg_set_gemv_shape(int J, int R, int ksplit, int teams_per_wg, int64_t teams, int xl, int engine,
-                       int lanes_per_row);
-
-/* Tuning knob for sweeps of qgemm_q4_0_prefill: fixes the number of
- * workgroups sharing one output tile along K (splits; more than one adds fp32
- * partial tiles atomically into a zero-filled Y) and the token tile (bm: 64 or
- * 128) for later calls from the calling thread.  0 keeps the built-in choice. */
-void qg_set_prefill_shape(int splits, int bm);
-
-/* Memory-bandwidth probe: a streaming 16-byte read of `bytes` (rounded down
- * to a multiple of 16) of device memory at `buf` by `wgs` workgroups of 256
- * threads; workgroup g writes one word to sink[g] (device, >= wgs words) so
- * the reads cannot be dropped.  The measured roofline beside the spec sheet
- * [sm8x-bench, methodology: a bandwidth probe gives the measured roofline]. */
-qg_status qg_read_probe(const void *buf, size_t bytes, uint32_t *sink, int wgs, void *stream);
 
 #ifdef __cplusplus
 }

@@ -1,0 +1,71 @@
+/*
+ * qgemv_tuning.h -- measurement and tuning hooks of libqgemv.so.
+ *
+ * Not part of the product surface (qgemv.h): these calls exist for launch-
+ * shape sweeps, kernel timing and the bandwidth probe.  Three of them set
+ * state of the CALLING THREAD that changes later calls of qgemv.h's entry
+ * points made from that thread:
+ *   - qg_set_gemv_shape / qg_set_prefill_shape fix launch-shape fields until
+ *     they are called again with zeros (-1 for xl and engine);
+ *   - qg_time_next_launch arms a one-shot timing hook for the next launch.
+ * A caller that never includes this header never sees that state.  Other
+ * threads are not affected.
+ */
+#ifndef QGEMV_TUNING_H
+#define QGEMV_TUNING_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "qgemv.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Arm kernel timing for the next launch this library makes from the calling
+ * thread: that kernel records its own start and end into `start` and `stop`
+ * (hipEvent_t, created by the caller) through hipExtLaunchKernel, so
+ * hipEventElapsedTime(start, stop) is the kernel's execution time without
+ * queueing gaps.  One-shot: the next launch consumes it.  Pass NULLs to
+ * disarm.  Entry points that launch more than one kernel time the first. */
+void qg_time_next_launch(void *start, void *stop);
+
+/* Number of compute units the launch heuristics assume on `device`
+ * (QG_ERR_DEVICE if the query fails). */
+qg_status qg_device_cus(int device, int *cus);
+
+/* Tuning knob for launch-shape sweeps of qgemv_* / qmoe_gemv_q4_0: fixes J
+ * (blocks per lane per row, J * M <= 8), R (row sets per group: 1, 2 or 4),
+ * ksplit (waves sharing a row along K), teams per workgroup, the total
+ * number of teams, xl (activations of 1-4 tokens staged once per workgroup
+ * in LDS, whole rows per wave: 1; kept in each lane's registers: 0), engine
+ * (vector-ALU kernel: 0; matrix-core kernel for 2..8 tokens and rows of at
+ * most 256 blocks, for q2w an even number: 1, where ksplit is its number of
+ * waves along K and teams its number of persistent workgroups) and
+ * lanes_per_row (lanes of a wave that share one row in the vector-ALU
+ * kernel: 16, 32 or 64; below 64 one token only) for later calls from the
+ * calling thread.  A zero (-1 for xl and engine) keeps the built-in
+ * per-shape choice for that field.  An impossible combination makes the
+ * later calls return QG_ERR_SHAPE. */
+void qg_set_gemv_shape(int J, int R, int ksplit, int teams_per_wg, int64_t teams, int xl, int engine,
+                       int lanes_per_row);
+
+/* Tuning knob for sweeps of qgemm_q4_0_prefill: fixes the number of
+ * workgroups sharing one output tile along K (splits; more than one adds fp32
+ * partial tiles atomically into a zero-filled Y) and the token tile (bm: 64 or
+ * 128) for later calls from the calling thread.  0 keeps the built-in choice. */
+void qg_set_prefill_shape(int splits, int bm);
+
+/* Memory-bandwidth probe: a streaming 16-byte read of `bytes` (rounded down
+ * to a multiple of 16) of device memory at `buf` by `wgs` workgroups of 256
+ * threads; workgroup g writes one word to sink[g] (device, >= wgs words) so
+ * the reads cannot be dropped.  The measured roofline beside the spec sheet
+ * [sm8x-bench, methodology: a bandwidth probe gives the measured roofline]. */
+qg_status qg_read_probe(const void *buf, size_t bytes, uint32_t *sink, int wgs, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMV_TUNING_H */

@@ -9,6 +9,7 @@
 #include <mutex>
 
 #include "qgemv.h"
+#include "qgemv_tuning.h"
 #include "qgemv_internal.h"
 
 namespace qg {
@@ -321,7 +322,7 @@ qg_status run_gemv(int fmt, const void *Wp, const int32_t *idx, int64_t P, const
     p.K = static_cast<int>(K);
     p.ksplit = s.ksplit;
     p.teams_per_wg = s.teams_per_wg;
-    (void)P;
+    p.pool = P;
     const int64_t wgs = (s.teams + s.teams_per_wg - 1) / s.teams_per_wg;
     dim3 grid(static_cast<unsigned>(wgs), static_cast<unsigned>(items), 1);
     dim3 block(64 * s.ksplit * s.teams_per_wg, 1, 1);

@@ -1,0 +1,7 @@
+// Vector-ALU GEMV kernels: Q8_0 weights, fp16 activations in registers (1-8 tokens).
+#include "qgemv_gemv_impl.h"
+
+namespace qg {
+template hipError_t launch_variant<kQ8_0, kModeF16, false>(int, int, int, int, const GemvParams &, dim3, dim3, size_t,
+                                                hipStream_t);
+}  // namespace qg

@@ -58,6 +58,7 @@ struct GemvParams {
     const float *xf;           // fp32 activations [M][K] (fp32-input modes)
     float *y;                  // fp32 outputs [items][M][N]
     int64_t matrix_stride;     // bytes between pool matrices (MoE)
+    int64_t pool;              // MoE: matrices in the pool (valid indices 0..pool-1)
     int64_t scale_offset;      // byte offset of the scale region in one matrix
     int N;
     int K;
@@ -126,6 +127,13 @@ size_t gemv_xl_lds_bytes(int K, int M, int mode);
 
 hipError_t launch_gemv(int fmt, int M, int G, int J, int R, bool xl, int mode, const GemvParams &p, dim3 grid,
                        dim3 block, hipStream_t stream);
+
+// Every launch shape (M tokens, G lanes per row, J blocks per lane, R row
+// sets per group) of one vector-ALU kernel variant; defined in
+// qgemv_gemv_impl.h and instantiated per variant in qgemv_gemv_*.hip.
+template <int FMT, int MODE, bool XL>
+hipError_t launch_variant(int M, int G, int J, int R, const GemvParams &p, dim3 grid, dim3 block, size_t shmem,
+                          hipStream_t stream);
 
 // Few-token GEMV on the matrix cores (qgemv_mfma.hip), fp16 activations x or
 // fp32 activations xf (Q4_0, non-null xf), with glu the SwiGLU of a stacked

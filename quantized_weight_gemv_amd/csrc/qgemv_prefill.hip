@@ -23,6 +23,7 @@
 #include <cstdint>
 
 #include "qgemv.h"
+#include "qgemv_tuning.h"
 #include "qgemv_internal.h"
 
 namespace qg {

@@ -1,10 +1,10 @@
 """Turn rocprofv3 CSV output of bench.py runs into the short summaries kept
 under profiles/.
 
-    python -m quantized_weight_gemv_amd.profiling stats <kernel_stats.csv> <kernel_trace.csv> <out.md> <command>
-    python -m quantized_weight_gemv_amd.profiling traffic <fetch_counter_collection.csv>
+    python rocprof_summary.py stats <kernel_stats.csv> <kernel_trace.csv> <out.md> <command>
+    python rocprof_summary.py traffic <fetch_counter_collection.csv>
            <write_counter_collection.csv> <out.json> <command-fetch> <command-write>
-    python -m quantized_weight_gemv_amd.profiling suite <kernel_stats.csv> <suite.jsonl> <out.md> <command>
+    python rocprof_summary.py suite <kernel_stats.csv> <suite.jsonl> <out.md> <command>
 
 Traffic calibration: the bench's own weight-copy kernels (__amd_rocclr_copyBuffer
 of known sizes, dispatched while it builds its workload) give the factor each
@@ -19,7 +19,7 @@ import os
 import statistics
 import sys
 
-HERE = os.path.dirname(os.path.abspath(__file__))
+HERE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "quantized_weight_gemv_amd")
 # the files that determine the GEMV kernel and its launch shapes
 GEMV_SOURCES = ["csrc/qgemv_gemv.hip", "csrc/qgemv_capi.hip", "csrc/qgemv_internal.h"]
 

@@ -1,5 +1,5 @@
 """Host-side checks of the HIP library (no GPU): it loads, exports every
-symbol include/qgemv.h declares, and its host quantizer writes exactly the
+symbol include/*.h declares, and its host quantizer writes exactly the
 oracle's bytes."""
 import os
 import re
@@ -23,7 +23,8 @@ def _qg():
 
 
 def declared_symbols():
-    src = open(os.path.join(ROOT, "include", "qgemv.h")).read()
+    inc = os.path.join(ROOT, "include")
+    src = "".join(open(os.path.join(inc, f)).read() for f in sorted(os.listdir(inc)) if f.endswith(".h"))
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(q[a-z0-9_]+)\s*\(", src)))
 
