@@ -10,25 +10,40 @@ call streams its weights from HBM and not from the 256 MB last-level cache
 [volta-kernel-bakeoff, "Making it fair": cycle enough copies that every call
 reads from memory].
 
-value    = algorithmic bytes of all K timed steps / wall time of the K steps
-           (inputs resident in HBM; launch gaps included), the K steps
-           replayed as one captured HIP graph (eager launch time reported
-           beside it; --no-graph times value eagerly).
+value    = algorithmic bytes of one step / the median time per step over R
+           rounds (default 30); a round is one replay of a captured HIP graph
+           of the K steps, the rounds run back to back with stream events
+           between them (inputs resident in HBM, launch gaps included), so
+           the graph's submission cost is not inside a round and value does
+           not depend on K.  The minimum and the spread of the rounds, and R
+           eagerly launched rounds of the same K steps, are reported beside it
+           [volta-kernel-bakeoff, "Making it fair": the median round, with
+           the fastest and slowest].
 roofline = the GEMV kernel's own time, from HIP events recorded by each
-           launch (hipExtLaunchKernel) over a second pass of K steps, against
+           launch (hipExtLaunchKernel) over a further K steps, against
            8 TB/s; algorithmic bytes per call = N*K/32*18 (codes + scales) +
            2*K (x) + 4*N (y).
+hbm_probe = a streaming read on the GEMV's load path (non-temporal 16-byte
+           buffer loads), swept over grid sizes and loads in flight: the best
+           rate on 4 GiB, and per shape the fastest read of that shape's
+           packed bytes from the same cycled copies (the measured floor).
+env      = GPU, ROCm/HIP and torch versions, host CPU, clocks / temperature /
+           power from rocm-smi before and after, sha256 of each shape's
+           packed weights and activations [sm8x-bench, methodology].
 cpu_baseline = the CPU oracle (fp64 C, OpenMP) on a bounded row sample of the
-           same shapes, in the same unit.
+           same shapes, in the same unit, on all host cores and on one.
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--rounds R] [--no-cpu-baseline] [--probe-only]
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
+import platform
+import subprocess
 import sys
 import time
 
@@ -83,12 +98,15 @@ def build_workload(qg, torch):
         for c in range(copies):
             buf[c * nb:(c + 1) * nb].copy_(first)
         del first
-        x = torch.from_numpy(si.activations(1, K, seed=0)).to("cuda")
+        xh = si.activations(1, K, seed=0)
+        sha = hashlib.sha256(packed.tobytes()).hexdigest()
+        sha_x = hashlib.sha256(xh.tobytes()).hexdigest()
+        x = torch.from_numpy(xh).to("cuda")
         y = torch.empty((1, N), dtype=torch.float32, device="cuda")
         # one validated call per copy: the timed loop only enqueues kernels
         calls = [qg.PreparedGemv(qg.Q4_0, buf[c * nb:(c + 1) * nb], x, y, N, K) for c in range(copies)]
         work.append(dict(N=N, K=K, nb=nb, copies=copies, buf=buf, x=x, y=y, next=0, calls=calls,
-                         bytes=algorithmic_bytes(N, K)))
+                         bytes=algorithmic_bytes(N, K), sha256_w=sha, sha256_x=sha_x))
         log(f"shape {N}x{K}: {copies} copies x {nb} B ({time.perf_counter() - t0:.1f} s)")
     torch.cuda.synchronize()
     return work
@@ -132,34 +150,132 @@ def per_shape_graph_us(qg, torch, work, calls_per_shape: int = 64) -> dict:
     return out
 
 
-def hbm_probe(qg, torch, gib: int = 4, reps: int = 5) -> float:
-    buf = torch.empty(gib << 30, dtype=torch.uint8, device="cuda")
-    buf.fill_(1)
-    wgs = qg.qg_device_cus() * 8
-    sink = torch.empty(wgs, dtype=torch.int32, device="cuda")
-    timer = qg.KernelTimer(reps + 1)
-    qg.qg_read_probe(buf, sink, wgs)
-    for _ in range(reps):
+PROBE_LOADS = (4, 8, 16)
+PROBE_WGS_PER_CU = (1, 2, 4, 8, 16)
+
+
+def _probe_us(qg, torch, buf, nbytes, copies, stride, sink, wgs, loads, reps):
+    """Median kernel time (us) of `reps` probe launches reading `nbytes` from
+    successive copies, each timed by the events its own launch records."""
+    timer = qg.KernelTimer(reps)
+    for i in range(reps):
+        c = i % copies
         timer.arm()
-        qg.qg_read_probe(buf, sink, wgs)
-    torch.cuda.synchronize()
-    ms = timer.elapsed_ms()
+        qg.qg_read_probe(buf[c * stride:], sink, wgs, loads, nbytes)
+    ms = np.array(timer.elapsed_ms())
     timer.close()
-    del buf
-    return (gib << 30) / (min(ms) * 1e-3) / 1e9
+    return float(np.median(ms) * 1e3)
 
 
-def cpu_baseline(seconds: float) -> dict:
-    """The oracle (fp64 C, OpenMP over rows) on a row sample of each shape."""
-    import oracle
-    o = oracle.get()
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+def hbm_probe(qg, torch, work, gib: int = 4) -> dict:
+    """The read probe: best rate on `gib` GiB over the swept launch shapes,
+    then per shape the fastest read of its packed bytes (per-launch events,
+    and back to back in a graph like the GEMV's own back-to-back time)."""
+    cus = qg.qg_device_cus()
+    sink = torch.empty(16 * cus, dtype=torch.int32, device="cuda")
+    big = torch.empty(gib << 30, dtype=torch.uint8, device="cuda")
+    big.fill_(1)
+    best = None
+    for loads in PROBE_LOADS:
+        for per_cu in PROBE_WGS_PER_CU:
+            wgs = per_cu * cus
+            qg.qg_read_probe(big, sink, wgs, loads)
+            us = _probe_us(qg, torch, big, big.numel(), 1, 0, sink, wgs, loads, 3)
+            gbps = big.numel() / us / 1e3
+            if best is None or gbps > best["GBps"]:
+                best = {"GBps": round(gbps, 1), "bytes": big.numel(), "loads_in_flight": loads,
+                        "workgroups": wgs, "us": round(us, 2)}
+    del big
+    torch.cuda.empty_cache()
+    floors = {}
+    for w in work:
+        nb = w["nb"]
+        top = None
+        for loads in PROBE_LOADS:
+            for per_cu in PROBE_WGS_PER_CU:
+                us = _probe_us(qg, torch, w["buf"], nb, w["copies"], nb, sink, per_cu * cus, loads, 24)
+                if top is None or us < top[0]:
+                    top = (us, loads, per_cu * cus)
+        us, loads, wgs = top
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        calls = 64
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for i in range(calls):
+                    c = i % w["copies"]
+                    qg.qg_read_probe(w["buf"][c * nb:], sink, wgs, loads, nb)
+        torch.cuda.synchronize()
+        g.replay()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s0.record()
+        g.replay()
+        s1.record()
+        torch.cuda.synchronize()
+        b2b = s0.elapsed_time(s1) * 1e3 / calls
+        del g
+        floors[f"{w['N']}x{w['K']}"] = {"bytes": nb, "us_median": round(us, 3), "GBps": round(nb / us / 1e3, 1),
+                                        "us_back_to_back": round(b2b, 3), "loads_in_flight": loads,
+                                        "workgroups": wgs}
+    return {"best": best, "per_shape_floor": floors,
+            "note": "non-temporal 16-byte buffer loads (the GEMV's load path); per-launch event times; per shape "
+                    "the fastest of the swept launch shapes reading that shape's packed bytes from its cycled "
+                    "copies, and the same launch back to back in a graph"}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def _smi() -> dict:
+    """Clocks, temperature and power of the first GPU from rocm-smi (read
+    only); whatever the tool prints under those names, or the error."""
+    try:
+        r = subprocess.run(["rocm-smi", "--showtemp", "--showpower", "--showclocks", "--json"],
+                           capture_output=True, text=True, timeout=30)
+        d = json.loads(r.stdout)
+    except (OSError, ValueError, subprocess.SubprocessError) as e:
+        return {"error": f"{type(e).__name__}: {e}"[:200]}
+    cards = [k for k in d if k.startswith("card")]
+    if not cards:
+        return {"error": "no card in rocm-smi output"}
+    keep = ("temp", "power", "clk", "clock")
+    return {k: v for k, v in d[sorted(cards)[0]].items() if any(t in k.lower() for t in keep)}
+
+
+def gpu_env(torch) -> dict:
+    props = torch.cuda.get_device_properties(0)
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    return {"gpu": props.name, "arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "hbm_GiB": round(props.total_memory / 2**30, 1),
+            "rocm": rocm, "hip_runtime": torch.version.hip, "torch": torch.__version__,
+            "cpu_model": _cpu_model(), "cpu_threads_available": len(os.sched_getaffinity(0)),
+            "host": platform.node()}
+
+
+def _oracle_rate(o, oracle, seconds: float, max_rows: int):
+    """Oracle GEMV throughput (GB/s of algorithmic bytes) on the first
+    min(N, max_rows) rows of each shape, ~seconds in total."""
     done_bytes = 0
     elapsed = 0.0
     per_shape = seconds / len(si.LLAMA3_8B_SHAPES)
     sample = []
     for (N, K) in si.LLAMA3_8B_SHAPES:
-        rows = min(N, 2048)
+        rows = min(N, max_rows)
         w = si.weights(rows, K, seed=0)   # the first `rows` rows' worth of the same distribution
         p = o.quantize(oracle.Q4_0, w)
         x = si.activations(1, K, seed=0)
@@ -173,9 +289,27 @@ def cpu_baseline(seconds: float) -> dict:
         done_bytes += reps * algorithmic_bytes(rows, K)
         elapsed += t_shape
         sample.append(f"{rows}x{K} x{reps}")
-    return {"value": round(done_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+    return done_bytes / elapsed / 1e9, sample
+
+
+def cpu_baseline(seconds: float) -> dict:
+    """The oracle (fp64 C, OpenMP over rows) on a row sample of each shape, on
+    every host core, then on one core."""
+    import oracle
+    o = oracle.get()
+    threads = len(os.sched_getaffinity(0))
+    o.set_threads(threads)
+    rate, sample = _oracle_rate(o, oracle, seconds, 2048)
+    o.set_threads(1)
+    rate1, sample1 = _oracle_rate(o, oracle, seconds / 3, 256)
+    o.set_threads(threads)
+    return {"value": round(rate, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "cpu_model": _cpu_model(),
             "sample": "oracle GEMV (fp64, M=1) on the first min(N, 2048) rows of each shape, repeated for "
-                      f"{seconds:.0f} s in total: " + ", ".join(sample)}
+                      f"{seconds:.0f} s in total on {threads} threads: " + ", ".join(sample),
+            "one_core": {"value": round(rate1, 4), "unit": "GB/s", "cores": 1,
+                         "sample": f"the first min(N, 256) rows of each shape, {seconds / 3:.0f} s in total: "
+                                   + ", ".join(sample1)}}
 
 
 # ------------------------------------------------------------------- suite
@@ -394,11 +528,14 @@ def suite(qg, torch, reps: int):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=20, help="steps per timed round (K)")
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--rounds", type=int, default=30, help="timed rounds of K steps (R); value from the median")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--probe-only", action="store_true",
+                    help="only the read probe (4 GiB sweep and per-shape floors); prints its JSON")
     ap.add_argument("--no-graph", action="store_true", help="time value with eager launches instead of a graph")
     ap.add_argument("--no-back-to-back", action="store_true",
                     help="skip the per-shape back-to-back pass (profiler runs: only interleaved steps)")
@@ -459,28 +596,54 @@ def main() -> int:
     work = build_workload(qg, torch)
     step_bytes = sum(w["bytes"] for w in work)
 
+    if args.probe_only:
+        print(json.dumps({"hbm_probe": hbm_probe(qg, torch, work), "env": gpu_env(torch)}), flush=True)
+        return 0
+
+    smi_before = _smi()
     for _ in range(args.warmup):
         run_step(work)
     torch.cuda.synchronize()
 
-    # Timed region 1 (value): K steps, captured once into a HIP graph and
-    # replayed (the launch-bound loop as a graph; the copy rotation continues
-    # exactly as eager launches would, so every call still reads cold copies),
-    # bracketed by synchronizations.  The same K steps launched eagerly are
-    # timed too and reported beside it.
-    def timed_eager():
+    def rounds_stats(ms_rounds):
+        per_step = np.array(ms_rounds) / args.steps
+        med = float(np.median(per_step))
+        return {"ms_per_step_median": round(med, 5), "ms_per_step_min": round(float(per_step.min()), 5),
+                "ms_per_step_max": round(float(per_step.max()), 5),
+                "spread_pct": round(float((per_step.max() - per_step.min()) / med * 100), 2),
+                "GBps_median": round(step_bytes / (med * 1e-3) / 1e9, 1),
+                "GBps_best": round(step_bytes / (float(per_step.min()) * 1e-3) / 1e9, 1)}
+
+    def timed_rounds(launch_round, count):
+        """`count` rounds back to back, stream events between them; the whole
+        region bracketed by synchronizations.  Returns (ms per round, wall s)."""
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(count + 1)]
         torch.cuda.synchronize()
-        t = time.perf_counter()
+        t0 = time.perf_counter()
+        ev[0].record()
+        for r in range(count):
+            launch_round()
+            ev[r + 1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return [ev[r].elapsed_time(ev[r + 1]) for r in range(count)], wall
+
+    # Eager rounds: K steps launched one call at a time (the copy rotation
+    # continues across rounds, so every call reads a cold copy).
+    def eager_round():
         for _ in range(args.steps):
             run_step(work)
-        torch.cuda.synchronize()
-        return time.perf_counter() - t
 
-    eager_wall = timed_eager()
-    wall = eager_wall
-    graph_used = False
-    if not args.no_graph:
-        nexts = [w["next"] for w in work]
+    eager_ms, eager_wall = timed_rounds(eager_round, max(5, args.rounds // 3))
+    eager = rounds_stats(eager_ms)
+
+    # Timed region (value): the K steps captured once into a HIP graph (the
+    # copy rotation continues exactly as eager launches would, so every call
+    # still reads cold copies; a replay repeats the same sequence, whose
+    # >= 1 GiB per shape cannot stay in the 256 MB last-level cache between
+    # repeats), replayed R times back to back.
+    graph_used = not args.no_graph
+    if graph_used:
         graph = torch.cuda.CUDAGraph()
         cap = torch.cuda.Stream()
         cap.wait_stream(torch.cuda.current_stream())
@@ -494,15 +657,12 @@ def main() -> int:
                         w["next"] = (c + 1) % w["copies"]
                         calls[c]()
         torch.cuda.synchronize()
-        for w, n in zip(work, nexts):   # warm the graph on the same copies, then time it
-            w["next"] = n
-        graph.replay()
+        graph.replay()   # warm the graph
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        graph.replay()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        graph_used = True
+        round_ms, wall = timed_rounds(graph.replay, args.rounds)
+    else:
+        round_ms, wall = timed_rounds(eager_round, args.rounds)
+    rounds = rounds_stats(round_ms)
 
     # Timed region 2 (roofline): the same K steps, every launch recording its
     # own start and end (hipExtLaunchKernel events).  The event path costs
@@ -516,7 +676,7 @@ def main() -> int:
     ms = np.array(timer.elapsed_ms()).reshape(args.steps, len(work))
     timer.close()
 
-    value = step_bytes * args.steps / wall / 1e9
+    value = rounds["GBps_median"]
     kern_us = ms.mean(axis=0) * 1e3
     per_shape = {}
     for w, us, med in zip(work, kern_us, np.median(ms, axis=0) * 1e3):
@@ -533,7 +693,13 @@ def main() -> int:
         rec["us_per_call_back_to_back"] = round(us, 3)
         rec["GBps_back_to_back"] = round(rec["algorithmic_bytes"] / (us * 1e-6) / 1e9, 1)
 
-    probe = None if args.no_probe else round(hbm_probe(qg, torch), 1)
+    probe = None if args.no_probe else hbm_probe(qg, torch, work)
+    smi_after = _smi()
+    env = gpu_env(torch)
+    env["smi_before"] = smi_before
+    env["smi_after"] = smi_after
+    env["inputs_sha256"] = {f"{w['N']}x{w['K']}": {"packed_weights": w["sha256_w"], "activations": w["sha256_x"]}
+                            for w in work}
 
     out = {
         "metric": METRIC,
@@ -542,10 +708,12 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 4),
-        "launch": "hip graph of the K steps" if graph_used else "eager",
-        "eager_ms_per_step": round(eager_wall / args.steps * 1e3, 4),
-        "eager_value": round(step_bytes * args.steps / eager_wall / 1e9, 1),
+        "ms_per_step": rounds["ms_per_step_median"],
+        "rounds": args.rounds,
+        "launch": "hip graph of the K steps, replayed once per round" if graph_used else "eager",
+        "round_stats": rounds,
+        "timed_wall_s": round(wall, 4),
+        "eager": eager,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -566,7 +734,8 @@ def main() -> int:
                              "times (HIP events recorded by each launch); traffic = HBM bytes of the six launches "
                              "from rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated on copies of known size"},
         "per_shape": per_shape,
-        "hbm_probe_GBps": probe,
+        "hbm_probe": probe,
+        "env": env,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")

@@ -57,12 +57,16 @@ void qg_set_gemv_shape(int J, int R, int ksplit, int teams_per_wg, int64_t teams
  * 128) for later calls from the calling thread.  0 keeps the built-in choice. */
 void qg_set_prefill_shape(int splits, int bm);
 
-/* Memory-bandwidth probe: a streaming 16-byte read of `bytes` (rounded down
- * to a multiple of 16) of device memory at `buf` by `wgs` workgroups of 256
- * threads; workgroup g writes one word to sink[g] (device, >= wgs words) so
- * the reads cannot be dropped.  The measured roofline beside the spec sheet
- * [sm8x-bench, methodology: a bandwidth probe gives the measured roofline]. */
-qg_status qg_read_probe(const void *buf, size_t bytes, uint32_t *sink, int wgs, void *stream);
+/* Memory-bandwidth probe on the GEMV kernels' load path: a streaming read of
+ * `bytes` (rounded down to a multiple of 16, at most 2^40) of device memory
+ * at `buf` (16-byte aligned) with non-temporal 16-byte buffer loads.  The
+ * buffer is cut into tiles of loads x 4 KiB, handed round-robin to `wgs`
+ * workgroups of 256 threads, each lane keeping `loads` (2, 4, 8 or 16)
+ * loads in flight per tile; workgroup g writes one word to sink[g] (device,
+ * >= wgs words) so the reads cannot be dropped.  The measured roofline
+ * beside the spec sheet [sm8x-bench, methodology: a bandwidth probe gives
+ * the measured roofline]. */
+qg_status qg_read_probe(const void *buf, size_t bytes, uint32_t *sink, int wgs, int loads, void *stream);
 
 #ifdef __cplusplus
 }

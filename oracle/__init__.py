@@ -97,6 +97,17 @@ class Oracle:
         L.orc_quantize_act8.argtypes = [u16p, i64, i64, i8p, f32p]
         L.orc_gemv_q8act.restype = None
         L.orc_gemv_q8act.argtypes = [ctypes.c_int, u8p, i64, i64, i8p, f32p, i64, f64p, f64p]
+        L.orc_set_threads.restype = None
+        L.orc_set_threads.argtypes = [ctypes.c_int]
+        L.orc_max_threads.restype = ctypes.c_int
+        L.orc_max_threads.argtypes = []
+
+    def set_threads(self, n: int):
+        """OpenMP threads of the row loops (no change to any result)."""
+        self._L.orc_set_threads(int(n))
+
+    def max_threads(self) -> int:
+        return int(self._L.orc_max_threads())
 
     # -- helpers ---------------------------------------------------------
     @staticmethod

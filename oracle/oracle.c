@@ -80,6 +80,7 @@
  *   total  : (S0 + 2 * N * K / 32) rounded up to a multiple of 256.
  */
 #include <math.h>
+#include <omp.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <string.h>
@@ -534,3 +535,9 @@ void orc_gemv_q8act(int fmt, const uint8_t *p, int64_t N, int64_t K, const int8_
         }
     }
 }
+
+/* ------------------------------------------------------ thread control */
+
+/* OpenMP threads for the loops over output rows (changes no arithmetic). */
+void orc_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+int orc_max_threads(void) { return omp_get_max_threads(); }

@@ -77,7 +77,7 @@ def lib() -> ctypes.CDLL:
         "qg_time_next_launch": (None, [vp, vp]),
         "qg_device_cus": (c_int, [c_int, ctypes.POINTER(c_int)]),
         "qg_set_gemv_shape": (None, [c_int, c_int, c_int, c_int, i64, c_int, c_int, c_int]),
-        "qg_read_probe": (c_int, [vp, sz, vp, c_int, vp]),
+        "qg_read_probe": (c_int, [vp, sz, vp, c_int, c_int, vp]),
         "qg_set_prefill_shape": (None, [c_int, c_int]),
     }
     for name, (res, args) in sig.items():
@@ -346,12 +346,15 @@ def qg_set_gemv_shape(J: int = 0, R: int = 0, ksplit: int = 0, teams_per_wg: int
     lib().qg_set_gemv_shape(J, R, ksplit, teams_per_wg, teams, xl, engine, lanes)
 
 
-def qg_read_probe(buf, sink, wgs: int):
-    """Streaming read of the whole uint8 device tensor `buf` (bandwidth probe)."""
+def qg_read_probe(buf, sink, wgs: int, loads: int = 8, nbytes: int | None = None):
+    """Streaming read of the uint8 device tensor `buf` (its first `nbytes`
+    bytes, default all) by `wgs` workgroups with `loads` 16-byte loads in
+    flight per lane (bandwidth probe)."""
     torch = _torch()
-    bp = _dev(buf, torch.uint8, "buf")
+    n = buf.numel() if nbytes is None else int(nbytes)
+    bp = _dev(buf, torch.uint8, "buf", n)
     sp = _dev(sink, torch.int32, "sink", wgs)
-    _check("qg_read_probe", lib().qg_read_probe(bp, buf.numel(), sp, wgs, _stream()))
+    _check("qg_read_probe", lib().qg_read_probe(bp, n, sp, wgs, loads, _stream()))
 
 
 def qg_set_prefill_shape(splits: int = 0, bm: int = 0):

@@ -573,26 +573,35 @@ namespace qg {
 namespace {
 
 struct ProbeArgs {
-    const uint4 *p;
-    int64_t n16;       // 16-byte words to read
+    const uint8_t *p;
+    int64_t bytes;     // multiple of 16
     uint32_t *sink;    // one word per workgroup keeps the loads live
 };
 
-// Streaming read of a buffer with 16-byte loads, grid-stride, four loads in
-// flight per lane: the achievable read bandwidth of the memory system.
+// Streaming read on the GEMV kernels' own load path: non-temporal 16-byte
+// buffer loads from a scalar descriptor.  The buffer is cut into tiles of
+// U x 4 KiB handed round-robin to the workgroups (consecutive workgroups read
+// consecutive tiles, as consecutive GEMV teams read consecutive rows); each
+// lane has U loads in flight per tile.  Loads past the end of the buffer
+// fall outside the tile's descriptor and return zeros without touching
+// memory.  [sm8x-bench, methodology: a bandwidth probe gives the measured
+// roofline beside the spec]
+template <int U>
 __global__ __launch_bounds__(256) void read_probe_kernel(ProbeArgs a)
 {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    constexpr int64_t kTile = (int64_t)U * 256 * 16;
+    const int64_t ntiles = (a.bytes + kTile - 1) / kTile;
     uint32_t acc = 0;
-    for (; i + 3 * stride < a.n16; i += 4 * stride) {
-        const uint4 v0 = a.p[i], v1 = a.p[i + stride], v2 = a.p[i + 2 * stride], v3 = a.p[i + 3 * stride];
-        acc ^= v0.x ^ v0.y ^ v0.z ^ v0.w ^ v1.x ^ v1.y ^ v1.z ^ v1.w;
-        acc ^= v2.x ^ v2.y ^ v2.z ^ v2.w ^ v3.x ^ v3.y ^ v3.z ^ v3.w;
-    }
-    for (; i < a.n16; i += stride) {
-        const uint4 v = a.p[i];
-        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const int64_t base = t * kTile;
+        const auto r = make_rsrc(a.p + base, min(kTile, a.bytes - base));
+        uint4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            v[u] = stream_load16(r, (uint32_t)(threadIdx.x + u * 256) * 16u);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
     }
     __shared__ uint32_t s[256];
     s[threadIdx.x] = acc;
@@ -608,16 +617,23 @@ __global__ __launch_bounds__(256) void read_probe_kernel(ProbeArgs a)
 }  // namespace
 }  // namespace qg
 
-extern "C" qg_status qg_read_probe(const void *buf, size_t bytes, uint32_t *sink, int wgs, void *stream)
+extern "C" qg_status qg_read_probe(const void *buf, size_t bytes, uint32_t *sink, int wgs, int loads, void *stream)
 {
     if (!buf || !sink)
         return QG_ERR_NULL;
-    if (bytes < 16 || wgs < 1)
+    if (bytes < 16 || wgs < 1 || bytes > ((size_t)1 << 40))
         return QG_ERR_SHAPE;
     if (!qg::aligned(buf, 16) || !qg::aligned(sink, 4))
         return QG_ERR_ALIGN;
-    qg::ProbeArgs a{static_cast<const uint4 *>(buf), static_cast<int64_t>(bytes / 16), sink};
-    hipError_t e = qg::launch_kernel(reinterpret_cast<const void *>(&qg::read_probe_kernel), dim3(wgs), dim3(256),
-                                     0, static_cast<hipStream_t>(stream), a);
+    const void *fn;
+    switch (loads) {
+    case 2: fn = reinterpret_cast<const void *>(&qg::read_probe_kernel<2>); break;
+    case 4: fn = reinterpret_cast<const void *>(&qg::read_probe_kernel<4>); break;
+    case 8: fn = reinterpret_cast<const void *>(&qg::read_probe_kernel<8>); break;
+    case 16: fn = reinterpret_cast<const void *>(&qg::read_probe_kernel<16>); break;
+    default: return QG_ERR_SHAPE;
+    }
+    qg::ProbeArgs a{static_cast<const uint8_t *>(buf), static_cast<int64_t>(bytes / 16 * 16), sink};
+    hipError_t e = qg::launch_kernel(fn, dim3(wgs), dim3(256), 0, static_cast<hipStream_t>(stream), a);
     return e == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
 }

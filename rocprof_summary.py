@@ -21,7 +21,8 @@ import sys
 
 HERE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "quantized_weight_gemv_amd")
 # the files that determine the GEMV kernel and its launch shapes
-GEMV_SOURCES = ["csrc/qgemv_gemv.hip", "csrc/qgemv_capi.hip", "csrc/qgemv_internal.h"]
+GEMV_SOURCES = ["csrc/qgemv_gemv_impl.h", "csrc/qgemv_gemv_q4_0.hip", "csrc/qgemv_gemv.hip", "csrc/qgemv_capi.hip",
+                "csrc/qgemv_internal.h"]
 
 LLAMA_SHAPES = [(4096, 4096), (6144, 4096), (14336, 4096), (4096, 14336), (28672, 4096), (128256, 4096)]
 

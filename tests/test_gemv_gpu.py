@@ -9,13 +9,13 @@ import pytest
 
 import oracle
 import seeded_inputs as si
-from gpu_util import Q2W, Q4_0, Q8_0, acts, assert_within, pack_both, qg, sample_rows, to_dev, torch_cuda, weights
+from gpu_util import (Q2W, Q4_0, Q8_0, acts, assert_within, check_equal, pack_both, qg, to_dev,
+                      torch_cuda, weights)
 
 pytestmark = pytest.mark.gpu
 
 FMTS = [Q4_0, Q8_0, Q2W]
 FNAME = {Q4_0: "q4_0", Q8_0: "q8_0", Q2W: "q2w"}
-CODE_BYTES = {Q4_0: 16, Q8_0: 32, Q2W: 8}
 
 
 def _gemv_fn(fmt):
@@ -54,8 +54,8 @@ def test_dequant_bit_exact(fmt, N, K):
     f16 = deq(Wd, N, K, fp16=True)
     torch.cuda.synchronize()
     o = oracle.get()
-    assert np.array_equal(f32.cpu().numpy().view(np.uint32), o.dequant(fmt, po, N, K, "f32").view(np.uint32))
-    assert np.array_equal(f16.cpu().numpy().view(np.uint16), o.dequant(fmt, po, N, K, "f16").view(np.uint16))
+    check_equal(f32.cpu().numpy(), o.dequant(fmt, po, N, K, "f32"), f"dequant {FNAME[fmt]} {N}x{K} fp32")
+    check_equal(f16.cpu().numpy(), o.dequant(fmt, po, N, K, "f16"), f"dequant {FNAME[fmt]} {N}x{K} fp16")
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FNAME[f])
@@ -87,34 +87,18 @@ def test_gemv_q4_0_2048_seed0():
     assert_within(y, y_ref, s, "2048x2048")
 
 
+@pytest.mark.parametrize("fmt", [Q4_0, Q2W], ids=lambda f: FNAME[f])
 @pytest.mark.parametrize("N,K", si.LLAMA3_8B_SHAPES)
-def test_gemv_q4_0_llama3_8b_full_size(N, K):
+def test_gemv_llama3_8b_full_size(fmt, N, K):
     """Full-size Llama-3-8B projection shapes at one token, in the launch
-    configuration the bench times, checked on sampled rows."""
+    configuration the bench times: every output against the oracle."""
     w = si.weights(N, K, seed=0)
     x = si.activations(1, K, seed=0)
-    pb, po = pack_both(Q4_0, w)
+    pb, po = pack_both(fmt, w)
     del w
-    y = _gemv(Q4_0, to_dev(pb), to_dev(x), N, K)
-    rows = sample_rows(N)
-    y_ref, s = oracle.get().gemv_rows(Q4_0, po, N, K, x, rows)
-    assert_within(y[:, rows], y_ref, s, f"{N}x{K}")
-    assert np.isfinite(y).all()
-
-
-@pytest.mark.parametrize("N,K", si.LLAMA3_8B_SHAPES)
-def test_gemv_q2w_llama3_8b_full_size(N, K):
-    """Plain 2-bit weights on the full-size Llama-3-8B shapes at one token,
-    checked on sampled rows."""
-    w = si.weights(N, K, seed=0)
-    x = si.activations(1, K, seed=0)
-    pb, po = pack_both(Q2W, w)
-    del w
-    y = _gemv(Q2W, to_dev(pb), to_dev(x), N, K)
-    rows = sample_rows(N)
-    y_ref, s = oracle.get().gemv_rows(Q2W, po, N, K, x, rows)
-    assert_within(y[:, rows], y_ref, s, f"q2w {N}x{K}")
-    assert np.isfinite(y).all()
+    y = _gemv(fmt, to_dev(pb), to_dev(x), N, K)
+    y_ref, s = oracle.get().gemv(fmt, po, N, K, x)
+    assert_within(y, y_ref, s, f"{FNAME[fmt]} {N}x{K}")
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FNAME[f])
@@ -146,7 +130,7 @@ def test_one_hot_columns_are_exact(fmt):
     for lo in range(0, len(cols), 8):
         y = _gemv(fmt, Wd, to_dev(x[lo:lo + 8]), N, K)
         for i, k in enumerate(cols[lo:lo + 8]):
-            assert np.array_equal(y[i], wh[:, k]), f"column {k}"
+            check_equal(y[i], wh[:, k], f"{FNAME[fmt]} one-hot column {k}", bits=False)
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FNAME[f])
@@ -231,35 +215,6 @@ def test_deterministic_and_copy_invariant(fmt):
     ys = [f(A, xd, N, K), f(B, xd, N, K), f(A, xd, N, K)]
     torch.cuda.synchronize()
     assert torch.equal(ys[0], ys[1]) and torch.equal(ys[0], ys[2])
-
-
-@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FNAME[f])
-def test_sabotaged_weights_fail_every_check(fmt):
-    """Corrupt the device copy (code bytes XOR 0x11, scale signs flipped); the
-    oracle keeps the clean bytes, so every packed-kernel check must fail
-    [volta-kernel-bakeoff, "Making it fair"]."""
-    torch = torch_cuda()
-    o = oracle.get()
-    failed = checks = 0
-    for (N, K, M) in ((64, 2048, 1), (130, 2560, 4), (257, 4096, 8)):
-        w = weights(N, K, seed=N)
-        x = acts(M, K, seed=N)
-        pb, po = pack_both(fmt, w)
-        bad = pb.copy()
-        nb = N * K // 32
-        cb = CODE_BYTES[fmt]
-        bad[:nb * cb] ^= 0x11
-        s0 = (nb * cb + 255) // 256 * 256
-        bad[s0 + 1:s0 + 2 * nb:2] ^= 0x80
-        y = _gemv(fmt, to_dev(bad), to_dev(x), N, K)
-        y_ref, s = o.gemv(fmt, po, N, K, x)
-        checks += 1
-        failed += int(not oracle.within_bound(y, y_ref, s).all())
-        deq = _dequant_fn(fmt)(to_dev(bad), N, K)
-        torch.cuda.synchronize()
-        checks += 1
-        failed += int(not np.array_equal(deq.cpu().numpy(), o.dequant(fmt, po, N, K, "f32")))
-    assert failed == checks
 
 
 def test_abi_errors_are_reported_before_launch():
@@ -373,7 +328,7 @@ def test_gemv_matrix_core_engine(fmt, N, K, M):
         y = _gemv(fmt, Wd, to_dev(xo), N, K)
         wh = oracle.get().dequant(fmt, po, N, K, "f32")
         for i, k in enumerate(cols):
-            assert np.array_equal(y[i], wh[:, k]), f"one-hot column {k}"
+            check_equal(y[i], wh[:, k], f"{FNAME[fmt]} mfma one-hot column {k}", bits=False)
     finally:
         q.qg_set_gemv_shape(0, 0, 0, 0, 0, -1, -1, 0)
     assert tried >= 2   # long rows admit only the larger wave counts (<= 32 blocks per wave)

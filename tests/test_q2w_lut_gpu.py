@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 import seeded_inputs as si
-from gpu_util import Q2W, assert_within, pack_both, qg, sample_rows, to_dev, torch_cuda
+from gpu_util import Q2W, assert_within, check_equal, check_ok, pack_both, qg, to_dev, torch_cuda
 
 pytestmark = pytest.mark.gpu
 
@@ -54,7 +54,7 @@ def test_q2w_lut_large_and_one_hot_activations():
         e = np.zeros((1, K), np.float16)
         e[0, k] = 1.0
         yk = _lut(Wd, e, N, K)
-        assert np.array_equal(yk[0], wh[:, k]), f"one-hot column {k}"
+        check_equal(yk[0], wh[:, k], f"q2w lut one-hot column {k}", bits=False)
 
 
 def test_q2w_lut_abi_errors():
@@ -78,16 +78,14 @@ def test_q2w_lut_abi_errors():
 @pytest.mark.parametrize("N,K", [(N, K) for (N, K) in si.LLAMA3_8B_SHAPES if K <= 4096])
 def test_q2w_lut_llama3_8b_full_size(N, K):
     """The Llama-3-8B shapes the tables fit (K <= 4096) at full size, in the
-    launch the suite times, checked on sampled rows; every output finite."""
+    launch the suite times: every output against the oracle."""
     w = si.weights(N, K, seed=0)
     x = si.activations(1, K, seed=0)
     pb, po = pack_both(Q2W, w)
     del w
     y = _lut(to_dev(pb), x, N, K)
-    rows = sample_rows(N)
-    y_ref, s = oracle.get().gemv_rows(Q2W, po, N, K, x, rows)
-    assert_within(y[:, rows], y_ref, s, f"q2w lut {N}x{K}")
-    assert np.isfinite(y).all()
+    y_ref, s = oracle.get().gemv(Q2W, po, N, K, x)
+    assert_within(y, y_ref, s, f"q2w lut {N}x{K}")
 
 
 def test_q2w_lut_matches_unpacking_kernel_within_bound():
@@ -104,3 +102,5 @@ def test_q2w_lut_matches_unpacking_kernel_within_bound():
     y_unp = qg().qgemv_q2w(Wd, to_dev(x), N, K).cpu().numpy()
     _, s = oracle.get().gemv_rows(Q2W, po, N, K, x, np.arange(N))
     assert (np.abs(y_lut.astype(np.float64) - y_unp) <= 2e-3 * s + 2e-6).all()
+    y_ref, _ = oracle.get().gemv(Q2W, po, N, K, x)
+    assert_within(y_lut, y_ref, s, "q2w lut 28672x4096")

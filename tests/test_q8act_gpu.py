@@ -6,7 +6,7 @@ import pytest
 
 import oracle
 import seeded_inputs as si
-from gpu_util import Q2W, Q4_0, assert_within, pack_both, qg, to_dev, torch_cuda
+from gpu_util import Q2W, Q4_0, assert_within, check_equal, check_ok, pack_both, qg, to_dev, torch_cuda
 
 pytestmark = pytest.mark.gpu
 
@@ -101,14 +101,15 @@ def test_q8act_codes_bit_exact():
     qx, dx = oracle.get().quantize_act8(x16)
     y_ref, s = oracle.get().gemv_q8act(po, N, K, x16)
     # one term per output: the fp32 result is the exact value rounded twice
-    assert (np.abs(y - y_ref) <= 2.5e-7 * np.abs(y_ref) + 1e-30).all()
+    check_ok(np.abs(y - y_ref) <= 2.5e-7 * np.abs(y_ref) + 1e-30, "q8act one term per output")
     # so the codes agree: output k over (dequantized weight k times dx of
     # k's block) is the activation code qx_k
     wk = oracle.get().dequant(Q4_0, po, N, K, "f64")[np.arange(N), np.arange(K)]
     assert (wk != 0).all()
     scale = np.repeat(dx.astype(np.float64), 32, axis=1) * wk[None, :]
     nz = scale != 0
-    assert np.array_equal(np.rint(y[nz] / scale[nz]), qx.astype(np.float64)[nz])
+    check_equal(np.rint(y[nz] / scale[nz]), qx.astype(np.float64)[nz], "q8act codes from one-term outputs",
+                bits=False)
     assert (y[~nz] == 0).all() and (qx[~nz] == 0).all()
 
 
