@@ -337,18 +337,32 @@ def _time_calls(qg, torch, calls, reps: int, warm: int = 5):
     return float(np.median(ms) * 1e3), float(ms.mean() * 1e3)
 
 
-def _time_wall(torch, fns, reps: int, warm: int = 5):
-    """Per-call time (us) from torch events around each call on the current
-    stream (includes every kernel a call launches and the gaps between them)."""
+def _time_graph(torch, fns, reps: int, warm: int = 5, calls: int = 20, rounds: int = 7):
+    """Per-call time (us) of `calls` calls captured back to back in one HIP
+    graph, the median of `rounds` replays timed by stream events: every kernel
+    a call launches and the gaps between them, without the host launch path
+    (`reps` and `warm` are the warm-up calls before capture)."""
     for i in range(warm):
         fns[i % len(fns)]()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for i in range(reps):
-        ev[i][0].record()
-        fns[(i + warm) % len(fns)]()
-        ev[i][1].record()
     torch.cuda.synchronize()
-    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            for i in range(calls):
+                fns[(i + warm) % len(fns)]()
+    torch.cuda.synchronize()
+    g.replay()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(rounds + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for r in range(rounds):
+        g.replay()
+        ev[r + 1].record()
+    torch.cuda.synchronize()
+    ms = np.array([ev[r].elapsed_time(ev[r + 1]) for r in range(rounds)]) / calls
+    del g
     return float(np.median(ms) * 1e3), float(ms.mean() * 1e3)
 
 
@@ -463,13 +477,13 @@ def suite(qg, torch, reps: int):
         y = torch.empty((M, N), dtype=torch.float32, device="cuda")
         fns = [lambda c=c: qg.qgemv_q4_0_f32in(buf[c * nb:(c + 1) * nb], x, N, K, y) for c in range(copies)]
         med, mean = _time_calls(qg, torch, fns, reps)
-        wmed, _ = _time_wall(torch, fns, reps)
+        wmed, _ = _time_graph(torch, fns, reps)
         two = [lambda c=c: qg.qgemv_q4_0(buf[c * nb:(c + 1) * nb], x.half(), N, K, y) for c in range(copies)]
-        smed, _ = _time_wall(torch, two, reps)
+        smed, _ = _time_graph(torch, two, reps)
         b = N * K // 32 * 18 + 4 * M * K + 4 * M * N
         rec(kind="f32in", fmt="q4_0", N=N, K=K, M=M, us_median=round(med, 3), us_mean=round(mean, 3),
             GBps=round(b / med / 1e3, 1), pct_of_8TBps=round(b / med / 1e3 / 80, 2), algorithmic_bytes=b,
-            wall_us_median=round(wmed, 3), separate_conversion_wall_us_median=round(smed, 3), copies=copies)
+            graph_us_median=round(wmed, 3), separate_conversion_graph_us_median=round(smed, 3), copies=copies)
         del buf
 
     # gate + up stacked in one 2N-row table with SwiGLU in the epilogue, beside
@@ -485,17 +499,17 @@ def suite(qg, torch, reps: int):
             fns = [lambda c=c: qg.qgemv_q4_0_swiglu_f32in(buf[c * nb:(c + 1) * nb], x, N, K, y)
                    for c in range(copies)]
             med, mean = _time_calls(qg, torch, fns, reps)
-            wmed, _ = _time_wall(torch, fns, reps)
+            wmed, _ = _time_graph(torch, fns, reps)
 
             def unfused(c):
                 qg.qgemv_q4_0(buf[c * nb:(c + 1) * nb], x.half(), 2 * N, K, gu)
                 torch.mul(torch.nn.functional.silu(gu[:, :N]), gu[:, N:], out=y)
             ufn = [lambda c=c: unfused(c) for c in range(copies)]
-            umed, _ = _time_wall(torch, ufn, reps)
+            umed, _ = _time_graph(torch, ufn, reps)
             b = 2 * N * K // 32 * 18 + 4 * M * K + 4 * M * N
             rec(kind="swiglu", fmt="q4_0", N=N, K=K, M=M, us_median=round(med, 3), us_mean=round(mean, 3),
                 GBps=round(b / med / 1e3, 1), pct_of_8TBps=round(b / med / 1e3 / 80, 2), algorithmic_bytes=b,
-                wall_us_median=round(wmed, 3), unfused_wall_us_median=round(umed, 3), copies=copies)
+                graph_us_median=round(wmed, 3), unfused_graph_us_median=round(umed, 3), copies=copies)
         del buf
         torch.cuda.empty_cache()
 
@@ -510,14 +524,13 @@ def suite(qg, torch, reps: int):
             X = torch.from_numpy(si.activations(M, K, seed=0)).to("cuda")
             Y = torch.empty((M, N), dtype=torch.float32, device="cuda")
             fns = [lambda c=c: qg.qgemm_q4_0_prefill(buf[c * nb:(c + 1) * nb], X, N, K, Y) for c in range(copies)]
-            kmed, _ = _time_calls(qg, torch, fns, reps)
-            med, mean = _time_wall(torch, fns, reps)
+            med, mean = _time_graph(torch, fns, reps)
             dense = [lambda c=c: torch.matmul(X, w16[c]) for c in range(len(w16))]
-            dmed, _ = _time_wall(torch, dense, reps)
+            dmed, _ = _time_graph(torch, dense, reps)
             flops = 2 * M * N * K
             b = N * K // 32 * 18 + 2 * M * K + 4 * M * N
             rec(kind="prefill", fmt="q4_0", N=N, K=K, M=M, us_median=round(med, 3), us_mean=round(mean, 3),
-                gemm_kernel_us_median=round(kmed, 3), TFLOPs=round(flops / med / 1e6, 1),
+                TFLOPs=round(flops / med / 1e6, 1),
                 pct_of_2500TF=round(flops / med / 1e6 / 25, 2), GBps=round(b / med / 1e3, 1),
                 dense_fp16_us_median=round(dmed, 3), speedup_vs_dense=round(dmed / med, 3), copies=copies)
         del buf, w16

@@ -51,11 +51,16 @@ qg_status qg_device_cus(int device, int *cus);
 void qg_set_gemv_shape(int J, int R, int ksplit, int teams_per_wg, int64_t teams, int xl, int engine,
                        int lanes_per_row);
 
-/* Tuning knob for sweeps of qgemm_q4_0_prefill: fixes the number of
- * workgroups sharing one output tile along K (splits; more than one adds fp32
- * partial tiles atomically into a zero-filled Y) and the token tile (bm: 64 or
- * 128) for later calls from the calling thread.  0 keeps the built-in choice. */
-void qg_set_prefill_shape(int splits, int bm);
+/* Tuning knob for sweeps of qgemm_q4_0_prefill, for later calls from the
+ * calling thread: `wgs` fixes the number of persistent workgroups among
+ * which the (tile, K step) iterations are split (a workgroup whose range
+ * covers part of a tile adds it atomically into a zero-filled Y); `tile`
+ * picks the tile configuration (tokens x rows): 64 (64 x 128, two
+ * workgroups per CU), 66 (64 x 256, two per CU), 128 (128 x 256, one per CU),
+ * 130 (128 x 128, two per CU), 257 (256 x 128, waves 2 x 2, one per CU).  0
+ * keeps the built-in choice; an unknown tile makes the later calls return
+ * QG_ERR_SHAPE. */
+void qg_set_prefill_shape(int wgs, int tile);
 
 /* Memory-bandwidth probe on the GEMV kernels' load path: a streaming read of
  * `bytes` (rounded down to a multiple of 16, at most 2^40) of device memory

@@ -1,22 +1,50 @@
 // Q4_0 prefill GEMM on the gfx950 matrix cores:
 //   Y[m][n] = sum_k X[m][k] * w[n][k],  w = (q - 8) * d
 //
-// With many tokens the work is a dense contraction, so it belongs on MFMA:
-// each workgroup stages a BM x 64 activation tile and a BN x 64 weight tile
-// in LDS per step, the weight tile dequantized on the way in (packed codes ->
-// fp16 values, the same round-to-nearest-even values qdequant_q4_0 writes),
-// and four waves multiply them with v_mfma_f32_32x32x16_f16 into fp32
-// accumulators [volta-kernel-bakeoff, "What's in the race" (tc_q4: unpack a
-// tile to shared memory, then matrix-core multiply) and "Stage 3" (unpack
-// inside the multiply instead of dequantize-to-fp16 followed by a dense GEMM)].
+// With many tokens the work is a dense contraction, so it belongs on MFMA
+// (v_mfma_f32_32x32x16_f16, fp32 accumulators) [volta-kernel-bakeoff, "What's
+// in the race" (tc_q4: unpack a tile, then matrix-core multiply) and
+// "Stage 3" (unpack inside the multiply instead of dequantize-to-fp16
+// followed by a dense GEMM)].
 //
-// Pipeline per 64-wide K step: the global loads of the next three steps are in
-// flight in registers; the MFMAs of step s run out of one of two LDS buffers
-// while the next step is dequantized into the other, one barrier per step.  Both tiles are stored in the same permuted
-// k order within each 32-element block (the order the nibble unpack produces),
-// which leaves the contraction unchanged.  When the output tiles are too few
-// to occupy the chip, K is split across workgroups that add their partial
-// tiles with fp32 atomics into a zero-filled Y.
+// Data path.  A 64-wide K step covers two Q4_0 blocks; four steps (eight
+// blocks, 128 code bytes per row) form a group.
+//   * Weights: each wave loads its own 32-row tiles a group at a time with
+//     whole-line loads (8 lanes per row, 16 bytes each), writes them to a
+//     wave-private LDS buffer (16-byte chunks XOR-swizzled by row, so the
+//     reads below hit distinct banks) and, per step, lane l reads back the 16
+//     code bytes of row l % 32, block 2s + l / 32.  Two v_permlane32_swap
+//     then leave every lane the 8 bytes of each block that its MFMA operand
+//     needs (the B operand of lane l holds k = 8 (l / 32) .. +7 of row
+//     l % 32: low nibbles of bytes 8 (l / 32) .. +7 for the block's first 16
+//     k, high nibbles for the last 16), in natural k order.  The nibbles
+//     become fp16 through the 0x6400 pattern (1024 + q, exact), the offset
+//     is removed exactly and one correctly rounded fp16 multiply by the block
+//     scale gives the same values qdequant_q4_0 writes with fp16 output.
+//     The eight scales of a row's group are one 16-byte load.  Loading a
+//     step's 32 bytes of each of 32 rows directly would touch 32 cache lines
+//     per instruction for a quarter line each; the request count, not the
+//     bytes, then bounds the kernel.
+//   * Activations: a plain copy of the tile's X rows into LDS per step
+//     (natural k order, rows padded to 72 halves: conflict-free 16-byte
+//     reads), read back as the A operands.
+//   * Each wave owns 32 TM tokens x 32 TN rows of the workgroup's tile (WM
+//     waves along M, 4 / WM along N); with WM = 1 no weight is unpacked twice.
+//
+// Work split (stream-K): the (tile, K step) iterations are numbered tile by
+// tile and cut into equal contiguous ranges of whole groups, one per
+// workgroup of a persistent grid, so the chip stays busy however few tiles
+// there are.  A workgroup whose range covers a whole tile stores it; partial
+// tiles are added with fp32 atomics into Y, which a small fill kernel zeroes
+// first (last-bit differences between runs, within the accuracy bound).
+//
+// Pipelining: the activation loads of the next four steps and the weight
+// loads of the next group are in flight in registers while the current step
+// is multiplied (one load counter counts them in issue order, so both lead
+// by four steps); the activation tile is double-buffered in LDS, one barrier
+// per step.  Every load is issued unconditionally (positions past a
+// workgroup's range repeat its last one and are never used), so the compiler
+// waits for exactly the stage a step consumes.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -33,9 +61,7 @@ typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f16x_t __attribute__((ext_vector_type(16)));
 
-constexpr int kBK = 64;          // K per pipeline step: two Q4_0 blocks
-constexpr int kDepth = 3;        // K steps of global loads in flight
-constexpr int kLdsStride = 72;   // halves per LDS tile row: 64 + 8 padding
+constexpr int kLdsStride = 72;   // halves per LDS activation row: 64 + 8 padding
 
 __device__ __forceinline__ h2_t as_h2(uint32_t u) { return __builtin_bit_cast(h2_t, u); }
 __device__ __forceinline__ uint32_t as_u32(h2_t h) { return __builtin_bit_cast(uint32_t, h); }
@@ -47,46 +73,36 @@ __device__ __forceinline__ uint32_t magic_reg()
     return m;
 }
 
-// One Q4_0 block -> 16 words of fp16 pairs (q - 8) * d, rounded to nearest
-// even, in the permuted order
-//   word 4t+0 = (e[4t], e[4t+2])      word 4t+2 = (e[4t+1], e[4t+3])
-//   word 4t+1 = (e[16+4t], e[18+4t])  word 4t+3 = (e[17+4t], e[19+4t])
-// (q - 8) is exact in fp16 (1024 + q from the 0x6400 pattern, minus 1032;
-// for the high nibbles (1024 + 16 q) / 16 - 72); the product with d is one
-// correctly rounded fp16 multiply.
-__device__ __forceinline__ void dequant_block_f16(const uint4 c, uint16_t dbits, uint32_t (&o)[16])
+// 8 code bytes of one block (p0 = bytes 0-3, p1 = bytes 4-7 of the lane's
+// half) -> two B operands in natural k order: lo = the 8 low nibbles (the
+// block's first 16 k for this lane's half), hi = the 8 high nibbles, each
+// weight (q - 8) * d rounded once to fp16.
+__device__ __forceinline__ void unpack8(uint32_t p0, uint32_t p1, h2_t d2, uint32_t magic, half8_t &lo, half8_t &hi)
 {
-    const uint32_t kMagic = magic_reg();
     const h2_t kOffLo = {(_Float16)-1032.0f, (_Float16)-1032.0f};
     const h2_t kScaleHi = {(_Float16)0.0625f, (_Float16)0.0625f};
     const h2_t kOffHi = {(_Float16)-72.0f, (_Float16)-72.0f};
-    const _Float16 dh = __builtin_bit_cast(_Float16, dbits);
-    const h2_t d2 = {dh, dh};
-    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    const uint32_t w[2] = {p0, p1};
+    uint32_t l[4], h[4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const uint32_t nl = w[t] & 0x0F0F0F0Fu;   // low nibbles, one per byte
+        const uint32_t nh = w[t] & 0xF0F0F0F0u;   // high nibbles, times 16
+        // bytes (n0, 0x64, n1, 0x64) and (n2, 0x64, n3, 0x64): the halves
+        // 1024 + n of consecutive elements
+        l[2 * t + 0] = __builtin_amdgcn_perm(magic, nl, 0x07010500u);
+        l[2 * t + 1] = __builtin_amdgcn_perm(magic, nl, 0x07030502u);
+        h[2 * t + 0] = __builtin_amdgcn_perm(magic, nh, 0x07010500u);
+        h[2 * t + 1] = __builtin_amdgcn_perm(magic, nh, 0x07030502u);
+    }
+    uint32_t ol[4], oh[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        const uint32_t a = w[t];
-        const uint32_t b = w[t] >> 8;
-        o[4 * t + 0] = as_u32((as_h2((a & 0x000F000Fu) | kMagic) + kOffLo) * d2);
-        o[4 * t + 1] = as_u32((as_h2((a & 0x00F000F0u) | kMagic) * kScaleHi + kOffHi) * d2);
-        o[4 * t + 2] = as_u32((as_h2((b & 0x000F000Fu) | kMagic) + kOffLo) * d2);
-        o[4 * t + 3] = as_u32((as_h2((b & 0x00F000F0u) | kMagic) * kScaleHi + kOffHi) * d2);
+        ol[t] = as_u32((as_h2(l[t]) + kOffLo) * d2);                // (q - 8) * d
+        oh[t] = as_u32((as_h2(h[t]) * kScaleHi + kOffHi) * d2);     // (1024 + 16 q) / 16 - 72 = q - 8
     }
-}
-
-__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
-__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
-
-// 32 activations (natural order, 16 words) -> the permuted order above.
-__device__ __forceinline__ void permute_x(const uint32_t (&d)[16], uint32_t (&o)[16])
-{
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        o[4 * t + 0] = pair_lo(d[2 * t], d[2 * t + 1]);
-        o[4 * t + 2] = pair_hi(d[2 * t], d[2 * t + 1]);
-        o[4 * t + 1] = pair_lo(d[8 + 2 * t], d[9 + 2 * t]);
-        o[4 * t + 3] = pair_hi(d[8 + 2 * t], d[9 + 2 * t]);
-    }
+    lo = __builtin_bit_cast(half8_t, make_uint4(ol[0], ol[1], ol[2], ol[3]));
+    hi = __builtin_bit_cast(half8_t, make_uint4(oh[0], oh[1], oh[2], oh[3]));
 }
 
 struct PrefillParams {
@@ -95,117 +111,213 @@ struct PrefillParams {
     float *Y;                  // fp32 [M][N]
     int64_t scale_offset;
     int M, N, K;
-    int steps_per_split;       // K steps (of 64) per workgroup along z
-    int atomic;                // 1: add partial tiles into Y (split K)
+    int tiles_n;               // output tiles along N
+    int steps;                 // K steps per tile: ceil(K / 64) rounded up to a group of 4
+    int chunks;                // tiles * steps / 4 (< 2^31 / 4, checked on the host)
 };
 
-// Per-thread staging registers for one K step.
-template <int BM, int BN>
-struct Stage {
-    static constexpr int kXChunks = (BM * 2 + 255) / 256;   // 32-element chunks per thread
-    static constexpr int kWBlocks = (BN * 2 + 255) / 256;   // Q4_0 blocks per thread
-    uint4 x[kXChunks][4];
-    uint4 code[kWBlocks];
-    uint16_t scale[kWBlocks];
+constexpr int kGroup = 4;      // K steps per weight group (8 blocks)
+
+// Position of an iteration: output tile (tm along M, tn along N, tn
+// fastest) and K step s within it.  Advanced one step at a time, with no
+// division.
+struct Pos {
+    int tm, tn, s;
 };
 
-template <int BM, int BN>
-__device__ __forceinline__ void load_stage(Stage<BM, BN> &st, const PrefillParams &p, int m0, int n0, int step)
+__device__ __forceinline__ Pos pos_of(const PrefillParams &p, int it, int S)
 {
-    const int tid = threadIdx.x;
-    const int KB = p.K >> 5;
-    // Every thread issues every load (threads past the tile repeat its last
-    // chunk): with no load under a condition the compiler can wait for
-    // exactly the stage it needs while the later stages stay in flight.
-#pragma unroll
-    for (int c = 0; c < Stage<BM, BN>::kXChunks; ++c) {
-        const int idx = min(tid + 256 * c, BM * 2 - 1);   // chunk index within the BM x 2 tile
-        const int r = idx >> 1, b = idx & 1;
-        const int m = min(m0 + r, p.M - 1);
-        const int kb = min(step * 2 + b, KB - 1);
-        const uint4 *src = reinterpret_cast<const uint4 *>(p.X + (int64_t)m * p.K + (int64_t)kb * 32);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            st.x[c][q] = src[q];
-    }
-#pragma unroll
-    for (int c = 0; c < Stage<BM, BN>::kWBlocks; ++c) {
-        const int idx = min(tid + 256 * c, BN * 2 - 1);
-        const int r = idx >> 1, b = idx & 1;
-        const int64_t n = min(n0 + r, p.N - 1);
-        const int kb = min(step * 2 + b, KB - 1);
-        const int64_t bi = n * KB + kb;
-        typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-        const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p.W + bi * 16));
-        st.code[c] = make_uint4(t.x, t.y, t.z, t.w);
-        st.scale[c] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(p.W + p.scale_offset) + bi);
-    }
+    const int tile = it / S;
+    return Pos{tile / p.tiles_n, tile % p.tiles_n, it % S};
 }
 
-template <int BM, int BN>
-__device__ __forceinline__ void store_stage(const Stage<BM, BN> &st, const PrefillParams &p, int m0, int n0, int step,
-                                            uint16_t (*Xs)[kLdsStride], uint16_t (*Ws)[kLdsStride])
+__device__ __forceinline__ void advance(Pos &q, const PrefillParams &p, int S)
 {
-    const int tid = threadIdx.x;
-    const int KB = p.K >> 5;
-    // Threads past the tile store a repeat of its last chunk: the same bytes
-    // to the same place, so no store needs a condition either.  Activation
-    // rows past M and blocks past K hold clamped copies of real activations
-    // and are stored as they are: rows past M only reach output rows that are
-    // never written, and blocks past K meet weights whose scale is zeroed
-    // below.  (With no select the step body is one basic block.)
-#pragma unroll
-    for (int c = 0; c < Stage<BM, BN>::kXChunks; ++c) {
-        const int idx = min(tid + 256 * c, BM * 2 - 1);
-        const int r = idx >> 1, b = idx & 1;
-        {
-            uint32_t d[16], o[16];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                d[4 * q + 0] = st.x[c][q].x;
-                d[4 * q + 1] = st.x[c][q].y;
-                d[4 * q + 2] = st.x[c][q].z;
-                d[4 * q + 3] = st.x[c][q].w;
-            }
-            permute_x(d, o);
-            uint4 *dst = reinterpret_cast<uint4 *>(&Xs[r][b * 32]);
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                dst[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
-        }
-    }
-#pragma unroll
-    for (int c = 0; c < Stage<BM, BN>::kWBlocks; ++c) {
-        const int idx = min(tid + 256 * c, BN * 2 - 1);
-        const int r = idx >> 1, b = idx & 1;
-        {
-            const bool ok = (n0 + r < p.N) && (step * 2 + b < KB);
-            uint32_t o[16];
-            dequant_block_f16(st.code[c], ok ? st.scale[c] : (uint16_t)0, o);
-            uint4 *dst = reinterpret_cast<uint4 *>(&Ws[r][b * 32]);
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                dst[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+    if (++q.s == S) {
+        q.s = 0;
+        if (++q.tn == p.tiles_n) {
+            q.tn = 0;
+            ++q.tm;
         }
     }
 }
 
-template <int BM, int BN>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p)
+template <int WM, int TM, int TN>
+struct Tiling {
+    static constexpr int WN = 4 / WM;
+    static constexpr int BM = 32 * TM * WM;   // tokens per tile
+    static constexpr int BN = 32 * TN * WN;   // rows per tile
+    static constexpr int AC = BM / 32;        // 16-byte activation chunks per thread per step
+};
+
+// Registers of one step's activations, and of one group's weights (per row
+// tile: this lane's four 16-byte chunks of whole lines, and the eight scales
+// of its row).
+template <int AC>
+struct AStage {
+    uint4 a[AC];
+};
+
+template <int TN>
+struct WGroup {
+    uint4 code[TN][4];
+    uint4 scale[TN];
+};
+
+// Load cursors hold a position and the per-lane byte offsets of its tile
+// (they change only when the tile does); the K step enters as the scalar
+// offset of the buffer loads, so a step spends no vector instruction on
+// addresses.
+//   Activations: chunk c of thread t is the 16 bytes of row (t + 256 c) / 8
+//   of the tile (clamped to M - 1: rows past M are never stored) at k chunk
+//   (t + 256 c) % 8 of the step.
+//   Weights: instruction i of row tile j (32 rows from row n0 + 32 (wn TN +
+//   j)) has lane l read the 16 bytes of row 8 i + l / 8 at block 8 g + l % 8
+//   of group g; the scales: lane l reads the eight of row l % 32.  Rows are
+//   clamped to N - 1 (their scale is zeroed).
+// Blocks past K (padding steps, or the tail of the last group) read the next
+// row's bytes or, past the end, zeros; their activations and scales are
+// zeroed.
+template <int AC>
+struct ACursor {
+    Pos ps;
+    int it;
+    uint32_t off[AC];
+};
+
+template <int TN>
+struct WCursor {
+    Pos ps;                 // first step of the group
+    int it;
+    uint32_t off[TN][4];    // code byte offsets (block 8 g + l % 8 of row 8 i + l / 8)
+    uint32_t soff[TN];      // scale byte offsets (row l % 32, block 0)
+};
+
+template <int BM, int AC>
+__device__ __forceinline__ void a_offsets(ACursor<AC> &c, const PrefillParams &p)
 {
-    constexpr int TM = BM / 64;   // 32 x 32 MFMA tiles per wave along M
-    constexpr int TN = BN / 64;   // ... along N
-    __shared__ __attribute__((aligned(16))) uint16_t Xs[2][BM][kLdsStride];
-    __shared__ __attribute__((aligned(16))) uint16_t Ws[2][BN][kLdsStride];
+#pragma unroll
+    for (int i = 0; i < AC; ++i) {
+        const int idx = (int)threadIdx.x + 256 * i;
+        const int r = idx >> 3, ch = idx & 7;
+        const int m = min(c.ps.tm * BM + r, p.M - 1);
+        c.off[i] = (uint32_t)m * (uint32_t)p.K * 2u + (uint32_t)(ch >> 2) * 64u + (uint32_t)(ch & 3) * 16u;
+    }
+}
+
+template <int BN, int TN>
+__device__ __forceinline__ void w_offsets(WCursor<TN> &c, const PrefillParams &p, int KB, int lane, int wn)
+{
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int r0 = c.ps.tn * BN + 32 * (wn * TN + j);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = min(r0 + 8 * i + (lane >> 3), p.N - 1);
+            c.off[j][i] = ((uint32_t)row * (uint32_t)KB + (uint32_t)(lane & 7)) * 16u;
+        }
+        const int row = min(r0 + (lane & 31), p.N - 1);
+        c.soff[j] = (uint32_t)row * (uint32_t)KB * 2u;
+    }
+}
+
+// Advance by one step (activations) or one group (weights), up to the
+// workgroup's last step (loads past its range repeat the last position).
+template <int BM, int AC>
+__device__ __forceinline__ void a_step(ACursor<AC> &c, const PrefillParams &p, int S, int it_end)
+{
+    if (c.it + 1 < it_end) {
+        ++c.it;
+        advance(c.ps, p, S);
+        if (c.ps.s == 0)
+            a_offsets<BM>(c, p);
+    }
+}
+
+template <int BN, int TN>
+__device__ __forceinline__ void w_step(WCursor<TN> &c, const PrefillParams &p, int S, int it_end, int KB, int lane,
+                                       int wn)
+{
+    if (c.it + kGroup < it_end) {
+        c.it += kGroup;
+#pragma unroll
+        for (int q = 0; q < kGroup; ++q)
+            advance(c.ps, p, S);
+        if (c.ps.s == 0)
+            w_offsets<BN>(c, p, KB, lane, wn);
+    }
+}
+
+struct Rsrc {
+    __amdgpu_buffer_rsrc_t x, w, s;
+};
+
+template <int AC>
+__device__ __forceinline__ void load_a(AStage<AC> &st, const Rsrc &rs, const ACursor<AC> &c)
+{
+    const int so = c.ps.s * 128;   // 64 fp16 per step
+#pragma unroll
+    for (int i = 0; i < AC; ++i) {
+        const auto t = __builtin_amdgcn_raw_buffer_load_b128(rs.x, c.off[i], so, 0);
+        st.a[i] = make_uint4(t[0], t[1], t[2], t[3]);
+    }
+}
+
+// SA: rows hold a whole number of groups (K / 32 a multiple of 8), so a
+// row's eight scales of a group are one 16-byte load inside the row (4-byte
+// aligned); otherwise eight 2-byte loads.  Non-temporal: every weight line is
+// used by one load, and the stream must not evict the activations, which
+// every workgroup reads, from L2.
+template <int TN, bool SA>
+__device__ __forceinline__ void load_w(WGroup<TN> &st, const Rsrc &rs, const WCursor<TN> &c)
+{
+    const int g8 = c.ps.s * 2;   // first block of the group (8 per group)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const auto t = __builtin_amdgcn_raw_buffer_load_b128(rs.w, c.off[j][i], g8 * 16, kNtAux);
+            st.code[j][i] = make_uint4(t[0], t[1], t[2], t[3]);
+        }
+        if constexpr (SA) {
+            const auto t = __builtin_amdgcn_raw_buffer_load_b128(rs.s, c.soff[j], g8 * 2, kNtAux);
+            st.scale[j] = make_uint4(t[0], t[1], t[2], t[3]);
+        } else {
+            uint32_t h[8];
+#pragma unroll
+            for (int b = 0; b < 8; ++b)
+                h[b] = __builtin_amdgcn_raw_buffer_load_b16(rs.s, c.soff[j], g8 * 2 + 2 * b, kNtAux);
+            st.scale[j] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                                     h[6] | (h[7] << 16));
+        }
+    }
+}
+
+template <int WM, int TM, int TN, int OCC, bool SA>
+__global__ __launch_bounds__(256, OCC) void prefill_kernel(PrefillParams p)
+{
+    using T = Tiling<WM, TM, TN>;
+    constexpr int AC = T::AC;
+    constexpr int DB = kGroup;   // steps (and activation stages) in flight: one group
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][T::BM][kLdsStride];
+    __shared__ uint4 Wl[4][TN][32][8];   // per wave: the current group's code bytes, chunks swizzled by row
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave >> 1, wn = wave & 1;   // 2 x 2 waves
-    const int n0 = blockIdx.x * BN;
-    const int m0 = blockIdx.y * BM;
-    const int nsteps = (p.K / 32 + 1) / 2;
-    const int s_beg = blockIdx.z * p.steps_per_split;
-    const int s_end = min(nsteps, s_beg + p.steps_per_split);
+    const int wm = wave % WM, wn = wave / WM;
+    const int KB = p.K >> 5;
+    const int S = p.steps;   // 64-wide K steps per tile, whole groups (steps past K multiply zeros)
+    // this workgroup's range: whole groups, so a group never spans two tiles
+    const int it_beg = (int)((int64_t)p.chunks * blockIdx.x / gridDim.x) * kGroup;
+    const int it_end = (int)((int64_t)p.chunks * (blockIdx.x + 1) / gridDim.x) * kGroup;
+    if (it_beg >= it_end)
+        return;   // uniform over the workgroup
+    const uint32_t magic = magic_reg();
+
+    Rsrc rs;
+    rs.x = make_rsrc(reinterpret_cast<const uint8_t *>(p.X), (int64_t)p.M * p.K * 2);
+    rs.w = make_rsrc(p.W, (int64_t)p.N * KB * 16);
+    rs.s = make_rsrc(p.W + p.scale_offset, (int64_t)p.N * KB * 2);
 
     f16x_t acc[TM][TN];
 #pragma unroll
@@ -216,91 +328,187 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p)
             for (int r = 0; r < 16; ++r)
                 acc[i][j][r] = 0.0f;
 
-    // A ring of kDepth register stages keeps the global loads of the next
-    // kDepth K steps in flight.  Each iteration first issues the MFMAs of
-    // step s (reading LDS buffer s & 1), then unpacks and stores step s + 1
-    // into the other buffer, so the vector-ALU dequantization runs while the
-    // matrix cores work; one barrier per step.  The buffer written in
-    // iteration s was last read in iteration s - 1, before its barrier.
-    //
-    // Every stage load is issued unconditionally, also past the workgroup's
-    // last step (load_stage clamps to valid blocks; such stages are never
-    // multiplied): with the same load order on every path into the loop the
-    // compiler waits only for the stage a step consumes, while the later
-    // stages stay in flight.
-    Stage<BM, BN> st[kDepth];
+    // Global loads are counted in issue order by one counter, so a wait for
+    // one load waits for every load issued before it.  Activation stage r %
+    // DB holds iteration r's activations (copied to LDS one iteration before
+    // they are multiplied); the weight group in registers is the next group.
+    // Issue order: the group's weights with its first step's activations.
+    const Pos first = pos_of(p, it_beg, S);
+    ACursor<AC> la;
+    la.ps = first;
+    la.it = it_beg;
+    a_offsets<T::BM>(la, p);
+    WCursor<TN> lw;
+    lw.ps = first;
+    lw.it = it_beg;
+    w_offsets<T::BN>(lw, p, KB, lane, wn);
+    AStage<AC> sa[DB];
+    WGroup<TN> wg;
+    load_w<TN, SA>(wg, rs, lw);
+    w_step<T::BN>(lw, p, S, it_end, KB, lane, wn);
 #pragma unroll
-    for (int q = 0; q < kDepth; ++q)
-        load_stage<BM, BN>(st[q], p, m0, n0, s_beg + q);
-    store_stage<BM, BN>(st[0], p, m0, n0, s_beg, Xs[0], Ws[0]);
-    load_stage<BM, BN>(st[0], p, m0, n0, s_beg + kDepth);
-    __syncthreads();
+    for (int q = 0; q < DB; ++q) {
+        load_a(sa[q], rs, la);
+        a_step<T::BM>(la, p, S, it_end);
+    }
 
-    auto multiply = [&](int buf) {
+    // Store the activations of a stage (at K step s) into LDS buffer `buf`,
+    // zeroing blocks past K.  Activation stage r % DB holds step r's
+    // activations; they are copied to LDS one step before their MFMAs.
+    auto store_a = [&](const AStage<AC> &sg, int s, int buf) {
+        const bool full = 2 * s + 2 <= KB;   // uniform: both blocks of the step inside K
 #pragma unroll
-        for (int kk = 0; kk < kBK / 16; ++kk) {
-            const int col = kk * 16 + (lane >> 5) * 8;
-            half8_t a[TM], b[TN];
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-                a[i] = *reinterpret_cast<const half8_t *>(&Xs[buf][wm * (BM / 2) + 32 * i + (lane & 31)][col]);
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-                b[j] = *reinterpret_cast<const half8_t *>(&Ws[buf][wn * (BN / 2) + 32 * j + (lane & 31)][col]);
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+        for (int c = 0; c < AC; ++c) {
+            const int idx = (int)threadIdx.x + 256 * c;
+            const int r = idx >> 3, ch = idx & 7;
+            const bool ok = full || 2 * s + (ch >> 2) < KB;
+            const uint4 v = ok ? sg.a[c] : make_uint4(0u, 0u, 0u, 0u);
+            *reinterpret_cast<uint4 *>(&As[buf][r][ch * 8]) = v;
         }
     };
 
-    // Steps s0 .. s0 + kDepth - 1 per iteration, ring slot (s - s_beg) %
-    // kDepth static once unrolled.  Staging step s + 1 = s_end (last step
-    // of the last iteration) fills the unused buffer with data never read.
-    int s0 = s_beg;
-    for (; s0 + kDepth <= s_end; s0 += kDepth) {
+    // The weight group in registers -> this wave's LDS buffer: instruction i
+    // of row tile j holds row 8 i + l / 8, chunk l % 8, stored at chunk
+    // (l % 8) ^ (row % 8).  Wave-private: LDS operations of a wave complete
+    // in order, so no barrier is needed between these writes and the reads.
+    auto store_w = [&](const WGroup<TN> &g) {
 #pragma unroll
-        for (int q = 0; q < kDepth; ++q) {
-            const int s = s0 + q;
-            const int buf = (s - s_beg) & 1;
-            multiply(buf);
-            const int qn = (q + 1) % kDepth;
-            store_stage<BM, BN>(st[qn], p, m0, n0, s + 1, Xs[buf ^ 1], Ws[buf ^ 1]);
-            load_stage<BM, BN>(st[qn], p, m0, n0, s + 1 + kDepth);
-            __syncthreads();
-        }
-    }
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
-    for (int q = 0; q < kDepth - 1; ++q) {
-        const int s = s0 + q;
-        if (s < s_end) {
-            const int buf = (s - s_beg) & 1;
-            multiply(buf);
-            if (s + 1 < s_end)
-                store_stage<BM, BN>(st[(q + 1) % kDepth], p, m0, n0, s + 1, Xs[buf ^ 1], Ws[buf ^ 1]);
-            __syncthreads();
-        }
-    }
+            for (int i = 0; i < 4; ++i) {
+                const int row = 8 * i + (lane >> 3);
+                Wl[wave][j][row][(lane & 7) ^ (row & 7)] = g.code[j][i];
+            }
+    };
 
-    // D layout of a 32 x 32 tile: lane l, register r -> row 8(r/4) + 4(l/32) + r%4, column l%32
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
+    // Scales of the current group, per row tile (row l % 32, blocks 8 g ..
+    // 8 g + 7), with those of rows past N zeroed.
+    uint4 scl[TN];
+    auto take_scales = [&](const WGroup<TN> &g, const Pos &ps) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            const int n = n0 + wn * (BN / 2) + 32 * j + (lane & 31);
+            const bool row_ok = ps.tn * T::BN + 32 * (wn * TN + j) + (lane & 31) < p.N;
+            scl[j] = row_ok ? g.scale[j] : make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+
+    // The B operands of one step (this wave's row tiles, both blocks, both k
+    // halves), unpacked from the group's codes in LDS: lane l takes row
+    // l % 32, block 2 q + l / 32 of the group.
+    half8_t bop[TN][2][2];
+    auto prep = [&](int q, const Pos &ps) {
+        const int b0 = 2 * ps.s;   // first block of the step (2 q of the group)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = m0 + wm * (BM / 2) + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (m < p.M && n < p.N) {
-                    float *dst = p.Y + (int64_t)m * p.N + n;
-                    if (p.atomic)
-                        unsafeAtomicAdd(dst, acc[i][j][r]);   // hardware fp32 add
-                    else
-                        *dst = acc[i][j][r];
-                }
+        for (int j = 0; j < TN; ++j) {
+            const int row = lane & 31;
+            const uint4 c = Wl[wave][j][row][(2 * q + (lane >> 5)) ^ (row & 7)];
+            const auto t = __builtin_amdgcn_permlane32_swap(c.x, c.z, false, false);
+            const auto u = __builtin_amdgcn_permlane32_swap(c.y, c.w, false, false);
+            const uint32_t sw = q == 0 ? scl[j].x : q == 1 ? scl[j].y : q == 2 ? scl[j].z : scl[j].w;
+            const uint32_t s0 = b0 < KB ? (sw & 0xFFFFu) : 0u;
+            const uint32_t s1 = b0 + 1 < KB ? (sw >> 16) : 0u;
+            const _Float16 d0 = __builtin_bit_cast(_Float16, (uint16_t)s0);
+            const _Float16 d1 = __builtin_bit_cast(_Float16, (uint16_t)s1);
+            unpack8((uint32_t)t[0], (uint32_t)u[0], h2_t{d0, d0}, magic, bop[j][0][0], bop[j][0][1]);
+            unpack8((uint32_t)t[1], (uint32_t)u[1], h2_t{d1, d1}, magic, bop[j][1][0], bop[j][1][1]);
+        }
+    };
+
+    // The step's MFMAs: A operands from LDS buffer `buf`, B operands from
+    // registers.
+    auto mma = [&](int buf) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int col = kk * 16 + (lane >> 5) * 8;   // block kk / 2, k half kk % 2
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const half8_t a =
+                    *reinterpret_cast<const half8_t *>(&As[buf][wm * 32 * TM + 32 * i + (lane & 31)][col]);
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bop[j][kk >> 1][kk & 1], acc[i][j], 0, 0, 0);
             }
         }
+    };
+
+    // D layout of a 32 x 32 tile: lane l, register r -> token 8 (r / 4) +
+    // 4 (l / 32) + r % 4, row l % 32.  A whole tile is stored; a part of one
+    // is added atomically (Y was zero-filled).  Tiles inside the matrix need
+    // no bounds test.
+    auto flush = [&](const Pos &ps, bool whole) {
+        const int mb = ps.tm * T::BM + wm * 32 * TM + 4 * (lane >> 5);
+        const int nb = ps.tn * T::BN + 32 * wn * TN + (lane & 31);
+        const bool inside = (ps.tm + 1) * T::BM <= p.M && (ps.tn + 1) * T::BN <= p.N;   // uniform
+        float *base = p.Y + (int64_t)mb * p.N + nb;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int dm = 32 * i + 8 * (r >> 2) + (r & 3);
+                    const bool ok = inside || (mb + dm < p.M && nb + 32 * j < p.N);
+                    float *dst = base + (int64_t)dm * p.N + 32 * j;
+                    if (ok) {
+                        if (whole)
+                            *dst = acc[i][j][r];
+                        else
+                            unsafeAtomicAdd(dst, acc[i][j][r]);   // hardware fp32 add
+                    }
+                    acc[i][j][r] = 0.0f;
+                }
+    };
+
+    // Step 0 of the range into LDS buffer 0 (its stage then reloads with
+    // step DB), the first group's codes into this wave's LDS buffer, the
+    // next group's loads issued, step 0's B operands unpacked.
+    store_a(sa[0], first.s, 0);
+    load_a(sa[0], rs, la);
+    a_step<T::BM>(la, p, S, it_end);
+    store_w(wg);
+    take_scales(wg, first);
+    load_w<TN, SA>(wg, rs, lw);
+    w_step<T::BN>(lw, p, S, it_end, KB, lane, wn);
+    prep(0, first);
+    __syncthreads();
+
+    // Step it (q = it - it0 within the group) issues its MFMAs (B operands
+    // already unpacked, A operands from LDS buffer q & 1), then, while the
+    // matrix cores work, unpacks the next step's B operands (after the last
+    // step of a group: the next group's codes go to LDS first, and the loads
+    // of the group after it are issued), copies activation stage (q + 1) % DB
+    // (step it + 1) into the other LDS buffer and reloads it with step it + 1
+    // + DB.  A tile is written out after its last group, or after the
+    // workgroup's last group.
+    Pos cur = first;
+    int seg_s0 = first.s;   // first K step of the current tile segment
+    for (int it0 = it_beg; it0 < it_end; it0 += DB) {
+        const Pos group = cur;
+#pragma unroll
+        for (int q = 0; q < DB; ++q) {
+            const int buf = q & 1;   // it0 - it_beg is a multiple of DB, which is even
+            mma(buf);
+            Pos nxt = cur;
+            advance(nxt, p, S);
+            if (q == DB - 1) {
+                // the next group's weights (clamped past the range: never used)
+                store_w(wg);
+                take_scales(wg, nxt);
+                load_w<TN, SA>(wg, rs, lw);
+                w_step<T::BN>(lw, p, S, it_end, KB, lane, wn);
+            }
+            prep((q + 1) % DB, nxt);
+            store_a(sa[(q + 1) % DB], nxt.s, buf ^ 1);
+            load_a(sa[(q + 1) % DB], rs, la);
+            a_step<T::BM>(la, p, S, it_end);
+            cur = nxt;
+            __syncthreads();
+        }
+        if (cur.s == 0 || it0 + DB == it_end) {
+            flush(group, seg_s0 == 0 && cur.s == 0);
+            seg_s0 = 0;
+        }
+    }
 }
 
 struct FillParams {
@@ -317,46 +525,65 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(FillParams f)
 
 inline bool aligned(const void *ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0; }
 
-thread_local int o_splits = 0, o_bm = 0;   // tuning override (0: built-in)
+thread_local int o_wgs = 0, o_tile = 0;   // tuning override (0: built-in)
 
-template <int BM, int BN>
+// Whether every workgroup's range of a stream-K split of `chunks` chunks
+// (`per_tile` per tile) over `wgs` workgroups starts and ends on tile
+// boundaries (then no tile is split).
+bool whole_tiles(int64_t chunks, int64_t per_tile, int64_t wgs)
+{
+    for (int64_t g = 0; g <= wgs; ++g)
+        if ((chunks * g / wgs) % per_tile != 0)
+            return false;
+    return true;
+}
+
+template <int WM, int TM, int TN, int OCC>
 hipError_t launch_prefill(PrefillParams p, int cus, hipStream_t stream)
 {
-    const int64_t tiles_n = (p.N + BN - 1) / BN;
-    const int64_t tiles_m = (p.M + BM - 1) / BM;
-    const int nsteps = (p.K / 32 + 1) / 2;
-    int splits = 1;
-    const int64_t tiles = tiles_n * tiles_m;
-    if (tiles < (int64_t)cus * 5 / 8) {
-        // Too few output tiles to occupy the chip: split K, about one
-        // workgroup per CU in total (three per four CUs with 64-token tiles).
-        // Each extra split adds an fp32 atomic per output element and needs a
-        // zero-filled Y, so splits stay few (sweeps on MI355X: 6144 x 2048 at
-        // 512 tokens 38.6 us unsplit against 47.0 us with 2 splits; 2560 x
-        // 6144 at 512 tokens best at 3; 12288 x 2560 at 64 tokens 28.7 us with
-        // 2 splits against 31.8 with 4 and more with 3, cycled copies).
-        const int64_t target = BM == 64 ? (int64_t)cus * 3 / 4 : (int64_t)cus;
-        splits = (int)std::min<int64_t>((target + tiles / 2) / tiles, std::max(1, nsteps / 4));
-        splits = std::max(1, std::min(splits, 16));
-    }
-    if (o_splits > 0)
-        splits = std::min(o_splits, nsteps);
-    p.steps_per_split = (nsteps + splits - 1) / splits;
-    splits = (nsteps + p.steps_per_split - 1) / p.steps_per_split;
-    p.atomic = splits > 1;
-    if (tiles_m > 65535 || splits > 65535 || tiles_n > INT32_MAX)
+    using T = Tiling<WM, TM, TN>;
+    const int64_t KB = p.K / 32;
+    constexpr int DB = kGroup;
+    const int64_t S = ((KB + 1) / 2 + DB - 1) / DB * DB;
+    const int64_t tiles_n = (p.N + T::BN - 1) / T::BN;
+    const int64_t tiles = tiles_n * ((p.M + T::BM - 1) / T::BM);
+    if (tiles * S > INT32_MAX - 64)
         return hipErrorInvalidValue;
-    if (p.atomic) {
+    p.tiles_n = (int)tiles_n;
+    p.steps = (int)S;
+    p.chunks = (int)(tiles * S / DB);
+    // Workgroups (sweeps on MI355X, graph-timed calls on cycled copies): one
+    // per tile when the tiles fill at least three quarters of the OCC slots
+    // per CU (12288 x 2560 at 512 tokens, 128 x 128 tiles: 384 workgroups
+    // 54.9 us against 68.1 with 512); with fewer tiles the iterations are
+    // split over every slot when each gets at least four groups (2560 x 6144
+    // at 512 tokens: 38.3 us against 44.9 with one per CU), else over one
+    // workgroup per CU (12288 x 2560 at 64 tokens: 21.3 us against 27.3
+    // with two per CU).
+    const int64_t slots = (int64_t)cus * OCC;
+    int64_t wgs;
+    if (tiles >= slots * 3 / 4)
+        wgs = std::min(tiles, slots);
+    else
+        wgs = p.chunks >= 4 * slots ? slots : std::min<int64_t>(cus, p.chunks);
+    if (o_wgs > 0)
+        wgs = std::min<int64_t>(o_wgs, p.chunks);
+    if (wgs > INT32_MAX)
+        return hipErrorInvalidValue;
+    if (!whole_tiles(p.chunks, S / DB, wgs)) {
         FillParams f{p.Y, (int64_t)p.M * p.N};
         void *a[] = {&f};
-        const int64_t wgs = std::min<int64_t>((f.n + 255) / 256, (int64_t)cus * 16);
-        hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&zero_fill_kernel), dim3((unsigned)wgs),
+        const int64_t fw = std::min<int64_t>((f.n + 255) / 256, (int64_t)cus * 16);
+        hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&zero_fill_kernel), dim3((unsigned)fw),
                                        dim3(256), a, 0, stream);
         if (e != hipSuccess)
             return e;
     }
-    return launch_kernel(reinterpret_cast<const void *>(&prefill_kernel<BM, BN>),
-                         dim3((unsigned)tiles_n, (unsigned)tiles_m, (unsigned)splits), dim3(256), 0, stream, p);
+    // a group's eight scales as one 16-byte load where no group crosses a row
+    // (nor the end of the scale region)
+    const void *fn = KB % 8 == 0 ? reinterpret_cast<const void *>(&prefill_kernel<WM, TM, TN, OCC, true>)
+                                 : reinterpret_cast<const void *>(&prefill_kernel<WM, TM, TN, OCC, false>);
+    return launch_kernel(fn, dim3((unsigned)wgs), dim3(256), 0, stream, p);
 }
 
 }  // namespace
@@ -368,7 +595,8 @@ extern "C" qg_status qgemm_q4_0_prefill(const void *Wp, const uint16_t *X, float
     using namespace qg;
     if (!Wp || !X || !Y)
         return QG_ERR_NULL;
-    if (M < 1 || N < 1 || K < 32 || K % 32 != 0 || M > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2 ||
+    // the kernel addresses X and the code region with 32-bit buffer offsets
+    if (M < 1 || N < 1 || K < 32 || K % 32 != 0 || M * K * 2 > INT32_MAX - 256 || N * (K / 32) * 16 > INT32_MAX ||
         M * N > ((int64_t)1 << 40))
         return QG_ERR_SHAPE;
     if (!aligned(Wp, 256) || !aligned(X, 16) || !aligned(Y, 4))
@@ -385,30 +613,35 @@ extern "C" qg_status qgemm_q4_0_prefill(const void *Wp, const uint16_t *X, float
     p.M = (int)M;
     p.N = (int)N;
     p.K = (int)K;
-    p.steps_per_split = 0;
-    p.atomic = 0;
+    p.tiles_n = 0;
+    p.steps = 0;
+    p.chunks = 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool small = o_bm ? (o_bm == 64) : (M <= 64);
-    // 128 x 192 tiles where they give every CU exactly one workgroup while
-    // 128 x 128 tiles would leave some CUs with two (MI355X: 12288 x 2560 at
-    // 512 tokens 79 against 86 us); elsewhere 128 x 128 (with fewer tiles
-    // than CUs the wider tile needs more K splits and loses).
-    const int64_t tiles_m = (M + 127) / 128;
-    const int64_t t128 = (N + 127) / 128 * tiles_m, t192 = (N + 191) / 192 * tiles_m;
-    const bool wide = !small && o_bm == 0 && t128 > cus && t192 <= cus && t192 * 8 >= (int64_t)cus * 7;
-    hipError_t e = small  ? launch_prefill<64, 128>(p, cus, s)
-                   : wide ? launch_prefill<128, 192>(p, cus, s)
-                          : launch_prefill<128, 128>(p, cus, s);
+    // Tile (sweeps on MI355X): 128 tokens x 128 rows where those tiles give
+    // every CU its two workgroups (12288 x 2560 at 512 tokens: 54.9 against
+    // 61.2 us), else 64 x 128 (one wave along M: no weight unpacked twice).
+    const int64_t t130 = (M + 127) / 128 * ((N + 127) / 128);
+    const int tile = o_tile ? o_tile : (M > 64 && t130 * 2 >= 3LL * cus ? 130 : 64);
+    hipError_t e;
+    switch (tile) {
+    case 64: e = launch_prefill<1, 2, 1, 2>(p, cus, s); break;
+    case 66: e = launch_prefill<1, 2, 2, 2>(p, cus, s); break;
+    case 128: e = launch_prefill<1, 4, 2, 1>(p, cus, s); break;
+    case 130: e = launch_prefill<1, 4, 1, 2>(p, cus, s); break;
+    case 257: e = launch_prefill<2, 4, 1, 1>(p, cus, s); break;
+    default: return QG_ERR_SHAPE;
+    }
     if (e == hipErrorInvalidValue)
         return QG_ERR_SHAPE;
     return e == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
 }
 
-// Tuning knob for sweeps: fixes the K split count and the token tile (64 or
-// 128) of later qgemm_q4_0_prefill calls from the calling thread; 0 keeps the
-// built-in choice.
-extern "C" void qg_set_prefill_shape(int splits, int bm)
+// Tuning knob for sweeps: fixes the number of persistent workgroups (the
+// stream-K split) and the token tile (64, 128 or 256) of later
+// qgemm_q4_0_prefill calls from the calling thread; 0 keeps the built-in
+// choice.
+extern "C" void qg_set_prefill_shape(int wgs, int tile)
 {
-    qg::o_splits = splits;
-    qg::o_bm = bm;
+    qg::o_wgs = wgs;
+    qg::o_tile = tile;
 }

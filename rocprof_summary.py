@@ -157,11 +157,11 @@ def suite(stats_csv, suite_jsonl, out_md, cmd):
                          f"(fp16 activations {r['fp16_activations_us_median']}) | {r['GBps']} GB/s |")
         elif r["kind"] == "f32in":
             lines.append(f"| GEMV {r['fmt']} fp32 activations in {r['N']}x{r['K']} M={r['M']} | {r['us_median']} "
-                         f"(wall {r['wall_us_median']}; with a separate conversion "
-                         f"{r['separate_conversion_wall_us_median']}) | {r['GBps']} GB/s |")
+                         f"(graph per call {r['graph_us_median']}; with a separate conversion "
+                         f"{r['separate_conversion_graph_us_median']}) | {r['GBps']} GB/s |")
         elif r["kind"] == "swiglu":
             lines.append(f"| gate+up+SwiGLU {r['fmt']} fp32 in, 2x{r['N']}x{r['K']} M={r['M']} | {r['us_median']} "
-                         f"(wall {r['wall_us_median']}; unfused {r['unfused_wall_us_median']}) | {r['GBps']} GB/s |")
+                         f"(graph per call {r['graph_us_median']}; unfused {r['unfused_graph_us_median']}) | {r['GBps']} GB/s |")
         elif r["kind"] == "moe":
             lines.append(f"| MoE {r['fmt']} {r['E']} of {r['P']} x {r['N']}x{r['K']} | {r['us_median']} | "
                          f"{r['GBps']} GB/s |")

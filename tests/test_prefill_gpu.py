@@ -16,15 +16,36 @@ def _prefill(Wd, X, N, K):
     return Y.cpu().numpy()
 
 
+# Launch settings the edge cases run under (persistent workgroups, tile
+# configuration): the built-in choice; one workgroup walking every tile
+# (whole tiles, plain stores); 3, 7 and 700 workgroups (ranges that cut tiles:
+# partial tiles added atomically into a zero-filled Y); every tile
+# configuration.
+PREFILL_SETTINGS = [(0, 0), (1, 64), (3, 64), (700, 66), (0, 128), (5, 128),
+                    (0, 130), (700, 130), (0, 257), (3, 257)]
+
+
+def _prefill_each_setting(Wd, X, N, K, Y_ref, S, what):
+    q = qg()
+    try:
+        for wgs, tile in PREFILL_SETTINGS:
+            q.qg_set_prefill_shape(wgs, tile)
+            Y = _prefill(Wd, X, N, K)
+            assert_within(Y, Y_ref, S, f"{what} workgroups={wgs} tile={tile}")
+    finally:
+        q.qg_set_prefill_shape(0, 0)
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 1, 32), (5, 33, 96), (64, 129, 2560), (65, 300, 640), (130, 257, 2048),
                                    (200, 64, 4096), (17, 1000, 32), (3, 4099, 160), (256, 128, 6144)])
 def test_prefill_small_parity(M, N, K):
+    """Ragged shapes (tokens, rows and blocks not multiples of a tile or a K
+    step) under every launch setting."""
     w = si.weights(N, K, seed=M + N)
     X = si.activations(M, K, seed=K)
     pb, po = pack_both(Q4_0, w)
-    Y = _prefill(to_dev(pb), X, N, K)
     Y_ref, S = oracle.get().prefill(po, N, K, X)
-    assert_within(Y, Y_ref, S, f"prefill M={M} {N}x{K}")
+    _prefill_each_setting(to_dev(pb), X, N, K, Y_ref, S, f"prefill M={M} {N}x{K}")
 
 
 @pytest.mark.parametrize("N,K", si.PREFILL_SHAPES)
@@ -64,17 +85,11 @@ def test_prefill_m512_full(N, K):
     control_within(Yd.cpu().numpy(), Y_ref, S, f"dense fp16 GEMM {N}x{K} M=512")
 
 
-def test_prefill_wide_tile_full():
-    """The 128 x 192 tile the launcher picks when it gives every CU exactly
-    one workgroup (384 tokens x 16000 rows on 256 CUs): every output against
-    the oracle, with a ragged last tile along N and an odd block count along
-    K (the last K step holds one block)."""
+def test_prefill_many_tiles_full():
+    """More tiles than workgroup slots (384 tokens x 16000 rows): every output
+    against the oracle, with a ragged last tile along N and an odd block
+    count along K (the last K step holds one block, the padding steps none)."""
     M, N, K = 384, 16000, 96
-    cus = qg().qg_device_cus()
-    t128 = -(-N // 128) * 3
-    t192 = -(-N // 192) * 3
-    if not (t128 > cus and t192 <= cus and t192 * 8 >= cus * 7):
-        pytest.skip(f"the wide tile is not chosen on {cus} CUs")
     w = si.weights(N, K, seed=7)
     X = si.activations(M, K, seed=7)
     pb, po = pack_both(Q4_0, w)
@@ -97,23 +112,6 @@ def test_prefill_one_hot_is_the_fp16_dequant_column():
     w16 = oracle.get().dequant(Q4_0, po, N, K, "f16").astype(np.float32)
     for i, k in enumerate(cols):
         check_equal(Y[i], w16[:, k], f"prefill one-hot column {k}", bits=False)
-
-
-# Launch settings the edge cases run under: the built-in choice, one
-# workgroup per tile (no split), K split two and three ways (fp32 partial
-# tiles added atomically), and both token tiles.
-PREFILL_SETTINGS = [(0, 0), (1, 64), (1, 128), (2, 64), (3, 128)]
-
-
-def _prefill_each_setting(Wd, X, N, K, Y_ref, S, what):
-    q = qg()
-    try:
-        for splits, bm in PREFILL_SETTINGS:
-            q.qg_set_prefill_shape(splits, bm)
-            Y = _prefill(Wd, X, N, K)
-            assert_within(Y, Y_ref, S, f"{what} splits={splits} bm={bm}")
-    finally:
-        q.qg_set_prefill_shape(0, 0)
 
 
 @pytest.mark.parametrize("kind", ["large", "tiny"])
