@@ -43,6 +43,7 @@ import json
 import math
 import os
 import platform
+import shutil
 import subprocess
 import sys
 import time
@@ -150,8 +151,8 @@ def per_shape_graph_us(qg, torch, work, calls_per_shape: int = 64) -> dict:
     return out
 
 
-PROBE_LOADS = (4, 8, 16)
-PROBE_WGS_PER_CU = (1, 2, 4, 8, 16)
+PROBE_LOADS = (2, 4, 8, 16)
+PROBE_WGS_PER_CU = (1, 2, 4, 8, 16, 32)
 
 
 def _probe_us(qg, torch, buf, nbytes, copies, stride, sink, wgs, loads, reps):
@@ -172,7 +173,7 @@ def hbm_probe(qg, torch, work, gib: int = 4) -> dict:
     then per shape the fastest read of its packed bytes (per-launch events,
     and back to back in a graph like the GEMV's own back-to-back time)."""
     cus = qg.qg_device_cus()
-    sink = torch.empty(16 * cus, dtype=torch.int32, device="cuda")
+    sink = torch.empty(max(PROBE_WGS_PER_CU) * cus, dtype=torch.int32, device="cuda")
     big = torch.empty(gib << 30, dtype=torch.uint8, device="cuda")
     big.fill_(1)
     best = None
@@ -240,8 +241,13 @@ def _smi() -> dict:
     """Clocks, temperature and power of the first GPU from rocm-smi (read
     only); whatever the tool prints under those names, or the error."""
     try:
-        r = subprocess.run(["rocm-smi", "--showtemp", "--showpower", "--showclocks", "--json"],
-                           capture_output=True, text=True, timeout=30)
+        # rocm-smi is a Python script whose "#!/usr/bin/env" line would make
+        # the child replace itself; run the script with this interpreter
+        tool = shutil.which("rocm-smi")
+        if tool is None:
+            return {"error": "rocm-smi not found"}
+        r = subprocess.run([sys.executable, os.path.realpath(tool), "--showtemp", "--showpower", "--showclocks",
+                            "--json"], capture_output=True, text=True, timeout=30)
         d = json.loads(r.stdout)
     except (OSError, ValueError, subprocess.SubprocessError) as e:
         return {"error": f"{type(e).__name__}: {e}"[:200]}
