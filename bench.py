@@ -486,10 +486,14 @@ def suite(qg, torch, reps: int):
         wmed, _ = _time_graph(torch, fns, reps)
         two = [lambda c=c: qg.qgemv_q4_0(buf[c * nb:(c + 1) * nb], x.half(), N, K, y) for c in range(copies)]
         smed, _ = _time_graph(torch, two, reps)
+        x16 = x.half()   # the fp16-activation GEMV on the same table: the cost of fp32 input
+        f16 = [lambda c=c: qg.qgemv_q4_0(buf[c * nb:(c + 1) * nb], x16, N, K, y) for c in range(copies)]
+        hmed, _ = _time_graph(torch, f16, reps)
         b = N * K // 32 * 18 + 4 * M * K + 4 * M * N
         rec(kind="f32in", fmt="q4_0", N=N, K=K, M=M, us_median=round(med, 3), us_mean=round(mean, 3),
             GBps=round(b / med / 1e3, 1), pct_of_8TBps=round(b / med / 1e3 / 80, 2), algorithmic_bytes=b,
-            graph_us_median=round(wmed, 3), separate_conversion_graph_us_median=round(smed, 3), copies=copies)
+            graph_us_median=round(wmed, 3), separate_conversion_graph_us_median=round(smed, 3),
+            fp16_input_graph_us_median=round(hmed, 3), copies=copies)
         del buf
 
     # gate + up stacked in one 2N-row table with SwiGLU in the epilogue, beside
@@ -512,10 +516,20 @@ def suite(qg, torch, reps: int):
                 torch.mul(torch.nn.functional.silu(gu[:, :N]), gu[:, N:], out=y)
             ufn = [lambda c=c: unfused(c) for c in range(copies)]
             umed, _ = _time_graph(torch, ufn, reps)
+            # the plain GEMV over the same 2N-row table, fp16 activations
+            # converted beforehand and fp32 ones: the epilogue's and the
+            # conversion's share of the fused call
+            x16 = x.half()
+            f16 = [lambda c=c: qg.qgemv_q4_0(buf[c * nb:(c + 1) * nb], x16, 2 * N, K, gu) for c in range(copies)]
+            hmed, _ = _time_graph(torch, f16, reps)
+            f32 = [lambda c=c: qg.qgemv_q4_0_f32in(buf[c * nb:(c + 1) * nb], x, 2 * N, K, gu) for c in range(copies)]
+            fmed, _ = _time_graph(torch, f32, reps)
             b = 2 * N * K // 32 * 18 + 4 * M * K + 4 * M * N
             rec(kind="swiglu", fmt="q4_0", N=N, K=K, M=M, us_median=round(med, 3), us_mean=round(mean, 3),
                 GBps=round(b / med / 1e3, 1), pct_of_8TBps=round(b / med / 1e3 / 80, 2), algorithmic_bytes=b,
-                graph_us_median=round(wmed, 3), unfused_graph_us_median=round(umed, 3), copies=copies)
+                graph_us_median=round(wmed, 3), unfused_graph_us_median=round(umed, 3),
+                stacked_fp16_gemv_graph_us_median=round(hmed, 3), stacked_f32in_gemv_graph_us_median=round(fmed, 3),
+                copies=copies)
         del buf
         torch.cuda.empty_cache()
 
@@ -565,6 +579,9 @@ def main() -> int:
     ap.add_argument("--q2w-calls", type=int, nargs=3, default=None, metavar=("N", "K", "CALLS"),
                     help="for counter passes: CALLS calls of the times-table kernel, then CALLS of the unpacking "
                          "q2w kernel, on one seeded N x K q2w table at one token; prints nothing else")
+    ap.add_argument("--gemv-calls", type=int, nargs=4, default=None, metavar=("N", "K", "M", "CALLS"),
+                    help="for counter passes: CALLS calls of the Q4_0 GEMV on one seeded N x K table and M tokens, "
+                         "then CALLS at one token; prints nothing else")
     ap.add_argument("--prefill-calls", type=int, nargs=4, default=None, metavar=("N", "K", "M", "CALLS"),
                     help="for counter passes: CALLS calls of the Q4_0 prefill on one seeded N x K table and M "
                          "tokens, then CALLS of the dense fp16 GEMM on its dequantized weights; prints nothing else")
@@ -589,6 +606,17 @@ def main() -> int:
         for fn in (qg.qgemv_q2w_lut, qg.qgemv_q2w):
             for _ in range(calls):
                 fn(W, x, N, K, y)
+        torch.cuda.synchronize()
+        return 0
+
+    if args.gemv_calls:
+        N, K, M, calls = args.gemv_calls
+        W = torch.from_numpy(qg.qquantize_q4_0(si.weights(N, K, seed=0))).to("cuda")
+        for m in (M, 1):
+            x = torch.from_numpy(si.activations(m, K, seed=0)).to("cuda")
+            call = qg.PreparedGemv(qg.Q4_0, W, x, torch.empty((m, N), dtype=torch.float32, device="cuda"), N, K)
+            for _ in range(calls):
+                call()
         torch.cuda.synchronize()
         return 0
 

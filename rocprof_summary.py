@@ -123,7 +123,7 @@ def stats(stats_csv, trace_csv, out_md, cmd):
     print("\n".join(lines))
 
 
-def suite(stats_csv, suite_jsonl, out_md, cmd):
+def suite(stats_csv, suite_jsonl, out_md, cmd, plain_cmd=""):
     """Kernel statistics of a rocprofv3 run of `bench.py --suite` plus the
     per-workload medians of a plain (unprofiled) suite run."""
     rows = list(csv.DictReader(open(stats_csv)))
@@ -139,8 +139,9 @@ def suite(stats_csv, suite_jsonl, out_md, cmd):
     for r in rows:
         lines.append(f"| `{r['Name'][:80]}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | "
                      f"{r['MaxNs']} |")
-    lines += ["", "Per-workload medians of a separate, unprofiled `bench.py --suite` run (kernel events; prefill: "
-                  "whole call incl. the zero fill of split-K launches):", "",
+    lines += ["", "Per-workload medians of a separate, unprofiled `bench.py --suite` run (median us: HIP events "
+                  "of each launch; graph: per call in a captured graph of 20 calls; prefill: graph, whole call "
+                  "incl. the zero fill of split-K launches):", ""] + (["```", plain_cmd, "```", ""] if plain_cmd else []) + [
               "| workload | median us | GB/s or TFLOP/s |", "|---|---|---|"]
     for r in recs:
         if r["kind"] == "gemv":
@@ -158,10 +159,13 @@ def suite(stats_csv, suite_jsonl, out_md, cmd):
         elif r["kind"] == "f32in":
             lines.append(f"| GEMV {r['fmt']} fp32 activations in {r['N']}x{r['K']} M={r['M']} | {r['us_median']} "
                          f"(graph per call {r['graph_us_median']}; with a separate conversion "
-                         f"{r['separate_conversion_graph_us_median']}) | {r['GBps']} GB/s |")
+                         f"{r['separate_conversion_graph_us_median']}; fp16 activations "
+                         f"{r.get('fp16_input_graph_us_median')}) | {r['GBps']} GB/s |")
         elif r["kind"] == "swiglu":
             lines.append(f"| gate+up+SwiGLU {r['fmt']} fp32 in, 2x{r['N']}x{r['K']} M={r['M']} | {r['us_median']} "
-                         f"(graph per call {r['graph_us_median']}; unfused {r['unfused_graph_us_median']}) | {r['GBps']} GB/s |")
+                         f"(graph per call {r['graph_us_median']}; unfused {r['unfused_graph_us_median']}; "
+                         f"plain GEMV of the 2N-row table: fp16 in {r.get('stacked_fp16_gemv_graph_us_median')}, "
+                         f"fp32 in {r.get('stacked_f32in_gemv_graph_us_median')}) | {r['GBps']} GB/s |")
         elif r["kind"] == "moe":
             lines.append(f"| MoE {r['fmt']} {r['E']} of {r['P']} x {r['N']}x{r['K']} | {r['us_median']} | "
                          f"{r['GBps']} GB/s |")
@@ -204,13 +208,44 @@ def counters(title, out_md, stats_csv, stats_cmd, *pairs):
     print("\n".join(lines))
 
 
+def probe(bench_json, out_md, cmd):
+    """The read probe's per-size floors beside the GEMV on the same byte
+    counts, from one bench.py JSON line."""
+    d = json.loads([l for l in open(bench_json) if l.strip().startswith("{")][-1])
+    p = d["hbm_probe"]
+    b = p["best"]
+    lines = ["# HBM read probe: per-size floors beside the Q4_0 GEMV (M=1, Llama-3-8B shapes)", "",
+             "The probe reads a buffer with the GEMV's load path (non-temporal 16-byte buffer loads, several in "
+             "flight per lane, whole 4 KiB tiles per workgroup round robin) and computes nothing; per size the "
+             "fastest of the swept launch shapes (loads in flight x workgroups) is the floor a one-launch read of "
+             "that many bytes reaches on this chip. Both sides cycle copies of >= 1 GiB so every launch reads HBM.",
+             "", "Command:", "", "```", cmd, "```", "",
+             f"Best streaming read: {b['GBps']} GB/s ({b['bytes']} bytes, {b['loads_in_flight']} loads in flight, "
+             f"{b['workgroups']} workgroups, {b['us']} us).", "",
+             "| shape N x K | bytes | probe us (events) | probe us (back to back) | probe launch | GEMV us (events) "
+             "| GEMV us (back to back) | GEMV / probe (back to back) |", "|---|---|---|---|---|---|---|---|"]
+    for shape, f in p["per_shape_floor"].items():
+        g = d["per_shape"][shape]
+        lines.append(f"| {shape} | {f['bytes']} | {f['us_median']} | {f['us_back_to_back']} | "
+                     f"{f['loads_in_flight']} loads x {f['workgroups']} WGs | {g['us_median']} | "
+                     f"{g['us_per_call_back_to_back']} | {g['us_per_call_back_to_back'] / f['us_back_to_back']:.3f} |")
+    env = d.get("env", {})
+    if env:
+        lines += ["", "Environment: " + json.dumps({k: env[k] for k in env if k != "inputs_sha256"})[:1500]]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         stats(*sys.argv[2:6])
     elif sys.argv[1] == "traffic":
         traffic(*sys.argv[2:7])
     elif sys.argv[1] == "suite":
-        suite(*sys.argv[2:6])
+        suite(*sys.argv[2:7])
+    elif sys.argv[1] == "probe":
+        probe(*sys.argv[2:5])
     elif sys.argv[1] == "counters":
         counters(*sys.argv[2:])
     else:
