@@ -35,6 +35,9 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <map>
+#include <mutex>
+#include <tuple>
 
 #include "qgemv_internal.h"
 
@@ -450,7 +453,9 @@ __device__ __forceinline__ uint32_t half2_bits(float a, float b)
 // Persistent over 16-row tiles: workgroup w takes tiles w, w + grid, ...;
 // its waves split K, stage their activation slices in LDS once, and prefetch
 // the next tile's codes and scales while the current tile is multiplied.
-// GLU: each tile is a gate tile and the up tile N rows below it (fp32 input).
+// GLU (fp32 input): a tile's gate rows and its up rows, N rows below them,
+// are multiplied one after the other, each while the other's loads are in
+// flight, and combined when both are summed.
 
 template <int FMT, int KWMAX, bool WS, bool F32, bool GLU>
 __global__ __launch_bounds__(512) void gemv_mfma_kernel(MfmaParams p)
@@ -502,12 +507,14 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(MfmaParams p)
     const uint32_t coff = (uint32_t)(c * KB + kbeg + gb) * (uint32_t)mfma_code_bytes<FMT>() +
                           ((FMT == kQ8_0) ? (uint32_t)(g & 1) * 16u : 0u);
     const uint32_t soff = WS ? (uint32_t)(c * KB + kbeg + g * (KWMAX / 4)) * 2u : (uint32_t)(c * KB + kbeg + gb) * 2u;
-    int tile = blockIdx.x;
     const int64_t rows = GLU ? 2 * (int64_t)p.N : (int64_t)p.N;   // rows of the packed table
-    TileRegs<FMT, KWMAX, WS> ta, tb, ua, ub;   // ua, ub: the up tiles (GLU)
-    load_tile<FMT, KWMAX, WS>(p, tile, ntiles, KB, coff, soff, ta, 0, rows);
-    if constexpr (GLU)
-        load_tile<FMT, KWMAX, WS>(p, tile, ntiles, KB, coff, soff, ua, p.N, rows);
+    // The workgroup walks units: tiles blockIdx.x, + grid, ...; with SwiGLU
+    // each tile is two units, its gate rows and then its up rows (N further
+    // down the table), so one unit's loads are in flight while the other is
+    // multiplied, with the registers of the plain kernel.
+    const int step = gridDim.x;
+    TileRegs<FMT, KWMAX, WS> ta, tb;
+    load_tile<FMT, KWMAX, WS>(p, blockIdx.x, ntiles, KB, coff, soff, ta, 0, rows);
     __builtin_amdgcn_sched_barrier(0);
 
     // 3. the activations into this wave's own LDS area, in MFMA operand
@@ -549,41 +556,61 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(MfmaParams p)
     const uint32_t magic = magic_reg();
     const int cm = min(c, p.M - 1);
     const int xq = (FMT == kQ8_0) ? (((g & 1) << 1) | (g >> 1)) : g;
-    const int step = gridDim.x;
     const int last = ntiles - 1;
-    for (int it = 0;; it += 2) {
-        // tile in `ta`; prefetch the next into `tb` (past the end: empty
-        // loads, never used)
-        const int t1 = tile + step;
-        load_tile<FMT, KWMAX, WS>(p, t1, ntiles, KB, coff, soff, tb, 0, rows);
-        if constexpr (GLU)
-            load_tile<FMT, KWMAX, WS>(p, t1, ntiles, KB, coff, soff, ub, p.N, rows);
-        __builtin_amdgcn_sched_barrier(0);
-        f4_t acc = compute_tile<FMT, KWMAX, WS>(ta, xs, p.M, cm, xq, kbeg, kend, nsteps, magic);
-        if constexpr (GLU) {
-            const f4_t accu = compute_tile<FMT, KWMAX, WS>(ua, xs, p.M, cm, xq, kbeg, kend, nsteps, magic);
-            reduce_store_glu(p, acc, accu, red, it, tile, wave, nwaves, lane, g, c);
-        } else {
+    if constexpr (GLU) {
+        // units: gate of tile t in ta, its up rows in tb; while one is
+        // multiplied the other's loads (or the next tile's gate) are in flight
+        for (int it = 0, tile = blockIdx.x;; ++it, tile += step) {
+            load_tile<FMT, KWMAX, WS>(p, tile, ntiles, KB, coff, soff, tb, p.N, rows);
+            __builtin_amdgcn_sched_barrier(0);
+            const f4_t accg = compute_tile<FMT, KWMAX, WS>(ta, xs, p.M, cm, xq, kbeg, kend, nsteps, magic);
+            const int t1 = tile + step;   // past the end: empty loads, never used
+            load_tile<FMT, KWMAX, WS>(p, t1, ntiles, KB, coff, soff, ta, 0, rows);
+            __builtin_amdgcn_sched_barrier(0);
+            const f4_t accu = compute_tile<FMT, KWMAX, WS>(tb, xs, p.M, cm, xq, kbeg, kend, nsteps, magic);
+            reduce_store_glu(p, accg, accu, red, it, tile, wave, nwaves, lane, g, c);
+            if (t1 > last)
+                break;
+        }
+    } else {
+        for (int it = 0, tile = blockIdx.x;; it += 2) {
+            // tile in `ta`; prefetch the next into `tb` (past the end: empty
+            // loads, never used)
+            const int t1 = tile + step;
+            load_tile<FMT, KWMAX, WS>(p, t1, ntiles, KB, coff, soff, tb, 0, rows);
+            __builtin_amdgcn_sched_barrier(0);
+            f4_t acc = compute_tile<FMT, KWMAX, WS>(ta, xs, p.M, cm, xq, kbeg, kend, nsteps, magic);
             reduce_store(p, acc, red, it, tile, wave, nwaves, lane, g, c);
-        }
-        if (t1 > last)
-            break;
-        const int t2 = t1 + step;
-        load_tile<FMT, KWMAX, WS>(p, t2, ntiles, KB, coff, soff, ta, 0, rows);
-        if constexpr (GLU)
-            load_tile<FMT, KWMAX, WS>(p, t2, ntiles, KB, coff, soff, ua, p.N, rows);
-        __builtin_amdgcn_sched_barrier(0);
-        acc = compute_tile<FMT, KWMAX, WS>(tb, xs, p.M, cm, xq, kbeg, kend, nsteps, magic);
-        if constexpr (GLU) {
-            const f4_t accu = compute_tile<FMT, KWMAX, WS>(ub, xs, p.M, cm, xq, kbeg, kend, nsteps, magic);
-            reduce_store_glu(p, acc, accu, red, it + 1, t1, wave, nwaves, lane, g, c);
-        } else {
+            if (t1 > last)
+                break;
+            const int t2 = t1 + step;
+            load_tile<FMT, KWMAX, WS>(p, t2, ntiles, KB, coff, soff, ta, 0, rows);
+            __builtin_amdgcn_sched_barrier(0);
+            acc = compute_tile<FMT, KWMAX, WS>(tb, xs, p.M, cm, xq, kbeg, kend, nsteps, magic);
             reduce_store(p, acc, red, it + 1, t1, wave, nwaves, lane, g, c);
+            if (t2 > last)
+                break;
+            tile = t2;
         }
-        if (t2 > last)
-            break;
-        tile = t2;
     }
+}
+
+// Workgroups of `fn` resident on one CU at once (at least 1), cached per
+// kernel, block size and LDS size.
+int resident_per_cu(const void *fn, int threads, size_t shmem)
+{
+    static std::mutex mu;
+    static std::map<std::tuple<const void *, int, size_t>, int> cache;
+    const auto key = std::make_tuple(fn, threads, shmem);
+    std::lock_guard<std::mutex> lock(mu);
+    const auto it = cache.find(key);
+    if (it != cache.end())
+        return it->second;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, threads, shmem) != hipSuccess || n < 1)
+        n = 1;
+    cache.emplace(key, n);
+    return n;
 }
 
 template <int FMT, int KWMAX, bool WS>
@@ -607,7 +634,6 @@ hipError_t launch_kw(const MfmaParams &p, int waves, int64_t wgs, int cus, hipSt
     }
     // every wave stages M x kw blocks of activations (64 bytes each); SwiGLU
     // keeps 16 KB more of partial tiles in static LDS
-    const size_t red_bytes = (size_t)(p.glu ? 4 : 2) * kMaxWavesPerWg * 64 * 16;
     const size_t shmem = (size_t)waves * p.kw * p.M * 64;
     if (shmem > kMaxLds - (p.glu ? 16384 : 0))
         return hipErrorInvalidValue;
@@ -619,14 +645,10 @@ hipError_t launch_kw(const MfmaParams &p, int waves, int64_t wgs, int cus, hipSt
     }
     const int64_t ntiles = (p.N + 15) / 16;
     if (wgs <= 0) {
-        // workgroups per CU that fit in LDS (160 KB, 16 KB of it for the
-        // partial tiles) and in the wave slots (32 per CU), at most 2; one
-        // for fp32 activations, which every workgroup reads and rounds again
-        // (MI355X, 8 tokens: 6144 x 2048 7.2 against 8.1 us, 14336 x 4096
-        // 16.2 against 17.6; equal on the other shapes)
-        const size_t per_wg = shmem + red_bytes;
-        const int64_t fit = std::max<int64_t>(1, std::min<int64_t>((160 * 1024) / per_wg, 32 / waves));
-        wgs = (int64_t)cus * std::min<int64_t>(p.xf ? 1 : 2, fit);
+        // as many workgroups as are resident at once (registers, LDS, wave
+        // slots), at most 2 per CU (MI355X, 8 tokens, 28672 x 4096: fp32
+        // activations 25.2 us at two per CU against 26.2 at one)
+        wgs = (int64_t)cus * std::min(2, resident_per_cu(fn, 64 * waves, shmem));
     }
     wgs = std::min(wgs, ntiles);
     const dim3 grid((unsigned)wgs), block(64 * waves);
