@@ -160,8 +160,8 @@ qg_status qgemv_q4_0_f32in(const void *Wp, const float *x, float *y, int M, int6
  *   y[m][n] = silu(g[m][n]) * u[m][n],   silu(v) = v / (1 + e^-v),
  * evaluated in fp32 on the fp32 sums; only y is written.  y: fp32 [M][N].
  * 1 <= N <= 2^30 - 1; K as for qgemv_q4_0_f32in at M tokens, and at 8
- * tokens K <= 7168 (5-8 tokens run the matrix-core kernel, each workgroup
- * pairing a gate tile with its up tile).  Accuracy: g and u meet the GEMV
+ * tokens K <= 7168 (5-8 tokens, and 4 on large tables, run the matrix-core
+ * kernel, each workgroup multiplying a tile's gate rows, then its up rows).  Accuracy: g and u meet the GEMV
  * bound, and y is within 1.1 eg (|u| + eu) + |g| eu + 1e-5 |y| of the exact
  * silu(g) u (eg, eu: the GEMV bounds of g and u).
  * [volta-kernel-bakeoff, "Results", the few-tokens bullet: gate and up

@@ -67,8 +67,10 @@ void qg_set_prefill_shape(int wgs, int tile);
  * at `buf` (16-byte aligned) with non-temporal 16-byte buffer loads.  The
  * buffer is cut into tiles of loads x 4 KiB, handed round-robin to `wgs`
  * workgroups of 256 threads, each lane keeping `loads` (2, 4, 8 or 16)
- * loads in flight per tile; workgroup g writes one word to sink[g] (device,
- * >= wgs words) so the reads cannot be dropped.  The measured roofline
+ * loads of a tile in flight and issuing its next tile's before folding the
+ * current one; a lane of workgroup g writes sink[g] (device, >= wgs words)
+ * only if its fold of the data equals a fixed value, so the reads cannot be
+ * dropped (sink's contents are meaningless).  The measured roofline
  * beside the spec sheet [sm8x-bench, methodology: a bandwidth probe gives
  * the measured roofline]. */
 qg_status qg_read_probe(const void *buf, size_t bytes, uint32_t *sink, int wgs, int loads, void *stream);

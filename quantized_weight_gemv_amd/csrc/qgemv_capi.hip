@@ -266,15 +266,19 @@ qg_status run_gemv(int fmt, const void *Wp, const int32_t *idx, int64_t P, const
     // from 6 tokens gain (2048 x 6144: Q4_0 9.0 against 9.6 us; q2w 7.8
     // against 7.9 at 6 tokens, 8.0 against 9.7 at 8, 7.4 against 6.2 at 4).
     // q2w needs an even number of blocks per row (its scales are loaded per
-    // lane group, 4-byte aligned).  fp32 activations (Q4_0) follow the Q4_0
-    // rule, and take the matrix-core kernel at 5-8 tokens whatever the shape
-    // (it rounds them to binary16 as it stages them; the vector kernel holds
-    // at most 4 tokens of raw fp32 words).
+    // lane group, 4-byte aligned).  fp32 activations (Q4_0) and SwiGLU
+    // follow the Q4_0 rule (N: the rows of one half for SwiGLU; 4 tokens,
+    // SwiGLU 2 x 14336 x 4096 23.5 against 26.3 us, 2 x 6144 x 2048 9.6
+    // against 10.6, 2 x 4096 x 4096 9.9 against 12.2; 2 x 2048 x 6144 16.0
+    // against 11.5 stays on the vector kernel), and take the matrix-core
+    // kernel at 5-8 tokens whatever the shape (it rounds them to binary16 as
+    // it stages them; the vector kernel holds at most 4 tokens of raw fp32
+    // words).
     const int64_t KB = K / 32;
     const bool tiles_fill = N >= 16LL * cus;
     const bool f32_many = (mode == kModeF32 || mode == kModeGlu) && M > 4;
     bool mfma = idx == nullptr && (mode == kModeF16 || mode == kModeF32 || mode == kModeGlu) &&
-                (f32_many || (mode != kModeGlu && tiles_fill && fmt == kQ4_0 && M >= 4 && KB <= 256) ||
+                (f32_many || (tiles_fill && fmt == kQ4_0 && M >= 4 && KB <= 256) ||
                  (tiles_fill && fmt == kQ8_0 && ((M >= 4 && KB <= 64) || (M >= 6 && KB <= 256))) ||
                  (N >= 8LL * cus && fmt == kQ4_0 && M == 8 && KB <= 256) ||
                  (fmt == kQ2W && KB % 2 == 0 && KB <= 256 &&
@@ -575,43 +579,68 @@ namespace {
 struct ProbeArgs {
     const uint8_t *p;
     int64_t bytes;     // multiple of 16
-    uint32_t *sink;    // one word per workgroup keeps the loads live
+    uint32_t *sink;    // >= gridDim.x words
+    uint32_t never;    // a fold the data does not produce (the write below keeps the loads live)
 };
 
 // Streaming read on the GEMV kernels' own load path: non-temporal 16-byte
 // buffer loads from a scalar descriptor.  The buffer is cut into tiles of
 // U x 4 KiB handed round-robin to the workgroups (consecutive workgroups read
 // consecutive tiles, as consecutive GEMV teams read consecutive rows); each
-// lane has U loads in flight per tile.  Loads past the end of the buffer
-// fall outside the tile's descriptor and return zeros without touching
-// memory.  [sm8x-bench, methodology: a bandwidth probe gives the measured
-// roofline beside the spec]
+// lane has U loads of a tile in flight, and those of its next tile are
+// issued before the current one is folded (two register sets, as the GEMV
+// keeps two groups).  Loads past the end of the buffer fall outside the
+// tile's descriptor (or meet an empty one) and return zeros without
+// touching memory.  Nothing is reduced across the workgroup: a lane stores
+// its fold only if it equals `never`, so the loads cannot be dropped and the
+// launch ends with its last load.  [sm8x-bench, methodology: a bandwidth
+// probe gives the measured roofline beside the spec]
+template <int U>
+__device__ __forceinline__ void probe_tile(const ProbeArgs &a, int64_t t, int64_t ntiles, uint4 (&v)[U])
+{
+    constexpr int64_t kTile = (int64_t)U * 256 * 16;
+    const int64_t base = t * kTile;
+    const auto r = t < ntiles ? make_rsrc(a.p + base, min(kTile, a.bytes - base)) : make_rsrc(a.p, 0);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        v[u] = stream_load16(r, (uint32_t)(threadIdx.x + u * 256) * 16u);
+}
+
+template <int U>
+__device__ __forceinline__ uint32_t probe_fold(const uint4 (&v)[U])
+{
+    uint32_t x = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    return x;
+}
+
 template <int U>
 __global__ __launch_bounds__(256) void read_probe_kernel(ProbeArgs a)
 {
     constexpr int64_t kTile = (int64_t)U * 256 * 16;
     const int64_t ntiles = (a.bytes + kTile - 1) / kTile;
+    const int64_t step = gridDim.x;
     uint32_t acc = 0;
-    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        const int64_t base = t * kTile;
-        const auto r = make_rsrc(a.p + base, min(kTile, a.bytes - base));
-        uint4 v[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            v[u] = stream_load16(r, (uint32_t)(threadIdx.x + u * 256) * 16u);
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    uint4 va[U], vb[U];
+    int64_t t = blockIdx.x;
+    probe_tile<U>(a, t, ntiles, va);
+    for (;;) {
+        probe_tile<U>(a, t + step, ntiles, vb);
+        __builtin_amdgcn_sched_barrier(0);   // the next tile's loads stay ahead of the fold
+        acc ^= probe_fold<U>(va);
+        if (t + step >= ntiles)
+            break;
+        probe_tile<U>(a, t + 2 * step, ntiles, va);
+        __builtin_amdgcn_sched_barrier(0);
+        acc ^= probe_fold<U>(vb);
+        if (t + 2 * step >= ntiles)
+            break;
+        t += 2 * step;
     }
-    __shared__ uint32_t s[256];
-    s[threadIdx.x] = acc;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t r = 0;
-        for (int t = 0; t < 256; ++t)
-            r ^= s[t];
-        a.sink[blockIdx.x] = r;
-    }
+    if (acc == a.never)
+        a.sink[blockIdx.x] = acc;
 }
 
 }  // namespace
@@ -633,7 +662,7 @@ extern "C" qg_status qg_read_probe(const void *buf, size_t bytes, uint32_t *sink
     case 16: fn = reinterpret_cast<const void *>(&qg::read_probe_kernel<16>); break;
     default: return QG_ERR_SHAPE;
     }
-    qg::ProbeArgs a{static_cast<const uint8_t *>(buf), static_cast<int64_t>(bytes / 16 * 16), sink};
+    qg::ProbeArgs a{static_cast<const uint8_t *>(buf), static_cast<int64_t>(bytes / 16 * 16), sink, 0x9E3779B9u};
     hipError_t e = qg::launch_kernel(fn, dim3(wgs), dim3(256), 0, static_cast<hipStream_t>(stream), a);
     return e == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
 }
