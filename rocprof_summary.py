@@ -186,7 +186,7 @@ def counters(title, out_md, stats_csv, stats_cmd, *pairs):
     for csv_path, cmd in zip(pairs[0::2], pairs[1::2]):
         cmds.append(cmd)
         for r in csv.DictReader(open(csv_path)):
-            if "copyBuffer" in r["Kernel_Name"]:
+            if "copyBuffer" in r["Kernel_Name"] or "fillBuffer" in r["Kernel_Name"]:
                 continue
             per.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
     lines = [f"# rocprofv3 counters: {title}", "", "Commands (counter passes each in a run of their own):", "", "```"]
@@ -194,6 +194,7 @@ def counters(title, out_md, stats_csv, stats_cmd, *pairs):
     for r in csv.DictReader(open(stats_csv)):
         if "copyBuffer" not in r["Name"]:
             lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']):.0f} |")
+    per = {k: d for k, d in per.items() if max(len(v) for v in d.values()) >= 5}   # the timed kernels only
     names = sorted({c for d in per.values() for c in d})
     lines += ["", "Median per dispatch:", "", "| counter | " + " | ".join(f"`{k[:60]}`" for k in per) + " |",
               "|---|" + "---|" * len(per)]
