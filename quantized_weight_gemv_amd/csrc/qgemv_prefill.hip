@@ -293,12 +293,13 @@ __device__ __forceinline__ void load_w(WGroup<TN> &st, const Rsrc &rs, const WCu
     }
 }
 
-template <int WM, int TM, int TN, int OCC, bool SA>
+template <int WM, int TM, int TN, int OCC, int DA, bool SA>
 __global__ __launch_bounds__(256, OCC) void prefill_kernel(PrefillParams p)
 {
+    static_assert(kGroup % DA == 0, "activation stages: a divisor of the group's steps");
     using T = Tiling<WM, TM, TN>;
     constexpr int AC = T::AC;
-    constexpr int DB = kGroup;   // steps (and activation stages) in flight: one group
+    constexpr int DB = kGroup;   // steps per weight group
     __shared__ __attribute__((aligned(16))) uint16_t As[2][T::BM][kLdsStride];
     __shared__ uint4 Wl[4][TN][32][8];   // per wave: the current group's code bytes, chunks swizzled by row
 
@@ -342,18 +343,18 @@ __global__ __launch_bounds__(256, OCC) void prefill_kernel(PrefillParams p)
     lw.ps = first;
     lw.it = it_beg;
     w_offsets<T::BN>(lw, p, KB, lane, wn);
-    AStage<AC> sa[DB];
+    AStage<AC> sa[DA];   // activations of the next DA steps in flight
     WGroup<TN> wg;
     load_w<TN, SA>(wg, rs, lw);
     w_step<T::BN>(lw, p, S, it_end, KB, lane, wn);
 #pragma unroll
-    for (int q = 0; q < DB; ++q) {
+    for (int q = 0; q < DA; ++q) {
         load_a(sa[q], rs, la);
         a_step<T::BM>(la, p, S, it_end);
     }
 
     // Store the activations of a stage (at K step s) into LDS buffer `buf`,
-    // zeroing blocks past K.  Activation stage r % DB holds step r's
+    // zeroing blocks past K.  Activation stage r % DA holds step r's
     // activations; they are copied to LDS one step before their MFMAs.
     auto store_a = [&](const AStage<AC> &sg, int s, int buf) {
         const bool full = 2 * s + 2 <= KB;   // uniform: both blocks of the step inside K
@@ -416,18 +417,31 @@ __global__ __launch_bounds__(256, OCC) void prefill_kernel(PrefillParams p)
 
     // The step's MFMAs: A operands from LDS buffer `buf`, B operands from
     // registers.
+    // The A fragments of the next 16-wide k slice are read while the current
+    // slice's MFMAs issue (two register sets; the scheduling barriers keep
+    // the compiler from sinking each read to just before its MFMA, which
+    // exposed an LDS round trip per MFMA).
     auto mma = [&](int buf) {
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+        half8_t a[2][TM];
+        auto read_a = [&](int kk, half8_t (&dst)[TM]) {
             const int col = kk * 16 + (lane >> 5) * 8;   // block kk / 2, k half kk % 2
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const half8_t a =
-                    *reinterpret_cast<const half8_t *>(&As[buf][wm * 32 * TM + 32 * i + (lane & 31)][col]);
+            for (int i = 0; i < TM; ++i)
+                dst[i] = *reinterpret_cast<const half8_t *>(&As[buf][wm * 32 * TM + 32 * i + (lane & 31)][col]);
+        };
+        read_a(0, a[0]);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            if (kk < 3)
+                read_a(kk + 1, a[(kk + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bop[j][kk >> 1][kk & 1], acc[i][j], 0, 0, 0);
-            }
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[kk & 1][i], bop[j][kk >> 1][kk & 1],
+                                                                       acc[i][j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
@@ -476,7 +490,7 @@ __global__ __launch_bounds__(256, OCC) void prefill_kernel(PrefillParams p)
     // already unpacked, A operands from LDS buffer q & 1), then, while the
     // matrix cores work, unpacks the next step's B operands (after the last
     // step of a group: the next group's codes go to LDS first, and the loads
-    // of the group after it are issued), copies activation stage (q + 1) % DB
+    // of the group after it are issued), copies activation stage (q + 1) % DA
     // (step it + 1) into the other LDS buffer and reloads it with step it + 1
     // + DB.  A tile is written out after its last group, or after the
     // workgroup's last group.
@@ -498,8 +512,8 @@ __global__ __launch_bounds__(256, OCC) void prefill_kernel(PrefillParams p)
                 w_step<T::BN>(lw, p, S, it_end, KB, lane, wn);
             }
             prep((q + 1) % DB, nxt);
-            store_a(sa[(q + 1) % DB], nxt.s, buf ^ 1);
-            load_a(sa[(q + 1) % DB], rs, la);
+            store_a(sa[(q + 1) % DA], nxt.s, buf ^ 1);
+            load_a(sa[(q + 1) % DA], rs, la);
             a_step<T::BM>(la, p, S, it_end);
             cur = nxt;
             __syncthreads();
@@ -538,7 +552,7 @@ bool whole_tiles(int64_t chunks, int64_t per_tile, int64_t wgs)
     return true;
 }
 
-template <int WM, int TM, int TN, int OCC>
+template <int WM, int TM, int TN, int OCC, int DA = kGroup>
 hipError_t launch_prefill(PrefillParams p, int cus, hipStream_t stream)
 {
     using T = Tiling<WM, TM, TN>;
@@ -581,8 +595,8 @@ hipError_t launch_prefill(PrefillParams p, int cus, hipStream_t stream)
     }
     // a group's eight scales as one 16-byte load where no group crosses a row
     // (nor the end of the scale region)
-    const void *fn = KB % 8 == 0 ? reinterpret_cast<const void *>(&prefill_kernel<WM, TM, TN, OCC, true>)
-                                 : reinterpret_cast<const void *>(&prefill_kernel<WM, TM, TN, OCC, false>);
+    const void *fn = KB % 8 == 0 ? reinterpret_cast<const void *>(&prefill_kernel<WM, TM, TN, OCC, DA, true>)
+                                 : reinterpret_cast<const void *>(&prefill_kernel<WM, TM, TN, OCC, DA, false>);
     return launch_kernel(fn, dim3((unsigned)wgs), dim3(256), 0, stream, p);
 }
 
