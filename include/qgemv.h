@@ -229,10 +229,14 @@ qg_status qmoe_gemv_q4_0(const void *pool, int64_t P, const int32_t *idx, const 
                          int E, int64_t N, int64_t K, void *stream);
 
 /* Prefill (many tokens), Q4_0: Y[m][n] = sum_k w[n][k] * X[m][k] for any
- * M >= 1.  Weight tiles are dequantized to fp16 (round to nearest even, the
- * same values qdequant_q4_0 writes with out_fp16 = 1) in LDS and multiplied
- * on the fp16 matrix cores with fp32 accumulation.  X: fp16 bits [M][K];
- * Y: fp32 [M][N].
+ * M >= 1.  The weights are unpacked to fp16 (round to nearest even, the same
+ * values qdequant_q4_0 writes with out_fp16 = 1) straight into the operands
+ * of the fp16 matrix cores, with fp32 accumulation: up to 64 tokens with
+ * every token's activations held in registers and the weights streamed once
+ * in 16-row tiles, beyond that in tiles of 64 or 128 tokens.  Where the work
+ * is split along K over workgroups, parts are added with fp32 atomics into Y
+ * after a fill kernel zeroes it (results may then differ in the last bits
+ * between runs, within the bound).  X: fp16 bits [M][K]; Y: fp32 [M][N].
  * [volta-kernel-bakeoff, "What's in the race" (tc_q4: unpack a tile to
  *  shared memory, then matrix-core multiply) and "Stage 3" (unpack inside
  *  the matrix multiply instead of dequantize-then-GEMM)] */

@@ -143,6 +143,16 @@ hipError_t launch_gemv_mfma(int fmt, const uint8_t *W, int64_t scale_offset, con
                             float *y, int M, int N, int K, int waves, int64_t wgs, int cus, hipStream_t stream,
                             bool glu = false);
 
+// Prefill for 1..64 tokens on the matrix cores (qgemv_mfma.hip): weights
+// streamed once in 16-row tiles, activations held as MFMA operands in
+// registers; `wgs` persistent workgroups along N (0: one per CU of `cus`).
+hipError_t launch_prefill_skinny(const uint8_t *W, int64_t scale_offset, const uint16_t *X, float *Y, int M, int N,
+                                 int K, int cus, int64_t wgs, hipStream_t stream);
+
+// Zero n floats of y (a small fill kernel, no memset: safe inside captured
+// graphs) before split work adds its parts into y (qgemv_prefill.hip).
+hipError_t launch_zero_fill(float *y, int64_t n, int cus, hipStream_t stream);
+
 // Times-table GEMV for q2w at one token (qgemv_lut.hip): LDS bytes of the
 // tables for rows of K weights (64 KB for 32 <= K <= 4096, else SIZE_MAX),
 // and the launcher (up to two workgroups per CU of `cus`).

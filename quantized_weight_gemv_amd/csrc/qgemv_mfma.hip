@@ -681,6 +681,255 @@ hipError_t launch_fmt(const MfmaParams &p, int kwmax, int waves, int64_t wgs, in
     }
 }
 
+// ----------------------------------------------------------- skinny prefill
+//
+// Q4_0 GEMM for 9..64 tokens (Y[m][n] = sum_k X[m][k] w[n][k], w rounded to
+// fp16 as in the tiled prefill): the weights are streamed once, in 16-row
+// tiles, as the few-token kernel streams them, and each wave keeps its K
+// slice of every token's activations in registers as ready MFMA A operands
+// for the whole launch [volta-kernel-bakeoff, "Where we lose: prompts" and
+// "Stage 3": the unpack inside the matrix multiply].  Per 32-weight block of
+// 16 rows the B operand is unpacked once (q4_operand), scaled by the block's
+// fp16 scale with one rounding (the values qdequant_q4_0 writes with fp16
+// output) and used by one v_mfma_f32_16x16x32_f16 per 16-token group, all
+// accumulating into fp32.  The waves' partial 16 x (16 MT) tiles are summed
+// through LDS in a fixed order; a launch whose workgroups each cover all of K
+// stores every output once (bitwise reproducible), one that splits K over
+// workgroups adds the parts with fp32 atomics into a zero-filled Y.
+
+struct SkinnyParams {
+    const uint8_t *W;
+    const uint16_t *X;     // fp16 [M][K]
+    float *Y;              // fp32 [M][N]
+    int64_t scale_offset;
+    int M, N, K;
+    int kw;                // blocks per wave (<= KWA)
+    int span;              // blocks per workgroup along K (waves * kw)
+    int atomic;            // 1: K split over workgroups (blockIdx.y), parts added into zero-filled Y
+};
+
+constexpr int kSkinnyWaves = 8;
+
+// uint4 of LDS before the LDS-held operands: the larger of the staging
+// windows (16 tokens x BB blocks per wave, padded rows) and the partial tiles
+constexpr int skinny_region_uint4(int MT, int BB)
+{
+    const int stage = kSkinnyWaves * 16 * (BB * 4 + 1);
+    const int red = 2 * kSkinnyWaves * MT * 64;
+    return stage > red ? stage : red;
+}
+
+template <int MT, int KWA, int KWL>
+__global__ __launch_bounds__(512) void skinny_kernel(SkinnyParams p)
+{
+    // KWA blocks per wave hold their A operands in registers, KWL more in
+    // LDS (read back per tile: registers run out first)
+    constexpr int KWT = KWA + KWL;
+    constexpr int KW = (KWT + 3) / 4 * 4;   // four blocks of 16 rows per 16-byte load step
+    constexpr int kSteps = KW / 4;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nwaves = blockDim.x >> 6;
+    const int g = lane >> 4;          // lane group
+    const int c = lane & 15;          // row of the tile (B) / token of the group (A)
+    const int KB = p.K >> 5;
+    const int ntiles = (p.N + 15) >> 4;
+    const int kbeg = blockIdx.y * p.span + wave * p.kw;
+    const int kend = min(KB, kbeg + p.kw);
+    const int nblk = max(0, kend - kbeg);
+    const int nsteps = (nblk + 3) / 4;
+
+    // the first tile's codes and scales go out first: their HBM latency
+    // overlaps the activation staging below (lane: row c, block b0 + g)
+    const MfmaParams mp{p.W, nullptr, nullptr, nullptr, p.scale_offset, p.M, p.N, p.K, p.kw, 0};
+    const uint32_t coff = (uint32_t)(c * KB + kbeg + g) * 16u;
+    const uint32_t soff = (uint32_t)(c * KB + kbeg + g) * 2u;
+    TileRegs<kQ4_0, KW, false> ta, tb;
+    int tile = blockIdx.x;
+    load_tile<kQ4_0, KW, false>(mp, tile, ntiles, KB, coff, soff, ta, 0, p.N);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 1. this wave's activations, every (block, token group), as A operands
+    //    in the unpack's pair order: lane group g holds words 4g..4g+3 of the
+    //    block's pair-ordered 16 words, i.e. (x[4g], x[4g+2]), (x[16+4g],
+    //    x[18+4g]), (x[4g+1], x[4g+3]), (x[17+4g], x[19+4g]) of its token.
+    //    Staged through this wave's LDS window eight blocks of 16 tokens at
+    //    a time: whole 16-byte chunks of each token's slice read coalesced
+    //    (32 lanes per 512-byte token row), then the 8-byte pieces each lane
+    //    needs read back (token rows padded by 16 bytes: the 16 tokens of a
+    //    read fall on different banks).  Tokens past M read token M - 1 (their
+    //    rows of the product are never stored); blocks past the slice read
+    //    the last block and are never multiplied.
+    // LDS: the staging windows, then (after them) the partial tiles
+    // [2][nwaves][MT][64] in the same bytes; the LDS-held operands
+    // [wave][KWL][MT][64 lanes] beyond both
+    extern __shared__ f4_t red_dyn[];
+    constexpr int BB = KWL > 0 ? 4 : 8;     // blocks per staging batch
+    constexpr int kRow = BB * 4 + 1;        // uint4 per staged token row: BB blocks x 64 bytes + padding
+    constexpr int kRegion = skinny_region_uint4(MT, BB);
+    uint4 *stage = reinterpret_cast<uint4 *>(red_dyn) + wave * 16 * kRow;
+    half8_t A[KWA][MT];
+    uint4 *alds = reinterpret_cast<uint4 *>(red_dyn) + kRegion + wave * KWL * MT * 64;
+#pragma unroll
+    for (int tg = 0; tg < MT; ++tg) {
+#pragma unroll
+        for (int bb = 0; bb < KWT; bb += BB) {
+            uint4 v[BB];
+#pragma unroll
+            for (int i = 0; i < BB; ++i) {
+                // chunk q: token q / (4 BB), block (q % (4 BB)) / 4, 16-byte part q % 4
+                const int q = lane + 64 * i;
+                const int t = q / (4 * BB), b = (q % (4 * BB)) >> 2, u = q & 3;
+                const int m = min(tg * 16 + t, p.M - 1);
+                const int blk = min(kbeg + bb + b, KB - 1);
+                v[i] = *reinterpret_cast<const uint4 *>(p.X + (int64_t)m * p.K + (int64_t)blk * 32 + 8 * u);
+            }
+#pragma unroll
+            for (int i = 0; i < BB; ++i) {
+                const int q = lane + 64 * i;
+                stage[(q / (4 * BB)) * kRow + q % (4 * BB)] = v[i];
+            }
+            // LDS keeps a wave's order: the reads below see these writes
+            const uint2 *st2 = reinterpret_cast<const uint2 *>(stage);
+#pragma unroll
+            for (int b = 0; b < BB; ++b) {
+                if (bb + b < KWT) {
+                    const int base = (c * kRow + b * 4) * 2 + (g & 1);   // uint2 units
+                    const uint2 lo = st2[base + 2 * (g >> 1)];            // bytes 8g..8g+7: x[4g..4g+3]
+                    const uint2 hi = st2[base + 2 * (2 + (g >> 1))];      // bytes 32+8g..: x[16+4g..19+4g]
+                    const half8_t f = pack8(pair_lo(lo.x, lo.y), pair_lo(hi.x, hi.y), pair_hi(lo.x, lo.y),
+                                            pair_hi(hi.x, hi.y));
+                    if (bb + b < KWA)
+                        A[(bb + b) < KWA ? bb + b : 0][tg] = f;
+                    else
+                        alds[((bb + b - KWA) * MT + tg) * 64 + lane] = __builtin_bit_cast(uint4, f);
+                }
+            }
+        }
+    }
+    __syncthreads();   // the staging windows become the partial-tile buffers
+
+    // 2. tiles w, w + grid, ...: codes and scales of the next tile in flight
+    //    while the current one is multiplied
+    const int step = gridDim.x;
+    const int last = ntiles - 1;
+    const uint32_t magic = magic_reg();
+
+    auto compute = [&](const TileRegs<kQ4_0, KW, false> &t, f4_t (&acc)[MT]) {
+#pragma unroll
+        for (int tg = 0; tg < MT; ++tg)
+            acc[tg] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+            if (s < nsteps) {
+                // scale of (row c, block 4s + j) to every lane group, and the
+                // 4 x 4 transpose of the code words (register j of lane group
+                // g: word g of block 4s + j), as the few-token kernel does
+                uint32_t sa = t.scl[s], sb = t.scl[s];
+                swap32(sa, sb);
+                uint32_t sa2 = sa, sb2 = sb;
+                swap16(sa, sa2);
+                swap16(sb, sb2);
+                const uint32_t sc[4] = {sa, sa2, sb, sb2};
+                uint32_t w0 = t.code[s].x, w1 = t.code[s].y, w2 = t.code[s].z, w3 = t.code[s].w;
+                swap32(w0, w2);
+                swap32(w1, w3);
+                swap16(w0, w1);
+                swap16(w2, w3);
+                const uint32_t wj[4] = {w0, w1, w2, w3};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int b = 4 * s + j;
+                    if (b < KWT && b < nblk) {
+                        const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)(sc[j] & 0xFFFFu));
+                        const half8_t dv = {d, d, d, d, d, d, d, d};
+                        const half8_t bop = q4_operand(wj[j], magic) * dv;   // (q - 8) d, rounded once
+#pragma unroll
+                        for (int tg = 0; tg < MT; ++tg) {
+                            const half8_t a = b < KWA ? A[b < KWA ? b : 0][tg]
+                                                      : __builtin_bit_cast(half8_t,
+                                                                           alds[((b - KWA) * MT + tg) * 64 + lane]);
+                            acc[tg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bop, acc[tg], 0, 0, 0);
+                        }
+                    }
+                }
+            }
+        }
+    };
+
+    // sum the waves' partial tiles (double-buffered by tile parity, one
+    // barrier per tile; token group tg is summed and stored by wave
+    // (tg + it) % nwaves, the waves in a fixed order)
+    auto reduce_store = [&](const f4_t (&acc)[MT], int it, int tile) {
+        const int par = it & 1;
+#pragma unroll
+        for (int tg = 0; tg < MT; ++tg)
+            red_dyn[((par * nwaves + wave) * MT + tg) * 64 + lane] = acc[tg];
+        __syncthreads();
+#pragma unroll
+        for (int tg = 0; tg < MT; ++tg) {
+            if (wave == (tg + it) % nwaves) {
+                f4_t sum = red_dyn[((par * nwaves) * MT + tg) * 64 + lane];
+                for (int w = 1; w < nwaves; ++w) {
+                    const f4_t v = red_dyn[((par * nwaves + w) * MT + tg) * 64 + lane];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        sum[r] += v[r];
+                }
+                const int n = tile * 16 + c;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = tg * 16 + 4 * g + r;
+                    if (m < p.M && n < p.N) {
+                        float *dst = p.Y + (int64_t)m * p.N + n;
+                        if (p.atomic)
+                            unsafeAtomicAdd(dst, sum[r]);
+                        else
+                            *dst = sum[r];
+                    }
+                }
+            }
+        }
+    };
+
+    for (int it = 0;; it += 2) {
+        f4_t acc[MT];
+        const int t1 = tile + step;   // past the end: empty loads, never used
+        load_tile<kQ4_0, KW, false>(mp, t1, ntiles, KB, coff, soff, tb, 0, p.N);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(ta, acc);
+        reduce_store(acc, it, tile);
+        if (t1 > last)
+            break;
+        const int t2 = t1 + step;
+        load_tile<kQ4_0, KW, false>(mp, t2, ntiles, KB, coff, soff, ta, 0, p.N);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(tb, acc);
+        reduce_store(acc, it + 1, t1);
+        if (t2 > last)
+            break;
+        tile = t2;
+    }
+}
+
+// The blocks per wave that each token-group count instantiates (their
+// activation registers, 4 KWA MT, stay within ~160 so the kernel keeps two
+// waves per SIMD without spilling).
+template <int MT, int KWA, int KWL = 0>
+hipError_t launch_skinny_kwa(const SkinnyParams &p, dim3 grid, dim3 block, size_t shmem, hipStream_t stream)
+{
+    const void *fn = reinterpret_cast<const void *>(&skinny_kernel<MT, KWA, KWL>);
+    static bool raised = false;   // allow the kernel's LDS (at most 160 KB) once
+    if (!raised) {
+        if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
+            return hipErrorInvalidValue;
+        raised = true;
+    }
+    if (shmem > 160 * 1024)
+        return hipErrorInvalidValue;
+    return launch_kernel(fn, grid, block, shmem, stream, p);
+}
+
 }  // namespace
 
 // Launch the matrix-core GEMV on fp16 activations x, or on fp32 activations
@@ -706,6 +955,62 @@ hipError_t launch_gemv_mfma(int fmt, const uint8_t *W, int64_t scale_offset, con
     case kQ4_0: return launch_fmt<kQ4_0>(p, kwmax, waves, wgs, cus, stream);
     case kQ8_0: return launch_fmt<kQ8_0>(p, kwmax, waves, wgs, cus, stream);
     case kQ2W: return launch_fmt<kQ2W>(p, kwmax, waves, wgs, cus, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+
+// Skinny prefill launcher (M = 1..64, Q4_0): eight waves per workgroup split
+// a workgroup's K range; the blocks per wave (KWA) come from the instantiated
+// set of the token-group count, the fewest K ranges first; one workgroup per
+// CU (`wgs` overrides the count along N).  With more than one K range Y is
+// zero-filled first and the ranges add into it.
+hipError_t launch_prefill_skinny(const uint8_t *W, int64_t scale_offset, const uint16_t *X, float *Y, int M, int N,
+                                 int K, int cus, int64_t wgs, hipStream_t stream)
+{
+    if (M < 1 || M > 64 || N < 1 || K < 32 || K % 32 != 0)
+        return hipErrorInvalidValue;
+    const int MT = (M + 15) / 16;
+    const int KB = K / 32;
+    constexpr int kWaves = kSkinnyWaves;
+    // KWA candidates per token-group count (largest last)
+    // (Four token groups: 10 = 7 in registers and 3 in LDS.)
+    static const int kwa_set[4][3] = {{8, 16, 32}, {8, 16, 16}, {8, 12, 12}, {8, 10, 10}};
+    int kwa = kwa_set[MT - 1][2];
+    int S = (KB + kWaves * kwa - 1) / (kWaves * kwa);
+    for (int i = 0; i < 3; ++i) {   // the smallest KWA that needs no more K ranges
+        const int cand = kwa_set[MT - 1][i];
+        if ((KB + kWaves * cand - 1) / (kWaves * cand) == S) {
+            kwa = cand;
+            break;
+        }
+    }
+    const int kw = (KB + S * kWaves - 1) / (S * kWaves);
+    const int64_t ntiles = (N + 15) / 16;
+    int64_t gx = wgs > 0 ? wgs : std::max<int64_t>(1, cus / S);
+    gx = std::min(gx, ntiles);
+    if (S > 1) {
+        const hipError_t e = launch_zero_fill(Y, (int64_t)M * N, cus, stream);
+        if (e != hipSuccess)
+            return e;
+    }
+    SkinnyParams p{W, X, Y, scale_offset, M, N, K, kw, kw * kWaves, S > 1 ? 1 : 0};
+    const dim3 grid((unsigned)gx, (unsigned)S), block(64 * kWaves);
+    // the partial tiles, or the activation staging windows (16 tokens x 8
+    // blocks per wave, padded rows) before them; then the LDS-held operands
+    const bool lds_ops = MT == 4 && kwa == 10;   // 7 blocks in registers, 3 in LDS
+    const size_t shmem = (size_t)skinny_region_uint4(MT, lds_ops ? 4 : 8) * 16 +
+                         (lds_ops ? (size_t)kWaves * 3 * MT * 64 * 16 : 0);
+    switch (MT * 100 + kwa) {
+    case 108: return launch_skinny_kwa<1, 8>(p, grid, block, shmem, stream);
+    case 116: return launch_skinny_kwa<1, 16>(p, grid, block, shmem, stream);
+    case 132: return launch_skinny_kwa<1, 32>(p, grid, block, shmem, stream);
+    case 208: return launch_skinny_kwa<2, 8>(p, grid, block, shmem, stream);
+    case 216: return launch_skinny_kwa<2, 16>(p, grid, block, shmem, stream);
+    case 308: return launch_skinny_kwa<3, 8>(p, grid, block, shmem, stream);
+    case 312: return launch_skinny_kwa<3, 12>(p, grid, block, shmem, stream);
+    case 408: return launch_skinny_kwa<4, 8>(p, grid, block, shmem, stream);
+    case 410: return launch_skinny_kwa<4, 7, 3>(p, grid, block, shmem, stream);
     }
     return hipErrorInvalidValue;
 }

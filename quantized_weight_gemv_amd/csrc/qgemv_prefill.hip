@@ -585,11 +585,7 @@ hipError_t launch_prefill(PrefillParams p, int cus, hipStream_t stream)
     if (wgs > INT32_MAX)
         return hipErrorInvalidValue;
     if (!whole_tiles(p.chunks, S / DB, wgs)) {
-        FillParams f{p.Y, (int64_t)p.M * p.N};
-        void *a[] = {&f};
-        const int64_t fw = std::min<int64_t>((f.n + 255) / 256, (int64_t)cus * 16);
-        hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&zero_fill_kernel), dim3((unsigned)fw),
-                                       dim3(256), a, 0, stream);
+        const hipError_t e = launch_zero_fill(p.Y, (int64_t)p.M * p.N, cus, stream);
         if (e != hipSuccess)
             return e;
     }
@@ -601,6 +597,17 @@ hipError_t launch_prefill(PrefillParams p, int cus, hipStream_t stream)
 }
 
 }  // namespace
+}  // namespace qg
+
+namespace qg {
+hipError_t launch_zero_fill(float *y, int64_t n, int cus, hipStream_t stream)
+{
+    FillParams f{y, n};
+    void *a[] = {&f};
+    const int64_t fw = std::min<int64_t>((n + 255) / 256, (int64_t)cus * 16);
+    return hipLaunchKernel(reinterpret_cast<const void *>(&zero_fill_kernel), dim3((unsigned)fw), dim3(256), a, 0,
+                           stream);
+}
 }  // namespace qg
 
 extern "C" qg_status qgemm_q4_0_prefill(const void *Wp, const uint16_t *X, float *Y, int64_t M, int64_t N, int64_t K,
@@ -631,13 +638,19 @@ extern "C" qg_status qgemm_q4_0_prefill(const void *Wp, const uint16_t *X, float
     p.steps = 0;
     p.chunks = 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    // Tile (sweeps on MI355X): 128 tokens x 128 rows where those tiles give
-    // every CU its two workgroups (12288 x 2560 at 512 tokens: 54.9 against
-    // 61.2 us), else 64 x 128 (one wave along M: no weight unpacked twice).
+    // Up to 64 tokens the skinny kernel (qgemv_mfma.hip; MI355X, 64 tokens:
+    // 12288 x 2560 18.1 against 21.8 us with 64 x 128 tiles, 6144 x 2048
+    // 11.9 against 16.2, 2560 x 6144 13.2 against 17.8).  Beyond, the tile
+    // (sweeps on MI355X): 128 tokens x 128 rows where those tiles give every
+    // CU its two workgroups (12288 x 2560 at 512 tokens: 54.9 against 61.2
+    // us), else 64 x 128 (one wave along M: no weight unpacked twice).
     const int64_t t130 = (M + 127) / 128 * ((N + 127) / 128);
-    const int tile = o_tile ? o_tile : (M > 64 && t130 * 2 >= 3LL * cus ? 130 : 64);
+    const int tile = o_tile ? o_tile : (M <= 64 ? 16 : t130 * 2 >= 3LL * cus ? 130 : 64);
     hipError_t e;
     switch (tile) {
+    case 16:
+        e = launch_prefill_skinny(p.W, p.scale_offset, X, Y, (int)M, (int)N, (int)K, cus, o_wgs, s);
+        break;
     case 64: e = launch_prefill<1, 2, 1, 2>(p, cus, s); break;
     case 66: e = launch_prefill<1, 2, 2, 2>(p, cus, s); break;
     case 128: e = launch_prefill<1, 4, 2, 1>(p, cus, s); break;

@@ -20,15 +20,18 @@ def _prefill(Wd, X, N, K):
 # configuration): the built-in choice; one workgroup walking every tile
 # (whole tiles, plain stores); 3, 7 and 700 workgroups (ranges that cut tiles:
 # partial tiles added atomically into a zero-filled Y); every tile
-# configuration.
+# configuration; the skinny kernel (tile 16, up to 64 tokens) with its
+# built-in grid, one workgroup, three, and more workgroups than tiles.
 PREFILL_SETTINGS = [(0, 0), (1, 64), (3, 64), (700, 66), (0, 128), (5, 128),
-                    (0, 130), (700, 130), (0, 257), (3, 257)]
+                    (0, 130), (700, 130), (0, 257), (3, 257), (0, 16), (1, 16), (3, 16), (700, 16)]
 
 
 def _prefill_each_setting(Wd, X, N, K, Y_ref, S, what):
     q = qg()
     try:
         for wgs, tile in PREFILL_SETTINGS:
+            if tile == 16 and X.shape[0] > 64:
+                continue   # the skinny kernel takes at most 64 tokens
             q.qg_set_prefill_shape(wgs, tile)
             Y = _prefill(Wd, X, N, K)
             assert_within(Y, Y_ref, S, f"{what} workgroups={wgs} tile={tile}")
@@ -46,6 +49,40 @@ def test_prefill_small_parity(M, N, K):
     pb, po = pack_both(Q4_0, w)
     Y_ref, S = oracle.get().prefill(po, N, K, X)
     _prefill_each_setting(to_dev(pb), X, N, K, Y_ref, S, f"prefill M={M} {N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 100, 2048), (7, 17, 32), (16, 4099, 2560), (17, 1000, 2080),
+                                   (33, 640, 8192), (48, 257, 6144), (64, 130, 8192), (64, 5000, 96),
+                                   (40, 2048, 2560), (64, 31, 16384)])
+def test_prefill_skinny_parity(M, N, K):
+    """The skinny kernel (up to 64 tokens: activations held in registers,
+    weights streamed once) on ragged token, row and block counts, rows of an
+    odd number of blocks, and rows long enough to be split over several
+    workgroups (parts added atomically into a zero-filled Y), under its
+    launch settings; one-hot activations return the fp16-rounded weight
+    column exactly."""
+    q = qg()
+    w = si.weights(N, K, seed=M + K)
+    X = si.activations(M, K, seed=N)
+    pb, po = pack_both(Q4_0, w)
+    Wd = to_dev(pb)
+    Y_ref, S = oracle.get().prefill(po, N, K, X)
+    try:
+        for wgs in (0, 1, 3, 700):
+            q.qg_set_prefill_shape(wgs, 16)
+            Y = _prefill(Wd, X, N, K)
+            assert_within(Y, Y_ref, S, f"skinny M={M} {N}x{K} workgroups={wgs}")
+        q.qg_set_prefill_shape(0, 16)
+        cols = [0, 31, K // 2, K - 1][:M]
+        Xo = np.zeros((len(cols), K), np.float16)
+        for i, k in enumerate(cols):
+            Xo[i, k] = 1.0
+        Yo = _prefill(Wd, Xo, N, K)
+        w16 = oracle.get().dequant(Q4_0, po, N, K, "f16").astype(np.float32)
+        for i, k in enumerate(cols):
+            check_equal(Yo[i], w16[:, k], f"skinny one-hot column {k}", bits=False)
+    finally:
+        q.qg_set_prefill_shape(0, 0)
 
 
 @pytest.mark.parametrize("N,K", si.PREFILL_SHAPES)
