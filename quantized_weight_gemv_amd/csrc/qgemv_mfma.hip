@@ -47,6 +47,8 @@ namespace {
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ h2_t as_h2(uint32_t u) { return __builtin_bit_cast(h2_t, u); }
 __device__ __forceinline__ uint32_t as_u32(h2_t h) { return __builtin_bit_cast(uint32_t, h); }
@@ -474,26 +476,36 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(MfmaParams p)
     const int nblk = max(0, kend - kbeg);
     const int nsteps = (nblk + kBlocksPerLoad - 1) / kBlocksPerLoad;
 
-    // 1. this wave's activations (M tokens x its blocks, 64 bytes each) with
-    //    coalesced 16-byte loads, issued first (they come from cache; loads
-    //    retire in order).  Pair i is (token i / nblk, block i % nblk); pairs
-    //    past the slice re-read a valid block.
-    //    fp32 input: the raw words stay in registers until the staging
-    //    below rounds them (their loads overlap the first tile's).
+    // 1. this wave's activations (M tokens x its blocks), issued first (they
+    //    come from cache; loads retire in order).  fp16: each lane loads the
+    //    64 bytes of its (token, block) pairs (pair i is (token i / nblk,
+    //    block i % nblk); pairs past the slice re-read a valid block).  fp32
+    //    (128 bytes a pair): whole lines at a time, lane l of load u taking
+    //    16-byte chunk l + 64 u of the token-major slice (a lane per pair put
+    //    each lane of an instruction on a different cache line; with fp32
+    //    the address unit then bounded the staging: 8 tokens of 14336 x 4096
+    //    18.4 -> 16.9 us); chunks past the slice re-read a valid one.
     constexpr int kXPer = 8 * KWMAX / 64;    // (token, block) pairs per lane, M <= 8
+    constexpr int kCpt = KWMAX * 8;          // fp32: 16-byte chunks per token row slot
+    constexpr int kCPer = F32 ? 8 * kCpt / 64 : 1;   // fp32: chunks per lane
     const int npairs = p.M * nblk;
-    uint4 xr[kXPer][F32 ? 8 : 4];
+    uint4 xr[F32 ? 1 : kXPer][4];
+    u32x4_t xc[kCPer];
+    if constexpr (F32) {
 #pragma unroll
-    for (int t = 0; t < kXPer; ++t) {
-        const int i = min(lane + 64 * t, max(npairs, 1) - 1);
-        const int m = i / max(nblk, 1), b = i - m * max(nblk, 1);
-        const int blk = min(kbeg + b, KB - 1);
-        if constexpr (F32) {
-            const uint4 *src = reinterpret_cast<const uint4 *>(p.xf + (int64_t)m * p.K + (int64_t)blk * 32);
+        for (int u = 0; u < kCPer; ++u) {
+            const int f = lane + 64 * u;
+            const int m = min(f / kCpt, p.M - 1);
+            const int b = min((f % kCpt) >> 3, max(nblk, 1) - 1);
+            const int blk = min(kbeg + b, KB - 1);
+            xc[u] = reinterpret_cast<const u32x4_t *>(p.xf + (int64_t)m * p.K + (int64_t)blk * 32)[f & 7];
+        }
+    } else {
 #pragma unroll
-            for (int q = 0; q < 8; ++q)
-                xr[t][q] = src[q];
-        } else {
+        for (int t = 0; t < kXPer; ++t) {
+            const int i = min(lane + 64 * t, max(npairs, 1) - 1);
+            const int m = i / max(nblk, 1), b = i - m * max(nblk, 1);
+            const int blk = min(kbeg + b, KB - 1);
             const uint4 *src = reinterpret_cast<const uint4 *>(p.x + (int64_t)m * p.K + (int64_t)blk * 32);
 #pragma unroll
             for (int q = 0; q < 4; ++q)
@@ -517,39 +529,63 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(MfmaParams p)
     load_tile<FMT, KWMAX, WS>(p, blockIdx.x, ntiles, KB, coff, soff, ta, 0, rows);
     __builtin_amdgcn_sched_barrier(0);
 
-    // 3. the activations into this wave's own LDS area, in MFMA operand
+    // 3. the activations into this wave's own LDS area in MFMA operand
     //    order; layout [block][token][64 bytes], 16-byte chunk q of (block b,
     //    token m) at position q ^ (b & 3) of its slot: consecutive lanes hold
     //    consecutive blocks, whose slots are M * 64 bytes apart (the same
     //    banks for M a multiple of 4), and the swizzle spreads four of them
-    //    over different banks.  The reads below are this wave's own writes:
-    //    LDS keeps a wave's order.
+    //    over different banks.  fp32 first goes in natural order
+    //    ([token][block][64 bytes], rounded to binary16 here) and is then
+    //    rearranged in place: every lane reads all its pairs before any lane
+    //    writes (both layouts cover the same M x nblk slots).  The area is
+    //    this wave's own and LDS keeps a wave's order: no barrier.  Lanes
+    //    past the slice repeat a valid chunk or pair (the same bytes to the
+    //    same place), so no write is conditional.
     extern __shared__ uint4 xs_dyn[];
     uint4 *xs = xs_dyn + (int64_t)wave * p.kw * p.M * 4;
+    uint4 xn[kXPer][4];
+    if constexpr (F32) {
 #pragma unroll
-    for (int t = 0; t < kXPer; ++t) {
-        const int i = lane + 64 * t;
-        if (i < npairs) {
-            const int m = i / max(nblk, 1), b = i - m * max(nblk, 1);
-            uint4 o[4];
-            if constexpr (F32) {
-                uint4 h[4];
+        for (int u = 0; u < kCPer; ++u) {
+            const int f = lane + 64 * u;
+            const int m = min(f / kCpt, p.M - 1);
+            const int b = min((f % kCpt) >> 3, max(nblk, 1) - 1);
+            // (each element copied out before the bit cast: this compiler
+            // bit-casts an element of a vector-typed value in place as
+            // element 0)
+            const u32x4_t v = xc[u];
+            const u32x2_t h = {half2_bits(__builtin_bit_cast(float, (uint32_t)v[0]), __builtin_bit_cast(float, (uint32_t)v[1])),
+                               half2_bits(__builtin_bit_cast(float, (uint32_t)v[2]), __builtin_bit_cast(float, (uint32_t)v[3]))};
+            reinterpret_cast<u32x2_t *>(xs)[(m * nblk + b) * 8 + (f & 7)] = h;
+        }
+        // the two layouts are accessed through different types: keep the
+        // compiler from moving the reads above the writes, or the writes
+        // below above the reads
+        asm volatile("" ::: "memory");
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const uint4 a = xr[t][2 * u], b = xr[t][2 * u + 1];
-                    h[u] = make_uint4(half2_bits(__builtin_bit_cast(float, a.x), __builtin_bit_cast(float, a.y)),
-                                      half2_bits(__builtin_bit_cast(float, a.z), __builtin_bit_cast(float, a.w)),
-                                      half2_bits(__builtin_bit_cast(float, b.x), __builtin_bit_cast(float, b.y)),
-                                      half2_bits(__builtin_bit_cast(float, b.z), __builtin_bit_cast(float, b.w)));
-                }
-                permute_x<FMT>(h, o);
-            } else {
-                permute_x<FMT>(xr[t], o);
-            }
+        for (int t = 0; t < kXPer; ++t) {
+            const int i = min(lane + 64 * t, max(npairs, 1) - 1);
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                xs[(b * p.M + m) * 4 + (q ^ (b & 3))] = o[q];
+                xn[t][q] = xs[i * 4 + q];
         }
+        asm volatile("" ::: "memory");
+    } else {
+#pragma unroll
+        for (int t = 0; t < kXPer; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                xn[t][q] = xr[t][q];
+    }
+#pragma unroll
+    for (int t = 0; t < kXPer; ++t) {
+        const int i = min(lane + 64 * t, max(npairs, 1) - 1);
+        const int m = i / max(nblk, 1), b = i - m * max(nblk, 1);
+        uint4 o[4];
+        permute_x<FMT>(xn[t], o);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            xs[(b * p.M + m) * 4 + (q ^ (b & 3))] = o[q];
     }
 
     __shared__ f4_t red[GLU ? 4 : 2][kMaxWavesPerWg][64];
