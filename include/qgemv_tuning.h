@@ -42,7 +42,9 @@ qg_status qg_device_cus(int device, int *cus);
  * in LDS, whole rows per wave: 1; kept in each lane's registers: 0), engine
  * (vector-ALU kernel: 0; matrix-core kernel for 2..8 tokens and rows of at
  * most 256 blocks, for q2w an even number: 1, where ksplit is its number of
- * waves along K and teams its number of persistent workgroups) and
+ * waves along K, teams_per_wg its teams of such waves per workgroup sharing
+ * one staged copy of the activations (1 or 2; 2 for slices of at most 16
+ * blocks per wave) and teams its number of persistent workgroups) and
  * lanes_per_row (lanes of a wave that share one row in the vector-ALU
  * kernel: 16, 32 or 64; below 64 one token only) for later calls from the
  * calling thread.  A zero (-1 for xl and engine) keeps the built-in

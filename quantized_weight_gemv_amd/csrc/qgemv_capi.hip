@@ -302,8 +302,8 @@ qg_status run_gemv(int fmt, const void *Wp, const int32_t *idx, int64_t P, const
         const bool glu = mode == kModeGlu;   // the packed table holds 2N rows (gate, then up)
         hipError_t e = launch_gemv_mfma(fmt, static_cast<const uint8_t *>(Wp), scale_offset(fmt, glu ? 2 * N : N, K),
                                         f32 ? nullptr : x, f32 ? xf : nullptr, y, M, static_cast<int>(N),
-                                        static_cast<int>(K), waves, o_teams, cus, static_cast<hipStream_t>(stream),
-                                        glu);
+                                        static_cast<int>(K), waves, o_teams_per_wg, o_teams, cus,
+                                        static_cast<hipStream_t>(stream), glu);
         if (e == hipErrorInvalidValue)
             return QG_ERR_SHAPE;
         return e == hipSuccess ? QG_OK : QG_ERR_LAUNCH;

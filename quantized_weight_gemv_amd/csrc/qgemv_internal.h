@@ -137,11 +137,14 @@ hipError_t launch_variant(int M, int G, int J, int R, const GemvParams &p, dim3 
 
 // Few-token GEMV on the matrix cores (qgemv_mfma.hip), fp16 activations x or
 // fp32 activations xf (Q4_0, non-null xf), with glu the SwiGLU of a stacked
-// gate + up table (Q4_0, fp32): `waves` waves split K; `wgs`
-// persistent workgroups (0: as many as fit, at most 2 per CU of `cus`).
+// gate + up table (Q4_0, fp32): `waves` waves split K; `teams` teams of
+// them per workgroup share one staged copy of the activations (1 or 2; 0:
+// two at 1.5-4 tiles of 16 rows per CU, else one); `wgs` persistent
+// workgroups (0: as many as fit, at most 2 per CU of `cus` with one team, 1
+// with two).
 hipError_t launch_gemv_mfma(int fmt, const uint8_t *W, int64_t scale_offset, const uint16_t *x, const float *xf,
-                            float *y, int M, int N, int K, int waves, int64_t wgs, int cus, hipStream_t stream,
-                            bool glu = false);
+                            float *y, int M, int N, int K, int waves, int teams, int64_t wgs, int cus,
+                            hipStream_t stream, bool glu = false);
 
 // Prefill for 1..64 tokens on the matrix cores (qgemv_mfma.hip): weights
 // streamed once in 16-row tiles, activations held as MFMA operands in

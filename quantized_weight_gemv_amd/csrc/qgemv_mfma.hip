@@ -36,6 +36,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <map>
+#include <set>
 #include <mutex>
 #include <tuple>
 
@@ -381,20 +382,22 @@ __device__ __forceinline__ f4_t compute_tile(TileRegs<FMT, KW, WS> &t, const uin
     return acc;
 }
 
-// Sum the waves' partial tiles in a fixed order (wave 0 first) and store.
+// Sum a team's partial tiles in a fixed order (its wave 0 first) and store.
 // `red` is double-buffered by tile parity: tile i writes red[i & 1] and one
 // barrier per tile separates every write from the reads of the same buffer.
 // The reducing wave rotates with the tile so no wave carries all stores.
-__device__ __forceinline__ void reduce_store(const MfmaParams &p, f4_t acc, f4_t (*red)[kMaxWavesPerWg][64], int it,
-                                             int tile, int wave, int nwaves, int lane, int g, int c)
+// A team is `nwaves` waves from wave `wbase`; `kw` is this wave's index in it.
+template <int NW>
+__device__ __forceinline__ void reduce_store(const MfmaParams &p, f4_t acc, f4_t (*red)[NW][64], int it, int tile,
+                                             int wave, int wbase, int kw, int nwaves, int lane, int g, int c)
 {
     const int par = it & 1;
     red[par][wave][lane] = acc;
     __syncthreads();
-    if (wave == it % nwaves) {
-        f4_t s = red[par][0][lane];
+    if (kw == it % nwaves) {
+        f4_t s = red[par][wbase][lane];
         for (int w = 1; w < nwaves; ++w) {
-            const f4_t t = red[par][w][lane];
+            const f4_t t = red[par][wbase + w][lane];
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 s[r] += t[r];
@@ -414,18 +417,19 @@ __device__ __forceinline__ void reduce_store(const MfmaParams &p, f4_t acc, f4_t
 // writes silu(g) * u, evaluated in fp32 as the vector kernel's epilogue
 // does [the CUDA-kernel diary's FFN fusion step: gate, up and SwiGLU in one
 // kernel, only the final product written].
-__device__ __forceinline__ void reduce_store_glu(const MfmaParams &p, f4_t accg, f4_t accu,
-                                                 f4_t (*red)[kMaxWavesPerWg][64], int it, int tile, int wave,
-                                                 int nwaves, int lane, int g, int c)
+template <int NW>
+__device__ __forceinline__ void reduce_store_glu(const MfmaParams &p, f4_t accg, f4_t accu, f4_t (*red)[NW][64],
+                                                 int it, int tile, int wave, int wbase, int kw, int nwaves, int lane,
+                                                 int g, int c)
 {
     const int par = it & 1;
     red[par][wave][lane] = accg;
     red[2 + par][wave][lane] = accu;
     __syncthreads();
-    if (wave == it % nwaves) {
-        f4_t sg = red[par][0][lane], su = red[2 + par][0][lane];
+    if (kw == it % nwaves) {
+        f4_t sg = red[par][wbase][lane], su = red[2 + par][wbase][lane];
         for (int w = 1; w < nwaves; ++w) {
-            const f4_t tg = red[par][w][lane], tu = red[2 + par][w][lane];
+            const f4_t tg = red[par][wbase + w][lane], tu = red[2 + par][wbase + w][lane];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 sg[r] += tg[r];
@@ -452,26 +456,37 @@ __device__ __forceinline__ uint32_t half2_bits(float a, float b)
            ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
 }
 
-// Persistent over 16-row tiles: workgroup w takes tiles w, w + grid, ...;
-// its waves split K, stage their activation slices in LDS once, and prefetch
-// the next tile's codes and scales while the current tile is multiplied.
+// Persistent over 16-row tiles: a workgroup holds TEAMS teams of waves;
+// team t of workgroup w takes tiles TEAMS w + t, + TEAMS grid, ...; a
+// team's waves split K and prefetch the next tile's codes and scales while
+// the current tile is multiplied.  The activation slices are staged in LDS
+// once per workgroup (by team 0) and read by every team: two teams of a
+// workgroup share one copy where two workgroups of one team each read their
+// own (every copy of x is read from L2; with a few tiles per workgroup the
+// copies approach the weight bytes).  Every team runs the same number of
+// iterations (one barrier each); a team past the last tile multiplies
+// zeros and stores nothing.
 // GLU (fp32 input): a tile's gate rows and its up rows, N rows below them,
 // are multiplied one after the other, each while the other's loads are in
 // flight, and combined when both are summed.
 
-template <int FMT, int KWMAX, bool WS, bool F32, bool GLU>
-__global__ __launch_bounds__(512) void gemv_mfma_kernel(MfmaParams p)
+template <int FMT, int KWMAX, bool WS, bool F32, bool GLU, int TEAMS>
+__global__ __launch_bounds__(512 * TEAMS) void gemv_mfma_kernel(MfmaParams p)
 {
     static_assert(!GLU || (F32 && FMT == kQ4_0), "SwiGLU: Q4_0 with fp32 activations");
+    static_assert(TEAMS == 1 || TEAMS == 2, "one or two teams per workgroup");
     constexpr int kBlocksPerLoad = blocks_per_load<FMT>();   // blocks of 16 rows per 16-byte load step
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int nwaves = blockDim.x >> 6;
+    const int nwaves = (blockDim.x >> 6) / TEAMS;   // waves per team
+    const int team = wave / nwaves;
+    const int kwv = wave - team * nwaves;            // this wave's K slice
+    const int wbase = team * nwaves;
     const int g = lane >> 4;          // lane group
     const int c = lane & 15;          // row within the tile / token of the A operand
     const int KB = p.K >> 5;
     const int ntiles = (p.N + 15) >> 4;
-    const int kbeg = wave * p.kw;
+    const int kbeg = kwv * p.kw;
     const int kend = min(KB, kbeg + p.kw);
     const int nblk = max(0, kend - kbeg);
     const int nsteps = (nblk + kBlocksPerLoad - 1) / kBlocksPerLoad;
@@ -491,7 +506,9 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(MfmaParams p)
     const int npairs = p.M * nblk;
     uint4 xr[F32 ? 1 : kXPer][4];
     u32x4_t xc[kCPer];
-    if constexpr (F32) {
+    const bool stager = team == 0;   // wave-uniform
+    if (!stager) {
+    } else if constexpr (F32) {
 #pragma unroll
         for (int u = 0; u < kCPer; ++u) {
             const int f = lane + 64 * u;
@@ -524,9 +541,10 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(MfmaParams p)
     // each tile is two units, its gate rows and then its up rows (N further
     // down the table), so one unit's loads are in flight while the other is
     // multiplied, with the registers of the plain kernel.
-    const int step = gridDim.x;
+    const int step = gridDim.x * TEAMS;
+    const int first = blockIdx.x * TEAMS + team;
     TileRegs<FMT, KWMAX, WS> ta, tb;
-    load_tile<FMT, KWMAX, WS>(p, blockIdx.x, ntiles, KB, coff, soff, ta, 0, rows);
+    load_tile<FMT, KWMAX, WS>(p, first, ntiles, KB, coff, soff, ta, 0, rows);
     __builtin_amdgcn_sched_barrier(0);
 
     // 3. the activations into this wave's own LDS area in MFMA operand
@@ -542,9 +560,10 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(MfmaParams p)
     //    past the slice repeat a valid chunk or pair (the same bytes to the
     //    same place), so no write is conditional.
     extern __shared__ uint4 xs_dyn[];
-    uint4 *xs = xs_dyn + (int64_t)wave * p.kw * p.M * 4;
+    uint4 *xs = xs_dyn + (int64_t)kwv * p.kw * p.M * 4;
     uint4 xn[kXPer][4];
-    if constexpr (F32) {
+    if (!stager) {
+    } else if constexpr (F32) {
 #pragma unroll
         for (int u = 0; u < kCPer; ++u) {
             const int f = lane + 64 * u;
@@ -577,18 +596,22 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(MfmaParams p)
             for (int q = 0; q < 4; ++q)
                 xn[t][q] = xr[t][q];
     }
+    if (stager) {
 #pragma unroll
-    for (int t = 0; t < kXPer; ++t) {
-        const int i = min(lane + 64 * t, max(npairs, 1) - 1);
-        const int m = i / max(nblk, 1), b = i - m * max(nblk, 1);
-        uint4 o[4];
-        permute_x<FMT>(xn[t], o);
+        for (int t = 0; t < kXPer; ++t) {
+            const int i = min(lane + 64 * t, max(npairs, 1) - 1);
+            const int m = i / max(nblk, 1), b = i - m * max(nblk, 1);
+            uint4 o[4];
+            permute_x<FMT>(xn[t], o);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            xs[(b * p.M + m) * 4 + (q ^ (b & 3))] = o[q];
+            for (int q = 0; q < 4; ++q)
+                xs[(b * p.M + m) * 4 + (q ^ (b & 3))] = o[q];
+        }
     }
+    if constexpr (TEAMS > 1)
+        __syncthreads();   // team 0's copy, read by every team
 
-    __shared__ f4_t red[GLU ? 4 : 2][kMaxWavesPerWg][64];
+    __shared__ f4_t red[GLU ? 4 : 2][kMaxWavesPerWg * TEAMS][64];
     const uint32_t magic = magic_reg();
     const int cm = min(c, p.M - 1);
     const int xq = (FMT == kQ8_0) ? (((g & 1) << 1) | (g >> 1)) : g;
@@ -596,7 +619,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(MfmaParams p)
     if constexpr (GLU) {
         // units: gate of tile t in ta, its up rows in tb; while one is
         // multiplied the other's loads (or the next tile's gate) are in flight
-        for (int it = 0, tile = blockIdx.x;; ++it, tile += step) {
+        for (int it = 0, tile = first;; ++it, tile += step) {
             load_tile<FMT, KWMAX, WS>(p, tile, ntiles, KB, coff, soff, tb, p.N, rows);
             __builtin_amdgcn_sched_barrier(0);
             const f4_t accg = compute_tile<FMT, KWMAX, WS>(ta, xs, p.M, cm, xq, kbeg, kend, nsteps, magic);
@@ -604,27 +627,29 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(MfmaParams p)
             load_tile<FMT, KWMAX, WS>(p, t1, ntiles, KB, coff, soff, ta, 0, rows);
             __builtin_amdgcn_sched_barrier(0);
             const f4_t accu = compute_tile<FMT, KWMAX, WS>(tb, xs, p.M, cm, xq, kbeg, kend, nsteps, magic);
-            reduce_store_glu(p, accg, accu, red, it, tile, wave, nwaves, lane, g, c);
-            if (t1 > last)
+            reduce_store_glu(p, accg, accu, red, it, tile, wave, wbase, kwv, nwaves, lane, g, c);
+            if (t1 - team > last)   // team 0's next tile: the same test for every wave
                 break;
         }
     } else {
-        for (int it = 0, tile = blockIdx.x;; it += 2) {
+        // (the loop ends on team 0's tiles, the same test for every wave; a
+        // team past the last tile gets empty loads and stores nothing)
+        for (int it = 0, tile = first;; it += 2) {
             // tile in `ta`; prefetch the next into `tb` (past the end: empty
             // loads, never used)
             const int t1 = tile + step;
             load_tile<FMT, KWMAX, WS>(p, t1, ntiles, KB, coff, soff, tb, 0, rows);
             __builtin_amdgcn_sched_barrier(0);
             f4_t acc = compute_tile<FMT, KWMAX, WS>(ta, xs, p.M, cm, xq, kbeg, kend, nsteps, magic);
-            reduce_store(p, acc, red, it, tile, wave, nwaves, lane, g, c);
-            if (t1 > last)
+            reduce_store(p, acc, red, it, tile, wave, wbase, kwv, nwaves, lane, g, c);
+            if (t1 - team > last)
                 break;
             const int t2 = t1 + step;
             load_tile<FMT, KWMAX, WS>(p, t2, ntiles, KB, coff, soff, ta, 0, rows);
             __builtin_amdgcn_sched_barrier(0);
             acc = compute_tile<FMT, KWMAX, WS>(tb, xs, p.M, cm, xq, kbeg, kend, nsteps, magic);
-            reduce_store(p, acc, red, it + 1, t1, wave, nwaves, lane, g, c);
-            if (t2 > last)
+            reduce_store(p, acc, red, it + 1, t1, wave, wbase, kwv, nwaves, lane, g, c);
+            if (t2 - team > last)
                 break;
             tile = t2;
         }
@@ -649,69 +674,90 @@ int resident_per_cu(const void *fn, int threads, size_t shmem)
     return n;
 }
 
-template <int FMT, int KWMAX, bool WS>
-hipError_t launch_kw(const MfmaParams &p, int waves, int64_t wgs, int cus, hipStream_t stream)
+template <int FMT, int KWMAX, bool WS, int TEAMS>
+const void *mfma_kernel_fn(int variant)
 {
-    // fp32 activations: Q4_0 only (the fp32-input entry point's format)
+    if constexpr (FMT == kQ4_0)
+        return variant == 2   ? reinterpret_cast<const void *>(&gemv_mfma_kernel<FMT, KWMAX, WS, true, true, TEAMS>)
+               : variant == 1 ? reinterpret_cast<const void *>(&gemv_mfma_kernel<FMT, KWMAX, WS, true, false, TEAMS>)
+                              : reinterpret_cast<const void *>(&gemv_mfma_kernel<FMT, KWMAX, WS, false, false, TEAMS>);
+    else
+        return reinterpret_cast<const void *>(&gemv_mfma_kernel<FMT, KWMAX, WS, false, false, TEAMS>);
+}
+
+template <int FMT, int KWMAX, bool WS>
+hipError_t launch_kw(const MfmaParams &p, int waves, int teams, int64_t wgs, int cus, hipStream_t stream)
+{
     // fp32 activations and SwiGLU: Q4_0 only (their entry points' format)
-    const void *fn;
     int variant = 0;
     if constexpr (FMT == kQ4_0) {
         variant = p.glu ? 2 : (p.xf ? 1 : 0);
         if (p.glu && !p.xf)
             return hipErrorInvalidValue;
-        fn = variant == 2   ? reinterpret_cast<const void *>(&gemv_mfma_kernel<FMT, KWMAX, WS, true, true>)
-             : variant == 1 ? reinterpret_cast<const void *>(&gemv_mfma_kernel<FMT, KWMAX, WS, true, false>)
-                            : reinterpret_cast<const void *>(&gemv_mfma_kernel<FMT, KWMAX, WS, false, false>);
     } else {
         if (p.xf || p.glu)
             return hipErrorInvalidValue;
-        fn = reinterpret_cast<const void *>(&gemv_mfma_kernel<FMT, KWMAX, WS, false, false>);
     }
-    // every wave stages M x kw blocks of activations (64 bytes each); SwiGLU
-    // keeps 16 KB more of partial tiles in static LDS
-    const size_t shmem = (size_t)waves * p.kw * p.M * 64;
-    if (shmem > kMaxLds - (p.glu ? 16384 : 0))
+    // two teams: 16 waves, at most 128 VGPRs each (slices of up to 16 blocks)
+    if (teams < 1 || teams > 2 || (teams == 2 && (KWMAX > 16 || waves > 8)))
         return hipErrorInvalidValue;
-    static bool raised[3] = {false, false, false};   // allow more than the default dynamic LDS once per kernel
-    if (!raised[variant]) {
-        if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds) != hipSuccess)
-            return hipErrorInvalidValue;
-        raised[variant] = true;
+    const void *fn = teams == 2 ? mfma_kernel_fn<FMT, KWMAX, WS, (KWMAX <= 16 ? 2 : 1)>(variant)
+                                : mfma_kernel_fn<FMT, KWMAX, WS, 1>(variant);
+    // the workgroup stages M x kw blocks of activations per wave of a team
+    // (64 bytes each); the partial tiles take (2, SwiGLU 4) x 8 KB per team of
+    // static LDS
+    const size_t shmem = (size_t)waves * p.kw * p.M * 64;
+    const size_t red = (size_t)(p.glu ? 4 : 2) * teams * 8192;
+    if (shmem > kMaxLds || shmem + red > kMaxLds + 16384)
+        return hipErrorInvalidValue;
+    static std::mutex mu;
+    static std::set<const void *> raised;   // dynamic LDS beyond the default allowed once per kernel
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        if (!raised.count(fn)) {
+            // at most what the static partial-tile buffers leave of 160 KB
+            const int cap = (int)std::min<size_t>(kMaxLds, 160 * 1024 - red);
+            if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, cap) != hipSuccess) {
+                (void)hipGetLastError();   // reported as a shape error, not left for the next runtime call
+                return hipErrorInvalidValue;
+            }
+            raised.insert(fn);
+        }
     }
-    const int64_t ntiles = (p.N + 15) / 16;
+    const int64_t units = ((p.N + 15) / 16 + teams - 1) / teams;   // tiles per team slot
     if (wgs <= 0) {
         // as many workgroups as are resident at once (registers, LDS, wave
-        // slots), at most 2 per CU (MI355X, 8 tokens, 28672 x 4096: fp32
-        // activations 25.2 us at two per CU against 26.2 at one)
-        wgs = (int64_t)cus * std::min(2, resident_per_cu(fn, 64 * waves, shmem));
+        // slots), at most 2 per CU with one team (MI355X, 8 tokens, 28672 x
+        // 4096: fp32 activations 25.2 us at two per CU against 26.2 at one)
+        // and 1 with two
+        wgs = (int64_t)cus * std::min(teams == 2 ? 1 : 2, resident_per_cu(fn, 64 * waves * teams, shmem));
     }
-    wgs = std::min(wgs, ntiles);
-    const dim3 grid((unsigned)wgs), block(64 * waves);
+    wgs = std::min(wgs, units);
+    const dim3 grid((unsigned)wgs), block(64 * waves * teams);
     return launch_kernel(fn, grid, block, shmem, stream, p);
 }
 
 template <int FMT>
-hipError_t launch_fmt(const MfmaParams &p, int kwmax, int waves, int64_t wgs, int cus, hipStream_t stream)
+hipError_t launch_fmt(const MfmaParams &p, int kwmax, int waves, int teams, int64_t wgs, int cus, hipStream_t stream)
 {
     const bool ws = (p.K / 32) % 2 == 0;   // every row's scales 4-byte aligned
     if constexpr (FMT == kQ2W) {
         if (!ws)
             return hipErrorInvalidValue;   // q2w: an even number of blocks per row
         switch (kwmax) {
-        case 8: return launch_kw<FMT, 8, true>(p, waves, wgs, cus, stream);
-        case 16: return launch_kw<FMT, 16, true>(p, waves, wgs, cus, stream);
-        case 32: return launch_kw<FMT, 32, true>(p, waves, wgs, cus, stream);
+        case 8: return launch_kw<FMT, 8, true>(p, waves, teams, wgs, cus, stream);
+        case 16: return launch_kw<FMT, 16, true>(p, waves, teams, wgs, cus, stream);
+        case 32: return launch_kw<FMT, 32, true>(p, waves, teams, wgs, cus, stream);
         }
         return hipErrorInvalidValue;
     } else {
         switch (kwmax) {
-        case 8: return ws ? launch_kw<FMT, 8, true>(p, waves, wgs, cus, stream)
-                          : launch_kw<FMT, 8, false>(p, waves, wgs, cus, stream);
-        case 16: return ws ? launch_kw<FMT, 16, true>(p, waves, wgs, cus, stream)
-                           : launch_kw<FMT, 16, false>(p, waves, wgs, cus, stream);
-        case 32: return ws ? launch_kw<FMT, 32, true>(p, waves, wgs, cus, stream)
-                           : launch_kw<FMT, 32, false>(p, waves, wgs, cus, stream);
+        case 8: return ws ? launch_kw<FMT, 8, true>(p, waves, teams, wgs, cus, stream)
+                          : launch_kw<FMT, 8, false>(p, waves, teams, wgs, cus, stream);
+        case 16: return ws ? launch_kw<FMT, 16, true>(p, waves, teams, wgs, cus, stream)
+                           : launch_kw<FMT, 16, false>(p, waves, teams, wgs, cus, stream);
+        case 32: return ws ? launch_kw<FMT, 32, true>(p, waves, teams, wgs, cus, stream)
+                           : launch_kw<FMT, 32, false>(p, waves, teams, wgs, cus, stream);
         }
         return hipErrorInvalidValue;
     }
@@ -975,22 +1021,32 @@ hipError_t launch_skinny_kwa(const SkinnyParams &p, dim3 grid, dim3 block, size_
 // kw = ceil(K/32 / waves) blocks rounded up to 4, at most 32; `wgs`
 // persistent workgroups walk the 16-row tiles (0: the built-in count).
 hipError_t launch_gemv_mfma(int fmt, const uint8_t *W, int64_t scale_offset, const uint16_t *x, const float *xf,
-                            float *y, int M, int N, int K, int waves, int64_t wgs, int cus, hipStream_t stream,
-                            bool glu)
+                            float *y, int M, int N, int K, int waves, int teams, int64_t wgs, int cus,
+                            hipStream_t stream, bool glu)
 {
     const int KB = K / 32;
-    if (M < 1 || M > 8 || waves < 1 || waves > kMaxWavesPerWg)
+    if (M < 1 || M > 8 || waves < 1 || waves > kMaxWavesPerWg || teams < 0 || teams > 2)
         return hipErrorInvalidValue;
     int kw = (KB + waves - 1) / waves;
     kw = (kw + 3) / 4 * 4;
     if (kw > 32)
         return hipErrorInvalidValue;
     const int kwmax = kw <= 8 ? 8 : (kw <= 16 ? 16 : 32);
+    if (teams == 0) {
+        // Two teams where a workgroup sees only a few tiles, so that the
+        // per-workgroup copy of x weighs against the weight bytes (1.5 to 4
+        // tiles per CU; MI355X, 8 tokens: 14336 x 4096 13.8 -> 13.0 us, fp32
+        // input 15.4 -> 13.7, SwiGLU 2 x 14336 x 4096 23.0 -> 21.5 and 24.3 ->
+        // 21.0 at 4 tokens, 2 x 6144 x 2048 9.6 -> 8.3; 28672 x 4096, 7 tiles
+        // per CU: 20.9 -> 21.8, one team kept).
+        const int64_t ntiles = ((int64_t)N + 15) / 16;
+        teams = (kwmax <= 16 && 2 * ntiles >= 3LL * cus && ntiles <= 4LL * cus) ? 2 : 1;
+    }
     MfmaParams p{W, x, xf, y, scale_offset, M, N, K, kw, glu ? 1 : 0};
     switch (fmt) {
-    case kQ4_0: return launch_fmt<kQ4_0>(p, kwmax, waves, wgs, cus, stream);
-    case kQ8_0: return launch_fmt<kQ8_0>(p, kwmax, waves, wgs, cus, stream);
-    case kQ2W: return launch_fmt<kQ2W>(p, kwmax, waves, wgs, cus, stream);
+    case kQ4_0: return launch_fmt<kQ4_0>(p, kwmax, waves, teams, wgs, cus, stream);
+    case kQ8_0: return launch_fmt<kQ8_0>(p, kwmax, waves, teams, wgs, cus, stream);
+    case kQ2W: return launch_fmt<kQ2W>(p, kwmax, waves, teams, wgs, cus, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -81,16 +81,17 @@ def test_f32in_matrix_core_engine_matches_fp16_call(M, N, K):
     try:
         for ks in (0, 1, 2, 4, 8):
             for wgs in (0, 1, 3):
-                q.qg_set_gemv_shape(0, 0, ks, 0, wgs, -1, 1, 0)
-                try:
-                    y = _f32in(Wd, x, N, K)
-                except q.QGError:
-                    continue
-                y16 = q.qgemv_q4_0(Wd, x16, N, K)
-                torch.cuda.synchronize()
-                tried += 1
-                assert np.array_equal(y, y16.cpu().numpy()), f"waves={ks} workgroups={wgs}"
-                assert_within(y, y_ref, s, f"f32in mfma M={M} waves={ks} workgroups={wgs}")
+                for tm in (0, 2):
+                    q.qg_set_gemv_shape(0, 0, ks, tm, wgs, -1, 1, 0)
+                    try:
+                        y = _f32in(Wd, x, N, K)
+                    except q.QGError:
+                        continue
+                    y16 = q.qgemv_q4_0(Wd, x16, N, K)
+                    torch.cuda.synchronize()
+                    tried += 1
+                    assert np.array_equal(y, y16.cpu().numpy()), f"waves={ks} teams={tm} workgroups={wgs}"
+                    assert_within(y, y_ref, s, f"f32in mfma M={M} waves={ks} teams={tm} workgroups={wgs}")
     finally:
         q.qg_set_gemv_shape(0, 0, 0, 0, 0, -1, -1, 0)
     assert tried >= 2
@@ -275,16 +276,17 @@ def test_swiglu_matrix_core_every_wave_count_and_grid():
             yv = buf[64:64 + M * N].view(M, N)
             for ks in (0, 1, 2, 4, 8):
                 for wgs in (0, 1, 3):
-                    q.qg_set_gemv_shape(0, 0, ks, 0, wgs, -1, 1, 0)
-                    try:
-                        q.qgemv_q4_0_swiglu_f32in(Wd, to_dev(x), N, K, yv)
-                    except q.QGError:
-                        continue
-                    torch.cuda.synchronize()
-                    tried += 1
-                    _check_swiglu(yv.cpu().numpy(), ref, f"swiglu mfma M={M} waves={ks} workgroups={wgs}")
-                    h = buf.cpu().numpy()
-                    assert (h[:64] == 7.0).all() and (h[64 + M * N:] == 7.0).all(), "wrote outside y"
+                    for tm in (0, 2):
+                        q.qg_set_gemv_shape(0, 0, ks, tm, wgs, -1, 1, 0)
+                        try:
+                            q.qgemv_q4_0_swiglu_f32in(Wd, to_dev(x), N, K, yv)
+                        except q.QGError:
+                            continue
+                        torch.cuda.synchronize()
+                        tried += 1
+                        _check_swiglu(yv.cpu().numpy(), ref, f"swiglu mfma M={M} waves={ks} teams={tm} workgroups={wgs}")
+                        h = buf.cpu().numpy()
+                        assert (h[:64] == 7.0).all() and (h[64 + M * N:] == 7.0).all(), "wrote outside y"
     finally:
         q.qg_set_gemv_shape(0, 0, 0, 0, 0, -1, -1, 0)
     assert tried >= 6

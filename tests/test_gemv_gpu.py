@@ -291,9 +291,10 @@ def test_gemv_every_launch_shape(fmt, N, K, M):
 @pytest.mark.parametrize("N,K,M", [(17, 32, 2), (257, 4096, 8), (100, 2560, 3), (33, 6144, 5), (130, 8192, 1),
                                    (64, 96, 8), (4099, 2048, 2), (100, 192, 4), (50, 320, 8), (31, 1472, 6)])
 def test_gemv_matrix_core_engine(fmt, N, K, M):
-    """The matrix-core few-token kernel, every wave count along K and a
-    persistent grid of the built-in size, one workgroup (it walks every tile)
-    and three (uneven tiles per workgroup), against the oracle; one-hot
+    """The matrix-core few-token kernel, every wave count along K, one or two
+    teams per workgroup and a persistent grid of the built-in size, one
+    workgroup (it walks every tile) and three (uneven tiles per workgroup),
+    against the oracle; one-hot
     columns stay exact on it (exact (q-8) operands, scale applied in fp32)."""
     q = qg()
     w = weights(N, K, seed=N + 1)
@@ -313,13 +314,14 @@ def test_gemv_matrix_core_engine(fmt, N, K, M):
     try:
         for ks in (0, 1, 2, 3, 4, 6, 7, 8):
             for wgs in (0, 1, 3):
-                q.qg_set_gemv_shape(0, 0, ks, 0, wgs, -1, 1, 0)
-                try:
-                    y = _gemv(fmt, Wd, xd, N, K)
-                except q.QGError:
-                    continue
-                tried += 1
-                assert_within(y, y_ref, s, f"mfma waves={ks} workgroups={wgs}")
+                for tm in (0, 2):   # one team per workgroup, or two sharing the staged activations
+                    q.qg_set_gemv_shape(0, 0, ks, tm, wgs, -1, 1, 0)
+                    try:
+                        y = _gemv(fmt, Wd, xd, N, K)
+                    except q.QGError:
+                        continue
+                    tried += 1
+                    assert_within(y, y_ref, s, f"mfma waves={ks} teams={tm} workgroups={wgs}")
         q.qg_set_gemv_shape(0, 0, 0, 0, 0, -1, 1, 0)
         cols = [0, 5, 16, 31, K - 1]
         xo = np.zeros((len(cols), K), np.float16)
