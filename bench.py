@@ -168,6 +168,40 @@ def _probe_us(qg, torch, buf, nbytes, copies, stride, sink, wgs, loads, reps):
     return float(np.median(ms) * 1e3)
 
 
+def probe_floor(qg, torch, buf, nb: int, stride: int, copies: int, sink, cus: int, reps: int = 24):
+    """The read floor of `nb` bytes: the fastest probe launch over the swept
+    shapes (per-launch events) reading copy c at byte c * stride of `buf`,
+    then that launch back to back in a graph.  Returns (events us, back to
+    back us, loads in flight, workgroups)."""
+    top = None
+    for loads in PROBE_LOADS:
+        for per_cu in PROBE_WGS_PER_CU:
+            us = _probe_us(qg, torch, buf, nb, copies, stride, sink, per_cu * cus, loads, reps)
+            if top is None or us < top[0]:
+                top = (us, loads, per_cu * cus)
+    us, loads, wgs = top
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    calls = 64
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            for i in range(calls):
+                c = i % copies
+                qg.qg_read_probe(buf[c * stride:], sink, wgs, loads, nb)
+    torch.cuda.synchronize()
+    g.replay()
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s0.record()
+    g.replay()
+    s1.record()
+    torch.cuda.synchronize()
+    b2b = s0.elapsed_time(s1) * 1e3 / calls
+    del g
+    return us, b2b, loads, wgs
+
+
 def hbm_probe(qg, torch, work, gib: int = 4) -> dict:
     """The read probe: best rate on `gib` GiB over the swept launch shapes,
     then per shape the fastest read of its packed bytes (per-launch events,
@@ -191,32 +225,7 @@ def hbm_probe(qg, torch, work, gib: int = 4) -> dict:
     floors = {}
     for w in work:
         nb = w["nb"]
-        top = None
-        for loads in PROBE_LOADS:
-            for per_cu in PROBE_WGS_PER_CU:
-                us = _probe_us(qg, torch, w["buf"], nb, w["copies"], nb, sink, per_cu * cus, loads, 24)
-                if top is None or us < top[0]:
-                    top = (us, loads, per_cu * cus)
-        us, loads, wgs = top
-        g = torch.cuda.CUDAGraph()
-        cap = torch.cuda.Stream()
-        cap.wait_stream(torch.cuda.current_stream())
-        calls = 64
-        with torch.cuda.stream(cap):
-            with torch.cuda.graph(g, stream=cap):
-                for i in range(calls):
-                    c = i % w["copies"]
-                    qg.qg_read_probe(w["buf"][c * nb:], sink, wgs, loads, nb)
-        torch.cuda.synchronize()
-        g.replay()
-        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        s0.record()
-        g.replay()
-        s1.record()
-        torch.cuda.synchronize()
-        b2b = s0.elapsed_time(s1) * 1e3 / calls
-        del g
+        us, b2b, loads, wgs = probe_floor(qg, torch, w["buf"], nb, nb, w["copies"], sink, cus)
         floors[f"{w['N']}x{w['K']}"] = {"bytes": nb, "us_median": round(us, 3), "GBps": round(nb / us / 1e3, 1),
                                         "us_back_to_back": round(b2b, 3), "loads_in_flight": loads,
                                         "workgroups": wgs}
@@ -347,14 +356,19 @@ def _time_graph(torch, fns, reps: int, warm: int = 5, calls: int = 20, rounds: i
     """Per-call time (us) of `calls` calls captured back to back in one HIP
     graph, the median of `rounds` replays timed by stream events: every kernel
     a call launches and the gaps between them, without the host launch path
-    (`reps` and `warm` are the warm-up calls before capture)."""
-    for i in range(warm):
-        fns[i % len(fns)]()
-    torch.cuda.synchronize()
+    (`reps` and `warm` are the warm-up calls before capture).  `fns` is a
+    list of calls that launch on the current stream, or a function returning
+    one, called on the capturing stream (for calls bound to the stream that
+    was current when they were made, such as PreparedGemv)."""
     g = torch.cuda.CUDAGraph()
     cap = torch.cuda.Stream()
     cap.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(cap):
+        if callable(fns):
+            fns = fns()
+        for i in range(warm):
+            fns[i % len(fns)]()
+        cap.synchronize()
         with torch.cuda.graph(g, stream=cap):
             for i in range(calls):
                 fns[(i + warm) % len(fns)]()
@@ -376,6 +390,7 @@ def suite(qg, torch, reps: int):
     """Every workload of the library, one JSON record each."""
     out = []
     cus = qg.qg_device_cus()
+    sink = torch.empty(max(PROBE_WGS_PER_CU) * cus, dtype=torch.int32, device="cuda")
 
     def rec(**kw):
         out.append(kw)
@@ -399,10 +414,17 @@ def suite(qg, torch, reps: int):
         y = torch.empty((M, N), dtype=torch.float32, device="cuda")
         calls = [qg.PreparedGemv(fmt, buf[c * nb:(c + 1) * nb], x, y, N, K) for c in range(copies)]
         med, mean = _time_calls(qg, torch, calls, reps)
+        gmed, _ = _time_graph(torch, lambda: [qg.PreparedGemv(fmt, buf[c * nb:(c + 1) * nb], x, y, N, K)
+                                              for c in range(copies)], reps)
         b = N * K // 32 * (18 if fmt == qg.Q4_0 else 34) + 2 * M * K + 4 * M * N
+        extra = {}
+        if M == 1:   # the read floor of the same packed bytes, back to back like us_graph
+            wb = N * K // 32 * (18 if fmt == qg.Q4_0 else 34)
+            _, pb2b, _, _ = probe_floor(qg, torch, buf, wb, nb, copies, sink, cus)
+            extra = {"probe_us_back_to_back": round(pb2b, 3), "graph_over_probe": round(gmed / pb2b, 3)}
         rec(kind="gemv", fmt="q4_0" if fmt == qg.Q4_0 else "q8_0", N=N, K=K, M=M, us_median=round(med, 3),
-            us_mean=round(mean, 3), GBps=round(b / med / 1e3, 1), pct_of_8TBps=round(b / med / 1e3 / 80, 2),
-            algorithmic_bytes=b, copies=copies)
+            us_mean=round(mean, 3), us_graph=round(gmed, 3), GBps=round(b / med / 1e3, 1),
+            pct_of_8TBps=round(b / med / 1e3 / 80, 2), algorithmic_bytes=b, copies=copies, **extra)
     packed_cache.clear()
 
     # MoE: a pool of P experts replicated to >= 1 GiB; fresh distinct indices per call
@@ -420,8 +442,19 @@ def suite(qg, torch, reps: int):
             pool_c = buf[(c % copies) * nb:(c % copies + 1) * nb]
             fns.append(lambda pc=pool_c, ic=idx[c % ncalls]: qg.qmoe_gemv_q4_0(pc, P, ic, x, N, K, y))
         med, mean = _time_calls(qg, torch, fns, reps)
+        gmed, _ = _time_graph(torch, fns, reps)
+        # the same with one index set for every call (cached, as when the
+        # router has just written it): the rest is the indirection's latency
+        i0 = idx[0]
+        same = [lambda pc=buf[(c % copies) * nb:(c % copies + 1) * nb]: qg.qmoe_gemv_q4_0(pc, P, i0, x, N, K, y)
+                for c in range(copies)]
+        smed, _ = _time_graph(torch, same, reps)
         b = E * (N * K // 32 * 18 + 2 * K + 4 * N)
+        # floor: one contiguous read of the E experts' packed bytes, back to back
+        _, pb2b, _, _ = probe_floor(qg, torch, buf, E * (nb // P), nb, copies, sink, cus)
         rec(kind="moe", fmt="q4_0", P=P, E=E, N=N, K=K, us_median=round(med, 3), us_mean=round(mean, 3),
+            us_graph=round(gmed, 3), us_graph_same_indices=round(smed, 3), probe_us_back_to_back=round(pb2b, 3),
+            graph_over_probe=round(gmed / pb2b, 3),
             GBps=round(b / med / 1e3, 1), pct_of_8TBps=round(b / med / 1e3 / 80, 2), algorithmic_bytes=b,
             pool_copies=copies)
         del buf
