@@ -25,9 +25,11 @@
 //     step's 32 bytes of each of 32 rows directly would touch 32 cache lines
 //     per instruction for a quarter line each; the request count, not the
 //     bytes, then bounds the kernel.
-//   * Activations: a plain copy of the tile's X rows into LDS per step
-//     (natural k order, rows padded to 72 halves: conflict-free 16-byte
-//     reads), read back as the A operands.
+//   * Activations: each step's X rows go straight from memory into LDS
+//     (buffer loads that write LDS: no registers, no copy instructions), in
+//     natural k order with the 16-byte chunks of row r at position c ^ (r %
+//     8) (conflict-free 16-byte reads without padding), and are read back as
+//     the A operands.
 //   * Each wave owns 32 TM tokens x 32 TN rows of the workgroup's tile (WM
 //     waves along M, 4 / WM along N); with WM = 1 no weight is unpacked twice.
 //
@@ -38,13 +40,13 @@
 // tiles are added with fp32 atomics into Y, which a small fill kernel zeroes
 // first (last-bit differences between runs, within the accuracy bound).
 //
-// Pipelining: the activation loads of the next four steps and the weight
-// loads of the next group are in flight in registers while the current step
-// is multiplied (one load counter counts them in issue order, so both lead
-// by four steps); the activation tile is double-buffered in LDS, one barrier
-// per step.  Every load is issued unconditionally (positions past a
-// workgroup's range repeat its last one and are never used), so the compiler
-// waits for exactly the stage a step consumes.
+// Pipelining: four LDS activation buffers, one per step of a group; the
+// copy of step s + 3 is issued at the start of step s (into the buffer step
+// s - 1 read) and the weight loads of the next group are in flight in
+// registers while the current group is multiplied; one barrier per step.
+// Every load is issued unconditionally (positions past a workgroup's range
+// repeat its last one and are never used), so the load counter, which
+// counts them in issue order, tells exactly when a step's copy has landed.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -60,8 +62,6 @@ namespace {
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f16x_t __attribute__((ext_vector_type(16)));
-
-constexpr int kLdsStride = 72;   // halves per LDS activation row: 64 + 8 padding
 
 __device__ __forceinline__ h2_t as_h2(uint32_t u) { return __builtin_bit_cast(h2_t, u); }
 __device__ __forceinline__ uint32_t as_u32(h2_t h) { return __builtin_bit_cast(uint32_t, h); }
@@ -150,14 +150,8 @@ struct Tiling {
     static constexpr int AC = BM / 32;        // 16-byte activation chunks per thread per step
 };
 
-// Registers of one step's activations, and of one group's weights (per row
-// tile: this lane's four 16-byte chunks of whole lines, and the eight scales
-// of its row).
-template <int AC>
-struct AStage {
-    uint4 a[AC];
-};
-
+// Registers of one group's weights (per row tile: this lane's four 16-byte
+// chunks of whole lines, and the eight scales of its row).
 template <int TN>
 struct WGroup {
     uint4 code[TN][4];
@@ -168,9 +162,10 @@ struct WGroup {
 // (they change only when the tile does); the K step enters as the scalar
 // offset of the buffer loads, so a step spends no vector instruction on
 // addresses.
-//   Activations: chunk c of thread t is the 16 bytes of row (t + 256 c) / 8
-//   of the tile (clamped to M - 1: rows past M are never stored) at k chunk
-//   (t + 256 c) % 8 of the step.
+//   Activations: lane l of instruction i of wave w writes the i-th kilobyte
+//   of the wave's share of the step, i.e. row 8 w + 32 i + l / 8 of the tile
+//   (clamped to M - 1: rows past M are never stored) at position l % 8, and
+//   reads the 16-byte chunk (l % 8) ^ (row % 8) of that row at the step.
 //   Weights: instruction i of row tile j (32 rows from row n0 + 32 (wn TN +
 //   j)) has lane l read the 16 bytes of row 8 i + l / 8 at block 8 g + l % 8
 //   of group g; the scales: lane l reads the eight of row l % 32.  Rows are
@@ -199,9 +194,9 @@ __device__ __forceinline__ void a_offsets(ACursor<AC> &c, const PrefillParams &p
 #pragma unroll
     for (int i = 0; i < AC; ++i) {
         const int idx = (int)threadIdx.x + 256 * i;
-        const int r = idx >> 3, ch = idx & 7;
+        const int r = idx >> 3, ch = (idx & 7) ^ (r & 7);
         const int m = min(c.ps.tm * BM + r, p.M - 1);
-        c.off[i] = (uint32_t)m * (uint32_t)p.K * 2u + (uint32_t)(ch >> 2) * 64u + (uint32_t)(ch & 3) * 16u;
+        c.off[i] = (uint32_t)m * (uint32_t)p.K * 2u + (uint32_t)ch * 16u;
     }
 }
 
@@ -252,15 +247,37 @@ struct Rsrc {
     __amdgpu_buffer_rsrc_t x, w, s;
 };
 
+// One step's activations straight into the LDS buffer `buf` (BM rows of
+// eight 16-byte chunks): no registers and no copy instructions.  Chunks of
+// blocks past K get an offset beyond the buffer, whose range check returns
+// zeros.
 template <int AC>
-__device__ __forceinline__ void load_a(AStage<AC> &st, const Rsrc &rs, const ACursor<AC> &c)
+__device__ __forceinline__ void dma_a(uint4 (*buf)[8], const Rsrc &rs, const ACursor<AC> &c, int KB, int wave)
 {
     const int so = c.ps.s * 128;   // 64 fp16 per step
+    const bool full = 2 * c.ps.s + 2 <= KB;   // uniform: both blocks of the step inside K
 #pragma unroll
     for (int i = 0; i < AC; ++i) {
-        const auto t = __builtin_amdgcn_raw_buffer_load_b128(rs.x, c.off[i], so, 0);
-        st.a[i] = make_uint4(t[0], t[1], t[2], t[3]);
+        uint32_t off = c.off[i];
+        if (!full) {
+            const int idx = (int)threadIdx.x + 256 * i;
+            const int r = idx >> 3, ch = (idx & 7) ^ (r & 7);
+            if (2 * c.ps.s + (ch >> 2) >= KB)
+                off = 0x80000000u;
+        }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs.x, (__attribute__((address_space(3))) void *)&buf[8 * wave + 32 * i][0], 16, off, so, 0, 0);
     }
+}
+
+// Wait until at most n vector memory operations of this wave are in flight
+// (gfx9 encoding of s_waitcnt: vmcnt in bits 3:0 and 15:14; expcnt and
+// lgkmcnt left at their maxima, so they are not waited for).
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 // SA: rows hold a whole number of groups (K / 32 a multiple of 8), so a
@@ -293,14 +310,18 @@ __device__ __forceinline__ void load_w(WGroup<TN> &st, const Rsrc &rs, const WCu
     }
 }
 
-template <int WM, int TM, int TN, int OCC, int DA, bool SA>
+template <int WM, int TM, int TN, int OCC, bool SA>
 __global__ __launch_bounds__(256, OCC) void prefill_kernel(PrefillParams p)
 {
-    static_assert(kGroup % DA == 0, "activation stages: a divisor of the group's steps");
     using T = Tiling<WM, TM, TN>;
     constexpr int AC = T::AC;
     constexpr int DB = kGroup;   // steps per weight group
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][T::BM][kLdsStride];
+    // activations: one swizzled buffer per step of a group, each a variable
+    // of its own, so the compiler knows which buffer an A-operand read
+    // touches and waits only for the copies into that one (with one array
+    // it waits for every load in flight before each read)
+    __shared__ uint4 Ad0[T::BM][8], Ad1[T::BM][8], Ad2[T::BM][8], Ad3[T::BM][8];
+    auto abuf = [&](int q) -> uint4(*)[8] { return q == 0 ? Ad0 : q == 1 ? Ad1 : q == 2 ? Ad2 : Ad3; };
     __shared__ uint4 Wl[4][TN][32][8];   // per wave: the current group's code bytes, chunks swizzled by row
 
     const int lane = threadIdx.x & 63;
@@ -330,10 +351,9 @@ __global__ __launch_bounds__(256, OCC) void prefill_kernel(PrefillParams p)
                 acc[i][j][r] = 0.0f;
 
     // Global loads are counted in issue order by one counter, so a wait for
-    // one load waits for every load issued before it.  Activation stage r %
-    // DB holds iteration r's activations (copied to LDS one iteration before
-    // they are multiplied); the weight group in registers is the next group.
-    // Issue order: the group's weights with its first step's activations.
+    // one load waits for every load issued before it.  Issue order: the
+    // activations of the range's first three steps (into buffers 0-2), then
+    // the first weight group.
     const Pos first = pos_of(p, it_beg, S);
     ACursor<AC> la;
     la.ps = first;
@@ -343,30 +363,15 @@ __global__ __launch_bounds__(256, OCC) void prefill_kernel(PrefillParams p)
     lw.ps = first;
     lw.it = it_beg;
     w_offsets<T::BN>(lw, p, KB, lane, wn);
-    AStage<AC> sa[DA];   // activations of the next DA steps in flight
     WGroup<TN> wg;
+    dma_a<AC>(Ad0, rs, la, KB, wave);
+    a_step<T::BM>(la, p, S, it_end);
+    dma_a<AC>(Ad1, rs, la, KB, wave);
+    a_step<T::BM>(la, p, S, it_end);
+    dma_a<AC>(Ad2, rs, la, KB, wave);
+    a_step<T::BM>(la, p, S, it_end);
     load_w<TN, SA>(wg, rs, lw);
     w_step<T::BN>(lw, p, S, it_end, KB, lane, wn);
-#pragma unroll
-    for (int q = 0; q < DA; ++q) {
-        load_a(sa[q], rs, la);
-        a_step<T::BM>(la, p, S, it_end);
-    }
-
-    // Store the activations of a stage (at K step s) into LDS buffer `buf`,
-    // zeroing blocks past K.  Activation stage r % DA holds step r's
-    // activations; they are copied to LDS one step before their MFMAs.
-    auto store_a = [&](const AStage<AC> &sg, int s, int buf) {
-        const bool full = 2 * s + 2 <= KB;   // uniform: both blocks of the step inside K
-#pragma unroll
-        for (int c = 0; c < AC; ++c) {
-            const int idx = (int)threadIdx.x + 256 * c;
-            const int r = idx >> 3, ch = idx & 7;
-            const bool ok = full || 2 * s + (ch >> 2) < KB;
-            const uint4 v = ok ? sg.a[c] : make_uint4(0u, 0u, 0u, 0u);
-            *reinterpret_cast<uint4 *>(&As[buf][r][ch * 8]) = v;
-        }
-    };
 
     // The weight group in registers -> this wave's LDS buffer: instruction i
     // of row tile j holds row 8 i + l / 8, chunk l % 8, stored at chunk
@@ -426,8 +431,10 @@ __global__ __launch_bounds__(256, OCC) void prefill_kernel(PrefillParams p)
         auto read_a = [&](int kk, half8_t (&dst)[TM]) {
             const int col = kk * 16 + (lane >> 5) * 8;   // block kk / 2, k half kk % 2
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
-                dst[i] = *reinterpret_cast<const half8_t *>(&As[buf][wm * 32 * TM + 32 * i + (lane & 31)][col]);
+            for (int i = 0; i < TM; ++i) {
+                const int r = wm * 32 * TM + 32 * i + (lane & 31);
+                dst[i] = *reinterpret_cast<const half8_t *>(&abuf(buf)[r][(col >> 3) ^ (r & 7)]);
+            }
         };
         read_a(0, a[0]);
 #pragma unroll
@@ -473,35 +480,43 @@ __global__ __launch_bounds__(256, OCC) void prefill_kernel(PrefillParams p)
                 }
     };
 
-    // Step 0 of the range into LDS buffer 0 (its stage then reloads with
-    // step DB), the first group's codes into this wave's LDS buffer, the
+    // The first group's codes into this wave's LDS buffer (the wait for
+    // them also covers the three activation copies issued before them), the
     // next group's loads issued, step 0's B operands unpacked.
-    store_a(sa[0], first.s, 0);
-    load_a(sa[0], rs, la);
-    a_step<T::BM>(la, p, S, it_end);
+    constexpr int nW = TN * (4 + (SA ? 1 : 8));   // loads of one weight group
     store_w(wg);
     take_scales(wg, first);
     load_w<TN, SA>(wg, rs, lw);
     w_step<T::BN>(lw, p, S, it_end, KB, lane, wn);
     prep(0, first);
-    __syncthreads();
+    // a bare barrier (every wave's copies of steps 0-2 have landed): the
+    // fence of __syncthreads would also wait for the next group's loads
+    __builtin_amdgcn_s_barrier();
 
-    // Step it (q = it - it0 within the group) issues its MFMAs (B operands
-    // already unpacked, A operands from LDS buffer q & 1), then, while the
-    // matrix cores work, unpacks the next step's B operands (after the last
-    // step of a group: the next group's codes go to LDS first, and the loads
-    // of the group after it are issued), copies activation stage (q + 1) % DA
-    // (step it + 1) into the other LDS buffer and reloads it with step it + 1
-    // + DB.  A tile is written out after its last group, or after the
-    // workgroup's last group.
+    // Step s (q = s - it0 within the group) first issues the copy of step s
+    // + 3 into buffer (q + 3) % 4, which step s - 1 read, then its MFMAs (B
+    // operands already unpacked, A operands from buffer q); while the matrix
+    // cores work it unpacks the next step's B operands (after the last step
+    // of a group: the next group's codes go to LDS first and the loads of
+    // the group after it are issued).  Before the barrier that ends the
+    // step each wave waits for its part of step s + 1's copy: younger than
+    // it are the copies of steps s + 2 and s + 3 and the weight group of
+    // whichever of steps s - 2 .. s ended a group (none when q = 2), a lower
+    // bound of what is in flight, so the wait is never short.  The barrier is
+    // bare: the fence of __syncthreads would also wait for the younger loads,
+    // and nothing else needs one (the buffer a copy overwrites was last read
+    // a step before, by reads that fed MFMAs and so had returned; the
+    // weight codes in LDS are private to each wave).  A tile is written out
+    // after its last group, or after the workgroup's last group.
     Pos cur = first;
     int seg_s0 = first.s;   // first K step of the current tile segment
     for (int it0 = it_beg; it0 < it_end; it0 += DB) {
         const Pos group = cur;
 #pragma unroll
         for (int q = 0; q < DB; ++q) {
-            const int buf = q & 1;   // it0 - it_beg is a multiple of DB, which is even
-            mma(buf);
+            dma_a<AC>(abuf((q + 3) % DB), rs, la, KB, wave);
+            a_step<T::BM>(la, p, S, it_end);
+            mma(q);
             Pos nxt = cur;
             advance(nxt, p, S);
             if (q == DB - 1) {
@@ -512,11 +527,12 @@ __global__ __launch_bounds__(256, OCC) void prefill_kernel(PrefillParams p)
                 w_step<T::BN>(lw, p, S, it_end, KB, lane, wn);
             }
             prep((q + 1) % DB, nxt);
-            store_a(sa[(q + 1) % DA], nxt.s, buf ^ 1);
-            load_a(sa[(q + 1) % DA], rs, la);
-            a_step<T::BM>(la, p, S, it_end);
+            if (q == 2)
+                wait_vm<2 * AC>();
+            else
+                wait_vm<2 * AC + nW>();
             cur = nxt;
-            __syncthreads();
+            __builtin_amdgcn_s_barrier();
         }
         if (cur.s == 0 || it0 + DB == it_end) {
             flush(group, seg_s0 == 0 && cur.s == 0);
@@ -552,7 +568,7 @@ bool whole_tiles(int64_t chunks, int64_t per_tile, int64_t wgs)
     return true;
 }
 
-template <int WM, int TM, int TN, int OCC, int DA = kGroup>
+template <int WM, int TM, int TN, int OCC>
 hipError_t launch_prefill(PrefillParams p, int cus, hipStream_t stream)
 {
     using T = Tiling<WM, TM, TN>;
@@ -591,8 +607,8 @@ hipError_t launch_prefill(PrefillParams p, int cus, hipStream_t stream)
     }
     // a group's eight scales as one 16-byte load where no group crosses a row
     // (nor the end of the scale region)
-    const void *fn = KB % 8 == 0 ? reinterpret_cast<const void *>(&prefill_kernel<WM, TM, TN, OCC, DA, true>)
-                                 : reinterpret_cast<const void *>(&prefill_kernel<WM, TM, TN, OCC, DA, false>);
+    const void *fn = KB % 8 == 0 ? reinterpret_cast<const void *>(&prefill_kernel<WM, TM, TN, OCC, true>)
+                                 : reinterpret_cast<const void *>(&prefill_kernel<WM, TM, TN, OCC, false>);
     return launch_kernel(fn, dim3((unsigned)wgs), dim3(256), 0, stream, p);
 }
 
