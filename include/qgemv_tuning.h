@@ -59,7 +59,8 @@ void qg_set_gemv_shape(int J, int R, int ksplit, int teams_per_wg, int64_t teams
  * covers part of a tile adds it atomically into a zero-filled Y); `tile`
  * picks the tile configuration (tokens x rows): 64 (64 x 128, two
  * workgroups per CU), 66 (64 x 256, two per CU), 128 (128 x 256, one per CU),
- * 130 (128 x 128, two per CU), 257 (256 x 64, waves 2 x 2, one per CU), or
+ * 130 (128 x 128, two per CU), 136 (128 x 256 with eight waves, one per
+ * CU), 257 (256 x 64, waves 2 x 2, one per CU), or
  * 16: the kernel for up to 64 tokens (activations in registers, 16-row
  * weight tiles; `wgs` is then its number of workgroups along N, and more
  * than 64 tokens return QG_ERR_SHAPE).  0 keeps the built-in choice; an

@@ -31,7 +31,8 @@
 //     8) (conflict-free 16-byte reads without padding), and are read back as
 //     the A operands.
 //   * Each wave owns 32 TM tokens x 32 TN rows of the workgroup's tile (WM
-//     waves along M, 4 / WM along N); with WM = 1 no weight is unpacked twice.
+//     waves along M, NW / WM along N, NW = 4 or 8 waves); with WM = 1 no
+//     weight is unpacked twice.
 //
 // Work split (stream-K): the (tile, K step) iterations are numbered tile by
 // tile and cut into equal contiguous ranges of whole groups, one per
@@ -142,12 +143,12 @@ __device__ __forceinline__ void advance(Pos &q, const PrefillParams &p, int S)
     }
 }
 
-template <int WM, int TM, int TN>
+template <int WM, int TM, int TN, int NW>
 struct Tiling {
-    static constexpr int WN = 4 / WM;
+    static constexpr int WN = NW / WM;
     static constexpr int BM = 32 * TM * WM;   // tokens per tile
     static constexpr int BN = 32 * TN * WN;   // rows per tile
-    static constexpr int AC = BM / 32;        // 16-byte activation chunks per thread per step
+    static constexpr int AC = BM * 8 / (64 * NW);   // 16-byte activation chunks per thread per step
 };
 
 // Registers of one group's weights (per row tile: this lane's four 16-byte
@@ -188,12 +189,12 @@ struct WCursor {
     uint32_t soff[TN];      // scale byte offsets (row l % 32, block 0)
 };
 
-template <int BM, int AC>
+template <int BM, int AC, int NT>
 __device__ __forceinline__ void a_offsets(ACursor<AC> &c, const PrefillParams &p)
 {
 #pragma unroll
     for (int i = 0; i < AC; ++i) {
-        const int idx = (int)threadIdx.x + 256 * i;
+        const int idx = (int)threadIdx.x + NT * i;
         const int r = idx >> 3, ch = (idx & 7) ^ (r & 7);
         const int m = min(c.ps.tm * BM + r, p.M - 1);
         c.off[i] = (uint32_t)m * (uint32_t)p.K * 2u + (uint32_t)ch * 16u;
@@ -218,14 +219,14 @@ __device__ __forceinline__ void w_offsets(WCursor<TN> &c, const PrefillParams &p
 
 // Advance by one step (activations) or one group (weights), up to the
 // workgroup's last step (loads past its range repeat the last position).
-template <int BM, int AC>
+template <int BM, int AC, int NT>
 __device__ __forceinline__ void a_step(ACursor<AC> &c, const PrefillParams &p, int S, int it_end)
 {
     if (c.it + 1 < it_end) {
         ++c.it;
         advance(c.ps, p, S);
         if (c.ps.s == 0)
-            a_offsets<BM>(c, p);
+            a_offsets<BM, AC, NT>(c, p);
     }
 }
 
@@ -251,7 +252,7 @@ struct Rsrc {
 // eight 16-byte chunks): no registers and no copy instructions.  Chunks of
 // blocks past K get an offset beyond the buffer, whose range check returns
 // zeros.
-template <int AC>
+template <int AC, int NT>
 __device__ __forceinline__ void dma_a(uint4 (*buf)[8], const Rsrc &rs, const ACursor<AC> &c, int KB, int wave)
 {
     const int so = c.ps.s * 128;   // 64 fp16 per step
@@ -260,13 +261,13 @@ __device__ __forceinline__ void dma_a(uint4 (*buf)[8], const Rsrc &rs, const ACu
     for (int i = 0; i < AC; ++i) {
         uint32_t off = c.off[i];
         if (!full) {
-            const int idx = (int)threadIdx.x + 256 * i;
+            const int idx = (int)threadIdx.x + NT * i;
             const int r = idx >> 3, ch = (idx & 7) ^ (r & 7);
             if (2 * c.ps.s + (ch >> 2) >= KB)
                 off = 0x80000000u;
         }
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs.x, (__attribute__((address_space(3))) void *)&buf[8 * wave + 32 * i][0], 16, off, so, 0, 0);
+            rs.x, (__attribute__((address_space(3))) void *)&buf[8 * wave + NT / 8 * i][0], 16, off, so, 0, 0);
     }
 }
 
@@ -310,10 +311,11 @@ __device__ __forceinline__ void load_w(WGroup<TN> &st, const Rsrc &rs, const WCu
     }
 }
 
-template <int WM, int TM, int TN, int OCC, bool SA>
-__global__ __launch_bounds__(256, OCC) void prefill_kernel(PrefillParams p)
+template <int WM, int TM, int TN, int OCC, bool SA, int NW>
+__global__ __launch_bounds__(64 * NW, OCC) void prefill_kernel(PrefillParams p)
 {
-    using T = Tiling<WM, TM, TN>;
+    using T = Tiling<WM, TM, TN, NW>;
+    constexpr int NT = 64 * NW;   // threads
     constexpr int AC = T::AC;
     constexpr int DB = kGroup;   // steps per weight group
     // activations: one swizzled buffer per step of a group, each a variable
@@ -322,7 +324,7 @@ __global__ __launch_bounds__(256, OCC) void prefill_kernel(PrefillParams p)
     // it waits for every load in flight before each read)
     __shared__ uint4 Ad0[T::BM][8], Ad1[T::BM][8], Ad2[T::BM][8], Ad3[T::BM][8];
     auto abuf = [&](int q) -> uint4(*)[8] { return q == 0 ? Ad0 : q == 1 ? Ad1 : q == 2 ? Ad2 : Ad3; };
-    __shared__ uint4 Wl[4][TN][32][8];   // per wave: the current group's code bytes, chunks swizzled by row
+    __shared__ uint4 Wl[NW][TN][32][8];   // per wave: the current group's code bytes, chunks swizzled by row
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -358,18 +360,18 @@ __global__ __launch_bounds__(256, OCC) void prefill_kernel(PrefillParams p)
     ACursor<AC> la;
     la.ps = first;
     la.it = it_beg;
-    a_offsets<T::BM>(la, p);
+    a_offsets<T::BM, AC, NT>(la, p);
     WCursor<TN> lw;
     lw.ps = first;
     lw.it = it_beg;
     w_offsets<T::BN>(lw, p, KB, lane, wn);
     WGroup<TN> wg;
-    dma_a<AC>(Ad0, rs, la, KB, wave);
-    a_step<T::BM>(la, p, S, it_end);
-    dma_a<AC>(Ad1, rs, la, KB, wave);
-    a_step<T::BM>(la, p, S, it_end);
-    dma_a<AC>(Ad2, rs, la, KB, wave);
-    a_step<T::BM>(la, p, S, it_end);
+    dma_a<AC, NT>(Ad0, rs, la, KB, wave);
+    a_step<T::BM, AC, NT>(la, p, S, it_end);
+    dma_a<AC, NT>(Ad1, rs, la, KB, wave);
+    a_step<T::BM, AC, NT>(la, p, S, it_end);
+    dma_a<AC, NT>(Ad2, rs, la, KB, wave);
+    a_step<T::BM, AC, NT>(la, p, S, it_end);
     load_w<TN, SA>(wg, rs, lw);
     w_step<T::BN>(lw, p, S, it_end, KB, lane, wn);
 
@@ -514,8 +516,8 @@ __global__ __launch_bounds__(256, OCC) void prefill_kernel(PrefillParams p)
         const Pos group = cur;
 #pragma unroll
         for (int q = 0; q < DB; ++q) {
-            dma_a<AC>(abuf((q + 3) % DB), rs, la, KB, wave);
-            a_step<T::BM>(la, p, S, it_end);
+            dma_a<AC, NT>(abuf((q + 3) % DB), rs, la, KB, wave);
+            a_step<T::BM, AC, NT>(la, p, S, it_end);
             mma(q);
             Pos nxt = cur;
             advance(nxt, p, S);
@@ -568,10 +570,10 @@ bool whole_tiles(int64_t chunks, int64_t per_tile, int64_t wgs)
     return true;
 }
 
-template <int WM, int TM, int TN, int OCC>
+template <int WM, int TM, int TN, int OCC, int NW = 4>
 hipError_t launch_prefill(PrefillParams p, int cus, hipStream_t stream)
 {
-    using T = Tiling<WM, TM, TN>;
+    using T = Tiling<WM, TM, TN, NW>;
     const int64_t KB = p.K / 32;
     constexpr int DB = kGroup;
     const int64_t S = ((KB + 1) / 2 + DB - 1) / DB * DB;
@@ -607,9 +609,9 @@ hipError_t launch_prefill(PrefillParams p, int cus, hipStream_t stream)
     }
     // a group's eight scales as one 16-byte load where no group crosses a row
     // (nor the end of the scale region)
-    const void *fn = KB % 8 == 0 ? reinterpret_cast<const void *>(&prefill_kernel<WM, TM, TN, OCC, true>)
-                                 : reinterpret_cast<const void *>(&prefill_kernel<WM, TM, TN, OCC, false>);
-    return launch_kernel(fn, dim3((unsigned)wgs), dim3(256), 0, stream, p);
+    const void *fn = KB % 8 == 0 ? reinterpret_cast<const void *>(&prefill_kernel<WM, TM, TN, OCC, true, NW>)
+                                 : reinterpret_cast<const void *>(&prefill_kernel<WM, TM, TN, OCC, false, NW>);
+    return launch_kernel(fn, dim3((unsigned)wgs), dim3(64 * NW), 0, stream, p);
 }
 
 }  // namespace
@@ -657,11 +659,20 @@ extern "C" qg_status qgemm_q4_0_prefill(const void *Wp, const uint16_t *X, float
     // Up to 64 tokens the skinny kernel (qgemv_mfma.hip; MI355X, 64 tokens:
     // 12288 x 2560 18.1 against 21.8 us with 64 x 128 tiles, 6144 x 2048
     // 11.9 against 16.2, 2560 x 6144 13.2 against 17.8).  Beyond, the tile
-    // (sweeps on MI355X): 128 tokens x 128 rows where those tiles give every
-    // CU its two workgroups (12288 x 2560 at 512 tokens: 54.9 against 61.2
-    // us), else 64 x 128 (one wave along M: no weight unpacked twice).
+    // (sweeps on MI355X, graph-timed calls): 128 tokens x 256 rows, eight
+    // waves, where those tiles fill three quarters of the CUs (each
+    // activation copy then serves 256 rows; 512 tokens: 12288 x 2560 48.1
+    // against 51.9 us with 128 x 128 tiles, 14336 x 4096 75.2 against 81.6);
+    // else 128 x 128 where those tiles give every CU its two workgroups; else
+    // 64 x 128 (one wave along M: no weight unpacked twice; 6144 x 2048 at
+    // 512 tokens 26.4 against 35.8 with 128 x 128).
+    const int64_t t136 = (M + 127) / 128 * ((N + 255) / 256);
     const int64_t t130 = (M + 127) / 128 * ((N + 127) / 128);
-    const int tile = o_tile ? o_tile : (M <= 64 ? 16 : t130 * 2 >= 3LL * cus ? 130 : 64);
+    const int tile = o_tile ? o_tile
+                            : (M <= 64                   ? 16
+                               : t136 * 4 >= 3LL * cus   ? 136
+                               : t130 * 2 >= 3LL * cus   ? 130
+                                                         : 64);
     hipError_t e;
     switch (tile) {
     case 16:
@@ -672,6 +683,7 @@ extern "C" qg_status qgemm_q4_0_prefill(const void *Wp, const uint16_t *X, float
     case 128: e = launch_prefill<1, 4, 2, 1>(p, cus, s); break;
     case 130: e = launch_prefill<1, 4, 1, 2>(p, cus, s); break;
     case 257: e = launch_prefill<2, 4, 1, 1>(p, cus, s); break;
+    case 136: e = launch_prefill<1, 4, 1, 1, 8>(p, cus, s); break;
     default: return QG_ERR_SHAPE;
     }
     if (e == hipErrorInvalidValue)

@@ -23,7 +23,8 @@ def _prefill(Wd, X, N, K):
 # configuration; the skinny kernel (tile 16, up to 64 tokens) with its
 # built-in grid, one workgroup, three, and more workgroups than tiles.
 PREFILL_SETTINGS = [(0, 0), (1, 64), (3, 64), (700, 66), (0, 128), (5, 128),
-                    (0, 130), (700, 130), (0, 257), (3, 257), (0, 16), (1, 16), (3, 16), (700, 16)]
+                    (0, 130), (700, 130), (0, 136), (3, 136), (0, 257), (3, 257),
+                    (0, 16), (1, 16), (3, 16), (700, 16)]
 
 
 def _prefill_each_setting(Wd, X, N, K, Y_ref, S, what):
