@@ -352,11 +352,13 @@ def _time_calls(qg, torch, calls, reps: int, warm: int = 5):
     return float(np.median(ms) * 1e3), float(ms.mean() * 1e3)
 
 
-def _time_graph(torch, fns, reps: int, warm: int = 5, calls: int = 20, rounds: int = 7):
+def _time_graph(torch, fns, reps: int, warm: int = 5, calls: int = 20, rounds: int = 7, warm_replays: int = 3):
     """Per-call time (us) of `calls` calls captured back to back in one HIP
-    graph, the median of `rounds` replays timed by stream events: every kernel
-    a call launches and the gaps between them, without the host launch path
-    (`reps` and `warm` are the warm-up calls before capture).  `fns` is a
+    graph, the median of `rounds` replays timed by stream events after
+    `warm_replays` untimed ones: every kernel a call launches and the gaps
+    between them, without the host launch path (`reps` and `warm` are the
+    warm-up calls before capture; the first replays of a fresh graph run up
+    to ~15% slower than the later ones on the large prefills).  `fns` is a
     list of calls that launch on the current stream, or a function returning
     one, called on the capturing stream (for calls bound to the stream that
     was current when they were made, such as PreparedGemv)."""
@@ -373,7 +375,8 @@ def _time_graph(torch, fns, reps: int, warm: int = 5, calls: int = 20, rounds: i
             for i in range(calls):
                 fns[(i + warm) % len(fns)]()
     torch.cuda.synchronize()
-    g.replay()
+    for _ in range(warm_replays):
+        g.replay()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(rounds + 1)]
     torch.cuda.synchronize()
     ev[0].record()

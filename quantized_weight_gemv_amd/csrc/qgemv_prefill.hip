@@ -27,9 +27,9 @@
 //     bytes, then bounds the kernel.
 //   * Activations: each step's X rows go straight from memory into LDS
 //     (buffer loads that write LDS: no registers, no copy instructions), in
-//     natural k order with the 16-byte chunks of row r at position c ^ (r %
-//     8) (conflict-free 16-byte reads without padding), and are read back as
-//     the A operands.
+//     natural k order with the 16-byte chunks of row r at position c ^ ((r /
+//     2) % 8) (conflict-free 16-byte reads without padding), and are read
+//     back as the A operands.
 //   * Each wave owns 32 TM tokens x 32 TN rows of the workgroup's tile (WM
 //     waves along M, NW / WM along N, NW = 4 or 8 waves); with WM = 1 no
 //     weight is unpacked twice.
@@ -164,9 +164,9 @@ struct WGroup {
 // offset of the buffer loads, so a step spends no vector instruction on
 // addresses.
 //   Activations: lane l of instruction i of wave w writes the i-th kilobyte
-//   of the wave's share of the step, i.e. row 8 w + 32 i + l / 8 of the tile
+//   of the wave's share of the step, i.e. row 8 w + 8 NW i + l / 8 of the tile
 //   (clamped to M - 1: rows past M are never stored) at position l % 8, and
-//   reads the 16-byte chunk (l % 8) ^ (row % 8) of that row at the step.
+//   reads the chunk stored there (`a_swz`) of that row at the step.
 //   Weights: instruction i of row tile j (32 rows from row n0 + 32 (wn TN +
 //   j)) has lane l read the 16 bytes of row 8 i + l / 8 at block 8 g + l % 8
 //   of group g; the scales: lane l reads the eight of row l % 32.  Rows are
@@ -174,6 +174,13 @@ struct WGroup {
 // Blocks past K (padding steps, or the tail of the last group) read the next
 // row's bytes or, past the end, zeros; their activations and scales are
 // zeroed.
+// Position of 16-byte chunk c of activation row r in its LDS row (128
+// bytes, 8 chunks): c ^ ((r / 2) % 8).  Rows are 32 banks apart, so rows r
+// and r + 2 share banks; the XOR gives each of 16 consecutive rows its own
+// four banks, and a 16-lane quarter of an A-operand read (16 rows, one
+// chunk each) touches all 64 banks once.
+__device__ __forceinline__ int a_swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+
 template <int AC>
 struct ACursor {
     Pos ps;
@@ -195,7 +202,7 @@ __device__ __forceinline__ void a_offsets(ACursor<AC> &c, const PrefillParams &p
 #pragma unroll
     for (int i = 0; i < AC; ++i) {
         const int idx = (int)threadIdx.x + NT * i;
-        const int r = idx >> 3, ch = (idx & 7) ^ (r & 7);
+        const int r = idx >> 3, ch = a_swz(r, idx & 7);
         const int m = min(c.ps.tm * BM + r, p.M - 1);
         c.off[i] = (uint32_t)m * (uint32_t)p.K * 2u + (uint32_t)ch * 16u;
     }
@@ -248,6 +255,7 @@ struct Rsrc {
     __amdgpu_buffer_rsrc_t x, w, s;
 };
 
+
 // One step's activations straight into the LDS buffer `buf` (BM rows of
 // eight 16-byte chunks): no registers and no copy instructions.  Chunks of
 // blocks past K get an offset beyond the buffer, whose range check returns
@@ -262,7 +270,7 @@ __device__ __forceinline__ void dma_a(uint4 (*buf)[8], const Rsrc &rs, const ACu
         uint32_t off = c.off[i];
         if (!full) {
             const int idx = (int)threadIdx.x + NT * i;
-            const int r = idx >> 3, ch = (idx & 7) ^ (r & 7);
+            const int r = idx >> 3, ch = a_swz(r, idx & 7);
             if (2 * c.ps.s + (ch >> 2) >= KB)
                 off = 0x80000000u;
         }
@@ -435,7 +443,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_kernel(PrefillParams p)
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
                 const int r = wm * 32 * TM + 32 * i + (lane & 31);
-                dst[i] = *reinterpret_cast<const half8_t *>(&abuf(buf)[r][(col >> 3) ^ (r & 7)]);
+                dst[i] = *reinterpret_cast<const half8_t *>(&abuf(buf)[r][a_swz(r, col >> 3)]);
             }
         };
         read_a(0, a[0]);
