@@ -132,7 +132,8 @@ def suite(stats_csv, suite_jsonl, out_md, cmd, plain_cmd=""):
              "GEMV Q4_0 2048x2048; small-batch GEMV Q4_0/Q8_0 at 1, 2, 4, 8 tokens on 6144x2048, 2048x6144, "
              "8192x2048;", "one-launch MoE (10 of 128 experts 640x2560, 8 of 256 experts 512x2048); Q4_0 prefill "
              "at 64 and 512 tokens", "on 12288x2560, 2560x6144, 6144x2048 with the dense fp16 GEMM on "
-             "pre-dequantized weights beside it; fp32-activation GEMV and stacked gate+up+SwiGLU with",
+             "pre-dequantized weights beside it (the faster of the weight layouts [N][K] and [K][N]); "
+             "fp32-activation GEMV and stacked gate+up+SwiGLU with",
              "their unfused steps beside them; the GEMV on 8-bit activations beside the fp16-activation one;",
              "plain 2-bit weights (q2w) beside Q4_0, with 8-bit activations and through lookup tables.", "", "Command:", "", "```", cmd, "```", "",
              "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
@@ -170,8 +171,10 @@ def suite(stats_csv, suite_jsonl, out_md, cmd, plain_cmd=""):
             lines.append(f"| MoE {r['fmt']} {r['E']} of {r['P']} x {r['N']}x{r['K']} | {r['us_median']} | "
                          f"{r['GBps']} GB/s |")
         else:
+            lay = (f": [N][K] {r['dense_nk_us_median']}, [K][N] {r['dense_kn_us_median']}"
+                   if "dense_nk_us_median" in r else "")
             lines.append(f"| prefill {r['fmt']} {r['N']}x{r['K']} M={r['M']} | {r['us_median']} (dense fp16 "
-                         f"{r['dense_fp16_us_median']}) | {r['TFLOPs']} TFLOP/s |")
+                         f"{r['dense_fp16_us_median']}{lay}) | {r['TFLOPs']} TFLOP/s |")
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
