@@ -67,6 +67,15 @@ typedef float f16x_t __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ h2_t as_h2(uint32_t u) { return __builtin_bit_cast(h2_t, u); }
 __device__ __forceinline__ uint32_t as_u32(h2_t h) { return __builtin_bit_cast(uint32_t, h); }
 
+// An empty asm statement that claims to modify v: the computation of v stays
+// before this point (the compiler cannot sink it past a statement with side
+// effects).
+template <typename V>
+__device__ __forceinline__ void pin(V &v)
+{
+    asm volatile("" : "+v"(v));
+}
+
 __device__ __forceinline__ uint32_t magic_reg()
 {
     uint32_t m;
@@ -77,33 +86,24 @@ __device__ __forceinline__ uint32_t magic_reg()
 // 8 code bytes of one block (p0 = bytes 0-3, p1 = bytes 4-7 of the lane's
 // half) -> two B operands in natural k order: lo = the 8 low nibbles (the
 // block's first 16 k for this lane's half), hi = the 8 high nibbles, each
-// weight (q - 8) * d rounded once to fp16.
-__device__ __forceinline__ void unpack8(uint32_t p0, uint32_t p1, h2_t d2, uint32_t magic, half8_t &lo, half8_t &hi)
+// weight (q - 8) * d rounded once to fp16.  One call makes element pair e
+// (0..3) of both: the nibbles of bytes 2 e and 2 e + 1.
+__device__ __forceinline__ void unpack_pair(uint32_t p0, uint32_t p1, h2_t d2, uint32_t magic, int e, uint32_t &lo,
+                                            uint32_t &hi)
 {
     const h2_t kOffLo = {(_Float16)-1032.0f, (_Float16)-1032.0f};
     const h2_t kScaleHi = {(_Float16)0.0625f, (_Float16)0.0625f};
     const h2_t kOffHi = {(_Float16)-72.0f, (_Float16)-72.0f};
-    const uint32_t w[2] = {p0, p1};
-    uint32_t l[4], h[4];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const uint32_t nl = w[t] & 0x0F0F0F0Fu;   // low nibbles, one per byte
-        const uint32_t nh = w[t] & 0xF0F0F0F0u;   // high nibbles, times 16
-        // bytes (n0, 0x64, n1, 0x64) and (n2, 0x64, n3, 0x64): the halves
-        // 1024 + n of consecutive elements
-        l[2 * t + 0] = __builtin_amdgcn_perm(magic, nl, 0x07010500u);
-        l[2 * t + 1] = __builtin_amdgcn_perm(magic, nl, 0x07030502u);
-        h[2 * t + 0] = __builtin_amdgcn_perm(magic, nh, 0x07010500u);
-        h[2 * t + 1] = __builtin_amdgcn_perm(magic, nh, 0x07030502u);
-    }
-    uint32_t ol[4], oh[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        ol[t] = as_u32((as_h2(l[t]) + kOffLo) * d2);                // (q - 8) * d
-        oh[t] = as_u32((as_h2(h[t]) * kScaleHi + kOffHi) * d2);     // (1024 + 16 q) / 16 - 72 = q - 8
-    }
-    lo = __builtin_bit_cast(half8_t, make_uint4(ol[0], ol[1], ol[2], ol[3]));
-    hi = __builtin_bit_cast(half8_t, make_uint4(oh[0], oh[1], oh[2], oh[3]));
+    const uint32_t w = (e >> 1) ? p1 : p0;
+    const uint32_t nl = w & 0x0F0F0F0Fu;   // low nibbles, one per byte
+    const uint32_t nh = w & 0xF0F0F0F0u;   // high nibbles, times 16
+    // bytes (n0, 0x64, n1, 0x64) or (n2, 0x64, n3, 0x64) of the word: the
+    // halves 1024 + n of two consecutive elements
+    const uint32_t sel = (e & 1) ? 0x07030502u : 0x07010500u;
+    const uint32_t l = __builtin_amdgcn_perm(magic, nl, sel);
+    const uint32_t h = __builtin_amdgcn_perm(magic, nh, sel);
+    lo = as_u32((as_h2(l) + kOffLo) * d2);                // (q - 8) * d
+    hi = as_u32((as_h2(h) * kScaleHi + kOffHi) * d2);     // (1024 + 16 q) / 16 - 72 = q - 8
 }
 
 struct PrefillParams {
@@ -261,22 +261,28 @@ struct Rsrc {
 // blocks past K get an offset beyond the buffer, whose range check returns
 // zeros.
 template <int AC, int NT>
-__device__ __forceinline__ void dma_a(uint4 (*buf)[8], const Rsrc &rs, const ACursor<AC> &c, int KB, int wave)
+__device__ __forceinline__ void dma_a_one(uint4 (*buf)[8], const Rsrc &rs, const ACursor<AC> &c, int KB, int wave,
+                                          int i)
 {
     const int so = c.ps.s * 128;   // 64 fp16 per step
     const bool full = 2 * c.ps.s + 2 <= KB;   // uniform: both blocks of the step inside K
-#pragma unroll
-    for (int i = 0; i < AC; ++i) {
-        uint32_t off = c.off[i];
-        if (!full) {
-            const int idx = (int)threadIdx.x + NT * i;
-            const int r = idx >> 3, ch = a_swz(r, idx & 7);
-            if (2 * c.ps.s + (ch >> 2) >= KB)
-                off = 0x80000000u;
-        }
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs.x, (__attribute__((address_space(3))) void *)&buf[8 * wave + NT / 8 * i][0], 16, off, so, 0, 0);
+    uint32_t off = c.off[i];
+    if (!full) {
+        const int idx = (int)threadIdx.x + NT * i;
+        const int r = idx >> 3, ch = a_swz(r, idx & 7);
+        if (2 * c.ps.s + (ch >> 2) >= KB)
+            off = 0x80000000u;
     }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs.x, (__attribute__((address_space(3))) void *)&buf[8 * wave + NT / 8 * i][0], 16, off, so, 0, 0);
+}
+
+template <int AC, int NT>
+__device__ __forceinline__ void dma_a(uint4 (*buf)[8], const Rsrc &rs, const ACursor<AC> &c, int KB, int wave)
+{
+#pragma unroll
+    for (int i = 0; i < AC; ++i)
+        dma_a_one<AC, NT>(buf, rs, c, KB, wave, i);
 }
 
 // Wait until at most n vector memory operations of this wave are in flight
@@ -409,56 +415,119 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_kernel(PrefillParams p)
     };
 
     // The B operands of one step (this wave's row tiles, both blocks, both k
-    // halves), unpacked from the group's codes in LDS: lane l takes row
-    // l % 32, block 2 q + l / 32 of the group.
-    half8_t bop[TN][2][2];
-    auto prep = [&](int q, const Pos &ps) {
-        const int b0 = 2 * ps.s;   // first block of the step (2 q of the group)
+    // halves) in two sets, as words (bw[o][j][b][h][e]: element pair e of
+    // row tile j, block b, k half h): the MFMAs of a step read one set while
+    // the next step's operands are unpacked into the other.  Lane l takes
+    // row l % 32, block 2 q + l / 32 of the group: its 16 code bytes are read
+    // from LDS first (wc); the unpacking then rides between the current
+    // step's MFMAs: after the first MFMA the lane-half swaps and the scales,
+    // then one element pair of each block per MFMA (per two with TM = 2).
+    uint32_t bw[2][TN][2][2][4];
+    uint4 wc[TN];
+    uint32_t wt[TN][2], wu[TN][2];
+    h2_t wd[TN][2];
+    auto bop = [&](int o, int j, int b, int h) {
+        return __builtin_bit_cast(half8_t, make_uint4(bw[o][j][b][h][0], bw[o][j][b][h][1], bw[o][j][b][h][2],
+                                                      bw[o][j][b][h][3]));
+    };
+    auto read_w = [&](int q) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const int row = lane & 31;
-            const uint4 c = Wl[wave][j][row][(2 * q + (lane >> 5)) ^ (row & 7)];
-            const auto t = __builtin_amdgcn_permlane32_swap(c.x, c.z, false, false);
-            const auto u = __builtin_amdgcn_permlane32_swap(c.y, c.w, false, false);
+            wc[j] = Wl[wave][j][row][(2 * q + (lane >> 5)) ^ (row & 7)];
+        }
+    };
+    auto swap_scales = [&](int q, const Pos &ps) {
+        const int b0 = 2 * ps.s;   // first block of the step (2 q of the group)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const auto t = __builtin_amdgcn_permlane32_swap(wc[j].x, wc[j].z, false, false);
+            const auto u = __builtin_amdgcn_permlane32_swap(wc[j].y, wc[j].w, false, false);
+            wt[j][0] = (uint32_t)t[0];
+            wt[j][1] = (uint32_t)t[1];
+            wu[j][0] = (uint32_t)u[0];
+            wu[j][1] = (uint32_t)u[1];
             const uint32_t sw = q == 0 ? scl[j].x : q == 1 ? scl[j].y : q == 2 ? scl[j].z : scl[j].w;
             const uint32_t s0 = b0 < KB ? (sw & 0xFFFFu) : 0u;
             const uint32_t s1 = b0 + 1 < KB ? (sw >> 16) : 0u;
             const _Float16 d0 = __builtin_bit_cast(_Float16, (uint16_t)s0);
             const _Float16 d1 = __builtin_bit_cast(_Float16, (uint16_t)s1);
-            unpack8((uint32_t)t[0], (uint32_t)u[0], h2_t{d0, d0}, magic, bop[j][0][0], bop[j][0][1]);
-            unpack8((uint32_t)t[1], (uint32_t)u[1], h2_t{d1, d1}, magic, bop[j][1][0], bop[j][1][1]);
+            wd[j][0] = h2_t{d0, d0};
+            wd[j][1] = h2_t{d1, d1};
+        }
+    };
+    // pair c of block b (row tile c / 4, element pair c % 4) into set o;
+    // the empty asm keeps it here: left free, the compiler sinks the
+    // unpacking to just before the next step's MFMAs, which would then wait
+    auto unpack_chunk = [&](int b, int c, int o) {
+        const int j = c >> 2, e = c & 3;
+        unpack_pair(wt[j][b], wu[j][b], wd[j][b], magic, e, bw[o][j][b][0][e], bw[o][j][b][1][e]);
+        pin(bw[o][j][b][0][e]);
+        pin(bw[o][j][b][1][e]);
+    };
+    auto prep = [&](int q, const Pos &ps, int o) {
+        read_w(q);
+        swap_scales(q, ps);
+#pragma unroll
+        for (int c = 0; c < 4 * TN; ++c) {
+            unpack_chunk(0, c, o);
+            unpack_chunk(1, c, o);
         }
     };
 
-    // The step's MFMAs: A operands from LDS buffer `buf`, B operands from
-    // registers.
-    // The A fragments of the next 16-wide k slice are read while the current
-    // slice's MFMAs issue (two register sets; the scheduling barriers keep
-    // the compiler from sinking each read to just before its MFMA, which
-    // exposed an LDS round trip per MFMA).
-    auto mma = [&](int buf) {
-        half8_t a[2][TM];
-        auto read_a = [&](int kk, half8_t (&dst)[TM]) {
-            const int col = kk * 16 + (lane >> 5) * 8;   // block kk / 2, k half kk % 2
+    // A operands, k slices 0 and 1 of a step: read in the step before it
+    // (its buffer is complete a step early), so each step starts its MFMAs
+    // at once and the LDS keeps streaming across the barrier.
+    half8_t apre[2][TM];
+    auto read_a = [&](int buf, int kk, half8_t (&dst)[TM]) {
+        const int col = kk * 16 + (lane >> 5) * 8;   // block kk / 2, k half kk % 2
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const int r = wm * 32 * TM + 32 * i + (lane & 31);
-                dst[i] = *reinterpret_cast<const half8_t *>(&abuf(buf)[r][a_swz(r, col >> 3)]);
-            }
-        };
-        read_a(0, a[0]);
+        for (int i = 0; i < TM; ++i) {
+            const int r = wm * 32 * TM + 32 * i + (lane & 31);
+            dst[i] = *reinterpret_cast<const half8_t *>(&abuf(buf)[r][a_swz(r, col >> 3)]);
+        }
+    };
+
+    // The step's MFMAs: A operands of slices 0-1 from apre, of slices 2-3
+    // read from LDS buffer `buf` while slices 0-1 multiply; during slices
+    // 2-3 the next step's slices 0-1 are read from buffer `nbuf`.  B operands
+    // from set o, with part (kk, m) of the next step's unpacking after MFMA m
+    // of slice kk (a scheduling barrier after each pair keeps the vector-ALU
+    // work where it overlaps the matrix cores, and each read a slice ahead of
+    // its MFMAs: left free, the compiler sinks a read to just before its
+    // MFMA, which exposes an LDS round trip per MFMA).
+    auto mma = [&](int buf, int nbuf, int o, auto &&part) {
+        half8_t acur[2][TM];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            if (kk < 3)
-                read_a(kk + 1, a[(kk + 1) & 1]);
+            if (kk < 2)
+                read_a(buf, kk + 2, acur[kk]);
+            else
+                read_a(nbuf, kk - 2, apre[kk - 2]);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[kk & 1][i], bop[j][kk >> 1][kk & 1],
-                                                                       acc[i][j], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
+                for (int j = 0; j < TN; ++j) {
+                    const half8_t av = kk < 2 ? apre[kk][i] : acur[kk - 2][i];
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bop(o, j, kk >> 1, kk & 1), acc[i][j], 0,
+                                                                       0, 0);
+                    part(kk, i * TN + j);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+        }
+    };
+    // the next step's unpacking spread over a step's MFMAs: swaps and scales
+    // after the first, block 0 over slice 1, block 1 over slice 2
+    constexpr int kPer = 4 / TM;   // element-pair chunks per MFMA
+    static_assert(TM * kPer == 4, "TM must be 1, 2 or 4");
+    auto next_part = [&](int q, const Pos &ps, int o, int kk, int m) {
+        if (kk == 0 && m == 0) {
+            swap_scales(q, ps);
+        } else if (kk == 1 || kk == 2) {
+#pragma unroll
+            for (int c = kPer * m; c < kPer * (m + 1); ++c)
+                unpack_chunk(kk - 1, c, o);
         }
     };
 
@@ -494,53 +563,74 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_kernel(PrefillParams p)
     // them also covers the three activation copies issued before them), the
     // next group's loads issued, step 0's B operands unpacked.
     constexpr int nW = TN * (4 + (SA ? 1 : 8));   // loads of one weight group
+    constexpr int kDmaGap = 4 * TM * TN / AC;      // MFMAs of a step per copy instruction
+    static_assert(kDmaGap >= 2, "every copy instruction needs its own MFMA slot");
     store_w(wg);
     take_scales(wg, first);
     load_w<TN, SA>(wg, rs, lw);
     w_step<T::BN>(lw, p, S, it_end, KB, lane, wn);
-    prep(0, first);
-    // a bare barrier (every wave's copies of steps 0-2 have landed): the
-    // fence of __syncthreads would also wait for the next group's loads
+    prep(0, first, 0);
+    // every wave's copies of steps 0-2 have landed (only the next group's
+    // loads may still be in flight), then a bare barrier: the fence of
+    // __syncthreads would also wait for those loads; step 0's first two
+    // k slices are read after it
+    wait_vm<nW>();
     __builtin_amdgcn_s_barrier();
+    read_a(0, 0, apre[0]);
+    read_a(0, 1, apre[1]);
 
-    // Step s (q = s - it0 within the group) first issues the copy of step s
-    // + 3 into buffer (q + 3) % 4, which step s - 1 read, then its MFMAs (B
-    // operands already unpacked, A operands from buffer q); while the matrix
-    // cores work it unpacks the next step's B operands (after the last step
-    // of a group: the next group's codes go to LDS first and the loads of
-    // the group after it are issued).  Before the barrier that ends the
-    // step each wave waits for its part of step s + 1's copy: younger than
-    // it are the copies of steps s + 2 and s + 3 and the weight group of
-    // whichever of steps s - 2 .. s ended a group (none when q = 2), a lower
-    // bound of what is in flight, so the wait is never short.  The barrier is
-    // bare: the fence of __syncthreads would also wait for the younger loads,
-    // and nothing else needs one (the buffer a copy overwrites was last read
-    // a step before, by reads that fed MFMAs and so had returned; the
-    // weight codes in LDS are private to each wave).  A tile is written out
-    // after its last group, or after the workgroup's last group.
+    // Step s (q = s - it0 within the group) multiplies the A operands of
+    // buffer q (slices 0-1 already in registers) with B operands unpacked
+    // during step s - 1; between its MFMAs it reads the next step's slices
+    // 0-1, unpacks the next step's B operands and issues the copy of step s +
+    // 3 into buffer (q + 3) % 4, which steps s - 2 (early reads) and s - 1
+    // read.  After the last step of a group the next group's codes go to LDS
+    // before the next step's codes are read, and the loads of the group after
+    // it are issued after the MFMAs.  Before the barrier that ends the step
+    // each wave waits for its part of step s + 2's copy (step s + 1 reads
+    // that buffer early): younger than it are the copy of step s + 3 and the
+    // weight group of whichever of steps s - 1 and s ended a group (none when
+    // q = 1 or 2), a lower bound of what is in flight, so the wait is never
+    // short.  The barrier is bare: the fence of __syncthreads would also wait
+    // for the younger loads, and nothing else needs one (the buffer a copy
+    // overwrites was last read by reads that fed MFMAs before the previous
+    // barrier and so had returned; the weight codes in LDS are private to
+    // each wave).  A tile is written out after its last group, or after the
+    // workgroup's last group.
     Pos cur = first;
     int seg_s0 = first.s;   // first K step of the current tile segment
     for (int it0 = it_beg; it0 < it_end; it0 += DB) {
         const Pos group = cur;
 #pragma unroll
         for (int q = 0; q < DB; ++q) {
-            dma_a<AC, NT>(abuf((q + 3) % DB), rs, la, KB, wave);
-            a_step<T::BM, AC, NT>(la, p, S, it_end);
-            mma(q);
             Pos nxt = cur;
             advance(nxt, p, S);
             if (q == DB - 1) {
-                // the next group's weights (clamped past the range: never used)
+                // the next group's codes to LDS and its scales, before the
+                // next step's codes are read
                 store_w(wg);
                 take_scales(wg, nxt);
+            }
+            read_w((q + 1) % DB);
+            mma(q, (q + 1) % DB, q & 1, [&](int kk, int m) {
+                next_part((q + 1) % DB, nxt, (q + 1) & 1, kk, m);
+                // the copy of step s + 3, one instruction every kDmaGap MFMAs
+                const int g = kk * TM * TN + m;
+#pragma unroll
+                for (int i = 0; i < AC; ++i)
+                    if (g == kDmaGap * i + 1)
+                        dma_a_one<AC, NT>(abuf((q + 3) % DB), rs, la, KB, wave, i);
+            });
+            a_step<T::BM, AC, NT>(la, p, S, it_end);
+            if (q == DB - 1) {
+                // the loads of the group after it (clamped past the range: never used)
                 load_w<TN, SA>(wg, rs, lw);
                 w_step<T::BN>(lw, p, S, it_end, KB, lane, wn);
             }
-            prep((q + 1) % DB, nxt);
-            if (q == 2)
-                wait_vm<2 * AC>();
+            if (q == 1 || q == 2)
+                wait_vm<AC>();
             else
-                wait_vm<2 * AC + nW>();
+                wait_vm<AC + nW>();
             cur = nxt;
             __builtin_amdgcn_s_barrier();
         }
@@ -593,16 +683,18 @@ hipError_t launch_prefill(PrefillParams p, int cus, hipStream_t stream)
     p.steps = (int)S;
     p.chunks = (int)(tiles * S / DB);
     // Workgroups (sweeps on MI355X, graph-timed calls on cycled copies): one
-    // per tile when the tiles fill at least three quarters of the OCC slots
-    // per CU (12288 x 2560 at 512 tokens, 128 x 128 tiles: 384 workgroups
-    // 54.9 us against 68.1 with 512); with fewer tiles the iterations are
-    // split over every slot when each gets at least four groups (2560 x 6144
-    // at 512 tokens: 38.3 us against 44.9 with one per CU), else over one
-    // workgroup per CU (12288 x 2560 at 64 tokens: 21.3 us against 27.3
-    // with two per CU).
+    // per tile, up to the OCC slots per CU, when the tiles fill at least
+    // three quarters of the CUs: whole tiles need no zero-fill and no atomics
+    // (64 x 128 tiles, 4096 x 4096 at 512 tokens: 256 workgroups 34.3 us
+    // against 38.3 with the tiles split over 512; 128 x 128 tiles, 14336 x
+    // 4096 at 256 tokens: 224 workgroups 45.8 against 60.0); with fewer
+    // tiles the iterations are split over every slot when each gets at least
+    // four groups (2560 x 6144 at 512 tokens, 64 x 128 tiles: 37.9 us
+    // against 47.6 with one workgroup per tile), else over one workgroup per
+    // CU (12288 x 2560 at 64 tokens: 21.3 us against 27.3 with two per CU).
     const int64_t slots = (int64_t)cus * OCC;
     int64_t wgs;
-    if (tiles >= slots * 3 / 4)
+    if (tiles * 4 >= (int64_t)cus * 3)
         wgs = std::min(tiles, slots);
     else
         wgs = p.chunks >= 4 * slots ? slots : std::min<int64_t>(cus, p.chunks);
@@ -667,17 +759,24 @@ extern "C" qg_status qgemm_q4_0_prefill(const void *Wp, const uint16_t *X, float
     // Up to 64 tokens the skinny kernel (qgemv_mfma.hip; MI355X, 64 tokens:
     // 12288 x 2560 18.1 against 21.8 us with 64 x 128 tiles, 6144 x 2048
     // 11.9 against 16.2, 2560 x 6144 13.2 against 17.8).  Beyond, the tile
-    // (sweeps on MI355X, graph-timed calls): 128 tokens x 256 rows, eight
-    // waves, where those tiles fill three quarters of the CUs (each
-    // activation copy then serves 256 rows; 512 tokens: 12288 x 2560 48.1
-    // against 51.9 us with 128 x 128 tiles, 14336 x 4096 75.2 against 81.6);
-    // else 128 x 128 where those tiles give every CU its two workgroups; else
-    // 64 x 128 (one wave along M: no weight unpacked twice; 6144 x 2048 at
-    // 512 tokens 26.4 against 35.8 with 128 x 128).
+    // (sweeps on MI355X, graph-timed calls): the largest of 128 tokens x 256
+    // rows (eight waves; each activation copy serves 256 rows), 128 x 128
+    // and 64 x 128 whose count fills three quarters to all of the CUs, each
+    // tile then a workgroup of its own on a CU of its own (14336 x 4096 at
+    // 256 tokens: 128 x 128 tiles 45.8 us against 51.9 with 448 of 64 x 128;
+    // 12288 x 2560 at 128 tokens: 64 x 128 tiles 24.6 against 28.0 split over
+    // 256 workgroups); else 128 x 256 where those tiles fill three quarters
+    // of the CUs, 128 x 128 where they give every CU its two workgroups, and
+    // 64 x 128 otherwise (one wave along M: no weight unpacked twice).
     const int64_t t136 = (M + 127) / 128 * ((N + 255) / 256);
     const int64_t t130 = (M + 127) / 128 * ((N + 127) / 128);
+    const int64_t t64 = (M + 63) / 64 * ((N + 127) / 128);
+    auto one_each = [&](int64_t t) { return 4 * t >= 3LL * cus && t <= cus; };
     const int tile = o_tile ? o_tile
                             : (M <= 64                   ? 16
+                               : one_each(t136)          ? 136
+                               : one_each(t130)          ? 130
+                               : one_each(t64)           ? 64
                                : t136 * 4 >= 3LL * cus   ? 136
                                : t130 * 2 >= 3LL * cus   ? 130
                                                          : 64);
