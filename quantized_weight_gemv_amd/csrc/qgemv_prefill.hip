@@ -41,13 +41,15 @@
 // tiles are added with fp32 atomics into Y, which a small fill kernel zeroes
 // first (last-bit differences between runs, within the accuracy bound).
 //
-// Pipelining: four LDS activation buffers, one per step of a group; the
-// copy of step s + 3 is issued at the start of step s (into the buffer step
-// s - 1 read) and the weight loads of the next group are in flight in
-// registers while the current group is multiplied; one barrier per step.
-// Every load is issued unconditionally (positions past a workgroup's range
-// repeat its last one and are never used), so the load counter, which
-// counts them in issue order, tells exactly when a step's copy has landed.
+// Pipelining: four LDS activation buffers, one per step of a group.  Between
+// the MFMAs of step s go the copy of step s + 3 (into the buffer steps s - 2
+// and s - 1 read), the unpacking of step s + 1's B operands and the reads of
+// step s + 1's first two k slices (its buffer is complete a step early); the
+// weight loads of the next group are in flight in registers while the
+// current group is multiplied; one barrier per step.  Every load is
+// issued unconditionally (positions past a workgroup's range repeat its last
+// one and are never used), so the load counter, which counts them in issue
+// order, tells exactly when a step's copy has landed.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
