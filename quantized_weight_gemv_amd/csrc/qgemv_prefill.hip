@@ -423,7 +423,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_kernel(PrefillParams p)
     // row l % 32, block 2 q + l / 32 of the group: its 16 code bytes are read
     // from LDS first (wc); the unpacking then rides between the current
     // step's MFMAs: after the first MFMA the lane-half swaps and the scales,
-    // then one element pair of each block per MFMA (per two with TM = 2).
+    // then block 0's element pairs after the MFMAs of k slice 1 and block
+    // 1's after those of slice 2, one pair per MFMA (two with TM = 2).
     uint32_t bw[2][TN][2][2][4];
     uint4 wc[TN];
     uint32_t wt[TN][2], wu[TN][2];
