@@ -123,6 +123,24 @@ def test_prefill_m512_full(N, K):
     control_within(Yd.cpu().numpy(), Y_ref, S, f"dense fp16 GEMM {N}x{K} M=512")
 
 
+@pytest.mark.parametrize("N,K,M", [(12288, 2560, 128), (4096, 4096, 512), (14336, 4096, 256)])
+def test_prefill_whole_tile_launches_full(N, K, M):
+    """Built-in launches whose tile count fills 3/4 to all of the CUs run one
+    workgroup per tile, every tile whole (plain stores, no zero fill; on 256
+    CUs: 192 tiles of 64 x 128, 256 of 64 x 128, 224 of 128 x 128): every
+    output against the oracle, and two calls give the same bits."""
+    w = si.weights(N, K, seed=M)
+    X = si.activations(M, K, seed=M)
+    pb, po = pack_both(Q4_0, w)
+    del w
+    Wd = to_dev(pb)
+    Y = _prefill(Wd, X, N, K)
+    Y_ref, S = oracle.get().prefill(po, N, K, X)
+    assert_within(Y, Y_ref, S, f"prefill M={M} {N}x{K}")
+    Y2 = _prefill(Wd, X, N, K)
+    assert np.array_equal(Y.view(np.uint32), Y2.view(np.uint32)), f"prefill M={M} {N}x{K}: not bitwise repeatable"
+
+
 def test_prefill_many_tiles_full():
     """More tiles than workgroup slots (384 tokens x 16000 rows): every output
     against the oracle, with a ragged last tile along N and an odd block
